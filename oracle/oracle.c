@@ -1,0 +1,519 @@
+/*
+ * oracle.c -- plain, slow, fp32 CPU reference of the greedy speculative
+ * decoding verify transaction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  The product path
+ * (libspecv) shares no source, header, table or helper with it.
+ *
+ * What it computes, and where the pages define it (citations name the page
+ * and the part of it; the pages have no numbered sections):
+ *   - A dense decoder trunk: RMSNorm, RoPE, GQA causal attention, SwiGLU MLP
+ *     and an LM head.  The pegainfer page (DFlash speculative decoding for
+ *     Qwen3-4B, performance and graph sections) lists these as the trunk's
+ *     dense ops.  Conventions the pages leave open (epsilon, RoPE base and
+ *     layout, untied embeddings) come from the model description passed in.
+ *   - The verify forward: one forward over the span [last, d1..dK] giving the
+ *     trunk argmax at every row (pegainfer page, transaction section, the
+ *     verify step).
+ *   - accept_greedy: the longest prefix of drafts each equal to the argmax of
+ *     the row before it, plus the trunk's own token at the first mismatch, so
+ *     a step commits between 1 and K+1 tokens (same section, the accept step).
+ *   - The cache advance: with m drafts accepted, rows [last, d1..dm] are the
+ *     cached ones, so the cache grows by m+1 (pegainfer page, draft-seed
+ *     alignment paragraph).  Rejected rows stay in memory past the length and
+ *     are never read (coreai-model-zoo dense n-gram note, the paragraph on
+ *     KV-only bundles: rollback is simply not advancing the position).
+ *   - The n-gram prompt-lookup proposer (TensorSharp speculative decoding
+ *     page, n-gram section; coreai note, adaptive-K section, which drafts only
+ *     off a match of two or more tokens), written as a brute-force search.
+ *   - Adaptive K: start at 1, add 2 after a fully accepted round, subtract 1
+ *     after any rejection, clamp to [1, cap] (coreai note, adaptive-K section).
+ *
+ * Row invariance: every dot product below is summed in one fixed sequential
+ * order over its reduction index, whatever other rows share the call, so a
+ * multi-row forward is bit-identical to the same rows decoded one at a time
+ * (the rows gate of the coreai note, section on gating the bundle).
+ *
+ * Build: gcc -O3 -fopenmp -ffp-contract=off (no -ffast-math: no reassociation).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORC_PLANT
+#define ORC_PLANT 0 /* >0 plants one deliberate mistake; used only to show the pins have teeth */
+#endif
+
+#define ORC_API __attribute__((visibility("default")))
+
+enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ECAPACITY = -2, ORC_ESTATE = -3, ORC_ENAN = -4, ORC_ENOMEM = -5 };
+enum { ORC_FMT_BF16 = 0, ORC_FMT_INT4G128 = 1 };
+enum { ORC_WQ = 0, ORC_WK, ORC_WV, ORC_WO, ORC_WG, ORC_WU, ORC_WD, ORC_NW };
+enum { ORC_MAT_EMB = 100, ORC_MAT_LM = 101 };
+enum { ORC_NORM_ATTN = 0, ORC_NORM_FFN = 1, ORC_NORM_FINAL = 2 };
+
+typedef struct {
+  int32_t n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab;
+  float eps;
+  double rope_theta;
+} orc_shape;
+
+typedef struct {
+  int fmt, rows, cols;
+  const uint16_t* bf16;   /* [rows][cols] bf16 bit patterns           */
+  const uint8_t* q4;      /* [rows][cols/2]: low nibble = even column */
+  const uint16_t* scales; /* [rows][cols/128] bf16 bit patterns        */
+} orc_mat;
+
+typedef struct orc_model {
+  orc_shape s;
+  int max_ctx, n_seq;
+  orc_mat* lay;           /* [n_layers][ORC_NW] */
+  const float** g_attn;   /* [n_layers] -> [hidden] */
+  const float** g_ffn;
+  const float* g_final;
+  orc_mat emb, lm;
+  float* kc;              /* [n_seq][n_layers][max_ctx][n_kv*head_dim] */
+  float* vc;
+  int* len;               /* cache length per sequence */
+} orc_model;
+
+/* ---------------------------------------------------------------- scalars */
+
+static inline float bf16_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)b << 16;
+  return v.f;
+}
+
+/* Weight element W[n][k] as an exact fp32 value.  int4: w = s * q with
+ * q in [-8, 7] two's complement and s the bf16 scale of the 128-column group;
+ * the product is exact in fp32 (bf16 mantissa times a 4-bit integer). */
+static inline float mat_at(const orc_mat* m, int n, int k) {
+  if (m->fmt == ORC_FMT_BF16) return bf16_to_f32(m->bf16[(size_t)n * m->cols + k]);
+  uint8_t byte = m->q4[(size_t)n * (m->cols / 2) + k / 2];
+  int nib = (k & 1) ? (byte >> 4) : (byte & 15);
+  int q = nib >= 8 ? nib - 16 : nib;
+  float s = bf16_to_f32(m->scales[(size_t)n * (m->cols / 128) + k / 128]);
+  return s * (float)q;
+}
+
+/* Y[r][n] = sum_k W[n][k] * X[r][k], each sum sequential over k in fp32.
+ * X is passed transposed (Xt[k][r]) so the per-k update over r vectorises
+ * without changing any single sum's order. */
+static void matmul(const orc_mat* W, const float* Xt, int R, float* Y) {
+  const int N = W->rows, K = W->cols;
+#pragma omp parallel
+  {
+    float* w = (float*)malloc(sizeof(float) * (size_t)K);
+    float* acc = (float*)malloc(sizeof(float) * (size_t)R);
+#pragma omp for schedule(static)
+    for (int n = 0; n < N; ++n) {
+      for (int k = 0; k < K; ++k) w[k] = mat_at(W, n, k);
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const float wk = w[k];
+        const float* xk = Xt + (size_t)k * R;
+        for (int r = 0; r < R; ++r) acc[r] = acc[r] + wk * xk[r];
+      }
+      for (int r = 0; r < R; ++r) Y[(size_t)r * N + n] = acc[r];
+    }
+    free(w);
+    free(acc);
+  }
+}
+
+static void transpose(const float* X, int R, int C, float* Xt) {
+  for (int r = 0; r < R; ++r)
+    for (int c = 0; c < C; ++c) Xt[(size_t)c * R + r] = X[(size_t)r * C + c];
+}
+
+/* Y[r][n] = sum_k W[n][k] X[r][k] for one matrix in either storage format,
+ * X row-major [R][cols]; the same product the forward uses. */
+ORC_API int orc_matvec(int fmt, int rows, int cols, const void* data, const void* scales,
+                       const float* X, int R, float* Y) {
+  if (!data || !X || !Y || rows <= 0 || cols <= 0 || R <= 0) return ORC_EINVAL;
+  if (fmt == ORC_FMT_INT4G128 && (cols % 128 || !scales)) return ORC_EINVAL;
+  orc_mat w = {fmt, rows, cols, NULL, NULL, NULL};
+  if (fmt == ORC_FMT_BF16) w.bf16 = (const uint16_t*)data;
+  else if (fmt == ORC_FMT_INT4G128) { w.q4 = (const uint8_t*)data; w.scales = (const uint16_t*)scales; }
+  else return ORC_EINVAL;
+  float* Xt = (float*)malloc(sizeof(float) * (size_t)R * cols);
+  if (!Xt) return ORC_ENOMEM;
+  transpose(X, R, cols, Xt);
+  matmul(&w, Xt, R, Y);
+  free(Xt);
+  return ORC_OK;
+}
+
+/* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g. */
+ORC_API void orc_rmsnorm(const float* x, const float* g, int H, float eps, float* y) {
+  float ss = 0.0f;
+  for (int i = 0; i < H; ++i) ss = ss + x[i] * x[i];
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int i = 0; i < H; ++i) {
+#if ORC_PLANT == 6
+    y[i] = x[i] * r;
+#else
+    y[i] = (x[i] * r) * g[i];
+#endif
+  }
+}
+
+/* Rotary embedding, rotate-half (NeoX) pairing: element i rotates with
+ * element i + d/2 by angle pos * theta^(-2i/d).  cos and sin are evaluated in
+ * fp64 and rounded to fp32. */
+ORC_API void orc_rope(float* v, int hd, int pos, double theta) {
+  const int half = hd / 2;
+  for (int i = 0; i < half; ++i) {
+    const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+    const double ang = (double)pos * inv;
+    const float c = (float)cos(ang);
+#if ORC_PLANT == 1
+    const float s = -(float)sin(ang);
+#else
+    const float s = (float)sin(ang);
+#endif
+    const float a = v[i], b = v[i + half];
+    v[i] = a * c - b * s;
+    v[i + half] = a * s + b * c;
+  }
+}
+
+/* Causal softmax attention of one query head over cached keys 0..t:
+ * s_j = (q . k_j) / sqrt(d), p = softmax(s), o = sum_j p_j v_j.
+ * K and V rows are `stride` floats apart (the cache row layout). */
+ORC_API void orc_attend(const float* q, const float* K, const float* V, int t, int stride, int hd,
+                        float* o, float* scratch /* t+1 floats */) {
+#if ORC_PLANT == 3
+  const float scale = 1.0f;
+#else
+  const float scale = (float)(1.0 / sqrt((double)hd));
+#endif
+  float mx = -INFINITY;
+  for (int j = 0; j <= t; ++j) {
+    float d = 0.0f;
+    const float* kj = K + (size_t)j * stride;
+    for (int e = 0; e < hd; ++e) d = d + q[e] * kj[e];
+    scratch[j] = d * scale;
+    if (scratch[j] > mx) mx = scratch[j];
+  }
+  float l = 0.0f;
+  for (int j = 0; j <= t; ++j) {
+    scratch[j] = expf(scratch[j] - mx);
+    l = l + scratch[j];
+  }
+  for (int e = 0; e < hd; ++e) o[e] = 0.0f;
+  for (int j = 0; j <= t; ++j) {
+    const float* vj = V + (size_t)j * stride;
+    for (int e = 0; e < hd; ++e) o[e] = o[e] + scratch[j] * vj[e];
+  }
+  for (int e = 0; e < hd; ++e) o[e] = o[e] / l;
+}
+
+ORC_API float orc_silu(float g) { return g / (1.0f + expf(-g)); }
+
+/* Largest value, lowest index on ties; NaN is an error (returns -1). */
+ORC_API int orc_argmax(const float* v, int n, float* margin) {
+  int best = -1;
+  float b1 = -INFINITY, b2 = -INFINITY;
+  for (int i = 0; i < n; ++i) {
+    const float x = v[i];
+    if (x != x) return -1;
+#if ORC_PLANT == 10
+    if (best < 0 || x >= b1) {
+#else
+    if (best < 0 || x > b1) {
+#endif
+      if (best >= 0) b2 = b1;
+      b1 = x;
+      best = i;
+    } else if (x > b2) {
+      b2 = x;
+    }
+  }
+  if (margin) *margin = (n > 1) ? b1 - b2 : INFINITY;
+  return best;
+}
+
+/* ------------------------------------------------------------------ model */
+
+ORC_API orc_model* orc_new(const orc_shape* s, int max_ctx, int n_seq) {
+  if (!s || max_ctx <= 0 || n_seq <= 0) return NULL;
+  if (s->head_dim % 2 || s->n_q % s->n_kv) return NULL;
+  orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
+  if (!m) return NULL;
+  m->s = *s;
+  m->max_ctx = max_ctx;
+  m->n_seq = n_seq;
+  m->lay = (orc_mat*)calloc((size_t)s->n_layers * ORC_NW, sizeof(orc_mat));
+  m->g_attn = (const float**)calloc((size_t)s->n_layers, sizeof(float*));
+  m->g_ffn = (const float**)calloc((size_t)s->n_layers, sizeof(float*));
+  const size_t kv = (size_t)n_seq * s->n_layers * max_ctx * s->n_kv * s->head_dim;
+  m->kc = (float*)calloc(kv, sizeof(float));
+  m->vc = (float*)calloc(kv, sizeof(float));
+  m->len = (int*)calloc((size_t)n_seq, sizeof(int));
+  if (!m->lay || !m->g_attn || !m->g_ffn || !m->kc || !m->vc || !m->len) {
+    free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len); free(m);
+    return NULL;
+  }
+  return m;
+}
+
+ORC_API void orc_free(orc_model* m) {
+  if (!m) return;
+  free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len);
+  free(m);
+}
+
+/* Borrow one weight matrix (the caller keeps the arrays alive).  which is
+ * ORC_WQ..ORC_WD for a layer matrix, ORC_MAT_EMB or ORC_MAT_LM otherwise. */
+ORC_API int orc_set_matrix(orc_model* m, int layer, int which, int fmt, int rows, int cols,
+                           const void* data, const void* scales) {
+  if (!m || !data) return ORC_EINVAL;
+  if (fmt == ORC_FMT_INT4G128 && (cols % 128 || !scales)) return ORC_EINVAL;
+  orc_mat w = {fmt, rows, cols, NULL, NULL, NULL};
+  if (fmt == ORC_FMT_BF16) w.bf16 = (const uint16_t*)data;
+  else if (fmt == ORC_FMT_INT4G128) { w.q4 = (const uint8_t*)data; w.scales = (const uint16_t*)scales; }
+  else return ORC_EINVAL;
+  if (which == ORC_MAT_EMB) { m->emb = w; return ORC_OK; }
+  if (which == ORC_MAT_LM) { m->lm = w; return ORC_OK; }
+  if (layer < 0 || layer >= m->s.n_layers || which < 0 || which >= ORC_NW) return ORC_EINVAL;
+  m->lay[(size_t)layer * ORC_NW + which] = w;
+  return ORC_OK;
+}
+
+ORC_API int orc_set_norm(orc_model* m, int layer, int which, const float* g) {
+  if (!m || !g) return ORC_EINVAL;
+  if (which == ORC_NORM_FINAL) { m->g_final = g; return ORC_OK; }
+  if (layer < 0 || layer >= m->s.n_layers) return ORC_EINVAL;
+  if (which == ORC_NORM_ATTN) m->g_attn[layer] = g;
+  else if (which == ORC_NORM_FFN) m->g_ffn[layer] = g;
+  else return ORC_EINVAL;
+  return ORC_OK;
+}
+
+ORC_API int orc_cache_len(const orc_model* m, int seq) {
+  if (!m || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
+  return m->len[seq];
+}
+
+/* Rewind only: the cache can be shortened, never lengthened. */
+ORC_API int orc_rewind(orc_model* m, int seq, int len) {
+  if (!m || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
+  if (len < 0 || len > m->len[seq]) return ORC_ESTATE;
+  m->len[seq] = len;
+  return ORC_OK;
+}
+
+static float* kv_row(const orc_model* m, float* base, int seq, int layer, int t) {
+  const size_t w = (size_t)m->s.n_kv * m->s.head_dim;
+  return base + (((size_t)seq * m->s.n_layers + layer) * m->max_ctx + t) * w;
+}
+
+/* Forward n rows of sequence `seq` at positions len..len+n-1, writing their
+ * K/V rows and advancing the cache length by n.  Logits are produced for rows
+ * lm_from..n-1 only (prefill needs only its last row).  argmax/margin/logits
+ * outputs are indexed from lm_from. */
+ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int lm_from,
+                        float* logits_out, int32_t* argmax_out, float* margin_out) {
+  if (!m || !toks || n <= 0 || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
+  if (lm_from < 0 || lm_from > n) return ORC_EINVAL;
+  const orc_shape* s = &m->s;
+  const int H = s->hidden, hd = s->head_dim, nq = s->n_q, nkv = s->n_kv, F = s->ffn, V = s->vocab;
+  const int G = nq / nkv, DQ = nq * hd, DK = nkv * hd;
+  const int p = m->len[seq];
+  if (p + n > m->max_ctx) return ORC_ECAPACITY;
+  for (int r = 0; r < n; ++r)
+    if (toks[r] < 0 || toks[r] >= V) return ORC_EINVAL;
+
+  const size_t big = (size_t)n * (size_t)(F > DQ ? (F > H ? F : H) : (DQ > H ? DQ : H));
+  float* X = (float*)malloc(sizeof(float) * (size_t)n * H);
+  float* U = (float*)malloc(sizeof(float) * big);
+  float* Ut = (float*)malloc(sizeof(float) * big);
+  float* Q = (float*)malloc(sizeof(float) * (size_t)n * DQ);
+  float* Kn = (float*)malloc(sizeof(float) * (size_t)n * DK);
+  float* Vn = (float*)malloc(sizeof(float) * (size_t)n * DK);
+  float* O = (float*)malloc(sizeof(float) * (size_t)n * DQ);
+  float* Y = (float*)malloc(sizeof(float) * (size_t)n * H);
+  float* Gt = (float*)malloc(sizeof(float) * (size_t)n * F);
+  float* Up = (float*)malloc(sizeof(float) * (size_t)n * F);
+  if (!X || !U || !Ut || !Q || !Kn || !Vn || !O || !Y || !Gt || !Up) {
+    free(X); free(U); free(Ut); free(Q); free(Kn); free(Vn); free(O); free(Y); free(Gt); free(Up);
+    return ORC_ENOMEM;
+  }
+  int rc = ORC_OK;
+
+  for (int r = 0; r < n; ++r)
+    for (int i = 0; i < H; ++i) X[(size_t)r * H + i] = mat_at(&m->emb, toks[r], i);
+
+  for (int l = 0; l < s->n_layers; ++l) {
+    const orc_mat* W = m->lay + (size_t)l * ORC_NW;
+    for (int r = 0; r < n; ++r) orc_rmsnorm(X + (size_t)r * H, m->g_attn[l], H, s->eps, U + (size_t)r * H);
+    transpose(U, n, H, Ut);
+    matmul(&W[ORC_WQ], Ut, n, Q);
+    matmul(&W[ORC_WK], Ut, n, Kn);
+    matmul(&W[ORC_WV], Ut, n, Vn);
+    for (int r = 0; r < n; ++r) {
+#if ORC_PLANT == 11
+      const int pos = r;
+#else
+      const int pos = p + r;
+#endif
+      for (int h = 0; h < nq; ++h) orc_rope(Q + (size_t)r * DQ + h * hd, hd, pos, s->rope_theta);
+      for (int h = 0; h < nkv; ++h) orc_rope(Kn + (size_t)r * DK + h * hd, hd, pos, s->rope_theta);
+#if ORC_PLANT == 12
+      memcpy(kv_row(m, m->kc, seq, l, p), Kn + (size_t)r * DK, sizeof(float) * DK);
+#else
+      memcpy(kv_row(m, m->kc, seq, l, p + r), Kn + (size_t)r * DK, sizeof(float) * DK);
+#endif
+      memcpy(kv_row(m, m->vc, seq, l, p + r), Vn + (size_t)r * DK, sizeof(float) * DK);
+    }
+#pragma omp parallel
+    {
+      float* scratch = (float*)malloc(sizeof(float) * (size_t)(p + n));
+#pragma omp for schedule(static) collapse(2)
+      for (int r = 0; r < n; ++r)
+        for (int h = 0; h < nq; ++h) {
+#if ORC_PLANT == 2
+          const int g = h % nkv;
+#else
+          const int g = h / G;
+#endif
+          orc_attend(Q + (size_t)r * DQ + h * hd, kv_row(m, m->kc, seq, l, 0) + g * hd,
+                     kv_row(m, m->vc, seq, l, 0) + g * hd, p + r, DK, hd, O + (size_t)r * DQ + h * hd,
+                     scratch);
+        }
+      free(scratch);
+    }
+    transpose(O, n, DQ, Ut);
+    matmul(&W[ORC_WO], Ut, n, Y);
+    for (size_t i = 0; i < (size_t)n * H; ++i) {
+#if ORC_PLANT == 4
+      X[i] = Y[i];
+#else
+      X[i] = X[i] + Y[i];
+#endif
+    }
+    for (int r = 0; r < n; ++r) orc_rmsnorm(X + (size_t)r * H, m->g_ffn[l], H, s->eps, U + (size_t)r * H);
+    transpose(U, n, H, Ut);
+    matmul(&W[ORC_WG], Ut, n, Gt);
+    matmul(&W[ORC_WU], Ut, n, Up);
+    for (size_t i = 0; i < (size_t)n * F; ++i) {
+#if ORC_PLANT == 5
+      U[i] = orc_silu(Up[i]) * Gt[i];
+#else
+      U[i] = orc_silu(Gt[i]) * Up[i];
+#endif
+    }
+    transpose(U, n, F, Ut);
+    matmul(&W[ORC_WD], Ut, n, Y);
+    for (size_t i = 0; i < (size_t)n * H; ++i) X[i] = X[i] + Y[i];
+  }
+
+  const int nl = n - lm_from;
+  if (nl > 0) {
+    for (int r = 0; r < nl; ++r)
+      orc_rmsnorm(X + (size_t)(lm_from + r) * H, m->g_final, H, s->eps, U + (size_t)r * H);
+    transpose(U, nl, H, Ut);
+    float* L = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)nl * V);
+    if (!L) rc = ORC_ENOMEM;
+    else {
+      matmul(&m->lm, Ut, nl, L);
+      for (int r = 0; r < nl; ++r) {
+        float mg;
+        const int a = orc_argmax(L + (size_t)r * V, V, &mg);
+        if (a < 0) rc = ORC_ENAN;
+        if (argmax_out) argmax_out[r] = a;
+        if (margin_out) margin_out[r] = mg;
+      }
+      if (!logits_out) free(L);
+    }
+  }
+  if (rc == ORC_OK) m->len[seq] = p + n;
+  free(X); free(U); free(Ut); free(Q); free(Kn); free(Vn); free(O); free(Y); free(Gt); free(Up);
+  return rc;
+}
+
+/* Prefill: reset the sequence, forward the prompt, return g0 = argmax of the
+ * last prompt row.  g0 itself is not cached: it becomes span[0] of the first
+ * verify (pegainfer page, draft-seed alignment paragraph). */
+ORC_API int orc_prefill(orc_model* m, int seq, const int32_t* toks, int n, int32_t* g0, float* margin) {
+  if (!m || seq < 0 || seq >= m->n_seq || n <= 0) return ORC_EINVAL;
+  m->len[seq] = 0;
+  return orc_forward(m, seq, toks, n, n - 1, NULL, g0, margin);
+}
+
+/* accept_greedy over argmax rows a[0..K] for drafts span[1..K]: the number of
+ * leading drafts with span[i] == a[i-1]. */
+ORC_API int orc_accept_greedy(const int32_t* span, const int32_t* a, int K) {
+  int mm = 0;
+#if ORC_PLANT == 7
+  while (mm < K && span[mm] == a[mm]) ++mm;
+#else
+  while (mm < K && span[mm + 1] == a[mm]) ++mm;
+#endif
+  return mm;
+}
+
+/* Verify span = [last, d1..dK] at p = cache length: forward K+1 rows, take
+ * the per-row argmax, accept, and leave the cache at p + m + 1. */
+ORC_API int orc_verify(orc_model* m, int seq, const int32_t* span, int K, int32_t* argmax_out,
+                       int32_t* accept_out, float* logits_out, float* margin_out) {
+  if (!m || !span || !argmax_out || !accept_out || K < 0 || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
+  const int p = m->len[seq];
+  const int rc = orc_forward(m, seq, span, K + 1, 0, logits_out, argmax_out, margin_out);
+  if (rc != ORC_OK) return rc;
+  const int mm = orc_accept_greedy(span, argmax_out, K);
+  *accept_out = mm;
+#if ORC_PLANT == 8
+  m->len[seq] = p + mm;
+#else
+  m->len[seq] = p + mm + 1;
+#endif
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- proposer */
+
+/* Brute-force n-gram prompt lookup over history h[0..L-1].  For n from n_max
+ * down to n_min, find the latest earlier occurrence of the last n tokens
+ * (an occurrence ending at e <= L-2) and propose the tokens that followed it,
+ * at most K and only tokens that already exist (up to h[L-1]).  Returns the
+ * number of drafts (0 when no order matches). */
+ORC_API int orc_ngram_propose(const int32_t* h, int L, int n_min, int n_max, int K, int32_t* drafts) {
+  if (!h || L < 0 || n_min < 1 || n_max < n_min || K < 0) return ORC_EINVAL;
+  if (K == 0) return 0;
+  for (int n = n_max; n >= n_min; --n) {
+    if (L < n + 1) continue;
+#if ORC_PLANT == 9
+    for (int e = L - 1; e >= n - 1; --e) {
+#else
+    for (int e = L - 2; e >= n - 1; --e) {
+#endif
+      int ok = 1;
+      for (int j = 0; j < n; ++j)
+        if (h[e - n + 1 + j] != h[L - n + j]) { ok = 0; break; }
+      if (!ok) continue;
+      int c = 0;
+      for (int i = e + 1; i <= L - 1 && c < K; ++i) drafts[c++] = h[i];
+      return c;
+    }
+  }
+  return 0;
+}
+
+/* Adaptive draft length after a round with `drafted` drafts of which
+ * `accepted` were accepted: full accept -> k+2, any rejection -> k-1,
+ * clamped to [1, cap]; a round with no drafts leaves k unchanged. */
+ORC_API int orc_adapt_k(int k, int drafted, int accepted, int cap) {
+  if (drafted <= 0) return k;
+  int next = (accepted >= drafted) ? k + 2 : k - 1;
+  if (next < 1) next = 1;
+  if (next > cap) next = cap;
+  return next;
+}
+
+ORC_API int orc_plant(void) { return ORC_PLANT; }
