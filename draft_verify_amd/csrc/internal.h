@@ -1,0 +1,113 @@
+// internal.h -- kernel parameter blocks shared by the libspecv runtime and its
+// gfx950 kernels.  Not part of the public ABI (include/specv.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specv {
+
+// Step modes, read by the accept stage from device memory so one captured
+// graph per shape serves all three.
+enum StepMode { MODE_VERIFY = 0, MODE_COMMIT_ALL = 1, MODE_NO_COMMIT = 2 };
+
+// GEMM epilogues.
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LM = 3 };
+
+// Device step block: written by one host-to-device copy before each forward.
+struct StepDev {
+  int32_t mode;
+  int32_t n_seq;
+  int32_t span;      // rows per sequence (S)
+  int32_t pad;
+  // followed by tokens[max_rows] and seq_ids[max_rows]
+};
+
+// Packed bf16 weights: fragments of 16 output rows x 32 inputs, 1 KiB each,
+// stored lane-major in the order the MFMA B operand is read:
+//   frag(t, s)[lane] = W[16t + lane%16][32s + 8*(lane/16) .. +8]
+// at ((t * (K/32) + s) * 64 + lane) * 16 bytes.
+inline size_t packed_bf16_bytes(int N, int K) { return (size_t)N * K * 2; }
+
+struct GemmParams {
+  const void* W;         // packed fragments [N/16][K/32][64] x 16 B
+  int N, K, R;           // outputs, inputs, rows
+  int nslices;           // K split into nslices slices of NK*32 inputs
+  const float* A;        // activation rows [R][lda] (fp32)
+  int lda;
+  const float* ss;       // RMSNorm: per-row partial sums of squares [R][ss_n], or null
+  int ss_n;
+  const float* gain;     // RMSNorm gain [K]
+  float eps, inv_dim;
+  float* part;           // split partial sums [nslices][R][N]
+  unsigned* cnt;         // arrival counter per 64-column block
+  // EPI_QKV
+  float* q;              // [R][n_q*hd] rotated queries
+  _Float16* kpool;       // this layer's K blocks [n_blocks][n_kv][16][hd]
+  _Float16* vpool;       // this layer's V blocks [n_blocks][n_kv][hd][16]
+  const int32_t* bt;     // block tables [max_seqs][bt_stride]
+  int bt_stride;
+  const int32_t* kv_len; // cache length per sequence (read-only here)
+  const int32_t* seq_ids;// [n_seq]
+  int S, n_q, n_kv, hd;
+  const float* rope;     // [max_ctx][hd/2][2] = cos, sin
+  // EPI_RESID
+  float* x;              // residual [R][N]
+  float* ss_out;         // [R][N/64] partial sums of squares of the new residual
+  // EPI_SWIGLU
+  float* h;              // [R][N/2]
+  // EPI_LM
+  unsigned long long* argkey; // per-row packed (value, index) maxima, zero between forwards
+  unsigned* lm_cnt;           // arrival counter over all column blocks
+  int32_t* status;            // bit 0: NaN logit seen
+  float* logits;              // [R][N] or null
+  const int32_t* tokens;      // [R] span tokens
+  const int32_t* mode;        // StepDev::mode
+  int32_t* result;            // [1 + n_seq*(S+1)]: status, then (m, a0..a(S-1)) per sequence
+  int32_t* kv_len_w;          // cache lengths, advanced by the accept stage
+  int n_seq;
+};
+
+struct AttnParams {
+  const float* q;        // [R][n_q*hd]
+  const _Float16* kpool; // [n_blocks][n_kv][16][hd]
+  const _Float16* vpool; // [n_blocks][n_kv][hd][16]
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* kv_len;
+  const int32_t* seq_ids;
+  int S, n_seq, n_q, n_kv;
+  float scale;
+  int max_splits;        // grid.x: 256-key splits of the longest context
+  float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
+  unsigned* cnt;         // [n_seq][n_kv]
+  float* out;            // [R][n_q*hd]
+};
+
+struct EmbedParams {
+  const uint16_t* emb;   // [V][H] bf16
+  const int32_t* tokens; // [R]
+  float* x;              // [R][H]
+  float* ss;             // [R][H/64]
+  int H;
+};
+
+// Launchers (kernels.hip).  All return hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmParams& p, int nk, int epi, hipStream_t st);
+hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
+hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
+// Repack canonical bf16 [rows][cols] into fragments of a fused matrix whose
+// row for source row s is map(s): kind 0 identity + row0, kind 1 RoPE pair
+// interleave within heads of hd rows (+ row0), kind 2 row 2s + row0.
+hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, int kind, int row0,
+                            int hd, hipStream_t st);
+hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t st);
+
+// Row of the fused QKV matrix holding source row s of a Q or K projection:
+// the pair (d, d + hd/2) of a head lands on adjacent rows (2d, 2d+1).
+__host__ __device__ inline int rope_pair_row(int s, int hd) {  // source row -> interleaved row
+  const int h = s / hd, d = s % hd, half = hd / 2;
+  return h * hd + (d < half ? 2 * d : 2 * (d - half) + 1);
+}
+
+}  // namespace specv

@@ -1,0 +1,587 @@
+// kernels.hip -- gfx950 (MI355X, CDNA4) kernels of the verify forward.
+//
+// One forward over S rows per sequence (the span [last, d1..dK], pegainfer
+// page "DFlash speculative decoding", transaction section) runs:
+//   embed -> per layer { QKV GEMM (+RMSNorm prologue, RoPE + KV-write
+//   epilogue), attention, O GEMM (+residual), gate/up GEMM (+RMSNorm
+//   prologue, SwiGLU epilogue), down GEMM (+residual) } -> LM-head GEMM with a
+//   fused per-row argmax and, in its last workgroup, accept_greedy and the
+//   cache advance.
+//
+// Numerics: weights bf16; activations enter the MFMA as a bf16 hi + lo pair
+// (two passes, ~16 mantissa bits); fp32 accumulation, residual and softmax;
+// fp16 KV cache, fp16 query and probabilities in attention.
+// Row invariance: every row runs the same 16-row MFMA tiles, the same
+// K-split per (N, K) and the same fixed-order reductions whatever S is, so a
+// row's result does not depend on the other rows of the forward.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "internal.h"
+
+namespace specv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Order-preserving key of (value, column): larger value wins, then the lower
+// column.  Zero is below every key, so a zeroed slot is the neutral element.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
+  if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal, as in the plain definition
+  uint32_t u = __float_as_uint(v);
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)col);
+}
+
+// ---------------------------------------------------------------- packing
+
+__global__ void k_pack_bf16(const uint16_t* __restrict__ src, int rows, int cols, u32x4* __restrict__ dst,
+                            int kind, int row0, int hd) {
+  const int chunks = cols / 8;
+  const size_t total = (size_t)rows * chunks;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int s = (int)(i / chunks), kc = (int)(i % chunks);
+    int n;
+    if (kind == 0) n = row0 + s;
+    else if (kind == 1) n = row0 + rope_pair_row(s, hd);
+    else n = row0 + 2 * s;
+    const u32x4 v = *(const u32x4*)(src + (size_t)s * cols + (size_t)kc * 8);
+    const int tile = n >> 4, r = n & 15, step = kc >> 2, g = kc & 3;
+    dst[((size_t)tile * (cols / 32) + step) * 64 + g * 16 + r] = v;
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t value, size_t count) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = value;
+}
+
+// -------------------------------------------------------------- embedding
+
+// One workgroup per row: x = E[token] in fp32, plus the sum of squares of
+// every 64-column block (the format the RMSNorm prologues consume).
+__global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
+  const int r = blockIdx.x;
+  const int tok = P.tokens[r];
+  const int H = P.H, nb = H / 64;
+  const uint16_t* e = P.emb + (size_t)tok * H;
+  for (int c0 = 0; c0 < H; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    if (c0 + (int)(threadIdx.x & ~63) < H) {  // whole waves in or out
+      const float v = bf16_bits_to_f32(e[c]);
+      P.x[(size_t)r * H + c] = v;
+      float t = v * v;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+      if ((threadIdx.x & 63) == 0) P.ss[(size_t)r * nb + c / 64] = t;
+    }
+  }
+}
+
+// ------------------------------------------------------------ skinny GEMM
+//
+// Y[R, N] = A'[R, K] W^T with A' = RMSNorm(A) (optional) split into bf16
+// hi + lo.  A workgroup (4 waves) owns 64 output columns x one K slice of
+// NK*32 inputs; wave w owns the 16-column tile 4*nb + w.  Each wave first
+// issues all NK fragment loads of its weights (contiguous NK KiB, streamed
+// with non-temporal loads), then stages A for 16 rows of the slice into LDS
+// in the MFMA A-operand order, then runs 2*NK MFMA 16x16x32 bf16.  The split
+// partial sums go to memory; the last workgroup of a column block to arrive
+// (counted with an atomic) adds the slices in slice order and runs the
+// epilogue, so the result is deterministic and independent of R.
+// Workgroup ids are mapped so every slice of a column block sits on the same
+// XCD (ids are dealt round-robin over the 8 XCDs), keeping the partial sums
+// in one L2.
+
+template <int EPI>
+__device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
+
+template <int NK, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
+  const int NB = P.N >> 6, ns = P.nslices;
+  const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
+  const int nb = (loc / ns) * 8 + xcd, sl = loc % ns;
+  if (nb >= NB) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int k0 = sl * NK * 32;
+  const int tile = nb * 4 + wave;
+
+  __shared__ u32x4 sA[NK * 2 * 64];
+  __shared__ float sR[16];
+  __shared__ int sLast;
+
+  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / 32) + (size_t)sl * NK) * 64 + lane;
+  u32x4 b[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+
+  for (int m0 = 0; m0 < P.R; m0 += 16) {
+    if (P.ss) {
+      if (tid < 16) {
+        const int r = m0 + tid;
+        float rs = 0.0f;
+        if (r < P.R) {
+          float s = 0.0f;
+          for (int q = 0; q < P.ss_n; ++q) s += P.ss[(size_t)r * P.ss_n + q];
+          rs = 1.0f / sqrtf(s * P.inv_dim + P.eps);
+        }
+        sR[tid] = rs;
+      }
+      __syncthreads();
+    }
+    // Stage 16 rows x NK*32 inputs: unit u = (row, step j, lane group g) of 8 inputs.
+    for (int u = tid; u < 16 * NK * 4; u += 256) {
+      const int g = u & 3, j = (u >> 2) % NK, row = u / (4 * NK);
+      const int r = m0 + row;
+      const int k = k0 + j * 32 + g * 8;
+      float v[8];
+      if (r < P.R) {
+        const f32x4* src = (const f32x4*)(P.A + (size_t)r * P.lda + k);
+        const f32x4 a0 = src[0], a1 = src[1];
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+        if (P.ss) {
+          const float rs = sR[row];
+          const f32x4* gp = (const f32x4*)(P.gain + k);
+          const f32x4 g0 = gp[0], g1 = gp[1];
+          const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * gg[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(v[e] - (float)h);
+      }
+      const int l = g * 16 + row;
+      sA[(j * 2) * 64 + l] = __builtin_bit_cast(u32x4, hi);
+      sA[(j * 2 + 1) * 64 + l] = __builtin_bit_cast(u32x4, lo);
+    }
+    __syncthreads();
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const bf16x8 bw = __builtin_bit_cast(bf16x8, b[j]);
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, sA[(j * 2) * 64 + lane]);
+      const bf16x8 al = __builtin_bit_cast(bf16x8, sA[(j * 2 + 1) * 64 + lane]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+    }
+    // D layout: lane holds column lane%16 of rows 4*(lane/16) + i.
+    const int col = tile * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + (lane >> 4) * 4 + i;
+      if (r < P.R) P.part[((size_t)sl * P.R + r) * P.N + col] = acc[i];
+    }
+    __syncthreads();  // sA is restaged for the next 16 rows
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = atomicAdd(&P.cnt[nb], 1u);
+    sLast = (old == (unsigned)(ns - 1));
+  }
+  __syncthreads();
+  if (!sLast) return;
+  __threadfence();
+  if (tid == 0) P.cnt[nb] = 0u;  // ready for the next launch
+  gemm_epilogue<EPI>(P, nb, (float*)sA);
+}
+
+// Column pair (c, c+1) of row r summed over the K slices in slice order.
+__device__ __forceinline__ void reduce_pair(const GemmParams& P, int r, int c, float& v0, float& v1) {
+  v0 = 0.0f;
+  v1 = 0.0f;
+  for (int s = 0; s < P.nslices; ++s) {
+    const float2 t = *(const float2*)(P.part + ((size_t)s * P.R + r) * P.N + c);
+    v0 += t.x;
+    v1 += t.y;
+  }
+}
+
+// Position of row r of the forward and its sequence.
+__device__ __forceinline__ void row_pos(const GemmParams& P, int r, int& seq, int& pos) {
+  const int b = r / P.S, i = r - b * P.S;
+  seq = P.seq_ids[b];
+  pos = P.kv_len[seq] + i;
+}
+
+template <>
+__device__ void gemm_epilogue<EPI_QKV>(const GemmParams& P, int nb, float*) {
+  const int hd = P.hd, half = hd / 2;
+  const int DQ = P.n_q * hd, DK = P.n_kv * hd;
+  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
+    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
+    float v0, v1;
+    reduce_pair(P, r, c, v0, v1);
+    int seq, pos;
+    row_pos(P, r, seq, pos);
+    const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
+    if (c < DQ + DK) {  // rotate the pair (d, d + hd/2) stored interleaved
+      const int local = c < DQ ? c : c - DQ;
+      const int head = local / hd, j = (local % hd) >> 1;
+      const float cs = P.rope[((size_t)pos * half + j) * 2], sn = P.rope[((size_t)pos * half + j) * 2 + 1];
+      const float o0 = v0 * cs - v1 * sn, o1 = v0 * sn + v1 * cs;
+      if (c < DQ) {
+        float* qr = P.q + (size_t)r * DQ + head * hd;
+        qr[j] = o0;
+        qr[j + half] = o1;
+      } else {
+        _Float16* kr = P.kpool + (((size_t)blk * P.n_kv + head) * 16 + slot) * hd;
+        kr[j] = (_Float16)o0;
+        kr[j + half] = (_Float16)o1;
+      }
+    } else {
+      const int local = c - DQ - DK;
+      const int head = local / hd, d = local % hd;
+      _Float16* vb = P.vpool + ((size_t)blk * P.n_kv + head) * hd * 16;
+      vb[(size_t)d * 16 + slot] = (_Float16)v0;
+      vb[(size_t)(d + 1) * 16 + slot] = (_Float16)v1;
+    }
+  }
+}
+
+template <>
+__device__ void gemm_epilogue<EPI_RESID>(const GemmParams& P, int nb, float*) {
+  const int NB = P.N >> 6;
+  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
+    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
+    float v0, v1;
+    reduce_pair(P, r, c, v0, v1);
+    float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
+    float2 x = *xp;
+    x.x = x.x + v0;
+    x.y = x.y + v1;
+    *xp = x;
+    float t = x.x * x.x + x.y * x.y;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+    if ((idx & 31) == 0) P.ss_out[(size_t)r * NB + nb] = t;
+  }
+}
+
+template <>
+__device__ void gemm_epilogue<EPI_SWIGLU>(const GemmParams& P, int nb, float*) {
+  const int F = P.N >> 1;
+  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
+    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
+    float g, u;
+    reduce_pair(P, r, c, g, u);
+    P.h[(size_t)r * F + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
+  }
+}
+
+template <>
+__device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) {
+  __shared__ int sFinal;
+  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
+    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
+    float v0, v1;
+    reduce_pair(P, r, c, v0, v1);
+    if (P.logits) {
+      float2* lp = (float2*)(P.logits + (size_t)r * P.N + c);
+      *lp = make_float2(v0, v1);
+    }
+    if (v0 != v0 || v1 != v1) atomicOr(P.status, 1);
+    unsigned long long k0 = argmax_key(v0, c), k1 = argmax_key(v1, c + 1);
+    unsigned long long k = k0 > k1 ? k0 : k1;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      const unsigned long long t = __shfl_xor(k, o);
+      k = t > k ? t : k;
+    }
+    if ((idx & 31) == 0) atomicMax(&P.argkey[r], k);
+  }
+  // Last column block to finish: read the row maxima, accept, advance the cache.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = atomicAdd(P.lm_cnt, 1u);
+    sFinal = (old == (unsigned)((P.N >> 6) - 1));
+  }
+  __syncthreads();
+  if (!sFinal) return;
+  __threadfence();
+  int* arg = (int*)sbuf;
+  for (int r = threadIdx.x; r < P.R; r += 256) {
+    const unsigned long long k = atomicExch(&P.argkey[r], 0ull);
+    arg[r] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+  }
+  __syncthreads();
+  const int mode = *P.mode, S = P.S;
+  for (int b = threadIdx.x; b < P.n_seq; b += 256) {
+    const int row0 = b * S;
+    int m;
+    if (mode == MODE_COMMIT_ALL) {
+      m = S - 1;
+    } else {
+      m = 0;
+      while (m < S - 1 && P.tokens[row0 + m + 1] == arg[row0 + m]) ++m;
+    }
+    const int seq = P.seq_ids[b];
+    if (mode == MODE_COMMIT_ALL) P.kv_len_w[seq] += S;
+    else if (mode == MODE_VERIFY) P.kv_len_w[seq] += m + 1;
+    int32_t* res = P.result + 1 + b * (S + 1);
+    res[0] = m;
+    for (int i = 0; i < S; ++i) res[1 + i] = arg[row0 + i];
+  }
+  if (threadIdx.x == 0) {
+    P.result[0] = *P.status;
+    *P.status = 0;
+    *P.lm_cnt = 0u;
+  }
+}
+
+// -------------------------------------------------------------- attention
+//
+// Grid (split, kv head, sequence); a split is 256 keys at absolute positions
+// [256*split, 256*split + 256), one 64-key chunk (four 16-token blocks) per
+// wave.  Scores are computed transposed, S^T = K Q^T, so the probabilities
+// come out of the MFMA already in the B-operand layout of O^T = V^T P^T and
+// never leave registers; V blocks are stored d-major ([hd][16 tokens]) so
+// the V^T operand is read straight from memory.  Query columns are
+// (span row, head of the GQA group).  Each wave's chunk softmax is combined
+// across the four waves in LDS in wave order, each split's (max, sum, o)
+// goes to memory, and the last split to arrive for a (sequence, kv head)
+// combines the splits in split order.  Row i attends keys [0, p+i]; a chunk
+// or split lying wholly past a row's position contributes exactly nothing.
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn(AttnParams P) {
+  constexpr int KST = (HD + 31) / 32;  // 32-wide steps over the head dim (zero padded)
+  constexpr int DT = HD / 16;          // 16-row tiles of O^T
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int seq = P.seq_ids[b];
+  const int p = P.kv_len[seq];
+  const int S = P.S, G = P.n_q / P.n_kv, QC = S * G;
+  const int total = p + S;
+  const int n_act = (total + 255) >> 8;
+  if (split >= n_act) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int DQ = P.n_q * HD;
+
+  __shared__ float sO[4][16][HD + 1];
+  __shared__ float sM[4][16], sL[4][16];
+  __shared__ int sLast;
+
+  // This wave's four blocks, loaded once and reused for every query tile.
+  const int kb0 = split * 16 + wave * 4;
+  f16x8 kf[4][KST];
+  f16x4 vf[4][DT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int kb = kb0 + t;
+    const bool ok = kb * 16 < total;
+    const int blk = ok ? P.bt[(size_t)seq * P.bt_stride + kb] : 0;
+    const _Float16* kbase = P.kpool + ((size_t)blk * P.n_kv + kvh) * 16 * HD;
+    const _Float16* vbase = P.vpool + ((size_t)blk * P.n_kv + kvh) * HD * 16;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int d = ks * 32 + g4 * 8;
+      if (ok && d < HD) kf[t][ks] = *(const f16x8*)(kbase + c16 * HD + d);
+      else kf[t][ks] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if (ok) vf[t][dt] = *(const f16x4*)(vbase + (dt * 16 + c16) * 16 + g4 * 4);
+      else vf[t][dt] = (f16x4){0, 0, 0, 0};
+    }
+  }
+
+  const int n_qt = (QC + 15) >> 4;
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int col = qt * 16 + c16;
+    const bool qok = col < QC;
+    const int iq = qok ? col / G : 0, hh = qok ? col % G : 0;
+    const int head = kvh * G + hh;
+    const int pos_q = p + iq;
+    const float* qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
+    f16x8 qf[KST];
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int d = ks * 32 + g4 * 8;
+      f16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (qok && d < HD) {
+        const f32x4 a0 = *(const f32x4*)(qrow + d), a1 = *(const f32x4*)(qrow + d + 4);
+        v[0] = (_Float16)a0.x; v[1] = (_Float16)a0.y; v[2] = (_Float16)a0.z; v[3] = (_Float16)a0.w;
+        v[4] = (_Float16)a1.x; v[5] = (_Float16)a1.y; v[6] = (_Float16)a1.z; v[7] = (_Float16)a1.w;
+      }
+      qf[ks] = v;
+    }
+    float s[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ks], qf[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = (kb0 + t) * 16 + g4 * 4 + i;
+        s[t][i] = (qok && key <= pos_q) ? acc[i] * P.scale : -INFINITY;
+        mx = fmaxf(mx, s[t][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float l = 0.0f;
+    f16x8 pf[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = (mx == -INFINITY) ? 0.0f : expf(s[t][i] - mx);
+        l += e;
+        pf[t >> 1][(t & 1) * 4 + i] = (_Float16)e;
+      }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f16x4 v0 = vf[2 * s2][dt], v1 = vf[2 * s2 + 1][dt];
+        const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[s2], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[wave][c16][dt * 16 + g4 * 4 + i] = acc[i];
+    }
+    if (g4 == 0) {
+      sM[wave][c16] = mx;
+      sL[wave][c16] = l;
+    }
+    __syncthreads();
+    // Combine the four chunks of this split, in wave order.
+    for (int e = tid; e < 16 * HD; e += 256) {
+      const int c = e / HD, d = e % HD;
+      const int qcol = qt * 16 + c;
+      if (qcol >= QC) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][c]);
+      float L = 0.0f, O = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f = expf(sM[w][c] - M);
+          L += sL[w][c] * f;
+          O += sO[w][c][d] * f;
+        }
+      }
+      float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+      dst[2 + d] = O;
+      if (d == 0) {
+        dst[0] = M;
+        dst[1] = L;
+      }
+    }
+    __syncthreads();
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = atomicAdd(&P.cnt[b * P.n_kv + kvh], 1u);
+    sLast = (old == (unsigned)(n_act - 1));
+  }
+  __syncthreads();
+  if (!sLast) return;
+  __threadfence();
+  if (tid == 0) P.cnt[b * P.n_kv + kvh] = 0u;
+  // Combine the splits that hold keys at or before each row's position.
+  for (int e = tid; e < QC * HD; e += 256) {
+    const int qcol = e / HD, d = e % HD;
+    const int iq = qcol / G, head = kvh * G + qcol % G;
+    const int nsp = ((p + iq) >> 8) + 1;
+    const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
+    const float* src = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, src[sp * stride]);
+    float L = 0.0f, O = 0.0f;
+    for (int sp = 0; sp < nsp; ++sp) {
+      const float f = expf(src[sp * stride] - M);
+      L += src[sp * stride + 1] * f;
+      O += src[sp * stride + 2 + d] * f;
+    }
+    P.out[(size_t)(b * S + iq) * DQ + head * HD + d] = O / L;
+  }
+}
+
+// -------------------------------------------------------------- launchers
+
+template <int EPI>
+static hipError_t launch_gemm_epi(const GemmParams& p, int nk, hipStream_t st) {
+  const int NB = p.N / 64;
+  const int grid = ((NB + 7) / 8) * 8 * p.nslices;
+  switch (nk) {
+    case 16: hipLaunchKernelGGL((k_gemm<16, EPI>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_gemm<8, EPI>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_gemm<4, EPI>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<2, EPI>), dim3(grid), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmParams& p, int nk, int epi, hipStream_t st) {
+  switch (epi) {
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, st);
+    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, st);
+    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(p, nk, st);
+    case EPI_LM: return launch_gemm_epi<EPI_LM>(p, nk, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
+  const dim3 grid(p.max_splits, p.n_kv, p.n_seq);
+  switch (hd) {
+    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL(k_attn<16>, grid, dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(R), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, int kind, int row0, int hd,
+                            hipStream_t st) {
+  const size_t total = (size_t)rows * (cols / 8);
+  const int grid = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_pack_bf16, dim3(grid), dim3(256), 0, st, src, rows, cols, (u32x4*)dst, kind, row0, hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  const int grid = (int)((count + 255) / 256 < 65535 ? (count + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid), dim3(256), 0, st, (uint32_t*)dst, value, count);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -1,0 +1,926 @@
+// runtime.hip -- host side of libspecv: buffer layout, weight packing, KV
+// block management, the launch sequence of one forward, HIP graphs per
+// (sequences, span) shape, and the C ABI of include/specv.h.
+//
+// Everything that changes between steps (span tokens, step mode, sequence
+// ids, cache lengths, block tables) lives in device memory, so a graph
+// captured once per exact shape is replayed unchanged; a graph is never
+// replayed at a shape other than the one it was captured at.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <chrono>
+#include <map>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/specv.h"
+#include "internal.h"
+
+using namespace specv;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Inputs per K slice for a GEMM of depth K: the largest of 512/256/128/64
+// dividing K.  Fixed per (N, K), independent of the row count.
+inline int slice_steps(int K) {
+  for (int nk : {16, 8, 4, 2})
+    if (K % (nk * 32) == 0) return nk;
+  return 0;
+}
+
+struct LayerOff {
+  size_t wqkv, wo, wgu, wd, g_attn, g_ffn;
+};
+
+// Byte layout of the three device buffers for one description.
+struct Layout {
+  int H, nq, nkv, hd, F, V, L, DQ, DK, Nqkv, Ngu;
+  int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
+  int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
+  // weights
+  std::vector<LayerOff> lay;
+  size_t emb, wlm, g_final, weights_bytes;
+  // kv
+  size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
+  // workspace
+  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
+      logits, workspace_bytes;
+  size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
+  int cnt_n;
+};
+
+bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
+  auto fail = [&](const char* m) {
+    err = m;
+    return false;
+  };
+  if (d.n_layers <= 0 || d.hidden <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.ffn <= 0 || d.vocab <= 0)
+    return fail("model dimensions must be positive");
+  if (d.weight_format != SPEC_WFMT_BF16) return fail("only SPEC_WFMT_BF16 weights are supported by this build");
+  if (!(d.head_dim == 16 || d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128))
+    return fail("head_dim must be 16, 32, 64 or 128");
+  if (d.n_q_heads % d.n_kv_heads) return fail("n_q_heads must be a multiple of n_kv_heads");
+  if (d.hidden % 64 || d.ffn % 32 || d.vocab % 64) return fail("hidden and vocab must be multiples of 64, ffn of 32");
+  if ((d.n_q_heads * d.head_dim) % 64 || ((d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim) % 64)
+    return fail("attention projection widths must be multiples of 64");
+  if (d.max_rows < 1 || d.max_rows > SPEC_MAX_ROWS) return fail("max_rows must be in [1, 128]");
+  if (d.max_ctx < 1 || d.max_seqs < 1) return fail("max_ctx and max_seqs must be positive");
+  if (!(d.rms_eps >= 0.0f) || !(d.rope_theta > 0.0)) return fail("rms_eps must be >= 0 and rope_theta > 0");
+  Lo.H = d.hidden; Lo.nq = d.n_q_heads; Lo.nkv = d.n_kv_heads; Lo.hd = d.head_dim; Lo.F = d.ffn; Lo.V = d.vocab;
+  Lo.L = d.n_layers;
+  Lo.DQ = Lo.nq * Lo.hd; Lo.DK = Lo.nkv * Lo.hd; Lo.Nqkv = Lo.DQ + 2 * Lo.DK; Lo.Ngu = 2 * Lo.F;
+  Lo.G = Lo.nq / Lo.nkv;
+  Lo.max_rows = d.max_rows; Lo.max_seqs = d.max_seqs; Lo.max_ctx = d.max_ctx;
+  Lo.bt_stride = (d.max_ctx + SPEC_BLOCK_TOKENS - 1) / SPEC_BLOCK_TOKENS;
+  Lo.n_blocks = d.n_blocks > 0 ? d.n_blocks : d.max_seqs * Lo.bt_stride;
+  Lo.max_splits = (d.max_ctx + 255) / 256;
+  Lo.nk_qkv = slice_steps(Lo.H); Lo.nk_o = slice_steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
+  Lo.nk_d = slice_steps(Lo.F); Lo.nk_lm = Lo.nk_qkv;
+  if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
+  if (Lo.F % 64) return fail("ffn must be a multiple of 64");
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  Lo.lay.resize((size_t)Lo.L);
+  for (auto& l : Lo.lay) {
+    l.wqkv = take(packed_bf16_bytes(Lo.Nqkv, Lo.H));
+    l.wo = take(packed_bf16_bytes(Lo.H, Lo.DQ));
+    l.wgu = take(packed_bf16_bytes(Lo.Ngu, Lo.H));
+    l.wd = take(packed_bf16_bytes(Lo.H, Lo.F));
+    l.g_attn = take((size_t)Lo.H * 4);
+    l.g_ffn = take((size_t)Lo.H * 4);
+  }
+  Lo.emb = take((size_t)Lo.V * Lo.H * 2);
+  Lo.wlm = take(packed_bf16_bytes(Lo.V, Lo.H));
+  Lo.g_final = take((size_t)Lo.H * 4);
+  Lo.weights_bytes = off;
+
+  Lo.kv_half_bytes = align_up((size_t)Lo.n_blocks * Lo.nkv * SPEC_BLOCK_TOKENS * Lo.hd * 2);
+  Lo.kv_layer_bytes = 2 * Lo.kv_half_bytes;
+  Lo.kv_bytes = Lo.kv_layer_bytes * Lo.L;
+
+  const size_t R = (size_t)Lo.max_rows;
+  off = 0;
+  Lo.x = take(R * Lo.H * 4);
+  Lo.ss = take(R * (Lo.H / 64) * 4);
+  Lo.q = take(R * Lo.DQ * 4);
+  Lo.o = take(R * Lo.DQ * 4);
+  Lo.h = take(R * Lo.F * 4);
+  size_t part = 0;
+  part = std::max(part, (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
+  part = std::max(part, (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
+  part = std::max(part, (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
+  part = std::max(part, (size_t)(Lo.F / (Lo.nk_d * 32)) * Lo.H);
+  part = std::max(part, (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
+  Lo.part = take(part * R * 4);
+  Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
+  Lo.cnt = take((size_t)Lo.cnt_n * 4);
+  Lo.attn_cnt = take(R * Lo.nkv * 4);
+  Lo.lm_cnt = take(4);
+  Lo.argkey = take(R * 8);
+  Lo.status = take(4);
+  Lo.step = take(sizeof(StepDev) + 2 * R * 4);
+  Lo.result = take((1 + 2 * R) * 4);
+  Lo.kv_len = take((size_t)Lo.max_seqs * 4);
+  Lo.bt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
+  Lo.rope = take((size_t)Lo.max_ctx * (Lo.hd / 2) * 2 * 4);
+  Lo.apart = take((size_t)Lo.nkv * Lo.max_splits * R * Lo.G * (Lo.hd + 2) * 4);
+  Lo.logits = (d.flags & SPEC_FLAG_KEEP_LOGITS) ? take(R * Lo.V * 4) : (size_t)-1;
+  Lo.workspace_bytes = off;
+
+  off = 0;
+  Lo.host_step = take(sizeof(StepDev) + 2 * R * 4);
+  Lo.host_result = take((1 + 2 * R) * 4);
+  Lo.host_kvlen = take((size_t)Lo.max_seqs * 4);
+  Lo.host_bt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
+  Lo.host_bytes = off;
+  return true;
+}
+
+}  // namespace
+
+struct spec_ctx {
+  spec_model_desc d;
+  Layout lo;
+  hipStream_t st;
+  uint8_t *W, *KV, *WS, *HB;
+  // host mirrors
+  std::vector<int> len, nblk;
+  std::vector<char> live;
+  std::vector<int> free_blocks;
+  std::vector<unsigned> loaded;  // bit per matrix/norm slot
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  spec_stats stats;
+  std::string err;
+  int last_rows = 0;
+
+  template <class T> T* ws(size_t off) { return (T*)(WS + off); }
+  int32_t* h_step() { return (int32_t*)(HB + lo.host_step); }
+  int32_t* h_result() { return (int32_t*)(HB + lo.host_result); }
+  int32_t* h_kvlen() { return (int32_t*)(HB + lo.host_kvlen); }
+  int32_t* h_bt() { return (int32_t*)(HB + lo.host_bt); }
+  _Float16* kpool(int l) { return (_Float16*)(KV + (size_t)l * lo.kv_layer_bytes); }
+  _Float16* vpool(int l) { return (_Float16*)(KV + (size_t)l * lo.kv_layer_bytes + lo.kv_half_bytes); }
+};
+
+namespace {
+
+int set_err(spec_ctx* c, int code, const std::string& m) {
+  c->err = m;
+  return code;
+}
+
+#define HIPCHK(ctx, call)                                                                    \
+  do {                                                                                       \
+    hipError_t e_ = (call);                                                                  \
+    if (e_ != hipSuccess) return set_err((ctx), SPEC_EHIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// Slots of the loaded bitmap: 9 per layer (Q, K, V, O, GATE, UP, DOWN, norm a, norm f) + 3 globals.
+int slot(const spec_ctx* c, int layer, int which) { return layer * 9 + which; }
+int n_slots(const spec_ctx* c) { return c->lo.L * 9 + 3; }
+bool all_loaded(const spec_ctx* c) {
+  for (int i = 0; i < n_slots(c); ++i)
+    if (!c->loaded[(size_t)i]) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------- blocks
+
+int ensure_blocks(spec_ctx* c, int seq, int need_len, bool* dirty) {
+  const int need = (need_len + SPEC_BLOCK_TOKENS - 1) / SPEC_BLOCK_TOKENS;
+  while (c->nblk[(size_t)seq] < need) {
+    if (c->free_blocks.empty()) return set_err(c, SPEC_ECAPACITY, "KV block pool exhausted");
+    const int blk = c->free_blocks.back();
+    c->free_blocks.pop_back();
+    c->h_bt()[(size_t)seq * c->lo.bt_stride + c->nblk[(size_t)seq]] = blk;
+    c->nblk[(size_t)seq]++;
+    *dirty = true;
+  }
+  return SPEC_OK;
+}
+
+// Return blocks wholly past `len` to the pool, last allocated first.
+void trim_blocks(spec_ctx* c, int seq, int len) {
+  const int keep = (len + SPEC_BLOCK_TOKENS - 1) / SPEC_BLOCK_TOKENS;
+  while (c->nblk[(size_t)seq] > keep) {
+    c->nblk[(size_t)seq]--;
+    c->free_blocks.push_back(c->h_bt()[(size_t)seq * c->lo.bt_stride + c->nblk[(size_t)seq]]);
+  }
+}
+
+int upload_bt_row(spec_ctx* c, int seq) {
+  const size_t o = (size_t)seq * c->lo.bt_stride;
+  HIPCHK(c, hipMemcpyAsync(c->ws<int32_t>(c->lo.bt) + o, c->h_bt() + o, (size_t)c->lo.bt_stride * 4,
+                           hipMemcpyHostToDevice, c->st));
+  return SPEC_OK;
+}
+
+int upload_kv_len(spec_ctx* c, int seq) {
+  c->h_kvlen()[seq] = c->len[(size_t)seq];
+  HIPCHK(c, hipMemcpyAsync(c->ws<int32_t>(c->lo.kv_len) + seq, c->h_kvlen() + seq, 4, hipMemcpyHostToDevice, c->st));
+  return SPEC_OK;
+}
+
+// -------------------------------------------------------- forward sequence
+
+GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) {
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.W = W;
+  p.N = N;
+  p.K = K;
+  p.R = R;
+  p.nslices = K / (nk * 32);
+  p.part = c->ws<float>(c->lo.part);
+  p.cnt = c->ws<unsigned>(c->lo.cnt);
+  p.eps = c->d.rms_eps;
+  p.inv_dim = 1.0f / (float)c->lo.H;
+  return p;
+}
+
+// Per-op event hook for spec_profile_ops (null in the normal path).
+struct OpTimer {
+  std::vector<hipEvent_t>* ev;
+  std::vector<int>* ops;
+};
+
+int mark(spec_ctx* c, OpTimer* t, int op) {
+  if (!t) return SPEC_OK;
+  hipEvent_t e;
+  HIPCHK(c, hipEventCreate(&e));
+  t->ev->push_back(e);
+  t->ops->push_back(op);
+  HIPCHK(c, hipEventRecord(e, c->st));
+  return SPEC_OK;
+}
+
+#define STEP(call)                 \
+  do {                             \
+    int rc_ = (call);              \
+    if (rc_ != SPEC_OK) return rc_; \
+  } while (0)
+
+int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
+  const Layout& L = c->lo;
+  const int R = n_seq * S;
+  const StepDev* sd = c->ws<StepDev>(L.step);
+  const int32_t* tokens = (const int32_t*)(sd + 1);
+  const int32_t* seq_ids = tokens + L.max_rows;
+  hipStream_t st = c->st;
+
+  EmbedParams ep;
+  ep.emb = (const uint16_t*)(c->W + L.emb);
+  ep.tokens = tokens;
+  ep.x = c->ws<float>(L.x);
+  ep.ss = c->ws<float>(L.ss);
+  ep.H = L.H;
+  STEP(mark(c, tm, SPEC_OP_EMBED));
+  HIPCHK(c, launch_embed(ep, R, st));
+
+  for (int l = 0; l < L.L; ++l) {
+    const LayerOff& lw = L.lay[(size_t)l];
+    // QKV + RoPE + KV write
+    GemmParams g = gemm_common(c, c->W + lw.wqkv, L.Nqkv, L.H, L.nk_qkv, R);
+    g.A = c->ws<float>(L.x);
+    g.lda = L.H;
+    g.ss = c->ws<float>(L.ss);
+    g.ss_n = L.H / 64;
+    g.gain = (const float*)(c->W + lw.g_attn);
+    g.q = c->ws<float>(L.q);
+    g.kpool = c->kpool(l);
+    g.vpool = c->vpool(l);
+    g.bt = c->ws<int32_t>(L.bt);
+    g.bt_stride = L.bt_stride;
+    g.kv_len = c->ws<int32_t>(L.kv_len);
+    g.seq_ids = seq_ids;
+    g.S = S;
+    g.n_q = L.nq;
+    g.n_kv = L.nkv;
+    g.hd = L.hd;
+    g.rope = c->ws<float>(L.rope);
+    STEP(mark(c, tm, SPEC_OP_QKV));
+    HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, st));
+
+    AttnParams a;
+    a.q = c->ws<float>(L.q);
+    a.kpool = c->kpool(l);
+    a.vpool = c->vpool(l);
+    a.bt = c->ws<int32_t>(L.bt);
+    a.bt_stride = L.bt_stride;
+    a.kv_len = c->ws<int32_t>(L.kv_len);
+    a.seq_ids = seq_ids;
+    a.S = S;
+    a.n_seq = n_seq;
+    a.n_q = L.nq;
+    a.n_kv = L.nkv;
+    a.scale = (float)(1.0 / sqrt((double)L.hd));
+    a.max_splits = L.max_splits;
+    a.part = c->ws<float>(L.apart);
+    a.cnt = c->ws<unsigned>(L.attn_cnt);
+    a.out = c->ws<float>(L.o);
+    STEP(mark(c, tm, SPEC_OP_ATTN));
+    HIPCHK(c, launch_attn(a, L.hd, st));
+
+    GemmParams go = gemm_common(c, c->W + lw.wo, L.H, L.DQ, L.nk_o, R);
+    go.A = c->ws<float>(L.o);
+    go.lda = L.DQ;
+    go.x = c->ws<float>(L.x);
+    go.ss_out = c->ws<float>(L.ss);
+    STEP(mark(c, tm, SPEC_OP_O));
+    HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, st));
+
+    GemmParams gu = gemm_common(c, c->W + lw.wgu, L.Ngu, L.H, L.nk_gu, R);
+    gu.A = c->ws<float>(L.x);
+    gu.lda = L.H;
+    gu.ss = c->ws<float>(L.ss);
+    gu.ss_n = L.H / 64;
+    gu.gain = (const float*)(c->W + lw.g_ffn);
+    gu.h = c->ws<float>(L.h);
+    STEP(mark(c, tm, SPEC_OP_GATEUP));
+    HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, st));
+
+    GemmParams gd = gemm_common(c, c->W + lw.wd, L.H, L.F, L.nk_d, R);
+    gd.A = c->ws<float>(L.h);
+    gd.lda = L.F;
+    gd.x = c->ws<float>(L.x);
+    gd.ss_out = c->ws<float>(L.ss);
+    STEP(mark(c, tm, SPEC_OP_DOWN));
+    HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, st));
+  }
+
+  GemmParams gl = gemm_common(c, c->W + L.wlm, L.V, L.H, L.nk_lm, R);
+  gl.A = c->ws<float>(L.x);
+  gl.lda = L.H;
+  gl.ss = c->ws<float>(L.ss);
+  gl.ss_n = L.H / 64;
+  gl.gain = (const float*)(c->W + L.g_final);
+  gl.argkey = c->ws<unsigned long long>(L.argkey);
+  gl.lm_cnt = c->ws<unsigned>(L.lm_cnt);
+  gl.status = c->ws<int32_t>(L.status);
+  gl.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
+  gl.tokens = tokens;
+  gl.mode = &sd->mode;
+  gl.result = c->ws<int32_t>(L.result);
+  gl.kv_len_w = c->ws<int32_t>(L.kv_len);
+  gl.seq_ids = seq_ids;
+  gl.S = S;
+  gl.n_seq = n_seq;
+  STEP(mark(c, tm, SPEC_OP_LM));
+  HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, st));
+  STEP(mark(c, tm, -1));
+  return SPEC_OK;
+}
+
+int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
+  auto key = std::make_pair(n_seq, S);
+  auto it = c->graphs.find(key);
+  if (it != c->graphs.end()) {
+    *out = it->second;
+    return SPEC_OK;
+  }
+  HIPCHK(c, hipStreamBeginCapture(c->st, hipStreamCaptureModeThreadLocal));
+  const int rc = enqueue_forward(c, n_seq, S, nullptr);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(c->st, &g);
+  if (rc != SPEC_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  hipGraphExec_t ge = nullptr;
+  const hipError_t e2 = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e2 != hipSuccess) return set_err(c, SPEC_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e2));
+  c->graphs[key] = ge;
+  c->stats.graphs++;
+  *out = ge;
+  return SPEC_OK;
+}
+
+// Stage the step block (mode, shape, tokens, sequence ids) and copy it.
+int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
+  const Layout& L = c->lo;
+  StepDev* sd = (StepDev*)c->h_step();
+  sd->mode = mode;
+  sd->n_seq = n_seq;
+  sd->span = S;
+  sd->pad = 0;
+  int32_t* tk = (int32_t*)(sd + 1);
+  memcpy(tk, tokens, sizeof(int32_t) * (size_t)n_seq * S);
+  memcpy(tk + L.max_rows, seq_ids, sizeof(int32_t) * (size_t)n_seq);
+  const size_t bytes = sizeof(StepDev) + (size_t)L.max_rows * 4 + (size_t)n_seq * 4;
+  // tokens of the whole row range and the used sequence ids, in one copy
+  HIPCHK(c, hipMemcpyAsync(c->ws<uint8_t>(L.step), c->h_step(), bytes, hipMemcpyHostToDevice, c->st));
+  return SPEC_OK;
+}
+
+int launch_forward(spec_ctx* c, int n_seq, int S) {
+  if (c->d.flags & SPEC_FLAG_NO_GRAPH) return enqueue_forward(c, n_seq, S, nullptr);
+  hipGraphExec_t ge;
+  STEP(get_graph(c, n_seq, S, &ge));
+  HIPCHK(c, hipGraphLaunch(ge, c->st));
+  return SPEC_OK;
+}
+
+// One forward and its result copy; synchronous.
+int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
+  STEP(upload_step(c, mode, n_seq, S, tokens, seq_ids));
+  STEP(launch_forward(c, n_seq, S));
+  HIPCHK(c, hipMemcpyAsync(c->h_result(), c->ws<int32_t>(c->lo.result), (size_t)(1 + n_seq * (S + 1)) * 4,
+                           hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  c->stats.forwards++;
+  c->last_rows = n_seq * S;
+  if (c->h_result()[0] & 1) return set_err(c, SPEC_ENAN, "a logit row held NaN");
+  return SPEC_OK;
+}
+
+int check_ready(spec_ctx* c) {
+  if (!all_loaded(c)) return set_err(c, SPEC_ESTATE, "weights not fully loaded");
+  return SPEC_OK;
+}
+
+int check_tokens(spec_ctx* c, const int32_t* t, int n) {
+  for (int i = 0; i < n; ++i)
+    if (t[i] < 0 || t[i] >= c->lo.V) return set_err(c, SPEC_EINVAL, "token outside [0, vocab)");
+  return SPEC_OK;
+}
+
+int check_seq(spec_ctx* c, int seq) {
+  if (seq < 0 || seq >= c->lo.max_seqs) return set_err(c, SPEC_EINVAL, "sequence id out of range");
+  return SPEC_OK;
+}
+
+}  // namespace
+
+// =================================================================== ABI
+
+extern "C" {
+
+int spec_query_buffers(const spec_model_desc* desc, spec_buffer_sizes* out) {
+  if (!desc || !out) return SPEC_EINVAL;
+  Layout L;
+  if (!build_layout(*desc, L, g_create_error)) return SPEC_EINVAL;
+  out->weights_bytes = L.weights_bytes;
+  out->kv_bytes = L.kv_bytes;
+  out->workspace_bytes = L.workspace_bytes;
+  out->host_bytes = L.host_bytes;
+  return SPEC_OK;
+}
+
+const char* spec_last_error(const spec_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void* hip_stream, spec_ctx** out) {
+  if (!desc || !b || !out) {
+    g_create_error = "null argument";
+    return SPEC_EINVAL;
+  }
+  *out = nullptr;
+  spec_ctx* c = new (std::nothrow) spec_ctx;
+  if (!c) {
+    g_create_error = "out of host memory";
+    return SPEC_ECAPACITY;
+  }
+  c->d = *desc;
+  if (!build_layout(*desc, c->lo, g_create_error)) {
+    delete c;
+    return SPEC_EINVAL;
+  }
+  const Layout& L = c->lo;
+  if (!b->weights || !b->kv || !b->workspace || !b->host || b->weights_bytes < L.weights_bytes ||
+      b->kv_bytes < L.kv_bytes || b->workspace_bytes < L.workspace_bytes || b->host_bytes < L.host_bytes) {
+    g_create_error = "a buffer is missing or smaller than spec_query_buffers reports";
+    delete c;
+    return SPEC_ECAPACITY;
+  }
+  if (((uintptr_t)b->weights | (uintptr_t)b->kv | (uintptr_t)b->workspace) & (kAlign - 1)) {
+    g_create_error = "device buffers must be 256-byte aligned";
+    delete c;
+    return SPEC_EINVAL;
+  }
+  if (!hip_stream) {
+    g_create_error = "a non-NULL HIP stream is required";
+    delete c;
+    return SPEC_EINVAL;
+  }
+  c->st = (hipStream_t)hip_stream;
+  c->W = (uint8_t*)b->weights;
+  c->KV = (uint8_t*)b->kv;
+  c->WS = (uint8_t*)b->workspace;
+  c->HB = (uint8_t*)b->host;
+  c->len.assign((size_t)L.max_seqs, 0);
+  c->nblk.assign((size_t)L.max_seqs, 0);
+  c->live.assign((size_t)L.max_seqs, 0);
+  for (int i = L.n_blocks - 1; i >= 0; --i) c->free_blocks.push_back(i);
+  c->loaded.assign((size_t)n_slots(c), 0u);
+  memset(&c->stats, 0, sizeof(c->stats));
+  memset(c->HB, 0, L.host_bytes);
+
+  // Zero the KV pool (masked keys multiply exact zeros, never stale NaN) and
+  // the workspace (counters, maxima and cache lengths start at zero).
+  hipError_t e = launch_fill_u32(c->KV, 0u, L.kv_bytes / 4, c->st);
+  if (e == hipSuccess) e = launch_fill_u32(c->WS, 0u, L.workspace_bytes / 4, c->st);
+  // RoPE table: angle pos * theta^(-2j/hd) in fp64, stored as fp32 (cos, sin).
+  std::vector<float> rope((size_t)L.max_ctx * (L.hd / 2) * 2);
+  for (int pos = 0; pos < L.max_ctx; ++pos)
+    for (int j = 0; j < L.hd / 2; ++j) {
+      const double ang = (double)pos * pow(desc->rope_theta, -2.0 * j / (double)L.hd);
+      rope[((size_t)pos * (L.hd / 2) + j) * 2] = (float)cos(ang);
+      rope[((size_t)pos * (L.hd / 2) + j) * 2 + 1] = (float)sin(ang);
+    }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->WS + L.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice, c->st);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->st);
+  if (e != hipSuccess) {
+    g_create_error = std::string("initialising device buffers: ") + hipGetErrorString(e);
+    delete c;
+    return SPEC_EHIP;
+  }
+  *out = c;
+  return SPEC_OK;
+}
+
+int spec_destroy(spec_ctx* c) {
+  if (!c) return SPEC_EINVAL;
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  delete c;
+  return SPEC_OK;
+}
+
+int spec_load_matrix(spec_ctx* c, int layer, int which, const void* src, const void* scales) {
+  (void)scales;
+  if (!c || !src) return c ? set_err(c, SPEC_EINVAL, "null source") : SPEC_EINVAL;
+  const Layout& L = c->lo;
+  const bool global = (which == SPEC_MAT_EMB || which == SPEC_MAT_LM);
+  if (which < 0 || which > SPEC_MAT_LM) return set_err(c, SPEC_EINVAL, "unknown matrix id");
+  if (!global && (layer < 0 || layer >= L.L)) return set_err(c, SPEC_EINVAL, "layer out of range");
+  const uint16_t* s = (const uint16_t*)src;
+  hipError_t e = hipSuccess;
+  int slot_id;
+  if (which == SPEC_MAT_EMB) {
+    e = hipMemcpyAsync(c->W + L.emb, src, (size_t)L.V * L.H * 2, hipMemcpyDeviceToDevice, c->st);
+    slot_id = L.L * 9 + 0;
+  } else if (which == SPEC_MAT_LM) {
+    e = launch_pack_bf16(s, L.V, L.H, c->W + L.wlm, 0, 0, 0, c->st);
+    slot_id = L.L * 9 + 1;
+  } else {
+    const LayerOff& lw = L.lay[(size_t)layer];
+    switch (which) {
+      case SPEC_MAT_Q: e = launch_pack_bf16(s, L.DQ, L.H, c->W + lw.wqkv, 1, 0, L.hd, c->st); break;
+      case SPEC_MAT_K: e = launch_pack_bf16(s, L.DK, L.H, c->W + lw.wqkv, 1, L.DQ, L.hd, c->st); break;
+      case SPEC_MAT_V: e = launch_pack_bf16(s, L.DK, L.H, c->W + lw.wqkv, 0, L.DQ + L.DK, 0, c->st); break;
+      case SPEC_MAT_O: e = launch_pack_bf16(s, L.H, L.DQ, c->W + lw.wo, 0, 0, 0, c->st); break;
+      case SPEC_MAT_GATE: e = launch_pack_bf16(s, L.F, L.H, c->W + lw.wgu, 2, 0, 0, c->st); break;
+      case SPEC_MAT_UP: e = launch_pack_bf16(s, L.F, L.H, c->W + lw.wgu, 2, 1, 0, c->st); break;
+      case SPEC_MAT_DOWN: e = launch_pack_bf16(s, L.H, L.F, c->W + lw.wd, 0, 0, 0, c->st); break;
+    }
+    slot_id = slot(c, layer, which);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(c->st);
+  if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("weight packing: ") + hipGetErrorString(e));
+  c->loaded[(size_t)slot_id] = 1u;
+  return SPEC_OK;
+}
+
+int spec_load_norm(spec_ctx* c, int layer, int which, const float* src) {
+  if (!c || !src) return c ? set_err(c, SPEC_EINVAL, "null source") : SPEC_EINVAL;
+  const Layout& L = c->lo;
+  size_t off;
+  int slot_id;
+  if (which == SPEC_NORM_FINAL) {
+    off = L.g_final;
+    slot_id = L.L * 9 + 2;
+  } else {
+    if (layer < 0 || layer >= L.L) return set_err(c, SPEC_EINVAL, "layer out of range");
+    if (which == SPEC_NORM_ATTN) off = L.lay[(size_t)layer].g_attn;
+    else if (which == SPEC_NORM_FFN) off = L.lay[(size_t)layer].g_ffn;
+    else return set_err(c, SPEC_EINVAL, "unknown norm id");
+    slot_id = slot(c, layer, 7 + which);
+  }
+  HIPCHK(c, hipMemcpyAsync(c->W + off, src, (size_t)L.H * 4, hipMemcpyDeviceToDevice, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  c->loaded[(size_t)slot_id] = 1u;
+  return SPEC_OK;
+}
+
+int spec_prefill_seq(spec_ctx* c, int seq, const int32_t* tokens, int n, int32_t* next_token) {
+  if (!c) return SPEC_EINVAL;
+  if (!tokens || !next_token || n <= 0) return set_err(c, SPEC_EINVAL, "prefill needs n >= 1 tokens");
+  STEP(check_seq(c, seq));
+  STEP(check_ready(c));
+  STEP(check_tokens(c, tokens, n));
+  if (n > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "prompt longer than max_ctx");
+  c->len[(size_t)seq] = 0;
+  c->live[(size_t)seq] = 0;
+  trim_blocks(c, seq, 0);
+  STEP(upload_kv_len(c, seq));
+  const int chunk = std::min(SPEC_MAX_SPAN, c->lo.max_rows);
+  int g = -1;
+  for (int off = 0; off < n; off += chunk) {
+    const int S = std::min(chunk, n - off);
+    bool dirty = false;
+    STEP(ensure_blocks(c, seq, off + S, &dirty));
+    if (dirty) STEP(upload_bt_row(c, seq));
+    const int32_t sid = seq;
+    STEP(run_forward(c, MODE_COMMIT_ALL, 1, S, tokens + off, &sid));
+    c->len[(size_t)seq] += S;
+    g = c->h_result()[1 + 1 + (S - 1)];
+  }
+  c->live[(size_t)seq] = 1;
+  *next_token = g;
+  return SPEC_OK;
+}
+
+int spec_prefill(spec_ctx* c, const int32_t* tokens, int n, int32_t* next_token) {
+  return spec_prefill_seq(c, 0, tokens, n, next_token);
+}
+
+int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
+                      int32_t* argmax, int32_t* accept_len) {
+  if (!c) return SPEC_EINVAL;
+  if (!seq_ids || !spans || !argmax || !accept_len || n_seq <= 0)
+    return set_err(c, SPEC_EINVAL, "null argument or n_seq < 1");
+  const int S = K + 1;
+  if (K < 0 || S > SPEC_MAX_SPAN) return set_err(c, SPEC_EINVAL, "K must be in [0, 15]");
+  if (n_seq * S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "n_seq*(K+1) exceeds max_rows");
+  STEP(check_ready(c));
+  STEP(check_tokens(c, spans, n_seq * S));
+  for (int b = 0; b < n_seq; ++b) {
+    STEP(check_seq(c, seq_ids[b]));
+    for (int j = 0; j < b; ++j)
+      if (seq_ids[j] == seq_ids[b]) return set_err(c, SPEC_EINVAL, "duplicate sequence id");
+    if (!c->live[(size_t)seq_ids[b]]) return set_err(c, SPEC_ESTATE, "verify before prefill");
+    if (c->len[(size_t)seq_ids[b]] + S > c->lo.max_ctx)
+      return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
+  }
+  for (int b = 0; b < n_seq; ++b) {
+    const int seq = seq_ids[b];
+    bool dirty = false;
+    const int rc = ensure_blocks(c, seq, c->len[(size_t)seq] + S, &dirty);
+    if (rc != SPEC_OK) {  // give back what this call took
+      for (int j = 0; j <= b; ++j) trim_blocks(c, seq_ids[j], c->len[(size_t)seq_ids[j]]);
+      return rc;
+    }
+    if (dirty) STEP(upload_bt_row(c, seq));
+  }
+  STEP(run_forward(c, MODE_VERIFY, n_seq, S, spans, seq_ids));
+  const int32_t* res = c->h_result() + 1;
+  for (int b = 0; b < n_seq; ++b) {
+    const int m = res[b * (S + 1)];
+    accept_len[b] = m;
+    memcpy(argmax + (size_t)b * S, res + b * (S + 1) + 1, sizeof(int32_t) * (size_t)S);
+    const int seq = seq_ids[b];
+    c->len[(size_t)seq] += m + 1;
+    trim_blocks(c, seq, c->len[(size_t)seq]);
+    c->stats.drafted += K;
+    c->stats.accepted += m;
+  }
+  c->stats.verify_calls++;
+  c->stats.forwards_by_span[S]++;
+  return SPEC_OK;
+}
+
+int spec_verify(spec_ctx* c, const int32_t* span, int K, int32_t* argmax, int32_t* accept_len) {
+  const int32_t sid = 0;
+  return spec_verify_batch(c, 1, &sid, span, K, argmax, accept_len);
+}
+
+int spec_rewind_seq(spec_ctx* c, int seq, int len) {
+  if (!c) return SPEC_EINVAL;
+  STEP(check_seq(c, seq));
+  if (len < 0 || len > c->len[(size_t)seq]) return set_err(c, SPEC_ESTATE, "rewind length outside [0, cache length]");
+  c->len[(size_t)seq] = len;
+  trim_blocks(c, seq, len);
+  STEP(upload_kv_len(c, seq));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return SPEC_OK;
+}
+
+int spec_rewind(spec_ctx* c, int len) { return spec_rewind_seq(c, 0, len); }
+
+int spec_cache_len_seq(spec_ctx* c, int seq, int* len) {
+  if (!c || !len) return SPEC_EINVAL;
+  STEP(check_seq(c, seq));
+  *len = c->len[(size_t)seq];
+  return SPEC_OK;
+}
+
+int spec_cache_len(spec_ctx* c, int* len) { return spec_cache_len_seq(c, 0, len); }
+
+int spec_release_seq(spec_ctx* c, int seq) {
+  if (!c) return SPEC_EINVAL;
+  STEP(check_seq(c, seq));
+  c->len[(size_t)seq] = 0;
+  c->live[(size_t)seq] = 0;
+  trim_blocks(c, seq, 0);
+  STEP(upload_kv_len(c, seq));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return SPEC_OK;
+}
+
+int spec_debug_logits(spec_ctx* c, float* host_out, int rows) {
+  if (!c || !host_out) return SPEC_EINVAL;
+  if (!(c->d.flags & SPEC_FLAG_KEEP_LOGITS)) return set_err(c, SPEC_ESTATE, "context built without KEEP_LOGITS");
+  if (rows < 0 || rows > c->last_rows) return set_err(c, SPEC_EINVAL, "rows beyond the last forward");
+  HIPCHK(c, hipMemcpyAsync(host_out, c->WS + c->lo.logits, (size_t)rows * c->lo.V * 4, hipMemcpyDeviceToHost, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return SPEC_OK;
+}
+
+int spec_get_stats(spec_ctx* c, spec_stats* out) {
+  if (!c || !out) return SPEC_EINVAL;
+  *out = c->stats;
+  return SPEC_OK;
+}
+
+int spec_time_verify(spec_ctx* c, int S, int iters, const int32_t* spans, float* ms_out) {
+  if (!c || !spans || !ms_out || iters <= 0) return c ? set_err(c, SPEC_EINVAL, "bad timing arguments") : SPEC_EINVAL;
+  if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
+  STEP(check_ready(c));
+  STEP(check_tokens(c, spans, S * iters));
+  if (!c->live[0]) return set_err(c, SPEC_ESTATE, "timing before prefill");
+  if (c->len[0] + S > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
+  bool dirty = false;
+  STEP(ensure_blocks(c, 0, c->len[0] + S, &dirty));
+  if (dirty) STEP(upload_bt_row(c, 0));
+  hipEvent_t e0, e1;
+  HIPCHK(c, hipEventCreate(&e0));
+  HIPCHK(c, hipEventCreate(&e1));
+  const int32_t sid = 0;
+  int rc = SPEC_OK;
+  for (int it = 0; it < iters && rc == SPEC_OK; ++it) {
+    rc = upload_step(c, MODE_NO_COMMIT, 1, S, spans + (size_t)it * S, &sid);
+    if (rc != SPEC_OK) break;
+    hipError_t e = hipEventRecord(e0, c->st);
+    if (e == hipSuccess) {
+      rc = launch_forward(c, 1, S);
+      if (rc != SPEC_OK) break;
+      e = hipEventRecord(e1, c->st);
+    }
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms_out[it], e0, e1);
+    if (e != hipSuccess) rc = set_err(c, SPEC_EHIP, std::string("timing: ") + hipGetErrorString(e));
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  trim_blocks(c, 0, c->len[0]);
+  c->last_rows = S;
+  return rc;
+}
+
+int spec_profile_ops(spec_ctx* c, int S, int iters, const int32_t* spans, float* us_out, int32_t* launches_out) {
+  if (!c || !spans || !us_out || !launches_out || iters <= 0)
+    return c ? set_err(c, SPEC_EINVAL, "bad profiling arguments") : SPEC_EINVAL;
+  if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
+  STEP(check_ready(c));
+  STEP(check_tokens(c, spans, S * iters));
+  if (!c->live[0]) return set_err(c, SPEC_ESTATE, "profiling before prefill");
+  if (c->len[0] + S > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
+  bool dirty = false;
+  STEP(ensure_blocks(c, 0, c->len[0] + S, &dirty));
+  if (dirty) STEP(upload_bt_row(c, 0));
+  double tot[SPEC_OP_COUNT] = {0};
+  int cnt[SPEC_OP_COUNT] = {0};
+  const int32_t sid = 0;
+  int rc = SPEC_OK;
+  for (int it = 0; it < iters && rc == SPEC_OK; ++it) {
+    std::vector<hipEvent_t> ev;
+    std::vector<int> ops;
+    OpTimer tm{&ev, &ops};
+    rc = upload_step(c, MODE_NO_COMMIT, 1, S, spans + (size_t)it * S, &sid);
+    if (rc == SPEC_OK) rc = enqueue_forward(c, 1, S, &tm);
+    if (rc == SPEC_OK) {
+      hipError_t e = hipStreamSynchronize(c->st);
+      for (size_t i = 0; e == hipSuccess && i + 1 < ev.size(); ++i) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+        if (e == hipSuccess && ops[i] >= 0) {
+          tot[ops[i]] += ms;
+          if (it == 0) cnt[ops[i]]++;
+        }
+      }
+      if (e != hipSuccess) rc = set_err(c, SPEC_EHIP, std::string("profiling: ") + hipGetErrorString(e));
+    }
+    for (auto e : ev) (void)hipEventDestroy(e);
+  }
+  trim_blocks(c, 0, c->len[0]);
+  c->last_rows = S;
+  if (rc != SPEC_OK) return rc;
+  for (int op = 0; op < SPEC_OP_COUNT; ++op) {
+    launches_out[op] = cnt[op];
+    us_out[op] = cnt[op] ? (float)(tot[op] * 1000.0 / ((double)cnt[op] * iters)) : 0.0f;
+  }
+  return SPEC_OK;
+}
+
+int spec_op_bytes(const spec_model_desc* d, int op, int S, int ctx_len, double* bytes_out) {
+  if (!d || !bytes_out || S < 1 || ctx_len < 0) return SPEC_EINVAL;
+  const double H = d->hidden, hd = d->head_dim, DQ = (double)d->n_q_heads * hd, DK = (double)d->n_kv_heads * hd;
+  const double F = d->ffn, V = d->vocab;
+  const double wb = 2.0;  // bf16 weight bytes
+  switch (op) {
+    case SPEC_OP_EMBED: *bytes_out = S * H * 2.0; break;
+    case SPEC_OP_QKV: *bytes_out = (DQ + 2 * DK) * H * wb + S * DK * 2 * 2.0; break;
+    case SPEC_OP_ATTN: *bytes_out = (double)(ctx_len + S) * DK * 2 * 2.0; break;
+    case SPEC_OP_O: *bytes_out = H * DQ * wb; break;
+    case SPEC_OP_GATEUP: *bytes_out = 2 * F * H * wb; break;
+    case SPEC_OP_DOWN: *bytes_out = H * F * wb; break;
+    case SPEC_OP_LM: *bytes_out = V * H * wb; break;
+    default: return SPEC_EINVAL;
+  }
+  return SPEC_OK;
+}
+
+// ------------------------------------------------------------ generation
+
+int spec_generate(spec_ctx* c, const int32_t* prompt, int n_prompt, int n_tokens, const spec_gen_params* gp,
+                  int32_t* out, spec_gen_stats* gs) {
+  using clk = std::chrono::steady_clock;
+  if (!c) return SPEC_EINVAL;
+  if (!prompt || n_prompt <= 0 || n_tokens <= 0 || !gp || !out || !gs)
+    return set_err(c, SPEC_EINVAL, "bad generation arguments");
+  if (gp->spec && gp->draft_source != SPEC_DRAFT_NGRAM && !gp->ref_stream)
+    return set_err(c, SPEC_EINVAL, "draft source needs ref_stream");
+  const int kcap = std::max(1, std::min(gp->fixed_k > 0 ? gp->fixed_k : gp->k_cap, SPEC_MAX_SPAN - 1));
+  memset(gs, 0, sizeof(*gs));
+  spec_ngram* ng = nullptr;
+  if (gp->spec && gp->draft_source == SPEC_DRAFT_NGRAM) {
+    int rc = spec_ngram_create(gp->n_min, gp->n_max, n_prompt + n_tokens + 1, &ng);
+    if (rc != SPEC_OK) return set_err(c, rc, "n-gram proposer arguments");
+  }
+  struct Guard {
+    spec_ngram* ng;
+    ~Guard() { spec_ngram_destroy(ng); }
+  } guard{ng};
+  const auto t0 = clk::now();
+  int32_t g0;
+  STEP(spec_prefill(c, prompt, n_prompt, &g0));
+  const auto t1 = clk::now();
+  gs->prefill_s = std::chrono::duration<double>(t1 - t0).count();
+  if (ng) {
+    STEP(spec_ngram_append(ng, prompt, n_prompt));
+    STEP(spec_ngram_append(ng, &g0, 1));
+  }
+  int n = 0;
+  out[n++] = g0;
+  int k = gp->fixed_k > 0 ? gp->fixed_k : 1;
+  int32_t span[SPEC_MAX_SPAN], am[SPEC_MAX_SPAN];
+  double in_verify = 0.0;
+  while (n < n_tokens) {
+    int kd = 0;
+    if (gp->spec) {
+      const int want = std::max(0, std::min(k, n_tokens - n - 1));
+      if (gp->draft_source == SPEC_DRAFT_NGRAM) {
+        kd = spec_ngram_propose(ng, want, span + 1);
+        if (kd < 0) return set_err(c, kd, "n-gram propose");
+      } else {
+        kd = std::min(want, n_tokens - n);
+        for (int i = 0; i < kd; ++i) {
+          const int32_t t = gp->ref_stream[n + i];
+          span[1 + i] = gp->draft_source == SPEC_DRAFT_WRONG ? (t + 1) % c->lo.V : t;
+        }
+      }
+    }
+    span[0] = out[n - 1];
+    int32_t m = 0;
+    const int p = c->len[0];
+    const auto tv = clk::now();
+    STEP(spec_verify(c, span, kd, am, &m));
+    in_verify += std::chrono::duration<double>(clk::now() - tv).count();
+    gs->forwards++;
+    gs->drafted += kd;
+    gs->accepted += m;
+    gs->accept_hist[m]++;
+    gs->forwards_by_span[kd + 1]++;
+    int commit = m + 1;
+    if (commit > n_tokens - n) {  // never expected: drafts are capped by the budget
+      commit = n_tokens - n;
+      STEP(spec_rewind(c, p + commit));
+    }
+    for (int i = 0; i < commit; ++i) out[n++] = am[i];
+    if (ng) STEP(spec_ngram_append(ng, am, commit));
+    if (gp->spec && gp->fixed_k <= 0) k = spec_adapt_k(k, kd, m, kcap);
+  }
+  const auto t2 = clk::now();
+  gs->decode_s = std::chrono::duration<double>(t2 - t1).count();
+  gs->host_s = gs->decode_s - in_verify;
+  return SPEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,255 @@
+/*
+ * specv.h -- C ABI of libspecv, the gfx950 (MI355X) verify transaction of
+ * greedy speculative decoding.
+ *
+ * The transaction (pegainfer page "DFlash speculative decoding", transaction
+ * section; TensorSharp speculative decoding page, protocol section):
+ *   propose K drafts -> ONE trunk forward over the span [last, d1..dK] that
+ *   yields the trunk argmax a0..aK of every row -> accept_greedy keeps the
+ *   longest prefix with d(i) == a(i-1) and adds the trunk's own token a(m),
+ *   so 1..K+1 tokens are committed -> the KV rows of [last, d1..dm] are kept
+ *   and the cache length becomes p+m+1 (draft-seed alignment paragraph of the
+ *   pegainfer page); rejected rows stay past the length and are overwritten
+ *   later (coreai-model-zoo dense n-gram note, KV-only rollback paragraph).
+ *
+ * General rules for every call:
+ *   - Return value: 0 on success, a negative SPEC_E* code on failure; no call
+ *     aborts or throws.  spec_last_error() gives the message of the last
+ *     failure on that context (or of the last spec_create failure for NULL).
+ *   - Device memory is owned by the caller (allocated with PyTorch): the
+ *     weight arena, the KV pool and the workspace are passed to spec_create
+ *     and must outlive the context.  The library never allocates device
+ *     memory.  It owns only host state and HIP graph objects.
+ *   - Host arrays passed to a call are borrowed for the duration of the call.
+ *   - One context per HIP stream; a context is not thread-safe.  Every
+ *     launch and copy is issued on the stream given to spec_create, and the
+ *     transaction calls return only after their results reached the host.
+ *   - Tokens are int32 in [0, vocab).
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------ error codes */
+#define SPEC_OK 0
+#define SPEC_EINVAL (-1)    /* bad argument: K out of range, token outside [0,vocab), NULL, bad id */
+#define SPEC_ECAPACITY (-2) /* p+K+1 > max_ctx, no free KV block, buffer too small (admission refusal) */
+#define SPEC_ESTATE (-3)    /* verify before prefill, rewind beyond the cache, weights not loaded */
+#define SPEC_EHIP (-4)      /* a HIP runtime call failed; the message holds hipGetErrorString */
+#define SPEC_ENAN (-5)      /* a logit row held NaN: the argmax is undefined */
+
+/* --------------------------------------------------------- model and flags */
+#define SPEC_WFMT_BF16 0     /* bf16 weights, canonical [out][in] row-major                   */
+#define SPEC_WFMT_INT4G128 1 /* int4 group-128: q4 uint8 [out][in/2] (low nibble = even col)  */
+                             /* plus bf16 scales [out][in/128]; w = scale * q, q in [-8, 7]    */
+
+#define SPEC_FLAG_KEEP_LOGITS 1u /* also store every row's logits (fp32) for spec_debug_logits */
+#define SPEC_FLAG_NO_GRAPH 2u    /* launch each kernel eagerly instead of replaying a HIP graph */
+
+#define SPEC_MAX_SPAN 16    /* rows per sequence per forward (K <= 15)      */
+#define SPEC_MAX_ROWS 128   /* rows per forward over all sequences           */
+#define SPEC_BLOCK_TOKENS 16 /* tokens per KV block                          */
+
+typedef struct spec_model_desc {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t weight_format; /* SPEC_WFMT_*; the embedding is always bf16 */
+  float rms_eps;         /* RMSNorm epsilon */
+  double rope_theta;     /* RoPE base; rotate-half pairs (i, i + head_dim/2) */
+  int32_t max_ctx;       /* tokens per sequence, including the verify span */
+  int32_t max_seqs;      /* sequences the KV pool serves */
+  int32_t max_rows;      /* rows per forward (n_seq * (K+1)), 1..SPEC_MAX_ROWS */
+  int32_t n_blocks;      /* 16-token KV blocks in the pool (0: max_seqs*ceil(max_ctx/16)) */
+  uint32_t flags;        /* SPEC_FLAG_* */
+} spec_model_desc;
+
+/* Sizes of the caller-owned buffers for a description. */
+typedef struct spec_buffer_sizes {
+  size_t weights_bytes;   /* device: packed weight arena */
+  size_t kv_bytes;        /* device: fp16 KV block pool */
+  size_t workspace_bytes; /* device: activations, partial sums, counters, tables */
+  size_t host_bytes;      /* pinned host: staging of spans and results */
+} spec_buffer_sizes;
+
+typedef struct spec_device_buffers {
+  void* weights;   size_t weights_bytes;
+  void* kv;        size_t kv_bytes;
+  void* workspace; size_t workspace_bytes;
+  void* host;      size_t host_bytes; /* pinned (page-locked) host memory */
+} spec_device_buffers;
+
+typedef struct spec_ctx spec_ctx;
+
+/* Matrix and norm identifiers for the weight loaders. */
+#define SPEC_MAT_Q 0    /* [n_q*head_dim][hidden]  */
+#define SPEC_MAT_K 1    /* [n_kv*head_dim][hidden] */
+#define SPEC_MAT_V 2    /* [n_kv*head_dim][hidden] */
+#define SPEC_MAT_O 3    /* [hidden][n_q*head_dim]  */
+#define SPEC_MAT_GATE 4 /* [ffn][hidden]           */
+#define SPEC_MAT_UP 5   /* [ffn][hidden]           */
+#define SPEC_MAT_DOWN 6 /* [hidden][ffn]           */
+#define SPEC_MAT_EMB 7  /* [vocab][hidden], bf16 in every format */
+#define SPEC_MAT_LM 8   /* [vocab][hidden]         */
+#define SPEC_NORM_ATTN 0
+#define SPEC_NORM_FFN 1
+#define SPEC_NORM_FINAL 2
+
+/* Buffer sizes for `desc`.  EINVAL for an unsupported description. */
+SPEC_API int spec_query_buffers(const spec_model_desc* desc, spec_buffer_sizes* out);
+
+/* Create a context over caller-owned buffers (each at least the size
+ * spec_query_buffers gives, device pointers 256-byte aligned) on `hip_stream`
+ * (a hipStream_t; not the legacy NULL stream, since forwards are captured into
+ * HIP graphs).  Clears the KV pool and the workspace.  Weights are then loaded
+ * with spec_load_matrix / spec_load_norm. */
+SPEC_API int spec_create(const spec_model_desc* desc, const spec_device_buffers* bufs, void* hip_stream,
+                spec_ctx** out);
+SPEC_API int spec_destroy(spec_ctx* ctx);
+SPEC_API const char* spec_last_error(const spec_ctx* ctx);
+
+/* Repack one canonical matrix from device memory into the arena.  `src` is
+ * bf16 [rows][cols] (or, for int4 models and which != SPEC_MAT_EMB, q4 bytes
+ * with `scales` bf16 [rows][cols/128]).  layer is ignored for EMB and LM.
+ * Synchronous; `src` may be freed on return. */
+SPEC_API int spec_load_matrix(spec_ctx* ctx, int layer, int which, const void* src, const void* scales);
+/* Copy one fp32 gain vector [hidden] from device memory. */
+SPEC_API int spec_load_norm(spec_ctx* ctx, int layer, int which, const float* src);
+
+/* ---------------------------------------------------------- transaction */
+
+/* Batch-1 calls act on sequence 0.
+ * spec_prefill: empty the sequence, forward the prompt (rows 0..n-1, in
+ * chunks of up to SPEC_MAX_SPAN rows, each committing all its rows) and
+ * return g0 = argmax of the last prompt row.  g0 is not cached; it is span[0]
+ * of the first verify. */
+SPEC_API int spec_prefill(spec_ctx* ctx, const int32_t* tokens, int n, int32_t* next_token);
+
+/* spec_verify: span = [last, d1..dK], K in [0, SPEC_MAX_SPAN-1]; span[0] is
+ * the token for position p = cache length.  Writes argmax[0..K] (the trunk
+ * argmax of every row, lowest index on ties) and *accept_len = m in [0, K];
+ * the committed tokens are argmax[0..m] and the cache length becomes p+m+1
+ * (set on the device by the accept kernel).  K = 0 is a plain decode step. */
+SPEC_API int spec_verify(spec_ctx* ctx, const int32_t* span, int K, int32_t* argmax, int32_t* accept_len);
+
+/* spec_rewind: shorten the cache to len (0 <= len <= cache length). */
+SPEC_API int spec_rewind(spec_ctx* ctx, int len);
+SPEC_API int spec_cache_len(spec_ctx* ctx, int* len);
+
+/* Multi-sequence calls over the paged pool (16-token blocks).
+ * spec_verify_batch: n_seq distinct sequences (seq_ids), each with a span of
+ * K+1 tokens, spans row-major [n_seq][K+1]; n_seq*(K+1) <= max_rows.  Writes
+ * argmax [n_seq][K+1] and accept_len [n_seq]; each sequence advances by its
+ * own m+1.  Blocks past a sequence's new length return to the free pool. */
+SPEC_API int spec_prefill_seq(spec_ctx* ctx, int seq, const int32_t* tokens, int n, int32_t* next_token);
+SPEC_API int spec_verify_batch(spec_ctx* ctx, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
+                      int32_t* argmax, int32_t* accept_len);
+SPEC_API int spec_rewind_seq(spec_ctx* ctx, int seq, int len);
+SPEC_API int spec_cache_len_seq(spec_ctx* ctx, int seq, int* len);
+/* Free every block of a sequence (cache length 0). */
+SPEC_API int spec_release_seq(spec_ctx* ctx, int seq);
+
+/* Logits of the rows of the last forward, fp32 [rows][vocab]; only for a
+ * context created with SPEC_FLAG_KEEP_LOGITS.  rows <= rows of that forward. */
+SPEC_API int spec_debug_logits(spec_ctx* ctx, float* host_out, int rows);
+
+/* --------------------------------------------------------- measurement */
+
+typedef struct spec_stats {
+  int64_t forwards;               /* forwards launched (prefill chunks included) */
+  int64_t verify_calls;           /* spec_verify + spec_verify_batch calls */
+  int64_t drafted, accepted;      /* drafts submitted / accepted over verify calls */
+  int64_t forwards_by_span[SPEC_MAX_SPAN + 1]; /* verify forwards by rows per sequence */
+  int64_t graphs;                 /* HIP graphs instantiated */
+} spec_stats;
+SPEC_API int spec_get_stats(spec_ctx* ctx, spec_stats* out);
+
+/* Time `iters` verify forwards of span length S (= K+1) over one sequence at
+ * its current cache length, measured with HIP events on the context stream
+ * from graph launch to the accept kernel's end, host excluded.  The cache is
+ * left unchanged (the forwards run in a no-commit mode).  spans: [iters][S]
+ * tokens; ms_out: [iters]. */
+SPEC_API int spec_time_verify(spec_ctx* ctx, int S, int iters, const int32_t* spans, float* ms_out);
+
+/* Per-kernel-class timing of `iters` eager forwards of span S at the current
+ * cache length (no commit): HIP events bracket every launch on the context
+ * stream.  us_out[SPEC_OP_COUNT] = mean microseconds per launch of each class,
+ * launches_out[SPEC_OP_COUNT] = launches per forward. */
+#define SPEC_OP_EMBED 0
+#define SPEC_OP_QKV 1
+#define SPEC_OP_ATTN 2
+#define SPEC_OP_O 3
+#define SPEC_OP_GATEUP 4
+#define SPEC_OP_DOWN 5
+#define SPEC_OP_LM 6
+#define SPEC_OP_COUNT 7
+SPEC_API int spec_profile_ops(spec_ctx* ctx, int S, int iters, const int32_t* spans, float* us_out,
+                     int32_t* launches_out);
+
+/* Algorithmic bytes one launch of an op class streams at span S and cache
+ * length ctx_len (weights, KV reads and writes; activations excluded). */
+SPEC_API int spec_op_bytes(const spec_model_desc* desc, int op, int S, int ctx_len, double* bytes_out);
+
+/* ----------------------------------------------------------- proposer */
+
+/* n-gram prompt-lookup proposer (TensorSharp speculative decoding page,
+ * n-gram section; coreai-model-zoo dense n-gram note, adaptive-K section):
+ * an exact index per order n in [n_min, n_max] maps each n-gram to its most
+ * recent end position, so propose() returns the continuation of the latest
+ * earlier occurrence of the longest matching suffix, at most K tokens and
+ * only tokens already in the history.  Host memory only. */
+typedef struct spec_ngram spec_ngram;
+SPEC_API int spec_ngram_create(int n_min, int n_max, int capacity, spec_ngram** out);
+SPEC_API int spec_ngram_destroy(spec_ngram* ng);
+SPEC_API int spec_ngram_append(spec_ngram* ng, const int32_t* toks, int n); /* ECAPACITY past capacity */
+SPEC_API int spec_ngram_truncate(spec_ngram* ng, int len);
+SPEC_API int spec_ngram_len(spec_ngram* ng);
+/* Returns the number of drafts written (0..K), or a negative code. */
+SPEC_API int spec_ngram_propose(spec_ngram* ng, int K, int32_t* drafts);
+
+/* Adaptive K (coreai note, adaptive-K section): after a round that proposed
+ * `drafted` >= 1 drafts of which `accepted` were accepted, K+2 on a full
+ * accept, K-1 otherwise, clamped to [1, k_cap]; drafted == 0 returns k.
+ * Pure function. */
+SPEC_API int spec_adapt_k(int k, int drafted, int accepted, int k_cap);
+
+/* ------------------------------------------------------ generation loop */
+
+#define SPEC_DRAFT_NGRAM 0   /* n-gram proposer over prompt + committed tokens */
+#define SPEC_DRAFT_STREAM 1  /* drafts read from `ref_stream` (perfect-draft bound) */
+#define SPEC_DRAFT_WRONG 2   /* ref_stream tokens + 1 mod vocab (all-rejected bound) */
+
+typedef struct spec_gen_params {
+  int32_t spec;        /* 0: plain greedy, one K=0 step per token; 1: speculative */
+  int32_t fixed_k;     /* > 0: fixed draft length; 0: adaptive K starting at 1 */
+  int32_t k_cap;       /* cap of adaptive K (<= SPEC_MAX_SPAN-1) */
+  int32_t n_min, n_max;
+  int32_t draft_source;        /* SPEC_DRAFT_* */
+  const int32_t* ref_stream;   /* [n_tokens] for SPEC_DRAFT_STREAM / WRONG */
+} spec_gen_params;
+
+typedef struct spec_gen_stats {
+  int64_t forwards, drafted, accepted;
+  int64_t accept_hist[SPEC_MAX_SPAN];           /* rounds by accepted drafts m */
+  int64_t forwards_by_span[SPEC_MAX_SPAN + 1];  /* rounds by span length K+1 */
+  double decode_s;  /* wall time from prefill return to the last token committed */
+  double host_s;    /* part of decode_s spent outside spec_verify (proposer, bookkeeping) */
+  double prefill_s;
+} spec_gen_stats;
+
+/* Greedy generation on sequence 0: prefill `prompt`, then commit n_tokens
+ * tokens counted from g0 (so decode covers n_tokens-1 committed after g0).
+ * No round drafts past the budget.  out_tokens: [n_tokens]. */
+SPEC_API int spec_generate(spec_ctx* ctx, const int32_t* prompt, int n_prompt, int n_tokens,
+                  const spec_gen_params* params, int32_t* out_tokens, spec_gen_stats* stats);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECV_H */
