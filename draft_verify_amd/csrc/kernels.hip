@@ -32,6 +32,24 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
+// Cross-workgroup hand-off inside one kernel.  Partial results are written
+// and read with device-coherent (agent-scope) relaxed accesses, which bypass
+// the per-XCD L2s' non-coherent copies, and a producer waits for its stores
+// to complete before it signals the arrival counter.  This avoids the L2
+// writeback + invalidate a full device-scope fence would issue in every
+// workgroup.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {  // 8-byte aligned pair
+  const unsigned long long v = __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Order-preserving key of (value, column): larger value wins, then the lower
 // column.  Zero is below every key, so a zeroed slot is the neutral element.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
@@ -125,16 +143,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 
   for (int m0 = 0; m0 < P.R; m0 += 16) {
     if (P.ss) {
-      if (tid < 16) {
-        const int r = m0 + tid;
-        float rs = 0.0f;
-        if (r < P.R) {
-          float s = 0.0f;
-          for (int q = 0; q < P.ss_n; ++q) s += P.ss[(size_t)r * P.ss_n + q];
-          rs = 1.0f / sqrtf(s * P.inv_dim + P.eps);
-        }
-        sR[tid] = rs;
-      }
+      // rstd of row m0 + tid/16: 16 lanes sum strided partials, then a fixed
+      // xor tree (the same order for every row count).
+      const int row = tid >> 4, part = tid & 15, r = m0 + row;
+      float s = 0.0f;
+      if (r < P.R)
+        for (int q = part; q < P.ss_n; q += 16) s += P.ss[(size_t)r * P.ss_n + q];
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      if (part == 0) sR[row] = r < P.R ? 1.0f / sqrtf(s * P.inv_dim + P.eps) : 0.0f;
       __syncthreads();
     }
     // Stage 16 rows x NK*32 inputs: unit u = (row, step j, lane group g) of 8 inputs.
@@ -186,12 +203,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = m0 + (lane >> 4) * 4 + i;
-      if (r < P.R) P.part[((size_t)sl * P.R + r) * P.N + col] = acc[i];
+      if (r < P.R) st_dev(P.part + ((size_t)sl * P.R + r) * P.N + col, acc[i]);
     }
     __syncthreads();  // sA is restaged for the next 16 rows
   }
 
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (tid == 0) {
     const unsigned old = atomicAdd(&P.cnt[nb], 1u);
@@ -199,7 +216,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   }
   __syncthreads();
   if (!sLast) return;
-  __threadfence();
   if (tid == 0) P.cnt[nb] = 0u;  // ready for the next launch
   gemm_epilogue<EPI>(P, nb, (float*)sA);
 }
@@ -209,7 +225,7 @@ __device__ __forceinline__ void reduce_pair(const GemmParams& P, int r, int c, f
   v0 = 0.0f;
   v1 = 0.0f;
   for (int s = 0; s < P.nslices; ++s) {
-    const float2 t = *(const float2*)(P.part + ((size_t)s * P.R + r) * P.N + c);
+    const float2 t = ld_dev2(P.part + ((size_t)s * P.R + r) * P.N + c);
     v0 += t.x;
     v1 += t.y;
   }
@@ -309,7 +325,7 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
     if ((idx & 31) == 0) atomicMax(&P.argkey[r], k);
   }
   // Last column block to finish: read the row maxima, accept, advance the cache.
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old = atomicAdd(P.lm_cnt, 1u);
@@ -317,7 +333,6 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
   }
   __syncthreads();
   if (!sFinal) return;
-  __threadfence();
   int* arg = (int*)sbuf;
   for (int r = threadIdx.x; r < P.R; r += 256) {
     const unsigned long long k = atomicExch(&P.argkey[r], 0ull);
@@ -342,8 +357,7 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
     for (int i = 0; i < S; ++i) res[1 + i] = arg[row0 + i];
   }
   if (threadIdx.x == 0) {
-    P.result[0] = *P.status;
-    *P.status = 0;
+    P.result[0] = atomicExch(P.status, 0);
     *P.lm_cnt = 0u;
   }
 }
@@ -488,16 +502,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
         }
       }
       float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-      dst[2 + d] = O;
+      st_dev(dst + 2 + d, O);
       if (d == 0) {
-        dst[0] = M;
-        dst[1] = L;
+        st_dev(dst, M);
+        st_dev(dst + 1, L);
       }
     }
     __syncthreads();
   }
 
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (tid == 0) {
     const unsigned old = atomicAdd(&P.cnt[b * P.n_kv + kvh], 1u);
@@ -505,24 +519,43 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   }
   __syncthreads();
   if (!sLast) return;
-  __threadfence();
   if (tid == 0) P.cnt[b * P.n_kv + kvh] = 0u;
-  // Combine the splits that hold keys at or before each row's position.
-  for (int e = tid; e < QC * HD; e += 256) {
-    const int qcol = e / HD, d = e % HD;
+  // Combine the splits that hold keys at or before each row's position:
+  // first the weight exp(m_s - M) / L of every (split, column), in LDS, then
+  // the values, in split order.
+  const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
+  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC) * (HD + 2);
+  float* sW = &sO[0][0][0];  // [n_act][QC], free after the tile loop
+  for (int qcol = tid; qcol < QC; qcol += 256) {
+    const int nsp = ((p + qcol / G) >> 8) + 1;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, ld_dev(base + sp * stride + (size_t)qcol * (HD + 2)));
+    float L = 0.0f;
+    for (int sp = 0; sp < nsp; ++sp) {
+      const float2 ml = ld_dev2(base + sp * stride + (size_t)qcol * (HD + 2));
+      const float f = expf(ml.x - M);
+      sW[sp * QC + qcol] = f;
+      L += ml.y * f;
+    }
+    for (int sp = 0; sp < nsp; ++sp) sW[sp * QC + qcol] /= L;
+  }
+  __syncthreads();
+  for (int e = tid; e < QC * (HD / 2); e += 256) {
+    const int qcol = e / (HD / 2), d = 2 * (e % (HD / 2));
     const int iq = qcol / G, head = kvh * G + qcol % G;
     const int nsp = ((p + iq) >> 8) + 1;
-    const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
-    const float* src = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, src[sp * stride]);
-    float L = 0.0f, O = 0.0f;
+    const float* src = base + (size_t)qcol * (HD + 2) + 2 + d;
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 4
     for (int sp = 0; sp < nsp; ++sp) {
-      const float f = expf(src[sp * stride] - M);
-      L += src[sp * stride + 1] * f;
-      O += src[sp * stride + 2 + d] * f;
+      const float2 v = ld_dev2(src + sp * stride);
+      const float f = sW[sp * QC + qcol];
+      o0 += v.x * f;
+      o1 += v.y * f;
     }
-    P.out[(size_t)(b * S + iq) * DQ + head * HD + d] = O / L;
+    float* op = P.out + (size_t)(b * S + iq) * DQ + head * HD + d;
+    op[0] = o0;
+    op[1] = o1;
   }
 }
 

@@ -89,6 +89,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.nk_d = slice_steps(Lo.F); Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
+  // the attention split-combine weights of one (sequence, kv head) live in LDS
+  if ((size_t)Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
+    return fail("max_ctx too long for this head geometry");
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

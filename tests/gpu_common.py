@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: sessions, the oracle twin, and the
+comparison protocol.
+
+Protocol (per verify step, teacher forced): the oracle replays the same span
+on the same committed prefix and
+  1. every row's logits agree within LOGIT_TOL max-abs;
+  2. the per-row argmax is equal wherever the oracle's top-2 margin is
+     >= MARGIN (elsewhere both tokens are correct readings of a near-tie);
+  3. the accept length is equal whenever the rows that decide it (rows
+     0..min(m_gpu, m_oracle, K-1)) all have margin >= MARGIN.
+After a step whose accept lengths legitimately differ, the oracle is re-synced
+to the GPU's committed history.
+"""
+import sys
+
+import numpy as np
+
+from draft_verify_amd import specv, synth
+from oracle import oracle as O
+
+LOGIT_TOL = 2e-2
+MARGIN = 0.05
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Twin:
+    """A GPU session and an oracle over the same seeded weights (sequence 0)."""
+
+    def __init__(self, shape, weights, max_ctx, max_seqs=1, max_rows=16, flags=specv.SPEC_FLAG_KEEP_LOGITS,
+                 oracle_ctx=None, host_weights=None):
+        self.shape = shape
+        self.sess = specv.Session(shape, specv.tree_weights(weights), max_ctx=max_ctx, max_seqs=max_seqs,
+                                  max_rows=max_rows, flags=flags)
+        hw = host_weights if host_weights is not None else synth.to_numpy(weights)
+        self.orc = O.Oracle(shape, hw, max_ctx=oracle_ctx or max_ctx, n_seq=max_seqs)
+        self.ctx = self.sess.ctx
+        self.history = []
+
+    def prefill(self, prompt, seq=0):
+        g = specv.spec_prefill_seq(self.ctx, seq, prompt)
+        go, mg = self.orc.prefill(prompt, seq)
+        assert g == go or mg < MARGIN, f"prefill token {g} != oracle {go} (margin {mg:.3f})"
+        self.history = [int(t) for t in prompt] + [g]
+        return g
+
+    def verify_checked(self, drafts):
+        """One verify of [last] + drafts on both sides (sequence 0), checked by
+        the protocol."""
+        seq = 0
+        span = [self.history[-1]] + [int(d) for d in drafts]
+        K = len(span) - 1
+        p = specv.spec_cache_len(self.ctx)
+        am, m = specv.spec_verify(self.ctx, span)
+        lg = specv.spec_debug_logits(self.ctx, K + 1, self.shape["vocab"])
+        amo, mo, mgo, lgo = self.orc.verify(span, seq, want_logits=True)
+        err = float(np.max(np.abs(lg - lgo)))
+        assert err < LOGIT_TOL, f"logits differ by {err:.3e} (K={K})"
+        sure = mgo >= MARGIN
+        assert np.array_equal(am[sure], amo[sure]), \
+            f"argmax differs on a sure row: gpu {am.tolist()} oracle {amo.tolist()} margins {mgo.round(3).tolist()}"
+        decide = min(m, mo, K - 1) if K > 0 else -1
+        if decide < 0 or bool(np.all(sure[: decide + 1])):
+            assert m == mo, f"accept length {m} != oracle {mo}"
+        assert 0 <= m <= K
+        assert specv.spec_cache_len_seq(self.ctx, seq) == p + m + 1
+        commit = [int(x) for x in am[: m + 1]]
+        self.history += commit
+        if m != mo or list(amo[: mo + 1]) != commit:
+            self.orc.prefill(self.history[:-1], seq)  # re-sync to the GPU's stream
+        return am, m, err
+
+    def close(self):
+        self.sess.close()
+        self.orc.close()

@@ -1,0 +1,138 @@
+"""GPU parity on the tiny decoder (2 layers, hidden 64, 4q/2kv heads of 16,
+FFN 128, vocab 256; prompt = an 8-token motif repeated 4 times; n-gram K=4;
+64 greedy tokens), through the C ABI, against the CPU oracle."""
+import numpy as np
+import pytest
+
+from draft_verify_amd import specv, synth
+from gpu_common import MARGIN, Twin, log
+
+pytestmark = pytest.mark.gpu
+SHAPE = synth.SHAPES["tiny"]
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.weights(SHAPE, seed=0)
+
+
+@pytest.fixture()
+def twin(weights):
+    t = Twin(SHAPE, weights, max_ctx=256)
+    yield t
+    t.close()
+
+
+def test_prefill_and_verify_every_span(twin):
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])
+    twin.prefill(prompt)
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for K in list(range(16)) + [15, 0, 7]:
+        drafts = rng.integers(0, SHAPE["vocab"], K)
+        _, _, err = twin.verify_checked(drafts)
+        worst = max(worst, err)
+    log(f"tiny: worst logit diff {worst:.2e} over spans 1..16")
+
+
+def test_planted_drafts_accept_exactly(twin):
+    """Drafts from the GPU's own greedy stream, corrupted at index j, accept j."""
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])
+    stream, _ = specv.spec_generate(twin.ctx, prompt, 12, spec=False)
+    K = 8
+    for j in range(K + 1):
+        g = specv.spec_prefill(twin.ctx, prompt)
+        assert g == stream[0]
+        drafts = [int(t) for t in stream[1:K + 1]]
+        if j < K:
+            drafts[j] = (drafts[j] + 1) % SHAPE["vocab"]
+        am, m = specv.spec_verify(twin.ctx, [g] + drafts)
+        assert m == j
+        assert list(am[: m + 1]) == [int(t) for t in stream[1:m + 2]]
+        assert specv.spec_cache_len(twin.ctx) == len(prompt) + m + 1
+
+
+def test_rows_gate_bit_exact(twin):
+    """One S-row forward gives bit-identical logits to S one-row decodes."""
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])
+    g = specv.spec_prefill(twin.ctx, prompt)
+    p = specv.spec_cache_len(twin.ctx)
+    span = [g] + [int(t) for t in synth.uniform_prompt(5, SHAPE["vocab"], 15)]
+    for S in (2, 5, 8, 16):
+        specv.spec_verify(twin.ctx, span[:S])
+        multi = specv.spec_debug_logits(twin.ctx, S, SHAPE["vocab"])
+        specv.spec_rewind(twin.ctx, p)
+        rows = []
+        for i in range(S):
+            specv.spec_verify(twin.ctx, [span[i]])
+            rows.append(specv.spec_debug_logits(twin.ctx, 1, SHAPE["vocab"])[0])
+        specv.spec_rewind(twin.ctx, p)
+        assert np.array_equal(multi, np.stack(rows)), f"rows gate failed at S={S}"
+
+
+def test_spec_on_equals_spec_off_and_oracle(twin):
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])
+    off, s_off = specv.spec_generate(twin.ctx, prompt, 64, spec=False)
+    fix, s_fix = specv.spec_generate(twin.ctx, prompt, 64, spec=True, fixed_k=4)
+    ada, s_ada = specv.spec_generate(twin.ctx, prompt, 64, spec=True, fixed_k=0, k_cap=7)
+    assert np.array_equal(off, fix) and np.array_equal(off, ada)
+    assert s_off["forwards"] == 63 and s_fix["forwards"] < 63 and s_fix["accepted"] > 0
+    assert sum(s_fix["accept_hist"][5:]) == 0  # m <= K
+    ref, _ = twin.orc.generate(prompt, 64, spec=False)
+    # first divergence from the oracle stream (if any) must sit at a near-tie
+    diff = [i for i in range(64) if int(off[i]) != ref[i]]
+    if diff:
+        i = diff[0]
+        twin.orc.rewind(0)
+        _, mg, _ = twin.orc.forward(np.array(list(prompt) + ref[:i]), lm_from=len(prompt) + i - 1)
+        assert mg[-1] < MARGIN, f"stream diverges at {i} with oracle margin {mg[-1]:.3f}"
+    log(f"tiny e2e: spec-off {s_off['forwards']} forwards, K=4 {s_fix['forwards']}, adaptive {s_ada['forwards']}; "
+        f"oracle-identical prefix {diff[0] if diff else 64}/64")
+
+
+def test_capture_shape_replays(weights):
+    """Graphs captured at one span and replayed after others match eager runs."""
+    spans = [[7] + list(range(20, 20 + k)) for k in (1, 15, 7, 15, 1, 3)]
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])
+    out = {}
+    for flags in (specv.SPEC_FLAG_KEEP_LOGITS | specv.SPEC_FLAG_NO_GRAPH, specv.SPEC_FLAG_KEEP_LOGITS):
+        s = specv.Session(SHAPE, specv.tree_weights(weights), max_ctx=256, flags=flags)
+        res = []
+        for sp in spans:
+            specv.spec_prefill(s.ctx, prompt)
+            am, m = specv.spec_verify(s.ctx, sp)
+            res.append((am.tolist(), m, specv.spec_debug_logits(s.ctx, len(sp), SHAPE["vocab"])))
+        if not flags & specv.SPEC_FLAG_NO_GRAPH:
+            assert specv.spec_get_stats(s.ctx)["graphs"] == 4  # spans 16 (prefill), 2, 8, 4
+        s.close()
+        out[flags] = res
+    a, b = out.values()
+    for (am0, m0, l0), (am1, m1, l1) in zip(a, b):
+        assert am0 == am1 and m0 == m1 and np.array_equal(l0, l1)
+
+
+def test_error_codes(weights):
+    s = specv.Session(SHAPE, specv.tree_weights(weights), max_ctx=48)
+    E = specv.SpecError
+    with pytest.raises(E) as e:
+        specv.spec_verify(s.ctx, [1, 2])
+    assert e.value.code == specv.SPEC_ESTATE          # verify before prefill
+    prompt = synth.motif_prompt(1, SHAPE["vocab"])    # 32 tokens
+    g = specv.spec_prefill(s.ctx, prompt)
+    with pytest.raises(E) as e:
+        specv.spec_verify(s.ctx, [g] + [1] * 16)     # K = 16
+    assert e.value.code == specv.SPEC_EINVAL
+    with pytest.raises(E) as e:
+        specv.spec_verify(s.ctx, [g, SHAPE["vocab"]])  # token out of range
+    assert e.value.code == specv.SPEC_EINVAL
+    with pytest.raises(E) as e:
+        specv.spec_rewind(s.ctx, 40)
+    assert e.value.code == specv.SPEC_ESTATE
+    specv.spec_verify(s.ctx, [g] + [3] * 14)          # 32 + 15 = 47 <= 48
+    n = specv.spec_cache_len(s.ctx)
+    with pytest.raises(E) as e:
+        specv.spec_verify(s.ctx, [g] * (48 - n + 1))  # would pass max_ctx
+    assert e.value.code == specv.SPEC_ECAPACITY
+    assert specv.spec_cache_len(s.ctx) == n           # refused, nothing changed
+    specv.spec_verify(s.ctx, [g])                     # still usable
+    s.close()
