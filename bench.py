@@ -1,0 +1,335 @@
+"""Benchmark of the verify transaction on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one speculative round of the whole hot path on the Qwen3-4B shape
+at batch 1: n-gram proposal over prompt + committed tokens, span upload, the
+verify forward (embedding, 36 x {RMSNorm, QKV + RoPE + KV write, attention,
+O + residual, RMSNorm, gate/up + SwiGLU, down + residual}, final norm, LM head
+with the fused per-row argmax), device-side accept_greedy and cache advance,
+and the host commit with adaptive K.  The prompt is 512 tokens of the
+repetition-heavy synthetic stream (random 16-48-token spans recurring 2-4
+times); the proposer drafts off matches of 2..4 tokens; K starts at 1, +2 on a
+full accept, -1 on a rejection, capped at 7.  W untimed rounds, then exactly K
+timed rounds; `value` is committed tokens per second over those K rounds.
+
+Also on the JSON line: the same rounds with drafting off (spec-off tok/s), the
+256-token end-to-end A/B of the page's protocol with the perfect- and
+all-wrong-draft bounds, the verify-cost sweep c_v(S) for S = 1..16 at an
+848-token context, the roofline of the dominant kernel (the gate/up GEMM:
+99.6 MB of bf16 weights per launch) and the CPU oracle timed on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "committed tok/s spec-on vs off (batch 1) + verify cost c_v(S=1..16), HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+PROMPT_TOKENS, CV_CTX = 512, 848
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "internal.h"):
+        with open(os.path.join(ROOT, "draft_verify_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, per_launch_bytes):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, when it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, prompt, budget_s=12.0, max_rounds=24):
+    """The oracle (plain fp32 C, OpenMP) on this host's cores: spec-on rounds
+    (n-gram proposer, adaptive K cap 7) from the same 512-token prompt; the
+    prefill is untimed.  Returns committed tokens per second over the rounds."""
+    import numpy as np
+    from draft_verify_amd import synth
+    from oracle import oracle as O
+    w = synth.to_numpy(synth.weights(shape, seed=0, device="cuda"))
+    orc = O.Oracle(shape, w, max_ctx=PROMPT_TOKENS + 256)
+    t = time.time()
+    g0, _ = orc.prefill(prompt)
+    prefill_s = time.time() - t
+    hist = [int(x) for x in prompt] + [g0]
+    k, committed, rounds = 1, 0, 0
+    t0 = time.time()
+    while rounds < max_rounds and time.time() - t0 < budget_s:
+        drafts = O.ngram_propose(hist, 2, 4, k)
+        am, m, _, _ = orc.verify([hist[-1]] + drafts)
+        hist += [int(x) for x in am[: m + 1]]
+        committed += m + 1
+        rounds += 1
+        k = O.adapt_k(k, len(drafts), m, 7)
+    dt = time.time() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(committed / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rounds} spec-on rounds ({committed} tokens) of the same workload after an "
+                      f"untimed {PROMPT_TOKENS}-token prefill ({prefill_s:.1f}s), fp32, "
+                      f"{len(os.sched_getaffinity(0))} host cores visible, {cpu}"}
+
+
+def counters_workload():
+    """Short workload for the rocprofv3 --pmc passes: ten S=1 verify forwards at
+    the 848-token context, then one device copy of exactly 1 GiB, whose
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["qwen3_4b"]
+    wg = synth.weights(shape, seed=0, device="cuda")
+    sess = specv.Session(shape, specv.tree_weights(wg), max_ctx=1024)
+    del wg
+    torch.cuda.empty_cache()
+    specv.spec_prefill(sess.ctx, synth.uniform_prompt(2, shape["vocab"], CV_CTX))
+    rng = np.random.default_rng(6)
+    specv.spec_time_verify(sess.ctx, rng.integers(0, shape["vocab"], (10, 1)).astype(np.int32))
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    sess.close()
+    print("counters workload done", flush=True)
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+GU_KERNEL = "k_gemm<16, 2>"
+
+
+def summarize_counters(fetch_csv, write_csv, out_dir):
+    """Per-launch HBM bytes of the gate/up GEMM from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the reading of
+    the 1 GiB calibration copy."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in _csv_rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "copyBuffer" in k)  # the runtime's device-to-device copy
+    gib_kib = (1 << 30) / 1024.0
+    f_scale = gib_kib / max(fetch[copy_name])
+    w_scale = gib_kib / max(write[copy_name])
+    gu = next(k for k in fetch if GU_KERNEL in k)
+    # the last 10 forwards' 36 launches are the S=1 timing loop
+    f_kib = sorted(fetch[gu][-360:])[180]
+    w_kib = sorted(write[gu][-360:])[180]
+    hbm = (f_kib * f_scale + w_kib * w_scale) * 1024.0
+    res = {"kernel_source_hash": kernel_source_hash(),
+           "calibration": {"kernel": copy_name[:60], "bytes": 1 << 30,
+                           "fetch_kib": max(fetch[copy_name]), "write_kib": max(write[copy_name]),
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {"gateup": {"name": gu[:60], "fetch_kib_median": f_kib, "write_kib_median": w_kib,
+                                  "hbm_bytes_per_launch": hbm,
+                                  "algorithmic_bytes_per_launch": 2 * 9728 * 2560 * 2}}}
+    with open(os.path.join(out_dir, "traffic_counters.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def summarize_trace(stats_csv, trace_csv, out_md, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = [r for r in _csv_rows(stats_csv) if "specv::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    tr = sorted((r for r in _csv_rows(trace_csv) if GU_KERNEL in r["Kernel_Name"]),
+                key=lambda r: int(r["Start_Timestamp"]))
+    last = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-180:]]
+    lines = [f"# rocprofv3 kernel summary", "", f"Command: `{command}`", "",
+             "| kernel | calls | total ms | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for r in rows[:12]:
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    if last:
+        lines += ["", f"Gate/up GEMM (`{GU_KERNEL}`), the last {len(last)} launches (the S=1 "
+                  f"back-to-back timing pass of bench.py, 5 passes x 36 layers): mean "
+                  f"{sum(last) / len(last):.2f} us, median {sorted(last)[len(last) // 2]:.2f} us."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cv-iters", type=int, default=30)
+    ap.add_argument("--counters", action="store_true", help="short workload for rocprofv3 --pmc passes")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
+    args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
+    if args.counters:
+        return counters_workload()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout "
+              f"is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+
+    shape = synth.SHAPES["qwen3_4b"]
+    K, W = args.steps, args.warmup
+    cap = 1 + 8 * (K + W)
+    max_ctx = max(1024, PROMPT_TOKENS + cap + 32, CV_CTX + 32)
+    t = time.time()
+    wg = synth.weights(shape, seed=0, device="cuda")
+    sess = specv.Session(shape, specv.tree_weights(wg), max_ctx=max_ctx)
+    del wg
+    torch.cuda.empty_cache()
+    ctx = sess.ctx
+    log(f"session ready in {time.time() - t:.1f}s")
+    prompt, pstats = synth.repetition_prompt(3, shape["vocab"], PROMPT_TOKENS, return_stats=True)
+
+    def timed_rounds(spec):
+        g = specv.spec_gen_handle(ctx, prompt, cap, spec=spec, fixed_k=0, k_cap=7, n_min=2, n_max=4)
+        g.step(W)
+        n0 = len(g.tokens())
+        f0 = g.stats()["forwards"]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        done = g.step(K)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        n1 = len(g.tokens())
+        st = g.stats()
+        g.close()
+        assert done == K, f"ran {done} of {K} rounds"
+        return (n1 - n0) / dt, dt, st, st["forwards"] - f0
+
+    on_tok_s, on_dt, on_st, _ = timed_rounds(True)
+    off_tok_s, off_dt, _, _ = timed_rounds(False)
+    log(f"timed {K} rounds: spec-on {on_tok_s:.1f} tok/s, spec-off {off_tok_s:.1f} tok/s")
+
+    # 256-token A/B of the end-to-end protocol, alternating pairs after one warm-up pair
+    e2e = {"off": [], "on": []}
+    streams_equal = True
+    for i in range(4):
+        off, s_off = specv.spec_generate(ctx, prompt, 256, spec=False)
+        on, s_on = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=0, k_cap=7)
+        streams_equal &= bool(np.array_equal(off, on))
+        if i:
+            e2e["off"].append(255 / s_off["decode_s"])
+            e2e["on"].append(255 / s_on["decode_s"])
+    _, s_perf = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=7,
+                                    draft_source=specv.SPEC_DRAFT_STREAM, ref_stream=off)
+    _, s_wrong = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=7,
+                                     draft_source=specv.SPEC_DRAFT_WRONG, ref_stream=off)
+    med = lambda v: float(np.median(v))
+    e2e_256 = {"off_tok_s": round(med(e2e["off"]), 2), "on_tok_s": round(med(e2e["on"]), 2),
+               "ratio": round(med(e2e["on"]) / med(e2e["off"]), 3),
+               "streams_equal": streams_equal, "forwards_on": s_on["forwards"],
+               "tok_per_forward_on": round(255 / s_on["forwards"], 3),
+               "accept_hist_on": s_on["accept_hist"][:8],
+               "forwards_by_span_on": s_on["forwards_by_span"][1:9],
+               "host_share_on": round(s_on["host_s"] / s_on["decode_s"], 4),
+               "perfect_drafts_k7_tok_s": round(255 / s_perf["decode_s"], 2),
+               "wrong_drafts_k7_tok_s": round(255 / s_wrong["decode_s"], 2),
+               "pairs": len(e2e["on"])}
+    log(f"e2e 256: {e2e_256}")
+
+    # verify-cost sweep at a fixed 848-token uniform context
+    specv.spec_prefill(ctx, synth.uniform_prompt(2, shape["vocab"], CV_CTX))
+    rng = np.random.default_rng(6)
+    cv_ms = []
+    for S in range(1, 17):
+        ms = specv.spec_time_verify(ctx, rng.integers(0, shape["vocab"], (args.cv_iters + 5, S)).astype(np.int32))
+        cv_ms.append(float(np.median(ms[5:])))
+    d = sess.desc
+    fwd_bytes = []
+    for S in range(1, 17):
+        b = specv.spec_op_bytes(d, "lm", S, CV_CTX) + specv.spec_op_bytes(d, "embed", S, CV_CTX)
+        b += shape["n_layers"] * sum(specv.spec_op_bytes(d, op, S, CV_CTX)
+                                     for op in ("qkv", "attn", "o", "gateup", "down"))
+        fwd_bytes.append(b)
+    cv = {"ctx": CV_CTX, "ms": [round(x, 4) for x in cv_ms],
+          "c_v": [round(x / cv_ms[0], 3) for x in cv_ms],
+          "gbps": [round(b / (x * 1e-3) / 1e9, 1) for b, x in zip(fwd_bytes, cv_ms)],
+          "hbm_frac_S1": round(fwd_bytes[0] / (cv_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"c_v: {cv['c_v']}")
+
+    # roofline of the dominant kernel: each op class launched back to back
+    # (5 passes over the 36 layers) between HIP events on the library stream
+    per_op = {op: specv.spec_time_op(ctx, op, 1, 5) for op in specv.OPS}
+    gu_us = per_op["gateup"]
+    gu_bytes = specv.spec_op_bytes(d, "gateup", 1, CV_CTX)
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    traffic = measured_traffic("gateup", gu_bytes)
+    roofline = {"bound": "hbm", "kernel": "k_gemm<16,2> (gate/up + SwiGLU, S=1)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3),
+                "per_op_us_S1": {k: round(v, 2) for k, v in per_op.items()}}
+    log(f"roofline: {roofline}")
+    sess.close()
+    del sess
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, prompt)
+        log(f"cpu baseline: {cpu}")
+
+    line = {"metric": METRIC, "value": round(on_tok_s, 3), "unit": "tok/s", "n_gpus": 1,
+            "steps": K, "warmup": W, "ms_per_step": round(on_dt / K * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic: seeded N(0,0.02) bf16 random-init weights; repetition-heavy "
+                    f"{PROMPT_TOKENS}-token prompt ({pstats['repeated_fraction']:.2f} of tokens in "
+                    "repeated spans); uniform 848-token context for c_v",
+            "config": {"workload": "Qwen3-4B-shaped verify transaction (36 layers, hidden 2560, "
+                                   "32q/8kv heads x 128, FFN 9728, vocab 151936), batch 1, "
+                                   f"{PROMPT_TOKENS}-token repetition-heavy prompt, n-gram proposer "
+                                   "(match 2..4), adaptive K (1, +2, -1, cap 7)",
+                       "batch": 1, "prompt_tokens": PROMPT_TOKENS, "parallelism": "single GPU"},
+            "spec_off_tok_s": round(off_tok_s, 3), "speedup": round(on_tok_s / off_tok_s, 4),
+            "tok_per_forward": round((on_st["accepted"] + on_st["forwards"]) / on_st["forwards"], 3),
+            "e2e_256": e2e_256, "cv": cv, "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,10 @@ __device__ __forceinline__ float2 ld_dev2(const float* p) {  // 8-byte aligned p
   const unsigned long long v = __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
+__device__ __forceinline__ void st_dev2(float* p, float a, float b) {  // 8-byte aligned pair
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Order-preserving key of (value, column): larger value wins, then the lower
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   const int DQ = P.n_q * HD;
 
   __shared__ float sO[4][16][HD + 1];
-  __shared__ float sM[4][16], sL[4][16];
+  __shared__ float sM[4][16], sL[4][16], sF[4][16];
   __shared__ int sLast;
 
   // This wave's four blocks, loaded once and reused for every query tile.
@@ -484,29 +488,41 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
       sL[wave][c16] = l;
     }
     __syncthreads();
-    // Combine the four chunks of this split, in wave order.
-    for (int e = tid; e < 16 * HD; e += 256) {
-      const int c = e / HD, d = e % HD;
-      const int qcol = qt * 16 + c;
-      if (qcol >= QC) continue;
+    // Combine the four chunks of this split, in wave order: the weight of
+    // each (wave, column) once, then the values.
+    if (tid < 16) {
+      const int c = tid;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][c]);
-      float L = 0.0f, O = 0.0f;
-      if (M != -INFINITY) {
+      float L = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float f = expf(sM[w][c] - M);
-          L += sL[w][c] * f;
-          O += sO[w][c][d] * f;
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float f = (M == -INFINITY) ? 0.0f : expf(sM[w][c] - M);
+        sF[w][c] = f;
+        L += sL[w][c] * f;
       }
-      float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-      st_dev(dst + 2 + d, O);
-      if (d == 0) {
+      const int qcol = qt * 16 + c;
+      if (qcol < QC) {
+        float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
         st_dev(dst, M);
         st_dev(dst + 1, L);
       }
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * (HD / 2); e += 256) {
+      const int c = e / (HD / 2), d = 2 * (e % (HD / 2));
+      const int qcol = qt * 16 + c;
+      if (qcol >= QC) continue;
+      float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = sF[w][c];
+        o0 += sO[w][c][d] * f;
+        o1 += sO[w][c][d + 1] * f;
+      }
+      float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+      st_dev2(dst + 2 + d, o0, o1);
     }
     __syncthreads();
   }

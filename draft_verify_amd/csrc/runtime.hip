@@ -67,7 +67,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   };
   if (d.n_layers <= 0 || d.hidden <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.ffn <= 0 || d.vocab <= 0)
     return fail("model dimensions must be positive");
-  if (d.weight_format != SPEC_WFMT_BF16) return fail("only SPEC_WFMT_BF16 weights are supported by this build");
+  if (d.weight_format != SPEC_WFMT_BF16) return fail("only SPEC_WFMT_BF16 weights are supported by this library version");
   if (!(d.head_dim == 16 || d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128))
     return fail("head_dim must be 16, 32, 64 or 128");
   if (d.n_q_heads % d.n_kv_heads) return fail("n_q_heads must be a multiple of n_kv_heads");
@@ -279,113 +279,135 @@ int mark(spec_ctx* c, OpTimer* t, int op) {
     if (rc_ != SPEC_OK) return rc_; \
   } while (0)
 
-int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
+// Launch one kernel of the forward: op class `op` of layer `l` (embed and LM
+// ignore l) for n_seq sequences of S rows.
+int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
   const Layout& L = c->lo;
   const int R = n_seq * S;
   const StepDev* sd = c->ws<StepDev>(L.step);
   const int32_t* tokens = (const int32_t*)(sd + 1);
   const int32_t* seq_ids = tokens + L.max_rows;
   hipStream_t st = c->st;
-
-  EmbedParams ep;
-  ep.emb = (const uint16_t*)(c->W + L.emb);
-  ep.tokens = tokens;
-  ep.x = c->ws<float>(L.x);
-  ep.ss = c->ws<float>(L.ss);
-  ep.H = L.H;
-  STEP(mark(c, tm, SPEC_OP_EMBED));
-  HIPCHK(c, launch_embed(ep, R, st));
-
-  for (int l = 0; l < L.L; ++l) {
-    const LayerOff& lw = L.lay[(size_t)l];
-    // QKV + RoPE + KV write
-    GemmParams g = gemm_common(c, c->W + lw.wqkv, L.Nqkv, L.H, L.nk_qkv, R);
-    g.A = c->ws<float>(L.x);
-    g.lda = L.H;
-    g.ss = c->ws<float>(L.ss);
-    g.ss_n = L.H / 64;
-    g.gain = (const float*)(c->W + lw.g_attn);
-    g.q = c->ws<float>(L.q);
-    g.kpool = c->kpool(l);
-    g.vpool = c->vpool(l);
-    g.bt = c->ws<int32_t>(L.bt);
-    g.bt_stride = L.bt_stride;
-    g.kv_len = c->ws<int32_t>(L.kv_len);
-    g.seq_ids = seq_ids;
-    g.S = S;
-    g.n_q = L.nq;
-    g.n_kv = L.nkv;
-    g.hd = L.hd;
-    g.rope = c->ws<float>(L.rope);
-    STEP(mark(c, tm, SPEC_OP_QKV));
-    HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, st));
-
-    AttnParams a;
-    a.q = c->ws<float>(L.q);
-    a.kpool = c->kpool(l);
-    a.vpool = c->vpool(l);
-    a.bt = c->ws<int32_t>(L.bt);
-    a.bt_stride = L.bt_stride;
-    a.kv_len = c->ws<int32_t>(L.kv_len);
-    a.seq_ids = seq_ids;
-    a.S = S;
-    a.n_seq = n_seq;
-    a.n_q = L.nq;
-    a.n_kv = L.nkv;
-    a.scale = (float)(1.0 / sqrt((double)L.hd));
-    a.max_splits = L.max_splits;
-    a.part = c->ws<float>(L.apart);
-    a.cnt = c->ws<unsigned>(L.attn_cnt);
-    a.out = c->ws<float>(L.o);
-    STEP(mark(c, tm, SPEC_OP_ATTN));
-    HIPCHK(c, launch_attn(a, L.hd, st));
-
-    GemmParams go = gemm_common(c, c->W + lw.wo, L.H, L.DQ, L.nk_o, R);
-    go.A = c->ws<float>(L.o);
-    go.lda = L.DQ;
-    go.x = c->ws<float>(L.x);
-    go.ss_out = c->ws<float>(L.ss);
-    STEP(mark(c, tm, SPEC_OP_O));
-    HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, st));
-
-    GemmParams gu = gemm_common(c, c->W + lw.wgu, L.Ngu, L.H, L.nk_gu, R);
-    gu.A = c->ws<float>(L.x);
-    gu.lda = L.H;
-    gu.ss = c->ws<float>(L.ss);
-    gu.ss_n = L.H / 64;
-    gu.gain = (const float*)(c->W + lw.g_ffn);
-    gu.h = c->ws<float>(L.h);
-    STEP(mark(c, tm, SPEC_OP_GATEUP));
-    HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, st));
-
-    GemmParams gd = gemm_common(c, c->W + lw.wd, L.H, L.F, L.nk_d, R);
-    gd.A = c->ws<float>(L.h);
-    gd.lda = L.F;
-    gd.x = c->ws<float>(L.x);
-    gd.ss_out = c->ws<float>(L.ss);
-    STEP(mark(c, tm, SPEC_OP_DOWN));
-    HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, st));
+  if (op == SPEC_OP_EMBED) {
+    EmbedParams ep;
+    ep.emb = (const uint16_t*)(c->W + L.emb);
+    ep.tokens = tokens;
+    ep.x = c->ws<float>(L.x);
+    ep.ss = c->ws<float>(L.ss);
+    ep.H = L.H;
+    HIPCHK(c, launch_embed(ep, R, st));
+    return SPEC_OK;
   }
+  if (op == SPEC_OP_LM) {
+    GemmParams gl = gemm_common(c, c->W + L.wlm, L.V, L.H, L.nk_lm, R);
+    gl.A = c->ws<float>(L.x);
+    gl.lda = L.H;
+    gl.ss = c->ws<float>(L.ss);
+    gl.ss_n = L.H / 64;
+    gl.gain = (const float*)(c->W + L.g_final);
+    gl.argkey = c->ws<unsigned long long>(L.argkey);
+    gl.lm_cnt = c->ws<unsigned>(L.lm_cnt);
+    gl.status = c->ws<int32_t>(L.status);
+    gl.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
+    gl.tokens = tokens;
+    gl.mode = &sd->mode;
+    gl.result = c->ws<int32_t>(L.result);
+    gl.kv_len_w = c->ws<int32_t>(L.kv_len);
+    gl.seq_ids = seq_ids;
+    gl.S = S;
+    gl.n_seq = n_seq;
+    HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, st));
+    return SPEC_OK;
+  }
+  const LayerOff& lw = L.lay[(size_t)l];
+  switch (op) {
+    case SPEC_OP_QKV: {  // QKV + RoPE + KV write
+      GemmParams g = gemm_common(c, c->W + lw.wqkv, L.Nqkv, L.H, L.nk_qkv, R);
+      g.A = c->ws<float>(L.x);
+      g.lda = L.H;
+      g.ss = c->ws<float>(L.ss);
+      g.ss_n = L.H / 64;
+      g.gain = (const float*)(c->W + lw.g_attn);
+      g.q = c->ws<float>(L.q);
+      g.kpool = c->kpool(l);
+      g.vpool = c->vpool(l);
+      g.bt = c->ws<int32_t>(L.bt);
+      g.bt_stride = L.bt_stride;
+      g.kv_len = c->ws<int32_t>(L.kv_len);
+      g.seq_ids = seq_ids;
+      g.S = S;
+      g.n_q = L.nq;
+      g.n_kv = L.nkv;
+      g.hd = L.hd;
+      g.rope = c->ws<float>(L.rope);
+      HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, st));
+      return SPEC_OK;
+    }
+    case SPEC_OP_ATTN: {
+      AttnParams a;
+      a.q = c->ws<float>(L.q);
+      a.kpool = c->kpool(l);
+      a.vpool = c->vpool(l);
+      a.bt = c->ws<int32_t>(L.bt);
+      a.bt_stride = L.bt_stride;
+      a.kv_len = c->ws<int32_t>(L.kv_len);
+      a.seq_ids = seq_ids;
+      a.S = S;
+      a.n_seq = n_seq;
+      a.n_q = L.nq;
+      a.n_kv = L.nkv;
+      a.scale = (float)(1.0 / sqrt((double)L.hd));
+      a.max_splits = L.max_splits;
+      a.part = c->ws<float>(L.apart);
+      a.cnt = c->ws<unsigned>(L.attn_cnt);
+      a.out = c->ws<float>(L.o);
+      HIPCHK(c, launch_attn(a, L.hd, st));
+      return SPEC_OK;
+    }
+    case SPEC_OP_O: {
+      GemmParams go = gemm_common(c, c->W + lw.wo, L.H, L.DQ, L.nk_o, R);
+      go.A = c->ws<float>(L.o);
+      go.lda = L.DQ;
+      go.x = c->ws<float>(L.x);
+      go.ss_out = c->ws<float>(L.ss);
+      HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, st));
+      return SPEC_OK;
+    }
+    case SPEC_OP_GATEUP: {
+      GemmParams gu = gemm_common(c, c->W + lw.wgu, L.Ngu, L.H, L.nk_gu, R);
+      gu.A = c->ws<float>(L.x);
+      gu.lda = L.H;
+      gu.ss = c->ws<float>(L.ss);
+      gu.ss_n = L.H / 64;
+      gu.gain = (const float*)(c->W + lw.g_ffn);
+      gu.h = c->ws<float>(L.h);
+      HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, st));
+      return SPEC_OK;
+    }
+    case SPEC_OP_DOWN: {
+      GemmParams gd = gemm_common(c, c->W + lw.wd, L.H, L.F, L.nk_d, R);
+      gd.A = c->ws<float>(L.h);
+      gd.lda = L.F;
+      gd.x = c->ws<float>(L.x);
+      gd.ss_out = c->ws<float>(L.ss);
+      HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, st));
+      return SPEC_OK;
+    }
+  }
+  return set_err(c, SPEC_EINVAL, "unknown op class");
+}
 
-  GemmParams gl = gemm_common(c, c->W + L.wlm, L.V, L.H, L.nk_lm, R);
-  gl.A = c->ws<float>(L.x);
-  gl.lda = L.H;
-  gl.ss = c->ws<float>(L.ss);
-  gl.ss_n = L.H / 64;
-  gl.gain = (const float*)(c->W + L.g_final);
-  gl.argkey = c->ws<unsigned long long>(L.argkey);
-  gl.lm_cnt = c->ws<unsigned>(L.lm_cnt);
-  gl.status = c->ws<int32_t>(L.status);
-  gl.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
-  gl.tokens = tokens;
-  gl.mode = &sd->mode;
-  gl.result = c->ws<int32_t>(L.result);
-  gl.kv_len_w = c->ws<int32_t>(L.kv_len);
-  gl.seq_ids = seq_ids;
-  gl.S = S;
-  gl.n_seq = n_seq;
+int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
+  STEP(mark(c, tm, SPEC_OP_EMBED));
+  STEP(launch_op(c, SPEC_OP_EMBED, 0, n_seq, S));
+  for (int l = 0; l < c->lo.L; ++l) {
+    for (int op : {SPEC_OP_QKV, SPEC_OP_ATTN, SPEC_OP_O, SPEC_OP_GATEUP, SPEC_OP_DOWN}) {
+      STEP(mark(c, tm, op));
+      STEP(launch_op(c, op, l, n_seq, S));
+    }
+  }
   STEP(mark(c, tm, SPEC_OP_LM));
-  HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, st));
+  STEP(launch_op(c, SPEC_OP_LM, 0, n_seq, S));
   STEP(mark(c, tm, -1));
   return SPEC_OK;
 }
@@ -832,6 +854,43 @@ int spec_profile_ops(spec_ctx* c, int S, int iters, const int32_t* spans, float*
   return SPEC_OK;
 }
 
+int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
+  if (!c || !us_out || reps <= 0) return c ? set_err(c, SPEC_EINVAL, "bad timing arguments") : SPEC_EINVAL;
+  if (op < 0 || op >= SPEC_OP_COUNT) return set_err(c, SPEC_EINVAL, "unknown op class");
+  if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
+  STEP(check_ready(c));
+  if (!c->live[0]) return set_err(c, SPEC_ESTATE, "timing before prefill");
+  if (c->len[0] + S > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
+  bool dirty = false;
+  STEP(ensure_blocks(c, 0, c->len[0] + S, &dirty));
+  if (dirty) STEP(upload_bt_row(c, 0));
+  std::vector<int32_t> span((size_t)S, 0);
+  const int32_t sid = 0;
+  STEP(upload_step(c, MODE_NO_COMMIT, 1, S, span.data(), &sid));
+  const bool per_layer = !(op == SPEC_OP_EMBED || op == SPEC_OP_LM);
+  const int per_rep = per_layer ? c->lo.L : 1;
+  // one untimed pass, then the timed passes back to back
+  for (int l = 0; l < per_rep; ++l) STEP(launch_op(c, op, l, 1, S));
+  hipEvent_t e0, e1;
+  HIPCHK(c, hipEventCreate(&e0));
+  HIPCHK(c, hipEventCreate(&e1));
+  int rc = SPEC_OK;
+  hipError_t e = hipEventRecord(e0, c->st);
+  for (int r = 0; r < reps && rc == SPEC_OK && e == hipSuccess; ++r)
+    for (int l = 0; l < per_rep && rc == SPEC_OK; ++l) rc = launch_op(c, op, l, 1, S);
+  if (rc == SPEC_OK && e == hipSuccess) e = hipEventRecord(e1, c->st);
+  if (rc == SPEC_OK && e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (rc == SPEC_OK && e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  trim_blocks(c, 0, c->len[0]);
+  if (rc != SPEC_OK) return rc;
+  if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("timing: ") + hipGetErrorString(e));
+  *us_out = ms * 1000.0f / (float)(reps * per_rep);
+  return SPEC_OK;
+}
+
 int spec_op_bytes(const spec_model_desc* d, int op, int S, int ctx_len, double* bytes_out) {
   if (!d || !bytes_out || S < 1 || ctx_len < 0) return SPEC_EINVAL;
   const double H = d->hidden, hd = d->head_dim, DQ = (double)d->n_q_heads * hd, DK = (double)d->n_kv_heads * hd;
@@ -852,55 +911,77 @@ int spec_op_bytes(const spec_model_desc* d, int op, int S, int ctx_len, double* 
 
 // ------------------------------------------------------------ generation
 
-int spec_generate(spec_ctx* c, const int32_t* prompt, int n_prompt, int n_tokens, const spec_gen_params* gp,
-                  int32_t* out, spec_gen_stats* gs) {
-  using clk = std::chrono::steady_clock;
+}  // extern "C"
+
+struct spec_gen {
+  spec_ctx* c;
+  spec_gen_params gp;
+  int capacity, kcap, k;
+  spec_ngram* ng;
+  std::vector<int32_t> out;
+  ~spec_gen() { spec_ngram_destroy(ng); }
+};
+
+extern "C" {
+
+int spec_gen_begin(spec_ctx* c, const int32_t* prompt, int n_prompt, int capacity, const spec_gen_params* gp,
+                   spec_gen** res) {
   if (!c) return SPEC_EINVAL;
-  if (!prompt || n_prompt <= 0 || n_tokens <= 0 || !gp || !out || !gs)
+  if (!prompt || n_prompt <= 0 || capacity <= 0 || !gp || !res)
     return set_err(c, SPEC_EINVAL, "bad generation arguments");
   if (gp->spec && gp->draft_source != SPEC_DRAFT_NGRAM && !gp->ref_stream)
     return set_err(c, SPEC_EINVAL, "draft source needs ref_stream");
-  const int kcap = std::max(1, std::min(gp->fixed_k > 0 ? gp->fixed_k : gp->k_cap, SPEC_MAX_SPAN - 1));
-  memset(gs, 0, sizeof(*gs));
-  spec_ngram* ng = nullptr;
-  if (gp->spec && gp->draft_source == SPEC_DRAFT_NGRAM) {
-    int rc = spec_ngram_create(gp->n_min, gp->n_max, n_prompt + n_tokens + 1, &ng);
-    if (rc != SPEC_OK) return set_err(c, rc, "n-gram proposer arguments");
+  spec_gen* g = new (std::nothrow) spec_gen;
+  if (!g) return set_err(c, SPEC_ECAPACITY, "out of host memory");
+  g->c = c;
+  g->gp = *gp;
+  g->capacity = capacity;
+  g->kcap = std::max(1, std::min(gp->fixed_k > 0 ? gp->fixed_k : gp->k_cap, SPEC_MAX_SPAN - 1));
+  g->k = gp->fixed_k > 0 ? std::min(gp->fixed_k, SPEC_MAX_SPAN - 1) : 1;
+  g->ng = nullptr;
+  int rc = SPEC_OK;
+  if (gp->spec && gp->draft_source == SPEC_DRAFT_NGRAM)
+    rc = spec_ngram_create(gp->n_min, gp->n_max, n_prompt + capacity + 1, &g->ng);
+  int32_t g0 = 0;
+  if (rc == SPEC_OK) rc = spec_prefill(c, prompt, n_prompt, &g0);
+  if (rc == SPEC_OK && g->ng) rc = spec_ngram_append(g->ng, prompt, n_prompt);
+  if (rc == SPEC_OK && g->ng) rc = spec_ngram_append(g->ng, &g0, 1);
+  if (rc != SPEC_OK) {
+    delete g;
+    return rc;
   }
-  struct Guard {
-    spec_ngram* ng;
-    ~Guard() { spec_ngram_destroy(ng); }
-  } guard{ng};
-  const auto t0 = clk::now();
-  int32_t g0;
-  STEP(spec_prefill(c, prompt, n_prompt, &g0));
-  const auto t1 = clk::now();
-  gs->prefill_s = std::chrono::duration<double>(t1 - t0).count();
-  if (ng) {
-    STEP(spec_ngram_append(ng, prompt, n_prompt));
-    STEP(spec_ngram_append(ng, &g0, 1));
-  }
-  int n = 0;
-  out[n++] = g0;
-  int k = gp->fixed_k > 0 ? gp->fixed_k : 1;
+  g->out.reserve((size_t)capacity);
+  g->out.push_back(g0);
+  *res = g;
+  return SPEC_OK;
+}
+
+int spec_gen_step(spec_gen* g, int rounds, spec_gen_stats* gs) {
+  using clk = std::chrono::steady_clock;
+  if (!g || !gs || rounds < 0) return SPEC_EINVAL;
+  spec_ctx* c = g->c;
+  const spec_gen_params& gp = g->gp;
   int32_t span[SPEC_MAX_SPAN], am[SPEC_MAX_SPAN];
+  const auto t0 = clk::now();
   double in_verify = 0.0;
-  while (n < n_tokens) {
+  int done = 0;
+  while (done < rounds && (int)g->out.size() < g->capacity) {
+    const int n = (int)g->out.size();
     int kd = 0;
-    if (gp->spec) {
-      const int want = std::max(0, std::min(k, n_tokens - n - 1));
-      if (gp->draft_source == SPEC_DRAFT_NGRAM) {
-        kd = spec_ngram_propose(ng, want, span + 1);
+    if (gp.spec) {
+      const int want = std::max(0, std::min(g->k, g->capacity - n - 1));
+      if (gp.draft_source == SPEC_DRAFT_NGRAM) {
+        kd = spec_ngram_propose(g->ng, want, span + 1);
         if (kd < 0) return set_err(c, kd, "n-gram propose");
       } else {
-        kd = std::min(want, n_tokens - n);
+        kd = want;
         for (int i = 0; i < kd; ++i) {
-          const int32_t t = gp->ref_stream[n + i];
-          span[1 + i] = gp->draft_source == SPEC_DRAFT_WRONG ? (t + 1) % c->lo.V : t;
+          const int32_t t = gp.ref_stream[n + i];
+          span[1 + i] = gp.draft_source == SPEC_DRAFT_WRONG ? (t + 1) % c->lo.V : t;
         }
       }
     }
-    span[0] = out[n - 1];
+    span[0] = g->out.back();
     int32_t m = 0;
     const int p = c->len[0];
     const auto tv = clk::now();
@@ -912,18 +993,47 @@ int spec_generate(spec_ctx* c, const int32_t* prompt, int n_prompt, int n_tokens
     gs->accept_hist[m]++;
     gs->forwards_by_span[kd + 1]++;
     int commit = m + 1;
-    if (commit > n_tokens - n) {  // never expected: drafts are capped by the budget
-      commit = n_tokens - n;
+    if (commit > g->capacity - n) {  // not expected: drafts never pass the budget
+      commit = g->capacity - n;
       STEP(spec_rewind(c, p + commit));
     }
-    for (int i = 0; i < commit; ++i) out[n++] = am[i];
-    if (ng) STEP(spec_ngram_append(ng, am, commit));
-    if (gp->spec && gp->fixed_k <= 0) k = spec_adapt_k(k, kd, m, kcap);
+    for (int i = 0; i < commit; ++i) g->out.push_back(am[i]);
+    if (g->ng) STEP(spec_ngram_append(g->ng, am, commit));
+    if (gp.spec && gp.fixed_k <= 0) g->k = spec_adapt_k(g->k, kd, m, g->kcap);
+    ++done;
   }
-  const auto t2 = clk::now();
-  gs->decode_s = std::chrono::duration<double>(t2 - t1).count();
-  gs->host_s = gs->decode_s - in_verify;
+  const double dt = std::chrono::duration<double>(clk::now() - t0).count();
+  gs->decode_s += dt;
+  gs->host_s += dt - in_verify;
+  return done;
+}
+
+int spec_gen_tokens(spec_gen* g, int32_t* out, int cap) {
+  if (!g || (cap > 0 && !out) || cap < 0) return SPEC_EINVAL;
+  const int n = std::min(cap, (int)g->out.size());
+  if (n > 0) memcpy(out, g->out.data(), sizeof(int32_t) * (size_t)n);
+  return (int)g->out.size();
+}
+
+int spec_gen_end(spec_gen* g) {
+  delete g;
   return SPEC_OK;
+}
+
+int spec_generate(spec_ctx* c, const int32_t* prompt, int n_prompt, int n_tokens, const spec_gen_params* gp,
+                  int32_t* out, spec_gen_stats* gs) {
+  using clk = std::chrono::steady_clock;
+  if (!c) return SPEC_EINVAL;
+  if (!out || !gs) return set_err(c, SPEC_EINVAL, "bad generation arguments");
+  memset(gs, 0, sizeof(*gs));
+  const auto t0 = clk::now();
+  spec_gen* g = nullptr;
+  STEP(spec_gen_begin(c, prompt, n_prompt, n_tokens, gp, &g));
+  gs->prefill_s = std::chrono::duration<double>(clk::now() - t0).count();
+  const int rc = spec_gen_step(g, n_tokens, gs);
+  if (rc >= 0) spec_gen_tokens(g, out, n_tokens);
+  spec_gen_end(g);
+  return rc < 0 ? rc : SPEC_OK;
 }
 
 }  // extern "C"

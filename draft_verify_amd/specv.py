@@ -111,6 +111,7 @@ def lib():
         "spec_time_verify": [P, I, I, i32p, f32p],
         "spec_profile_ops": [P, I, I, i32p, f32p, i32p],
         "spec_op_bytes": [C.POINTER(spec_model_desc), I, I, I, dp],
+        "spec_time_op": [P, I, I, I, f32p],
         "spec_ngram_create": [I, I, I, C.POINTER(P)],
         "spec_ngram_destroy": [P],
         "spec_ngram_append": [P, i32p, I],
@@ -119,6 +120,10 @@ def lib():
         "spec_ngram_propose": [P, I, i32p],
         "spec_adapt_k": [I, I, I, I],
         "spec_generate": [P, i32p, I, I, C.POINTER(spec_gen_params), i32p, C.POINTER(spec_gen_stats)],
+        "spec_gen_begin": [P, i32p, I, I, C.POINTER(spec_gen_params), C.POINTER(P)],
+        "spec_gen_step": [P, I, C.POINTER(spec_gen_stats)],
+        "spec_gen_tokens": [P, i32p, I],
+        "spec_gen_end": [P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -266,6 +271,12 @@ def spec_profile_ops(ctx, spans):
     return {OPS[i]: (float(us[i]), int(n[i])) for i in range(SPEC_OP_COUNT)}
 
 
+def spec_time_op(ctx, op, S, reps):
+    us = C.c_float()
+    _check(lib().spec_time_op(ctx, OPS.index(op) if isinstance(op, str) else op, S, reps, C.byref(us)), ctx)
+    return us.value
+
+
 def spec_op_bytes(desc, op, S, ctx_len):
     b = C.c_double()
     _check(lib().spec_op_bytes(C.byref(desc), OPS.index(op) if isinstance(op, str) else op, S, ctx_len,
@@ -317,10 +328,54 @@ def spec_generate(ctx, prompt, n_tokens, spec=True, fixed_k=0, k_cap=7, n_min=2,
                              refp if ref is not None else None)
     st = spec_gen_stats()
     _check(lib().spec_generate(ctx, pp, len(p), n_tokens, C.byref(params), op, C.byref(st)), ctx)
-    stats = {"forwards": st.forwards, "drafted": st.drafted, "accepted": st.accepted,
-             "accept_hist": list(st.accept_hist), "forwards_by_span": list(st.forwards_by_span),
-             "decode_s": st.decode_s, "host_s": st.host_s, "prefill_s": st.prefill_s}
-    return out.copy(), stats
+    return out.copy(), _gen_stats_dict(st)
+
+
+def _gen_stats_dict(st):
+    return {"forwards": st.forwards, "drafted": st.drafted, "accepted": st.accepted,
+            "accept_hist": list(st.accept_hist), "forwards_by_span": list(st.forwards_by_span),
+            "decode_s": st.decode_s, "host_s": st.host_s, "prefill_s": st.prefill_s}
+
+
+class spec_gen_handle:
+    """spec_gen_begin / spec_gen_step / spec_gen_tokens / spec_gen_end."""
+
+    def __init__(self, ctx, prompt, capacity, spec=True, fixed_k=0, k_cap=7, n_min=2, n_max=4,
+                 draft_source=SPEC_DRAFT_NGRAM, ref_stream=None):
+        self.ctx = ctx
+        self._p, pp = _i32(prompt)
+        self._ref = None
+        refp = None
+        if ref_stream is not None:
+            self._ref, refp = _i32(ref_stream)
+        self.params = spec_gen_params(int(spec), fixed_k, k_cap, n_min, n_max, draft_source, refp)
+        h = C.c_void_p()
+        _check(lib().spec_gen_begin(ctx, pp, len(self._p), capacity, C.byref(self.params), C.byref(h)), ctx)
+        self.h = h.value
+        self.capacity = capacity
+        self.st = spec_gen_stats()
+
+    def step(self, rounds):
+        return _check(lib().spec_gen_step(self.h, rounds, C.byref(self.st)), self.ctx)
+
+    def stats(self):
+        return _gen_stats_dict(self.st)
+
+    def tokens(self):
+        out, op = _i32(np.zeros(self.capacity, np.int32))
+        n = _check(lib().spec_gen_tokens(self.h, op, self.capacity), self.ctx)
+        return out[:n].copy()
+
+    def close(self):
+        if self.h:
+            lib().spec_gen_end(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ----------------------------------------------------------------- session

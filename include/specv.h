@@ -192,6 +192,13 @@ SPEC_API int spec_time_verify(spec_ctx* ctx, int S, int iters, const int32_t* sp
 SPEC_API int spec_profile_ops(spec_ctx* ctx, int S, int iters, const int32_t* spans, float* us_out,
                      int32_t* launches_out);
 
+/* Mean microseconds per launch of one op class launched back to back: `reps`
+ * passes over every layer (one launch per pass for EMBED and LM) at span S on
+ * sequence 0's current cache, timed with HIP events around the passes on the
+ * context stream (no commit).  The KV rows of positions p..p+S-1 are
+ * rewritten, as a verify would. */
+SPEC_API int spec_time_op(spec_ctx* ctx, int op, int S, int reps, float* us_per_launch);
+
 /* Algorithmic bytes one launch of an op class streams at span S and cache
  * length ctx_len (weights, KV reads and writes; activations excluded). */
 SPEC_API int spec_op_bytes(const spec_model_desc* desc, int op, int S, int ctx_len, double* bytes_out);
@@ -248,6 +255,20 @@ typedef struct spec_gen_stats {
  * No round drafts past the budget.  out_tokens: [n_tokens]. */
 SPEC_API int spec_generate(spec_ctx* ctx, const int32_t* prompt, int n_prompt, int n_tokens,
                   const spec_gen_params* params, int32_t* out_tokens, spec_gen_stats* stats);
+
+/* The same loop in resumable form.  spec_gen_begin prefills `prompt` on
+ * sequence 0 and commits g0 (budget: `capacity` committed tokens, g0
+ * included; ref_stream, if used, must hold `capacity` tokens and outlive the
+ * handle).  spec_gen_step runs up to `rounds` propose -> verify -> commit
+ * rounds, stopping early at the budget, adds its counts and times to *stats
+ * and returns the number of rounds run.  spec_gen_tokens copies the committed
+ * tokens (up to cap) and returns how many there are. */
+typedef struct spec_gen spec_gen;
+SPEC_API int spec_gen_begin(spec_ctx* ctx, const int32_t* prompt, int n_prompt, int capacity,
+                   const spec_gen_params* params, spec_gen** out);
+SPEC_API int spec_gen_step(spec_gen* gen, int rounds, spec_gen_stats* stats);
+SPEC_API int spec_gen_tokens(spec_gen* gen, int32_t* out, int cap);
+SPEC_API int spec_gen_end(spec_gen* gen);
 
 #ifdef __cplusplus
 }
