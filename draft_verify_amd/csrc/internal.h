@@ -92,6 +92,43 @@ struct EmbedParams {
   int H;
 };
 
+// Everything one persistent forward launch needs (forward.hip).
+struct FwdParams {
+  // shape
+  int L, H, nq, nkv, hd, F, V, DQ, DK, Nqkv, Ngu;
+  int R, S, n_seq;       // rows of this forward, rows per sequence, sequences
+  int nk_h, nk_o, nk_d;  // 32-input steps per K slice for K = H, n_q*hd, F
+  float eps, inv_dim, scale;
+  int max_splits, bt_stride;
+  // weights: one arena, layers at a fixed stride
+  const uint8_t* W;
+  size_t lay_stride, off_wqkv, off_wo, off_wgu, off_wd, off_gattn, off_gffn;
+  const uint16_t* emb;
+  const void* wlm;
+  const float* g_final;
+  // KV pool: per layer K blocks then V blocks
+  uint8_t* KV;
+  size_t kv_layer_bytes, kv_half_bytes;
+  // activations and scratch (workspace)
+  float *x, *ss, *q, *o, *h, *part, *apart, *logits;
+  const float* rope;
+  unsigned *cnt, *attn_cnt, *lm_cnt, *done, *exit_cnt;
+  int n_phases;
+  unsigned long long* argkey;
+  int32_t *status, *err;
+  unsigned long long* clock;  // per-phase start stamps of workgroup 0, or null
+  // step
+  const StepDev* step;
+  const int32_t *tokens, *seq_ids;
+  int32_t* kv_len;
+  const int32_t* bt;
+  int32_t* result;
+};
+
+bool forward_supported(int nk_h, int nk_o, int nk_d, int hd);
+int forward_occupancy(int nk_h, int nk_o, int nk_d, int hd);
+hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
+
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);

@@ -55,7 +55,8 @@ struct Layout {
   size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
   // workspace
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
-      logits, workspace_bytes;
+      logits, done, exit_cnt, err, clock, workspace_bytes;
+  int n_phases;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
 };
@@ -89,9 +90,14 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.nk_d = slice_steps(Lo.F); Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
-  // the attention split-combine weights of one (sequence, kv head) live in LDS
-  if ((size_t)Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
+  if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
+    return fail("no persistent forward is compiled for this shape");
+  // the attention split-combine (max, sum, weight) of one (sequence, kv head) live in LDS
+  if ((size_t)2 * Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
     return fail("max_ctx too long for this head geometry");
+  // the split-K partial sums of a column pair are reduced from registers
+  for (int K : {Lo.H, Lo.DQ, Lo.F})
+    if (K / (slice_steps(K) * 32) > 32) return fail("a GEMM depth needs more than 32 K slices");
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -144,6 +150,11 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.rope = take((size_t)Lo.max_ctx * (Lo.hd / 2) * 2 * 4);
   Lo.apart = take((size_t)Lo.nkv * Lo.max_splits * R * Lo.G * (Lo.hd + 2) * 4);
   Lo.logits = (d.flags & SPEC_FLAG_KEEP_LOGITS) ? take(R * Lo.V * 4) : (size_t)-1;
+  Lo.n_phases = 2 + 5 * Lo.L;
+  Lo.done = take((size_t)Lo.n_phases * 4);
+  Lo.exit_cnt = take(4);
+  Lo.err = take(4);
+  Lo.clock = take((size_t)(Lo.n_phases + 2) * 8);
   Lo.workspace_bytes = off;
 
   off = 0;
@@ -171,6 +182,8 @@ struct spec_ctx {
   spec_stats stats;
   std::string err;
   int last_rows = 0;
+  int fwd_grid = 0;      // workgroups of the persistent forward (all co-resident)
+  bool per_op = true;    // the per-kernel launch sequence (else the persistent forward)
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   int32_t* h_step() { return (int32_t*)(HB + lo.host_step); }
@@ -455,7 +468,49 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   return SPEC_OK;
 }
 
-int launch_forward(spec_ctx* c, int n_seq, int S) {
+FwdParams fwd_params(spec_ctx* c, int n_seq, int S, bool with_clock) {
+  const Layout& L = c->lo;
+  FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.L = L.L; p.H = L.H; p.nq = L.nq; p.nkv = L.nkv; p.hd = L.hd; p.F = L.F; p.V = L.V;
+  p.DQ = L.DQ; p.DK = L.DK; p.Nqkv = L.Nqkv; p.Ngu = L.Ngu;
+  p.R = n_seq * S; p.S = S; p.n_seq = n_seq;
+  p.nk_h = L.nk_qkv; p.nk_o = L.nk_o; p.nk_d = L.nk_d;
+  p.eps = c->d.rms_eps; p.inv_dim = 1.0f / (float)L.H; p.scale = (float)(1.0 / sqrt((double)L.hd));
+  p.max_splits = L.max_splits; p.bt_stride = L.bt_stride;
+  p.W = c->W;
+  p.lay_stride = L.L > 1 ? L.lay[1].wqkv - L.lay[0].wqkv : 0;
+  p.off_wqkv = L.lay[0].wqkv; p.off_wo = L.lay[0].wo; p.off_wgu = L.lay[0].wgu; p.off_wd = L.lay[0].wd;
+  p.off_gattn = L.lay[0].g_attn; p.off_gffn = L.lay[0].g_ffn;
+  p.emb = (const uint16_t*)(c->W + L.emb);
+  p.wlm = c->W + L.wlm;
+  p.g_final = (const float*)(c->W + L.g_final);
+  p.KV = c->KV; p.kv_layer_bytes = L.kv_layer_bytes; p.kv_half_bytes = L.kv_half_bytes;
+  p.x = c->ws<float>(L.x); p.ss = c->ws<float>(L.ss); p.q = c->ws<float>(L.q); p.o = c->ws<float>(L.o);
+  p.h = c->ws<float>(L.h); p.part = c->ws<float>(L.part); p.apart = c->ws<float>(L.apart);
+  p.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
+  p.rope = c->ws<float>(L.rope);
+  p.cnt = c->ws<unsigned>(L.cnt); p.attn_cnt = c->ws<unsigned>(L.attn_cnt); p.lm_cnt = c->ws<unsigned>(L.lm_cnt);
+  p.done = c->ws<unsigned>(L.done); p.exit_cnt = c->ws<unsigned>(L.exit_cnt); p.n_phases = L.n_phases;
+  p.argkey = c->ws<unsigned long long>(L.argkey);
+  p.status = c->ws<int32_t>(L.status); p.err = c->ws<int32_t>(L.err);
+  p.clock = with_clock ? c->ws<unsigned long long>(L.clock) : nullptr;
+  const StepDev* sd = c->ws<StepDev>(L.step);
+  p.step = sd;
+  p.tokens = (const int32_t*)(sd + 1);
+  p.seq_ids = p.tokens + L.max_rows;
+  p.kv_len = c->ws<int32_t>(L.kv_len);
+  p.bt = c->ws<int32_t>(L.bt);
+  p.result = c->ws<int32_t>(L.result);
+  return p;
+}
+
+int launch_forward(spec_ctx* c, int n_seq, int S, bool with_clock = false) {
+  if (!c->per_op) {
+    const FwdParams p = fwd_params(c, n_seq, S, with_clock);
+    HIPCHK(c, launch_forward_kernel(p, c->fwd_grid, c->st));
+    return SPEC_OK;
+  }
   if (c->d.flags & SPEC_FLAG_NO_GRAPH) return enqueue_forward(c, n_seq, S, nullptr);
   hipGraphExec_t ge;
   STEP(get_graph(c, n_seq, S, &ge));
@@ -472,6 +527,17 @@ int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   HIPCHK(c, hipStreamSynchronize(c->st));
   c->stats.forwards++;
   c->last_rows = n_seq * S;
+  if (c->h_result()[0] & 2) {
+    // a timed-out launch leaves counters mid-count: clear every counter,
+    // key and flag before the context is used again
+    const Layout& L = c->lo;
+    const size_t spans[][2] = {{L.cnt, (size_t)L.cnt_n * 4}, {L.attn_cnt, (size_t)L.max_rows * L.nkv * 4},
+                               {L.lm_cnt, 4}, {L.argkey, (size_t)L.max_rows * 8}, {L.status, 4},
+                               {L.done, (size_t)L.n_phases * 4}, {L.exit_cnt, 4}, {L.err, 4}};
+    for (const auto& sp : spans) HIPCHK(c, launch_fill_u32(c->WS + sp[0], 0u, sp[1] / 4, c->st));
+    HIPCHK(c, hipStreamSynchronize(c->st));
+    return set_err(c, SPEC_EHIP, "forward watchdog: a phase wait timed out (counters cleared)");
+  }
   if (c->h_result()[0] & 1) return set_err(c, SPEC_ENAN, "a logit row held NaN");
   return SPEC_OK;
 }
@@ -576,6 +642,18 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
     g_create_error = std::string("initialising device buffers: ") + hipGetErrorString(e);
     delete c;
     return SPEC_EHIP;
+  }
+  c->per_op = (desc->flags & SPEC_FLAG_PERSISTENT) == 0;
+  if (!c->per_op) {
+    int dev = 0, cus = 0;
+    const int occ = forward_occupancy(L.nk_qkv, L.nk_o, L.nk_d, L.hd);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || occ <= 0 || cus <= 0) {
+      g_create_error = "cannot size the persistent forward grid";
+      delete c;
+      return SPEC_EHIP;
+    }
+    c->fwd_grid = std::min(occ, 2) * cus;
   }
   *out = c;
   return SPEC_OK;
@@ -856,7 +934,7 @@ int spec_profile_ops(spec_ctx* c, int S, int iters, const int32_t* spans, float*
 
 int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
   if (!c || !us_out || reps <= 0) return c ? set_err(c, SPEC_EINVAL, "bad timing arguments") : SPEC_EINVAL;
-  if (op < 0 || op >= SPEC_OP_COUNT) return set_err(c, SPEC_EINVAL, "unknown op class");
+  if ((op & 0xFF) < 0 || (op & 0xFF) >= SPEC_OP_COUNT) return set_err(c, SPEC_EINVAL, "unknown op class");
   if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
   STEP(check_ready(c));
   if (!c->live[0]) return set_err(c, SPEC_ESTATE, "timing before prefill");
@@ -888,6 +966,59 @@ int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
   if (rc != SPEC_OK) return rc;
   if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("timing: ") + hipGetErrorString(e));
   *us_out = ms * 1000.0f / (float)(reps * per_rep);
+  return SPEC_OK;
+}
+
+int spec_profile_phases(spec_ctx* c, int S, int iters, const int32_t* spans, float* us_out, int32_t* count_out) {
+  if (!c || !spans || !us_out || !count_out || iters <= 0)
+    return c ? set_err(c, SPEC_EINVAL, "bad profiling arguments") : SPEC_EINVAL;
+  if (c->per_op) return set_err(c, SPEC_ESTATE, "phase profiling needs the persistent forward");
+  if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
+  STEP(check_ready(c));
+  STEP(check_tokens(c, spans, S * iters));
+  if (!c->live[0]) return set_err(c, SPEC_ESTATE, "profiling before prefill");
+  if (c->len[0] + S > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
+  bool dirty = false;
+  STEP(ensure_blocks(c, 0, c->len[0] + S, &dirty));
+  if (dirty) STEP(upload_bt_row(c, 0));
+  const Layout& L = c->lo;
+  const int np = L.n_phases;
+  std::vector<unsigned long long> clk((size_t)np + 2);
+  double tot[SPEC_OP_COUNT] = {0};
+  int cnt[SPEC_OP_COUNT] = {0};
+  const int32_t sid = 0;
+  for (int it = 0; it < iters; ++it) {
+    STEP(upload_step(c, MODE_NO_COMMIT, 1, S, spans + (size_t)it * S, &sid));
+    STEP(launch_forward(c, 1, S, true));
+    HIPCHK(c, hipMemcpyAsync(clk.data(), c->WS + L.clock, clk.size() * 8, hipMemcpyDeviceToHost, c->st));
+    HIPCHK(c, hipStreamSynchronize(c->st));
+    // clock[ph] = when workgroup 0 finished waiting on phase ph, i.e. the start
+    // of the phase after it; 100 MHz constant clock.
+    auto us = [&](unsigned long long a, unsigned long long b) { return (double)(b - a) / 100.0; };
+    for (int l = 0; l < L.L; ++l) {
+      const unsigned long long q0 = clk[(size_t)(5 * l)];
+      const int ops[5] = {SPEC_OP_QKV, SPEC_OP_ATTN, SPEC_OP_O, SPEC_OP_GATEUP, SPEC_OP_DOWN};
+      unsigned long long prev = q0;
+      for (int k = 0; k < 5; ++k) {
+        const unsigned long long nx = clk[(size_t)(5 * l + 1 + k)];
+        tot[ops[k]] += us(prev, nx);
+        if (it == 0) cnt[ops[k]]++;
+        prev = nx;
+      }
+    }
+    tot[SPEC_OP_EMBED] += us(clk[(size_t)np], clk[0]);
+    tot[SPEC_OP_LM] += us(clk[(size_t)(5 * L.L)], clk[(size_t)np + 1]);
+    if (it == 0) {
+      cnt[SPEC_OP_EMBED]++;
+      cnt[SPEC_OP_LM]++;
+    }
+  }
+  trim_blocks(c, 0, c->len[0]);
+  c->last_rows = S;
+  for (int op = 0; op < SPEC_OP_COUNT; ++op) {
+    count_out[op] = cnt[op];
+    us_out[op] = cnt[op] ? (float)(tot[op] / ((double)cnt[op] * iters)) : 0.0f;
+  }
   return SPEC_OK;
 }
 

@@ -53,6 +53,8 @@ extern "C" {
 
 #define SPEC_FLAG_KEEP_LOGITS 1u /* also store every row's logits (fp32) for spec_debug_logits */
 #define SPEC_FLAG_NO_GRAPH 2u    /* launch each kernel eagerly instead of replaying a HIP graph */
+#define SPEC_FLAG_PERSISTENT 4u  /* run each forward as one persistent cooperative kernel (only the
+                                  * shapes it is compiled for; spec_create fails on others) */
 
 #define SPEC_MAX_SPAN 16    /* rows per sequence per forward (K <= 15)      */
 #define SPEC_MAX_ROWS 128   /* rows per forward over all sequences           */
@@ -198,6 +200,13 @@ SPEC_API int spec_profile_ops(spec_ctx* ctx, int S, int iters, const int32_t* sp
  * context stream (no commit).  The KV rows of positions p..p+S-1 are
  * rewritten, as a verify would. */
 SPEC_API int spec_time_op(spec_ctx* ctx, int op, int S, int reps, float* us_per_launch);
+
+/* Per-phase timing of the persistent forward: `iters` forwards of span S at
+ * sequence 0's current cache (no commit) with device timestamps taken by
+ * workgroup 0 as each phase begins (100 MHz clock).  us_out[SPEC_OP_COUNT] =
+ * mean microseconds per phase of each class, count_out = phases per forward. */
+SPEC_API int spec_profile_phases(spec_ctx* ctx, int S, int iters, const int32_t* spans, float* us_out,
+                                 int32_t* count_out);
 
 /* Algorithmic bytes one launch of an op class streams at span S and cache
  * length ctx_len (weights, KV reads and writes; activations excluded). */
