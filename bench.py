@@ -97,6 +97,103 @@ def cpu_baseline(shape, prompt, budget_s=12.0, max_rounds=24):
                       f"{len(os.sched_getaffinity(0))} host cores visible, {cpu}"}
 
 
+BATCH_SEQS, BATCH_K, BATCH_CTX = 16, 7, (512, 4096)
+
+
+def batched_bench(steps, warmup, log_every=8):
+    """16 sequences on the paged KV pool (16-token blocks), contexts drawn
+    uniformly from [512, 4096] (seed 4), each prompt repetition-heavy (seed
+    4000 + sequence index).  Every step proposes K = 7 n-gram drafts per
+    sequence (short drafts padded with the last history token), runs one
+    batched verify forward of 16 x 8 = 128 rows, accepts and rewinds per
+    sequence, and commits on the host.  Then the spec-off batched step (16
+    rows, one per sequence) from the same prefilled state."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["qwen3_4b"]
+    n, K = BATCH_SEQS, BATCH_K
+    S = K + 1
+    rng = np.random.default_rng(4)
+    ctxs = [int(x) for x in rng.integers(BATCH_CTX[0], BATCH_CTX[1] + 1, n)]
+    max_ctx = BATCH_CTX[1] + S * (steps + warmup + 2) + 64
+    wg = synth.weights(shape, seed=0, device="cuda")
+    sess = specv.Session(shape, specv.tree_weights(wg), max_ctx=max_ctx, max_seqs=n, max_rows=n * S)
+    del wg
+    torch.cuda.empty_cache()
+    c = sess.ctx
+    prompts = [synth.repetition_prompt(4000 + i, shape["vocab"], L) for i, L in enumerate(ctxs)]
+    t = time.time()
+    g0 = [specv.spec_prefill_seq(c, i, p) for i, p in enumerate(prompts)]
+    log(f"batched: prefilled {n} sequences ({sum(ctxs)} tokens) in {time.time() - t:.1f}s")
+    ids = list(range(n))
+    d = sess.desc
+
+    def step_bytes(rows_per_seq, cur):
+        b = specv.spec_op_bytes(d, "embed", n * rows_per_seq, 0) + specv.spec_op_bytes(d, "lm", 1, 0)
+        b += shape["n_layers"] * sum(specv.spec_op_bytes(d, op, n * rows_per_seq, 0) for op in ("qkv", "o", "gateup", "down"))
+        b += shape["n_layers"] * sum(specv.spec_op_bytes(d, "attn", rows_per_seq, L) for L in cur)
+        return b
+
+    def run(spec, n_steps, n_warm):
+        hist = [[int(x) for x in p] + [g] for p, g in zip(prompts, g0)]
+        ngs = []
+        for h in hist:
+            ng = specv.spec_ngram_create(2, 4, max_ctx + 16)
+            specv.spec_ngram_append(ng, h)
+            ngs.append(ng)
+        for i in ids:
+            specv.spec_rewind_seq(c, i, ctxs[i])
+        committed, t_total, t_verify, byts, acc_hist = 0, 0.0, 0.0, 0.0, np.zeros(S, np.int64)
+        per_seq = np.zeros(n, np.int64)
+        for it in range(n_steps + n_warm):
+            cur = [len(h) - 1 for h in hist]
+            t0 = time.perf_counter()
+            if spec:
+                spans = np.empty((n, S), np.int32)
+                for b in ids:
+                    dr = specv.spec_ngram_propose(ngs[b], K)
+                    spans[b] = [hist[b][-1]] + dr + [hist[b][-1]] * (K - len(dr))
+            else:
+                spans = np.array([[h[-1]] for h in hist], np.int32)
+            t1 = time.perf_counter()
+            am, acc = specv.spec_verify_batch(c, ids, spans)
+            t2 = time.perf_counter()
+            for b in ids:
+                m = int(acc[b])
+                new = [int(x) for x in am[b][: m + 1]]
+                hist[b] += new
+                specv.spec_ngram_append(ngs[b], new)
+                if it >= n_warm:
+                    committed += m + 1
+                    per_seq[b] += m + 1
+                    acc_hist[m] += 1
+            t3 = time.perf_counter()
+            if it >= n_warm:
+                t_total += t3 - t0
+                t_verify += t2 - t1
+                byts += step_bytes(spans.shape[1], cur)
+            if log_every and it % log_every == 0:
+                log(f"  batched {'on' if spec else 'off'} step {it}: verify {1e3 * (t2 - t1):.2f} ms")
+        for ng in ngs:
+            specv.spec_ngram_destroy(ng)
+        return {"tok_s": round(committed / t_total, 2), "ms_per_step": round(1e3 * t_total / n_steps, 4),
+                "verify_ms_per_step": round(1e3 * t_verify / n_steps, 4),
+                "hbm_gbps_verify": round(byts / t_verify / 1e9, 1),
+                "hbm_frac_verify": round(byts / t_verify / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_step": round(byts / n_steps), "committed": int(committed),
+                "accept_hist": acc_hist.tolist() if spec else None,
+                "per_seq_tok_per_step": [round(x / n_steps, 3) for x in per_seq] if spec else None}
+
+    on = run(True, steps, warmup)
+    off = run(False, steps, warmup)
+    sess.close()
+    del sess
+    torch.cuda.empty_cache()
+    return {"sequences": n, "K": K, "rows": n * S, "contexts": ctxs, "steps": steps, "warmup": warmup,
+            "on": on, "off": off, "ratio": round(on["tok_s"] / off["tok_s"], 3)}
+
+
 def counters_workload():
     """Short workload for the rocprofv3 --pmc passes: ten S=1 verify forwards at
     the 848-token context, then one device copy of exactly 1 GiB, whose
@@ -193,6 +290,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cv-iters", type=int, default=30)
+    ap.add_argument("--batch-steps", type=int, default=32)
+    ap.add_argument("--batch-warmup", type=int, default=5)
+    ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--counters", action="store_true", help="short workload for rocprofv3 --pmc passes")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
@@ -309,6 +409,11 @@ def main():
     del sess
     torch.cuda.empty_cache()
 
+    batched = None
+    if not args.no_batched:
+        batched = batched_bench(args.batch_steps, args.batch_warmup)
+        log(f"batched: {batched}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, prompt)
@@ -327,7 +432,8 @@ def main():
                        "batch": 1, "prompt_tokens": PROMPT_TOKENS, "parallelism": "single GPU"},
             "spec_off_tok_s": round(off_tok_s, 3), "speedup": round(on_tok_s / off_tok_s, 4),
             "tok_per_forward": round((on_st["accepted"] + on_st["forwards"]) / on_st["forwards"], 3),
-            "e2e_256": e2e_256, "cv": cv, "roofline": roofline, "cpu_baseline": cpu}
+            "e2e_256": e2e_256, "cv": cv, "batched_paged": batched, "roofline": roofline,
+            "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 

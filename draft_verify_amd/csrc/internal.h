@@ -7,6 +7,8 @@
 
 namespace specv {
 
+constexpr int kMaxRows = 128;  // rows per forward (the library-wide limit of the C ABI)
+
 // Step modes, read by the accept stage from device memory so one captured
 // graph per shape serves all three.
 enum StepMode { MODE_VERIFY = 0, MODE_COMMIT_ALL = 1, MODE_NO_COMMIT = 2 };

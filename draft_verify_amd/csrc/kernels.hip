@@ -126,8 +126,12 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
 template <int EPI>
 __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
 
+constexpr int kMaxSsIter = 8;  // RMSNorm partial sums per row / 16 (hidden <= 8192, host-checked)
+
 template <int NK, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
+  constexpr int UNITS = 16 * NK * 4;          // (row, step, lane group) units of 8 inputs per 16-row chunk
+  constexpr int UPT = (UNITS + 255) / 256;    // units per thread
   const int NB = P.N >> 6, ns = P.nslices;
   const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
   const int nb = (loc / ns) * 8 + xcd, sl = loc % ns;
@@ -137,49 +141,75 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   const int tile = nb * 4 + wave;
 
   __shared__ u32x4 sA[NK * 2 * 64];
-  __shared__ float sR[16];
+  __shared__ float sR[kMaxRows];
+  __shared__ float sG[NK * 32];
   __shared__ int sLast;
+
+  // Loads are issued in the order they are needed: the RMSNorm partial sums
+  // and gain, then A of the first 16 rows, and the weights last, so the
+  // prologue's arithmetic overlaps the weights' DRAM latency.
+  const int ss_row = tid >> 4, ss_part = tid & 15;
+  if (P.ss)
+    for (int e = tid; e < NK * 32; e += 256) sG[e] = P.gain[k0 + e];
+  f32x4 pa[UPT][2];
+  auto load_a = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * 256;
+      const int g = u & 3, j = (u >> 2) % NK, row = u / (4 * NK);
+      const int r = m0 + row;
+      if (u < UNITS && r < P.R) {
+        const f32x4* src = (const f32x4*)(P.A + (size_t)r * P.lda + k0 + j * 32 + g * 8);
+        pa[i][0] = src[0];
+        pa[i][1] = src[1];
+      } else {
+        pa[i][0] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        pa[i][1] = pa[i][0];
+      }
+    }
+  };
+  load_a(0);
 
   const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / 32) + (size_t)sl * NK) * 64 + lane;
   u32x4 b[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
 
-  for (int m0 = 0; m0 < P.R; m0 += 16) {
-    if (P.ss) {
-      // rstd of row m0 + tid/16: 16 lanes sum strided partials, then a fixed
-      // xor tree (the same order for every row count).
-      const int row = tid >> 4, part = tid & 15, r = m0 + row;
-      float s = 0.0f;
-      if (r < P.R)
-        for (int q = part; q < P.ss_n; q += 16) s += P.ss[(size_t)r * P.ss_n + q];
+  if (P.ss) {
+    // rstd of every row: 16 lanes per row sum the partials strided by 16 in
+    // increasing order, then a fixed xor tree -- the same order for any R.
+#pragma unroll 2
+    for (int pass = 0; pass * 16 < P.R; ++pass) {
+      const int r = pass * 16 + ss_row;
+      float v[kMaxSsIter];
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-      if (part == 0) sR[row] = r < P.R ? 1.0f / sqrtf(s * P.inv_dim + P.eps) : 0.0f;
-      __syncthreads();
+      for (int i = 0; i < kMaxSsIter; ++i) {
+        const int q = ss_part + 16 * i;
+        v[i] = (r < P.R && q < P.ss_n) ? P.ss[(size_t)r * P.ss_n + q] : 0.0f;
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kMaxSsIter; ++i) acc += v[i];
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      if (ss_part == 0) sR[r] = r < P.R ? 1.0f / sqrtf(acc * P.inv_dim + P.eps) : 0.0f;
     }
-    // Stage 16 rows x NK*32 inputs: unit u = (row, step j, lane group g) of 8 inputs.
-    for (int u = tid; u < 16 * NK * 4; u += 256) {
+    __syncthreads();
+  }
+
+  for (int m0 = 0; m0 < P.R; m0 += 16) {
+    // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo.
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + i * 256;
+      if (u >= UNITS) continue;
       const int g = u & 3, j = (u >> 2) % NK, row = u / (4 * NK);
-      const int r = m0 + row;
-      const int k = k0 + j * 32 + g * 8;
-      float v[8];
-      if (r < P.R) {
-        const f32x4* src = (const f32x4*)(P.A + (size_t)r * P.lda + k);
-        const f32x4 a0 = src[0], a1 = src[1];
-        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
-        if (P.ss) {
-          const float rs = sR[row];
-          const f32x4* gp = (const f32x4*)(P.gain + k);
-          const f32x4 g0 = gp[0], g1 = gp[1];
-          const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+      if (P.ss) {
+        const int r = m0 + row;
+        const float rs = r < P.R ? sR[r] : 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * gg[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * sG[j * 32 + g * 8 + e];
       }
       bf16x8 hi, lo;
 #pragma unroll
@@ -193,6 +223,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
       sA[(j * 2 + 1) * 64 + l] = __builtin_bit_cast(u32x4, lo);
     }
     __syncthreads();
+    if (m0 + 16 < P.R) load_a(m0 + 16);  // the next chunk's A loads fly during this chunk's MFMA
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -224,14 +255,47 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   gemm_epilogue<EPI>(P, nb, (float*)sA);
 }
 
-// Column pair (c, c+1) of row r summed over the K slices in slice order.
-__device__ __forceinline__ void reduce_pair(const GemmParams& P, int r, int c, float& v0, float& v1) {
-  v0 = 0.0f;
-  v1 = 0.0f;
-  for (int s = 0; s < P.nslices; ++s) {
-    const float2 t = ld_dev2(P.part + ((size_t)s * P.R + r) * P.N + c);
-    v0 += t.x;
-    v1 += t.y;
+// The epilogue's column pairs: pair idx = (row idx/32, columns nb*64 +
+// 2*(idx%32) + {0,1}), summed over the K slices in slice order.  Each thread
+// takes two pairs at a time and issues every slice load of them (up to 8
+// slices per round) before the first add, so the gather costs one memory
+// round trip per two pairs and per 8 slices.
+template <class F>
+__device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
+  constexpr int U = 2;
+  const int n = P.R * 32, ns = P.nslices;
+  const unsigned stride = (unsigned)P.R * (unsigned)P.N;  // floats; the partial buffer is < 4 GiB
+  for (int base = 0; base < n; base += U * 256) {
+    float v0[U], v1[U];
+    unsigned off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * 256 + threadIdx.x;
+      v0[u] = v1[u] = 0.0f;
+      off[u] = (unsigned)(idx >> 5) * (unsigned)P.N + (unsigned)(nb * 64 + 2 * (idx & 31));
+    }
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float2 t[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (base + u * 256 + (int)threadIdx.x < n && s0 + i < ns)
+            t[u][i] = ld_dev2(P.part + (off[u] + (unsigned)(s0 + i) * stride));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (base + u * 256 + (int)threadIdx.x < n && s0 + i < ns) {
+            v0[u] += t[u][i].x;
+            v1[u] += t[u][i].y;
+          }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * 256 + threadIdx.x;
+      if (idx < n) f(idx, idx >> 5, nb * 64 + 2 * (idx & 31), v0[u], v1[u]);
+    }
   }
 }
 
@@ -246,10 +310,7 @@ template <>
 __device__ void gemm_epilogue<EPI_QKV>(const GemmParams& P, int nb, float*) {
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
-  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
-    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
-    float v0, v1;
-    reduce_pair(P, r, c, v0, v1);
+  for_pairs(P, nb, [&](int, int r, int c, float v0, float v1) {
     int seq, pos;
     row_pos(P, r, seq, pos);
     const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
@@ -274,16 +335,13 @@ __device__ void gemm_epilogue<EPI_QKV>(const GemmParams& P, int nb, float*) {
       vb[(size_t)d * 16 + slot] = (_Float16)v0;
       vb[(size_t)(d + 1) * 16 + slot] = (_Float16)v1;
     }
-  }
+  });
 }
 
 template <>
 __device__ void gemm_epilogue<EPI_RESID>(const GemmParams& P, int nb, float*) {
   const int NB = P.N >> 6;
-  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
-    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
-    float v0, v1;
-    reduce_pair(P, r, c, v0, v1);
+  for_pairs(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
     float2 x = *xp;
     x.x = x.x + v0;
@@ -293,27 +351,21 @@ __device__ void gemm_epilogue<EPI_RESID>(const GemmParams& P, int nb, float*) {
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o);
     if ((idx & 31) == 0) P.ss_out[(size_t)r * NB + nb] = t;
-  }
+  });
 }
 
 template <>
 __device__ void gemm_epilogue<EPI_SWIGLU>(const GemmParams& P, int nb, float*) {
   const int F = P.N >> 1;
-  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
-    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
-    float g, u;
-    reduce_pair(P, r, c, g, u);
+  for_pairs(P, nb, [&](int, int r, int c, float g, float u) {
     P.h[(size_t)r * F + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
-  }
+  });
 }
 
 template <>
 __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) {
   __shared__ int sFinal;
-  for (int idx = threadIdx.x; idx < P.R * 32; idx += 256) {
-    const int r = idx >> 5, c = nb * 64 + 2 * (idx & 31);
-    float v0, v1;
-    reduce_pair(P, r, c, v0, v1);
+  for_pairs(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     if (P.logits) {
       float2* lp = (float2*)(P.logits + (size_t)r * P.N + c);
       *lp = make_float2(v0, v1);
@@ -327,7 +379,7 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
       k = t > k ? t : k;
     }
     if ((idx & 31) == 0) atomicMax(&P.argkey[r], k);
-  }
+  });
   // Last column block to finish: read the row maxima, accept, advance the cache.
   wait_mem();
   __syncthreads();

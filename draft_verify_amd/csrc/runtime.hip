@@ -24,6 +24,8 @@
 
 using namespace specv;
 
+static_assert(kMaxRows == SPEC_MAX_ROWS, "kernel row limit must match the ABI");
+
 namespace {
 
 thread_local std::string g_create_error;
@@ -73,6 +75,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     return fail("head_dim must be 16, 32, 64 or 128");
   if (d.n_q_heads % d.n_kv_heads) return fail("n_q_heads must be a multiple of n_kv_heads");
   if (d.hidden % 64 || d.ffn % 32 || d.vocab % 64) return fail("hidden and vocab must be multiples of 64, ffn of 32");
+  if (d.hidden > 8192) return fail("hidden must be at most 8192");
   if ((d.n_q_heads * d.head_dim) % 64 || ((d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim) % 64)
     return fail("attention projection widths must be multiples of 64");
   if (d.max_rows < 1 || d.max_rows > SPEC_MAX_ROWS) return fail("max_rows must be in [1, 128]");
@@ -87,7 +90,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.n_blocks = d.n_blocks > 0 ? d.n_blocks : d.max_seqs * Lo.bt_stride;
   Lo.max_splits = (d.max_ctx + 255) / 256;
   Lo.nk_qkv = slice_steps(Lo.H); Lo.nk_o = slice_steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
-  Lo.nk_d = slice_steps(Lo.F); Lo.nk_lm = Lo.nk_qkv;
+  Lo.nk_d = slice_steps(Lo.F);
+  // The LM head runs ~10^4 workgroups; half-depth slices keep more of them resident.
+  Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
