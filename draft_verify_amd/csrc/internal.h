@@ -31,8 +31,25 @@ struct StepDev {
 // at ((t * (K/32) + s) * 64 + lane) * 16 bytes.
 inline size_t packed_bf16_bytes(int N, int K) { return (size_t)N * K * 2; }
 
+// Weight formats of the GEMMs (the embedding is always bf16).
+enum WFmt { FMT_BF16 = 0, FMT_INT4 = 1 };
+
+// Packed int4 group-128 weights: per 16-row tile t and 128-input group g one
+// 1 KiB fragment, lane-major in the order the MFMA B operand is read:
+//   frag(t, g)[lane] dword d (d = 0..3, the four 32-input steps of the group)
+//   holds W[16t + lane%16][128g + 32d + 8*(lane/16) + e], e = 0..7, as offset
+//   nibbles u = q + 8 at bit 4*(e/2) + 16*(e%2),
+// so ((dword >> 4j) & 0x000F000F) holds the pair (e = 2j, 2j+1) in the two
+// halves of a packed fp16 pair.  Fragments at ((t * (K/128) + g) * 64 + lane)
+// * 16 bytes; then the scales, bf16 [N/16][16][K/128] (tile, row, group).
+inline size_t packed_int4_frag_bytes(int N, int K) { return (size_t)N * K / 2; }
+inline size_t packed_int4_bytes(int N, int K) {
+  return packed_int4_frag_bytes(N, K) + (size_t)N * (K / 128) * 2;
+}
+
 struct GemmParams {
-  const void* W;         // packed fragments [N/16][K/32][64] x 16 B
+  const void* W;         // packed fragments (bf16: [N/16][K/32][64] x 16 B; int4: [N/16][K/128][64] x 16 B)
+  const uint16_t* scales;// int4 only: bf16 group scales [N/16][16][K/128]
   int N, K, R;           // outputs, inputs, rows
   int nslices;           // K split into nslices slices of NK*32 inputs
   const float* A;        // activation rows [R][lda] (fp32)
@@ -132,7 +149,7 @@ int forward_occupancy(int nk_h, int nk_o, int nk_d, int hd);
 hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
 
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
-hipError_t launch_gemm(const GemmParams& p, int nk, int epi, hipStream_t st);
+hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
 // Repack canonical bf16 [rows][cols] into fragments of a fused matrix whose
@@ -140,6 +157,11 @@ hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
 // interleave within heads of hd rows (+ row0), kind 2 row 2s + row0.
 hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, int kind, int row0,
                             int hd, hipStream_t st);
+// The same for canonical int4 group-128 (q4 bytes [rows][cols/2], low nibble
+// = even column; bf16 scales [rows][cols/128]) into int4 fragments and the
+// matrix's scale block.
+hipError_t launch_pack_int4(const uint8_t* q4, const uint16_t* scales, int rows, int cols, void* dst_frag,
+                            uint16_t* dst_scales, int kind, int row0, int hd, hipStream_t st);
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t st);
 
 // Row of the fused QKV matrix holding source row s of a Q or K projection:

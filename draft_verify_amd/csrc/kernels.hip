@@ -81,6 +81,37 @@ __global__ void k_pack_bf16(const uint16_t* __restrict__ src, int rows, int cols
   }
 }
 
+// One thread per (source row, 128-input group): 64 source bytes become one
+// dword per (step d, lane group gq) of the fragment, plus the group's scale.
+__global__ void k_pack_int4(const uint8_t* __restrict__ q4, const uint16_t* __restrict__ sc, int rows, int cols,
+                            uint32_t* __restrict__ dst, uint16_t* __restrict__ dsc, int kind, int row0, int hd) {
+  const int KG = cols / 128;
+  const size_t total = (size_t)rows * KG;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int s = (int)(i / KG), g = (int)(i % KG);
+    int n;
+    if (kind == 0) n = row0 + s;
+    else if (kind == 1) n = row0 + rope_pair_row(s, hd);
+    else n = row0 + 2 * s;
+    const int tile = n >> 4, r = n & 15;
+    const uint32_t* src = (const uint32_t*)(q4 + (size_t)s * (cols / 2) + (size_t)g * 64);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const uint32_t w = src[d * 4 + gq];  // nibble e (input 32d + 8gq + e) at bits 4e
+        uint32_t out = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = ((w >> (4 * e)) & 0xFu) ^ 0x8u;  // two's complement -> offset q + 8
+          out |= u << ((e & 1) ? 16 + 4 * (e >> 1) : 4 * (e >> 1));
+        }
+        dst[(((size_t)tile * KG + g) * 64 + gq * 16 + r) * 4 + d] = out;
+      }
+    dsc[((size_t)tile * 16 + r) * KG + g] = sc[(size_t)s * KG + g];
+  }
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t value, size_t count) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
     dst[i] = value;
@@ -128,8 +159,25 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
 
 constexpr int kMaxSsIter = 8;  // RMSNorm partial sums per row / 16 (hidden <= 8192, host-checked)
 
-template <int NK, int EPI>
+// Offset nibbles -> exact fp16 q: (1024 + u) - 1032 in packed fp16.
+__device__ __forceinline__ f16x8 dequant8(uint32_t x) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t o = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+    const h2 v = __builtin_bit_cast(h2, o) - off;
+    r[2 * j] = v[0];
+    r[2 * j + 1] = v[1];
+  }
+  return r;
+}
+
+template <int NK, int EPI, int FMT>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
+  static_assert(FMT == FMT_BF16 || NK % 4 == 0, "int4 slices hold whole 128-input groups");
+  constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per wave per slice
   constexpr int UNITS = 16 * NK * 4;          // (row, step, lane group) units of 8 inputs per 16-row chunk
   constexpr int UPT = (UNITS + 255) / 256;    // units per thread
   const int NB = P.N >> 6, ns = P.nslices;
@@ -170,15 +218,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   };
   load_a(0);
 
-  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / 32) + (size_t)sl * NK) * 64 + lane;
-  u32x4 b[NK];
+  // bf16: one fragment per 32-input step; int4: one per 128-input group.
+  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / (32 * NK / NF)) + (size_t)sl * NF) * 64 + lane;
+  u32x4 b[NF];
 #pragma unroll
-  for (int j = 0; j < NK; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+  for (int j = 0; j < NF; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+  float gs[FMT == FMT_INT4 ? NF : 1];  // int4: this lane's column's group scales
+  if constexpr (FMT == FMT_INT4) {
+    const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * (P.K / 128) + (size_t)sl * NF;
+#pragma unroll
+    for (int g = 0; g < NF; ++g) gs[g] = bf16_bits_to_f32(sp[g]);
+  }
 
   if (P.ss) {
     // rstd of every row: 16 lanes per row sum the partials strided by 16 in
     // increasing order, then a fixed xor tree -- the same order for any R.
-#pragma unroll 2
     for (int pass = 0; pass * 16 < P.R; ++pass) {
       const int r = pass * 16 + ss_row;
       float v[kMaxSsIter];
@@ -211,27 +265,63 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * sG[j * 32 + g * 8 + e];
       }
-      bf16x8 hi, lo;
+      u32x4 hw, lw;
+      if constexpr (FMT == FMT_INT4) {  // fp16 hi + lo: the operand type of the fp16 MFMA on exact q
+        f16x8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)v[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(v[e] - (float)h);
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 h = (_Float16)v[e];
+          hi[e] = h;
+          lo[e] = (_Float16)(v[e] - (float)h);
+        }
+        hw = __builtin_bit_cast(u32x4, hi);
+        lw = __builtin_bit_cast(u32x4, lo);
+      } else {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 h = (__bf16)v[e];
+          hi[e] = h;
+          lo[e] = (__bf16)(v[e] - (float)h);
+        }
+        hw = __builtin_bit_cast(u32x4, hi);
+        lw = __builtin_bit_cast(u32x4, lo);
       }
       const int l = g * 16 + row;
-      sA[(j * 2) * 64 + l] = __builtin_bit_cast(u32x4, hi);
-      sA[(j * 2 + 1) * 64 + l] = __builtin_bit_cast(u32x4, lo);
+      sA[(j * 2) * 64 + l] = hw;
+      sA[(j * 2 + 1) * 64 + l] = lw;
     }
     __syncthreads();
     if (m0 + 16 < P.R) load_a(m0 + 16);  // the next chunk's A loads fly during this chunk's MFMA
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FMT == FMT_INT4) {
+      // Per group: exact integer weights times the activation pair, summed
+      // over the group's four steps in fp32, then scaled by the column's
+      // group scale and added in group order.
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, b[j]);
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, sA[(j * 2) * 64 + lane]);
-      const bf16x8 al = __builtin_bit_cast(bf16x8, sA[(j * 2 + 1) * 64 + lane]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+      for (int gi = 0; gi < NF; ++gi) {
+        f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int j = gi * 4 + d;
+          const f16x8 bq = dequant8(b[gi][d]);
+          const f16x8 ah = __builtin_bit_cast(f16x8, sA[(j * 2) * 64 + lane]);
+          const f16x8 al = __builtin_bit_cast(f16x8, sA[(j * 2 + 1) * 64 + lane]);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += t[i] * gs[gi];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const bf16x8 bw = __builtin_bit_cast(bf16x8, b[j]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, sA[(j * 2) * 64 + lane]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, sA[(j * 2 + 1) * 64 + lane]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+      }
     }
     // D layout: lane holds column lane%16 of rows 4*(lane/16) + i.
     const int col = tile * 16 + (lane & 15);
@@ -593,17 +683,33 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   // the values, in split order.
   const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
   const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC) * (HD + 2);
-  float* sW = &sO[0][0][0];  // [n_act][QC], free after the tile loop
+  float* sW = &sO[0][0][0];  // [n_act][QC] weights, free after the tile loop (host-checked to fit)
   for (int qcol = tid; qcol < QC; qcol += 256) {
     const int nsp = ((p + qcol / G) >> 8) + 1;
+    const float* ml0 = base + (size_t)qcol * (HD + 2);
     float M = -INFINITY;
-    for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, ld_dev(base + sp * stride + (size_t)qcol * (HD + 2)));
+    for (int s0 = 0; s0 < nsp; s0 += 8) {  // split maxima, eight loads in flight
+      float m[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < nsp) m[i] = ld_dev(ml0 + (size_t)(s0 + i) * stride);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < nsp) M = fmaxf(M, m[i]);
+    }
     float L = 0.0f;
-    for (int sp = 0; sp < nsp; ++sp) {
-      const float2 ml = ld_dev2(base + sp * stride + (size_t)qcol * (HD + 2));
-      const float f = expf(ml.x - M);
-      sW[sp * QC + qcol] = f;
-      L += ml.y * f;
+    for (int s0 = 0; s0 < nsp; s0 += 8) {  // weights exp(m_s - M) and the sum, in split order
+      float2 ml[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < nsp) ml[i] = ld_dev2(ml0 + (size_t)(s0 + i) * stride);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < nsp) {
+          const float f = expf(ml[i].x - M);
+          sW[(s0 + i) * QC + qcol] = f;
+          L += ml[i].y * f;
+        }
     }
     for (int sp = 0; sp < nsp; ++sp) sW[sp * QC + qcol] /= L;
   }
@@ -630,25 +736,36 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 // -------------------------------------------------------------- launchers
 
 template <int EPI>
-static hipError_t launch_gemm_epi(const GemmParams& p, int nk, hipStream_t st) {
+static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStream_t st) {
   const int NB = p.N / 64;
   const int grid = ((NB + 7) / 8) * 8 * p.nslices;
+  if (fmt == FMT_INT4) {
+    if (!p.scales) return hipErrorInvalidValue;
+    switch (nk) {
+      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (fmt != FMT_BF16) return hipErrorInvalidValue;
   switch (nk) {
-    case 16: hipLaunchKernelGGL((k_gemm<16, EPI>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_gemm<8, EPI>), dim3(grid), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_gemm<4, EPI>), dim3(grid), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm<2, EPI>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmParams& p, int nk, int epi, hipStream_t st) {
+hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, st);
-    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, st);
-    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(p, nk, st);
-    case EPI_LM: return launch_gemm_epi<EPI_LM>(p, nk, st);
+    case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, fmt, st);
+    case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, fmt, st);
+    case EPI_SWIGLU: return launch_gemm_epi<EPI_SWIGLU>(p, nk, fmt, st);
+    case EPI_LM: return launch_gemm_epi<EPI_LM>(p, nk, fmt, st);
   }
   return hipErrorInvalidValue;
 }
@@ -675,6 +792,16 @@ hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, 
   const size_t total = (size_t)rows * (cols / 8);
   const int grid = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
   hipLaunchKernelGGL(k_pack_bf16, dim3(grid), dim3(256), 0, st, src, rows, cols, (u32x4*)dst, kind, row0, hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_int4(const uint8_t* q4, const uint16_t* scales, int rows, int cols, void* dst_frag,
+                            uint16_t* dst_scales, int kind, int row0, int hd, hipStream_t st) {
+  if (cols % 128) return hipErrorInvalidValue;
+  const size_t total = (size_t)rows * (cols / 128);
+  const int grid = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
+  hipLaunchKernelGGL(k_pack_int4, dim3(grid), dim3(256), 0, st, q4, scales, rows, cols, (uint32_t*)dst_frag,
+                     dst_scales, kind, row0, hd);
   return hipGetLastError();
 }
 

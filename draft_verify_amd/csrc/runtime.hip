@@ -41,12 +41,20 @@ inline int slice_steps(int K) {
   return 0;
 }
 
+// int4: slices hold whole 128-input groups (16, 8 or 4 steps).
+inline int slice_steps_int4(int K) {
+  for (int nk : {16, 8, 4})
+    if (K % (nk * 32) == 0) return nk;
+  return 0;
+}
+
 struct LayerOff {
   size_t wqkv, wo, wgu, wd, g_attn, g_ffn;
 };
 
 // Byte layout of the three device buffers for one description.
 struct Layout {
+  int fmt;  // FMT_BF16 or FMT_INT4 (GEMM weights; the embedding is bf16)
   int H, nq, nkv, hd, F, V, L, DQ, DK, Nqkv, Ngu;
   int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
   int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
@@ -63,6 +71,10 @@ struct Layout {
   int cnt_n;
 };
 
+inline size_t mat_bytes(int fmt, int N, int K) {
+  return fmt == FMT_INT4 ? packed_int4_bytes(N, K) : packed_bf16_bytes(N, K);
+}
+
 bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   auto fail = [&](const char* m) {
     err = m;
@@ -70,7 +82,13 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   };
   if (d.n_layers <= 0 || d.hidden <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.ffn <= 0 || d.vocab <= 0)
     return fail("model dimensions must be positive");
-  if (d.weight_format != SPEC_WFMT_BF16) return fail("only SPEC_WFMT_BF16 weights are supported by this library version");
+  if (d.weight_format != SPEC_WFMT_BF16 && d.weight_format != SPEC_WFMT_INT4G128)
+    return fail("weight_format must be SPEC_WFMT_BF16 or SPEC_WFMT_INT4G128");
+  Lo.fmt = d.weight_format == SPEC_WFMT_INT4G128 ? FMT_INT4 : FMT_BF16;
+  if (Lo.fmt == FMT_INT4 && (d.flags & SPEC_FLAG_PERSISTENT))
+    return fail("the persistent forward is compiled for bf16 weights only");
+  if (Lo.fmt == FMT_INT4 && (d.hidden % 128 || d.ffn % 128 || (d.n_q_heads * d.head_dim) % 128))
+    return fail("int4 group-128 weights need hidden, ffn and n_q_heads*head_dim multiples of 128");
   if (!(d.head_dim == 16 || d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128))
     return fail("head_dim must be 16, 32, 64 or 128");
   if (d.n_q_heads % d.n_kv_heads) return fail("n_q_heads must be a multiple of n_kv_heads");
@@ -89,20 +107,25 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.bt_stride = (d.max_ctx + SPEC_BLOCK_TOKENS - 1) / SPEC_BLOCK_TOKENS;
   Lo.n_blocks = d.n_blocks > 0 ? d.n_blocks : d.max_seqs * Lo.bt_stride;
   Lo.max_splits = (d.max_ctx + 255) / 256;
-  Lo.nk_qkv = slice_steps(Lo.H); Lo.nk_o = slice_steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
-  Lo.nk_d = slice_steps(Lo.F);
+  auto steps = [&](int K) { return Lo.fmt == FMT_INT4 ? slice_steps_int4(K) : slice_steps(K); };
+  Lo.nk_qkv = steps(Lo.H); Lo.nk_o = steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
+  Lo.nk_d = steps(Lo.F);
   // The LM head runs ~10^4 workgroups; half-depth slices keep more of them resident.
   Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
+  if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
     return fail("no persistent forward is compiled for this shape");
-  // the attention split-combine (max, sum, weight) of one (sequence, kv head) live in LDS
-  if ((size_t)2 * Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
-    return fail("max_ctx too long for this head geometry");
+  // the attention split-combine's weight of every (split, query column) of one
+  // (sequence, kv head) lives in the 4 x 16 x (hd+1) floats of LDS (the
+  // persistent forward keeps the split maxima and sums there, two per pair)
+  const size_t combine = (size_t)Lo.max_splits * SPEC_MAX_SPAN * Lo.G * ((d.flags & SPEC_FLAG_PERSISTENT) ? 2 : 1);
+  if (combine > (size_t)4 * 16 * (Lo.hd + 1)) return fail("max_ctx too long for this head geometry");
   // the split-K partial sums of a column pair are reduced from registers
-  for (int K : {Lo.H, Lo.DQ, Lo.F})
-    if (K / (slice_steps(K) * 32) > 32) return fail("a GEMM depth needs more than 32 K slices");
+  if (d.flags & SPEC_FLAG_PERSISTENT)
+    for (int K : {Lo.H, Lo.DQ, Lo.F})
+      if (K / (slice_steps(K) * 32) > 32) return fail("a GEMM depth needs more than 32 K slices");
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -112,15 +135,15 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   };
   Lo.lay.resize((size_t)Lo.L);
   for (auto& l : Lo.lay) {
-    l.wqkv = take(packed_bf16_bytes(Lo.Nqkv, Lo.H));
-    l.wo = take(packed_bf16_bytes(Lo.H, Lo.DQ));
-    l.wgu = take(packed_bf16_bytes(Lo.Ngu, Lo.H));
-    l.wd = take(packed_bf16_bytes(Lo.H, Lo.F));
+    l.wqkv = take(mat_bytes(Lo.fmt, Lo.Nqkv, Lo.H));
+    l.wo = take(mat_bytes(Lo.fmt, Lo.H, Lo.DQ));
+    l.wgu = take(mat_bytes(Lo.fmt, Lo.Ngu, Lo.H));
+    l.wd = take(mat_bytes(Lo.fmt, Lo.H, Lo.F));
     l.g_attn = take((size_t)Lo.H * 4);
     l.g_ffn = take((size_t)Lo.H * 4);
   }
   Lo.emb = take((size_t)Lo.V * Lo.H * 2);
-  Lo.wlm = take(packed_bf16_bytes(Lo.V, Lo.H));
+  Lo.wlm = take(mat_bytes(Lo.fmt, Lo.V, Lo.H));
   Lo.g_final = take((size_t)Lo.H * 4);
   Lo.weights_bytes = off;
 
@@ -264,6 +287,7 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.W = W;
+  if (c->lo.fmt == FMT_INT4) p.scales = (const uint16_t*)((const uint8_t*)W + packed_int4_frag_bytes(N, K));
   p.N = N;
   p.K = K;
   p.R = R;
@@ -334,7 +358,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.seq_ids = seq_ids;
     gl.S = S;
     gl.n_seq = n_seq;
-    HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, st));
+    HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, L.fmt, st));
     return SPEC_OK;
   }
   const LayerOff& lw = L.lay[(size_t)l];
@@ -358,7 +382,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.n_kv = L.nkv;
       g.hd = L.hd;
       g.rope = c->ws<float>(L.rope);
-      HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, st));
+      HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, L.fmt, st));
       return SPEC_OK;
     }
     case SPEC_OP_ATTN: {
@@ -388,7 +412,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, st));
+      HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, L.fmt, st));
       return SPEC_OK;
     }
     case SPEC_OP_GATEUP: {
@@ -399,7 +423,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.ss_n = L.H / 64;
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
-      HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, st));
+      HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, L.fmt, st));
       return SPEC_OK;
     }
     case SPEC_OP_DOWN: {
@@ -408,7 +432,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.lda = L.F;
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, st));
+      HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, L.fmt, st));
       return SPEC_OK;
     }
   }
@@ -671,32 +695,42 @@ int spec_destroy(spec_ctx* c) {
   return SPEC_OK;
 }
 
+// Pack one canonical matrix (rows x cols, source row s -> fused row map(s))
+// into the fused matrix at dst of the context's weight format.
+static hipError_t pack_matrix(spec_ctx* c, const void* src, const void* scales, int rows, int cols, uint8_t* dst,
+                              int fused_rows, int kind, int row0, int hd) {
+  if (c->lo.fmt == FMT_INT4)
+    return launch_pack_int4((const uint8_t*)src, (const uint16_t*)scales, rows, cols, dst,
+                            (uint16_t*)(dst + packed_int4_frag_bytes(fused_rows, cols)), kind, row0, hd, c->st);
+  return launch_pack_bf16((const uint16_t*)src, rows, cols, dst, kind, row0, hd, c->st);
+}
+
 int spec_load_matrix(spec_ctx* c, int layer, int which, const void* src, const void* scales) {
-  (void)scales;
   if (!c || !src) return c ? set_err(c, SPEC_EINVAL, "null source") : SPEC_EINVAL;
+  if (c->lo.fmt == FMT_INT4 && which != SPEC_MAT_EMB && !scales)
+    return set_err(c, SPEC_EINVAL, "int4 matrices need their scales");
   const Layout& L = c->lo;
   const bool global = (which == SPEC_MAT_EMB || which == SPEC_MAT_LM);
   if (which < 0 || which > SPEC_MAT_LM) return set_err(c, SPEC_EINVAL, "unknown matrix id");
   if (!global && (layer < 0 || layer >= L.L)) return set_err(c, SPEC_EINVAL, "layer out of range");
-  const uint16_t* s = (const uint16_t*)src;
   hipError_t e = hipSuccess;
   int slot_id;
   if (which == SPEC_MAT_EMB) {
     e = hipMemcpyAsync(c->W + L.emb, src, (size_t)L.V * L.H * 2, hipMemcpyDeviceToDevice, c->st);
     slot_id = L.L * 9 + 0;
   } else if (which == SPEC_MAT_LM) {
-    e = launch_pack_bf16(s, L.V, L.H, c->W + L.wlm, 0, 0, 0, c->st);
+    e = pack_matrix(c, src, scales, L.V, L.H, c->W + L.wlm, L.V, 0, 0, 0);
     slot_id = L.L * 9 + 1;
   } else {
     const LayerOff& lw = L.lay[(size_t)layer];
     switch (which) {
-      case SPEC_MAT_Q: e = launch_pack_bf16(s, L.DQ, L.H, c->W + lw.wqkv, 1, 0, L.hd, c->st); break;
-      case SPEC_MAT_K: e = launch_pack_bf16(s, L.DK, L.H, c->W + lw.wqkv, 1, L.DQ, L.hd, c->st); break;
-      case SPEC_MAT_V: e = launch_pack_bf16(s, L.DK, L.H, c->W + lw.wqkv, 0, L.DQ + L.DK, 0, c->st); break;
-      case SPEC_MAT_O: e = launch_pack_bf16(s, L.H, L.DQ, c->W + lw.wo, 0, 0, 0, c->st); break;
-      case SPEC_MAT_GATE: e = launch_pack_bf16(s, L.F, L.H, c->W + lw.wgu, 2, 0, 0, c->st); break;
-      case SPEC_MAT_UP: e = launch_pack_bf16(s, L.F, L.H, c->W + lw.wgu, 2, 1, 0, c->st); break;
-      case SPEC_MAT_DOWN: e = launch_pack_bf16(s, L.H, L.F, c->W + lw.wd, 0, 0, 0, c->st); break;
+      case SPEC_MAT_Q: e = pack_matrix(c, src, scales, L.DQ, L.H, c->W + lw.wqkv, L.Nqkv, 1, 0, L.hd); break;
+      case SPEC_MAT_K: e = pack_matrix(c, src, scales, L.DK, L.H, c->W + lw.wqkv, L.Nqkv, 1, L.DQ, L.hd); break;
+      case SPEC_MAT_V: e = pack_matrix(c, src, scales, L.DK, L.H, c->W + lw.wqkv, L.Nqkv, 0, L.DQ + L.DK, 0); break;
+      case SPEC_MAT_O: e = pack_matrix(c, src, scales, L.H, L.DQ, c->W + lw.wo, L.H, 0, 0, 0); break;
+      case SPEC_MAT_GATE: e = pack_matrix(c, src, scales, L.F, L.H, c->W + lw.wgu, L.Ngu, 2, 0, 0); break;
+      case SPEC_MAT_UP: e = pack_matrix(c, src, scales, L.F, L.H, c->W + lw.wgu, L.Ngu, 2, 1, 0); break;
+      case SPEC_MAT_DOWN: e = pack_matrix(c, src, scales, L.H, L.F, c->W + lw.wd, L.H, 0, 0, 0); break;
     }
     slot_id = slot(c, layer, which);
   }
@@ -1031,7 +1065,8 @@ int spec_op_bytes(const spec_model_desc* d, int op, int S, int ctx_len, double* 
   if (!d || !bytes_out || S < 1 || ctx_len < 0) return SPEC_EINVAL;
   const double H = d->hidden, hd = d->head_dim, DQ = (double)d->n_q_heads * hd, DK = (double)d->n_kv_heads * hd;
   const double F = d->ffn, V = d->vocab;
-  const double wb = 2.0;  // bf16 weight bytes
+  // weight bytes per element: bf16 2; int4 0.5 plus one bf16 scale per 128
+  const double wb = d->weight_format == SPEC_WFMT_INT4G128 ? 0.5 + 2.0 / 128.0 : 2.0;
   switch (op) {
     case SPEC_OP_EMBED: *bytes_out = S * H * 2.0; break;
     case SPEC_OP_QKV: *bytes_out = (DQ + 2 * DK) * H * wb + S * DK * 2 * 2.0; break;

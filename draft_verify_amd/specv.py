@@ -399,14 +399,15 @@ class Session:
     wq..wd, g_attn, g_ffn) or "global" (emb, lm, g_final)."""
 
     def __init__(self, shape: dict, weights, max_ctx: int, max_seqs: int = 1, max_rows: int = 16,
-                 n_blocks: int = 0, flags: int = 0, device: int = 0):
+                 n_blocks: int = 0, flags: int = 0, device: int = 0, fmt: str = "bf16"):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("libspecv needs an MI355X (gfx950) GPU; none is visible")
         self.torch = torch
         self.shape = dict(shape)
         self.dev = torch.device("cuda", device)
-        self.desc = make_desc(shape, max_ctx, max_seqs, max_rows, n_blocks, flags)
+        wfmt = {"bf16": SPEC_WFMT_BF16, "int4": SPEC_WFMT_INT4G128}[fmt]
+        self.desc = make_desc(shape, max_ctx, max_seqs, max_rows, n_blocks, flags, wfmt)
         sz = spec_query_buffers(self.desc)
         self.sizes = sz
         u8 = torch.uint8
@@ -422,25 +423,32 @@ class Session:
         self.ctx = spec_create(self.desc, bufs, self.stream.cuda_stream)
         self._load(weights)
 
+    def _load_matrix(self, layer, which, t):
+        """One canonical matrix: a bf16 tensor, or an int4 dict {q4, scales}."""
+        torch = self.torch
+        if isinstance(t, dict):
+            q = t["q4"].to(self.dev).contiguous()
+            sc = t["scales"].to(self.dev).contiguous()
+            torch.cuda.synchronize(self.dev)
+            spec_load_matrix(self.ctx, layer, which, q.data_ptr(), sc.data_ptr())
+        else:
+            t = t.to(self.dev).contiguous()
+            torch.cuda.synchronize(self.dev)
+            spec_load_matrix(self.ctx, layer, which, t.data_ptr())
+
     def _load(self, weights):
         torch = self.torch
         sh = self.shape
         with torch.cuda.stream(self.stream):
             for l in range(sh["n_layers"]):
                 for name, which in MAT_IDS.items():
-                    t = weights("layer", l, name).to(self.dev).contiguous()
-                    torch.cuda.synchronize(self.dev)
-                    spec_load_matrix(self.ctx, l, which, t.data_ptr())
-                    del t
+                    self._load_matrix(l, which, weights("layer", l, name))
                 for name, which in (("g_attn", SPEC_NORM_ATTN), ("g_ffn", SPEC_NORM_FFN)):
                     t = weights("layer", l, name).to(self.dev, torch.float32).contiguous()
                     torch.cuda.synchronize(self.dev)
                     spec_load_norm(self.ctx, l, which, t.data_ptr())
             for name, which in (("emb", SPEC_MAT_EMB), ("lm", SPEC_MAT_LM)):
-                t = weights("global", 0, name).to(self.dev).contiguous()
-                torch.cuda.synchronize(self.dev)
-                spec_load_matrix(self.ctx, 0, which, t.data_ptr())
-                del t
+                self._load_matrix(0, which, weights("global", 0, name))
             t = weights("global", 0, "g_final").to(self.dev, torch.float32).contiguous()
             torch.cuda.synchronize(self.dev)
             spec_load_norm(self.ctx, 0, SPEC_NORM_FINAL, t.data_ptr())

@@ -27,6 +27,9 @@ SHAPES = {
                  eps=1e-6, rope_theta=1e6),
     "qwen3_4b": dict(n_layers=36, hidden=2560, n_q=32, n_kv=8, head_dim=128, ffn=9728,
                      vocab=151936, eps=1e-6, rope_theta=1e6),
+    # the smallest decoder whose GEMM depths hold whole int4 groups of 128
+    "tiny_int4": dict(n_layers=2, hidden=128, n_q=4, n_kv=2, head_dim=32, ffn=256, vocab=256,
+                      eps=1e-6, rope_theta=1e6),
     "dense_32b": dict(n_layers=64, hidden=5120, n_q=64, n_kv=8, head_dim=128, ffn=25600,
                       vocab=151936, eps=1e-6, rope_theta=1e6),
 }

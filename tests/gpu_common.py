@@ -31,11 +31,11 @@ class Twin:
     """A GPU session and an oracle over the same seeded weights (sequence 0)."""
 
     def __init__(self, shape, weights, max_ctx, max_seqs=1, max_rows=16, flags=specv.SPEC_FLAG_KEEP_LOGITS,
-                 oracle_ctx=None, host_weights=None, orc=None):
+                 oracle_ctx=None, host_weights=None, orc=None, fmt="bf16"):
         """`orc`: an existing oracle over the same weights to share (not closed here)."""
         self.shape = shape
         self.sess = specv.Session(shape, specv.tree_weights(weights), max_ctx=max_ctx, max_seqs=max_seqs,
-                                  max_rows=max_rows, flags=flags)
+                                  max_rows=max_rows, flags=flags, fmt=fmt)
         self.own_orc = orc is None
         if orc is None:
             hw = host_weights if host_weights is not None else synth.to_numpy(weights)

@@ -45,10 +45,33 @@ def test_unsupported_shapes_are_rejected(bad):
     assert e.value.code == specv.SPEC_EINVAL
 
 
-def test_int4_format_is_refused_by_this_build():
-    d = specv.make_desc(synth.SHAPES["tiny"], max_ctx=64, weight_format=specv.SPEC_WFMT_INT4G128)
+def test_int4_needs_whole_groups():
+    """int4 group-128 weights need every GEMM depth to hold whole groups: the
+    tiny decoder (hidden 64) is refused, its group-aligned sibling and the
+    32B-class shape are accepted, and the persistent forward is bf16 only."""
+    i4 = specv.SPEC_WFMT_INT4G128
     with pytest.raises(specv.SpecError):
-        specv.spec_query_buffers(d)
+        specv.spec_query_buffers(specv.make_desc(synth.SHAPES["tiny"], max_ctx=64, weight_format=i4))
+    for name in ("tiny_int4", "dense_32b"):
+        specv.spec_query_buffers(specv.make_desc(synth.SHAPES[name], max_ctx=64, weight_format=i4))
+    with pytest.raises(specv.SpecError):
+        specv.spec_query_buffers(specv.make_desc(synth.SHAPES["tiny_int4"], max_ctx=64, weight_format=i4,
+                                                 flags=specv.SPEC_FLAG_PERSISTENT))
+
+
+def test_int4_op_bytes_match_the_32b_stream():
+    """Per forward of the 32B-class int4 model: 0.5 byte per weight plus one
+    bf16 scale per 128 weights (16.49 GB), and (ctx + S) x 262,144 B of KV."""
+    sh = synth.SHAPES["dense_32b"]
+    d = specv.make_desc(sh, max_ctx=8192 + 16, weight_format=specv.SPEC_WFMT_INT4G128)
+    L = sh["n_layers"]
+    per_fwd = sum(specv.spec_op_bytes(d, op, 1, 8192) for op in ("qkv", "o", "gateup", "down")) * L
+    per_fwd += specv.spec_op_bytes(d, "lm", 1, 8192)
+    params = L * (10240 * 5120 + 5120 * 8192 + 2 * 25600 * 5120 + 5120 * 25600) + 151936 * 5120
+    weights = per_fwd - L * 1 * 8 * 128 * 2 * 2
+    assert abs(weights - params * (0.5 + 2 / 128)) < 1
+    assert abs(weights - 16.49e9) < 0.01e9
+    assert abs(specv.spec_op_bytes(d, "attn", 1, 8192) * L - (8192 + 1) * 262_144) < 1
 
 
 def test_op_bytes_match_the_4b_stream():
