@@ -154,8 +154,13 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
 // XCD (ids are dealt round-robin over the 8 XCDs), keeping the partial sums
 // in one L2.
 
-template <int EPI>
+template <int EPI, int CT>
 __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
+
+// 16-column tiles per wave: int4 fragments are a quarter the bytes of bf16
+// ones, so an int4 wave takes four tiles (a 256-column block per workgroup)
+// to stream as many weight bytes per staged activation tile.
+constexpr int gemm_tiles_per_wave(int fmt) { return fmt == FMT_INT4 ? 4 : 1; }
 
 constexpr int kMaxSsIter = 8;  // RMSNorm partial sums per row / 16 (hidden <= 8192, host-checked)
 
@@ -177,16 +182,17 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t x) {
 template <int NK, int EPI, int FMT>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   static_assert(FMT == FMT_BF16 || NK % 4 == 0, "int4 slices hold whole 128-input groups");
-  constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per wave per slice
+  constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per tile per slice
+  constexpr int CT = gemm_tiles_per_wave(FMT);       // 16-column tiles per wave
   constexpr int UNITS = 16 * NK * 4;          // (row, step, lane group) units of 8 inputs per 16-row chunk
   constexpr int UPT = (UNITS + 255) / 256;    // units per thread
-  const int NB = P.N >> 6, ns = P.nslices;
+  const int NB = (P.N + 64 * CT - 1) / (64 * CT), ns = P.nslices;
   const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
   const int nb = (loc / ns) * 8 + xcd, sl = loc % ns;
   if (nb >= NB) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k0 = sl * NK * 32;
-  const int tile = nb * 4 + wave;
+  const int tile0 = (nb * 4 + wave) * CT;  // this wave's first tile; tiles past N (a ragged last block) idle
 
   __shared__ u32x4 sA[NK * 2 * 64];
   __shared__ float sR[kMaxRows];
@@ -219,15 +225,28 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   load_a(0);
 
   // bf16: one fragment per 32-input step; int4: one per 128-input group.
-  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / (32 * NK / NF)) + (size_t)sl * NF) * 64 + lane;
-  u32x4 b[NF];
+  u32x4 b[CT][NF];
+  float gs[CT][FMT == FMT_INT4 ? NF : 1];  // int4: this lane's column's group scales
 #pragma unroll
-  for (int j = 0; j < NF; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
-  float gs[FMT == FMT_INT4 ? NF : 1];  // int4: this lane's column's group scales
-  if constexpr (FMT == FMT_INT4) {
-    const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * (P.K / 128) + (size_t)sl * NF;
+  for (int c = 0; c < CT; ++c) {
+    const int tile = tile0 + c;
+    if (tile * 16 < P.N) {
+      const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * (P.K / (32 * NK / NF)) + (size_t)sl * NF) * 64 + lane;
 #pragma unroll
-    for (int g = 0; g < NF; ++g) gs[g] = bf16_bits_to_f32(sp[g]);
+      for (int j = 0; j < NF; ++j) b[c][j] = __builtin_nontemporal_load(wp + j * 64);
+      if constexpr (FMT == FMT_INT4) {
+        const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * (P.K / 128) + (size_t)sl * NF;
+#pragma unroll
+        for (int g = 0; g < NF; ++g) gs[c][g] = bf16_bits_to_f32(sp[g]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) b[c][j] = (u32x4){0u, 0u, 0u, 0u};
+      if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+        for (int g = 0; g < NF; ++g) gs[c][g] = 0.0f;
+      }
+    }
   }
 
   if (P.ss) {
@@ -293,42 +312,64 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     }
     __syncthreads();
     if (m0 + 16 < P.R) load_a(m0 + 16);  // the next chunk's A loads fly during this chunk's MFMA
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (FMT == FMT_INT4) {
       // Per group: exact integer weights times the activation pair, summed
       // over the group's four steps in fp32, then scaled by the column's
-      // group scale and added in group order.
+      // group scale and added in group order.  The A fragments of a step
+      // serve every tile of the wave.
 #pragma unroll
       for (int gi = 0; gi < NF; ++gi) {
-        f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 t[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) t[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const int j = gi * 4 + d;
-          const f16x8 bq = dequant8(b[gi][d]);
           const f16x8 ah = __builtin_bit_cast(f16x8, sA[(j * 2) * 64 + lane]);
           const f16x8 al = __builtin_bit_cast(f16x8, sA[(j * 2 + 1) * 64 + lane]);
-          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
-          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            // Opaque per row chunk, so the dequantised operands are rebuilt
+            // from the packed nibbles each time instead of being hoisted out
+            // of the chunk loop into 4x the registers.
+            uint32_t w = b[c][gi][d];
+            asm volatile("" : "+v"(w));
+            const f16x8 bq = dequant8(w);
+            t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t[c], 0, 0, 0);
+            t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t[c], 0, 0, 0);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += t[i] * gs[gi];
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[c][i] += t[c][i] * gs[c][gi];
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
-        const bf16x8 bw = __builtin_bit_cast(bf16x8, b[j]);
         const bf16x8 ah = __builtin_bit_cast(bf16x8, sA[(j * 2) * 64 + lane]);
         const bf16x8 al = __builtin_bit_cast(bf16x8, sA[(j * 2 + 1) * 64 + lane]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const bf16x8 bw = __builtin_bit_cast(bf16x8, b[c][j]);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[c], 0, 0, 0);
+        }
       }
     }
     // D layout: lane holds column lane%16 of rows 4*(lane/16) + i.
-    const int col = tile * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m0 + (lane >> 4) * 4 + i;
-      if (r < P.R) st_dev(P.part + ((size_t)sl * P.R + r) * P.N + col, acc[i]);
+    for (int c = 0; c < CT; ++c) {
+      const int col = (tile0 + c) * 16 + (lane & 15);
+      if (col < P.N)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + (lane >> 4) * 4 + i;
+          if (r < P.R) st_dev(P.part + ((size_t)sl * P.R + r) * P.N + col, acc[c][i]);
+        }
     }
     __syncthreads();  // sA is restaged for the next 16 rows
   }
@@ -342,27 +383,33 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   __syncthreads();
   if (!sLast) return;
   if (tid == 0) P.cnt[nb] = 0u;  // ready for the next launch
-  gemm_epilogue<EPI>(P, nb, (float*)sA);
+  gemm_epilogue<EPI, CT>(P, nb, (float*)sA);
 }
 
-// The epilogue's column pairs: pair idx = (row idx/32, columns nb*64 +
-// 2*(idx%32) + {0,1}), summed over the K slices in slice order.  Each thread
-// takes two pairs at a time and issues every slice load of them (up to 8
-// slices per round) before the first add, so the gather costs one memory
-// round trip per two pairs and per 8 slices.
-template <class F>
+// The epilogue's column pairs of block nb (64*CT columns): pair idx = (row
+// idx/(32CT), columns nb*64CT + 2*(idx%(32CT)) + {0,1}), summed over the K
+// slices in slice order; pairs past N (a ragged last block) are skipped, 64
+// columns at a time.  Each thread takes two pairs at a time and issues every
+// slice load of them (up to 8 slices per round) before the first add, so the
+// gather costs one memory round trip per two pairs and per 8 slices.  Every
+// 32 consecutive pairs are 64 columns of one row (the shuffle groups of the
+// epilogues).
+template <int CT, class F>
 __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
-  constexpr int U = 2;
-  const int n = P.R * 32, ns = P.nslices;
+  constexpr int U = 2, PR = 32 * CT;
+  const int n = P.R * PR, ns = P.nslices;
   const unsigned stride = (unsigned)P.R * (unsigned)P.N;  // floats; the partial buffer is < 4 GiB
   for (int base = 0; base < n; base += U * 256) {
     float v0[U], v1[U];
     unsigned off[U];
+    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = base + u * 256 + threadIdx.x;
+      const int c = nb * 64 * CT + 2 * (idx % PR);
       v0[u] = v1[u] = 0.0f;
-      off[u] = (unsigned)(idx >> 5) * (unsigned)P.N + (unsigned)(nb * 64 + 2 * (idx & 31));
+      ok[u] = idx < n && c < P.N;
+      off[u] = (unsigned)(idx / PR) * (unsigned)P.N + (unsigned)c;
     }
     for (int s0 = 0; s0 < ns; s0 += 8) {
       float2 t[U][8];
@@ -370,13 +417,12 @@ __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (base + u * 256 + (int)threadIdx.x < n && s0 + i < ns)
-            t[u][i] = ld_dev2(P.part + (off[u] + (unsigned)(s0 + i) * stride));
+          if (ok[u] && s0 + i < ns) t[u][i] = ld_dev2(P.part + (off[u] + (unsigned)(s0 + i) * stride));
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (base + u * 256 + (int)threadIdx.x < n && s0 + i < ns) {
+          if (ok[u] && s0 + i < ns) {
             v0[u] += t[u][i].x;
             v1[u] += t[u][i].y;
           }
@@ -384,7 +430,7 @@ __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = base + u * 256 + threadIdx.x;
-      if (idx < n) f(idx, idx >> 5, nb * 64 + 2 * (idx & 31), v0[u], v1[u]);
+      if (ok[u]) f(idx, idx / PR, nb * 64 * CT + 2 * (idx % PR), v0[u], v1[u]);
     }
   }
 }
@@ -396,11 +442,11 @@ __device__ __forceinline__ void row_pos(const GemmParams& P, int r, int& seq, in
   pos = P.kv_len[seq] + i;
 }
 
-template <>
-__device__ void gemm_epilogue<EPI_QKV>(const GemmParams& P, int nb, float*) {
+template <int CT>
+__device__ void epi_qkv(const GemmParams& P, int nb) {
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
-  for_pairs(P, nb, [&](int, int r, int c, float v0, float v1) {
+  for_pairs<CT>(P, nb, [&](int, int r, int c, float v0, float v1) {
     int seq, pos;
     row_pos(P, r, seq, pos);
     const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
@@ -428,10 +474,10 @@ __device__ void gemm_epilogue<EPI_QKV>(const GemmParams& P, int nb, float*) {
   });
 }
 
-template <>
-__device__ void gemm_epilogue<EPI_RESID>(const GemmParams& P, int nb, float*) {
-  const int NB = P.N >> 6;
-  for_pairs(P, nb, [&](int idx, int r, int c, float v0, float v1) {
+template <int CT>
+__device__ void epi_resid(const GemmParams& P, int nb) {
+  const int NB = P.N >> 6;  // RMSNorm partial sums: one per 64 columns
+  for_pairs<CT>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
     float2 x = *xp;
     x.x = x.x + v0;
@@ -440,22 +486,22 @@ __device__ void gemm_epilogue<EPI_RESID>(const GemmParams& P, int nb, float*) {
     float t = x.x * x.x + x.y * x.y;
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-    if ((idx & 31) == 0) P.ss_out[(size_t)r * NB + nb] = t;
+    if ((idx & 31) == 0) P.ss_out[(size_t)r * NB + (c >> 6)] = t;
   });
 }
 
-template <>
-__device__ void gemm_epilogue<EPI_SWIGLU>(const GemmParams& P, int nb, float*) {
+template <int CT>
+__device__ void epi_swiglu(const GemmParams& P, int nb) {
   const int F = P.N >> 1;
-  for_pairs(P, nb, [&](int, int r, int c, float g, float u) {
+  for_pairs<CT>(P, nb, [&](int, int r, int c, float g, float u) {
     P.h[(size_t)r * F + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
   });
 }
 
-template <>
-__device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) {
+template <int CT>
+__device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
   __shared__ int sFinal;
-  for_pairs(P, nb, [&](int idx, int r, int c, float v0, float v1) {
+  for_pairs<CT>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     if (P.logits) {
       float2* lp = (float2*)(P.logits + (size_t)r * P.N + c);
       *lp = make_float2(v0, v1);
@@ -475,7 +521,7 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old = atomicAdd(P.lm_cnt, 1u);
-    sFinal = (old == (unsigned)((P.N >> 6) - 1));
+    sFinal = (old == (unsigned)((P.N + 64 * CT - 1) / (64 * CT) - 1));
   }
   __syncthreads();
   if (!sFinal) return;
@@ -508,6 +554,14 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
   }
 }
 
+template <int EPI, int CT>
+__device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
+  if constexpr (EPI == EPI_QKV) epi_qkv<CT>(P, nb);
+  else if constexpr (EPI == EPI_RESID) epi_resid<CT>(P, nb);
+  else if constexpr (EPI == EPI_SWIGLU) epi_swiglu<CT>(P, nb);
+  else epi_lm<CT>(P, nb, sbuf);
+}
+
 // -------------------------------------------------------------- attention
 //
 // Grid (split, kv head, sequence); a split is 256 keys at absolute positions
@@ -518,9 +572,9 @@ __device__ void gemm_epilogue<EPI_LM>(const GemmParams& P, int nb, float* sbuf) 
 // the V^T operand is read straight from memory.  Query columns are
 // (span row, head of the GQA group).  Each wave's chunk softmax is combined
 // across the four waves in LDS in wave order, each split's (max, sum, o)
-// goes to memory, and the last split to arrive for a (sequence, kv head)
-// combines the splits in split order.  Row i attends keys [0, p+i]; a chunk
-// or split lying wholly past a row's position contributes exactly nothing.
+// goes to memory, and k_attn_combine merges the splits of every query
+// column.  Row i attends keys [0, p+i]; a chunk or split lying wholly past a
+// row's position contributes exactly nothing.
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
@@ -539,7 +593,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 
   __shared__ float sO[4][16][HD + 1];
   __shared__ float sM[4][16], sL[4][16], sF[4][16];
-  __shared__ int sLast;
 
   // This wave's four blocks, loaded once and reused for every query tile.
   const int kb0 = split * 16 + wave * 4;
@@ -669,67 +722,65 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
     __syncthreads();
   }
 
-  wait_mem();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomicAdd(&P.cnt[b * P.n_kv + kvh], 1u);
-    sLast = (old == (unsigned)(n_act - 1));
-  }
-  __syncthreads();
-  if (!sLast) return;
-  if (tid == 0) P.cnt[b * P.n_kv + kvh] = 0u;
-  // Combine the splits that hold keys at or before each row's position:
-  // first the weight exp(m_s - M) / L of every (split, column), in LDS, then
-  // the values, in split order.
+}
+
+// Split combine: grid (ceil(QC/4), kv head, sequence); wave w combines query
+// column 4*blockIdx.x + w over the splits holding keys at or before its
+// row's position.  Lane i reduces splits i, i+64, ...: the maximum and the
+// sum of l_s exp(m_s - M) by fixed xor trees, then every lane takes output
+// pairs and sums w_s o_s in split order with eight split loads in flight.
+// The order depends only on the row's position, never on the other rows.
+constexpr int kMaxCombineSplits = 256;  // host-checked: max_ctx <= 65536
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = P.n_q / P.n_kv, S = P.S, QC = S * G;
+  const int qcol = blockIdx.x * 4 + wave;
+  __shared__ float sW[4][kMaxCombineSplits];
+  if (qcol >= QC) return;  // whole waves; no barrier below
+  const int seq = P.seq_ids[b];
+  const int p = P.kv_len[seq];
+  const int iq = qcol / G, head = kvh * G + qcol % G;
+  const int nsp = ((p + iq) >> 8) + 1;
   const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
-  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC) * (HD + 2);
-  float* sW = &sO[0][0][0];  // [n_act][QC] weights, free after the tile loop (host-checked to fit)
-  for (int qcol = tid; qcol < QC; qcol += 256) {
-    const int nsp = ((p + qcol / G) >> 8) + 1;
-    const float* ml0 = base + (size_t)qcol * (HD + 2);
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < nsp; s0 += 8) {  // split maxima, eight loads in flight
-      float m[8];
+  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+  float M = -INFINITY;
+  for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, base[sp * stride]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float L = 0.0f;
+  for (int sp = lane; sp < nsp; sp += 64) {
+    const float2 ml = *(const float2*)(base + sp * stride);
+    const float f = expf(ml.x - M);
+    sW[wave][sp] = f;
+    L += ml.y * f;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  const float inv = 1.0f / L;
+  for (int sp = lane; sp < nsp; sp += 64) sW[wave][sp] *= inv;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  const int DQ = P.n_q * HD;
+  for (int dp = lane; dp < HD / 2; dp += 64) {
+    const float* src = base + 2 + 2 * dp;
+    float o0 = 0.0f, o1 = 0.0f;
+    for (int s0 = 0; s0 < nsp; s0 += 8) {
+      float2 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) m[i] = ld_dev(ml0 + (size_t)(s0 + i) * stride);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) M = fmaxf(M, m[i]);
-    }
-    float L = 0.0f;
-    for (int s0 = 0; s0 < nsp; s0 += 8) {  // weights exp(m_s - M) and the sum, in split order
-      float2 ml[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) ml[i] = ld_dev2(ml0 + (size_t)(s0 + i) * stride);
+        if (s0 + i < nsp) v[i] = *(const float2*)(src + (size_t)(s0 + i) * stride);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (s0 + i < nsp) {
-          const float f = expf(ml[i].x - M);
-          sW[(s0 + i) * QC + qcol] = f;
-          L += ml[i].y * f;
+          const float w = sW[wave][s0 + i];
+          o0 += v[i].x * w;
+          o1 += v[i].y * w;
         }
     }
-    for (int sp = 0; sp < nsp; ++sp) sW[sp * QC + qcol] /= L;
-  }
-  __syncthreads();
-  for (int e = tid; e < QC * (HD / 2); e += 256) {
-    const int qcol = e / (HD / 2), d = 2 * (e % (HD / 2));
-    const int iq = qcol / G, head = kvh * G + qcol % G;
-    const int nsp = ((p + iq) >> 8) + 1;
-    const float* src = base + (size_t)qcol * (HD + 2) + 2 + d;
-    float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll 4
-    for (int sp = 0; sp < nsp; ++sp) {
-      const float2 v = ld_dev2(src + sp * stride);
-      const float f = sW[sp * QC + qcol];
-      o0 += v.x * f;
-      o1 += v.y * f;
-    }
-    float* op = P.out + (size_t)(b * S + iq) * DQ + head * HD + d;
-    op[0] = o0;
-    op[1] = o1;
+    *(float2*)(P.out + (size_t)(b * S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0, o1);
   }
 }
 
@@ -737,7 +788,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 
 template <int EPI>
 static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStream_t st) {
-  const int NB = p.N / 64;
+  const int bw = 64 * gemm_tiles_per_wave(fmt);
+  const int NB = (p.N + bw - 1) / bw;
   const int grid = ((NB + 7) / 8) * 8 * p.nslices;
   if (fmt == FMT_INT4) {
     if (!p.scales) return hipErrorInvalidValue;
@@ -771,12 +823,26 @@ hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_
 }
 
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
+  if (p.max_splits > kMaxCombineSplits) return hipErrorInvalidValue;
   const dim3 grid(p.max_splits, p.n_kv, p.n_seq);
+  const dim3 cgrid((p.S * (p.n_q / p.n_kv) + 3) / 4, p.n_kv, p.n_seq);
   switch (hd) {
-    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, p); break;
-    case 32: hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, st, p); break;
-    case 16: hipLaunchKernelGGL(k_attn<16>, grid, dim3(256), 0, st, p); break;
+    case 128:
+      hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, st, p);
+      break;
+    case 64:
+      hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, st, p);
+      break;
+    case 32:
+      hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_attn_combine<32>, cgrid, dim3(256), 0, st, p);
+      break;
+    case 16:
+      hipLaunchKernelGGL(k_attn<16>, grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL(k_attn_combine<16>, cgrid, dim3(256), 0, st, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

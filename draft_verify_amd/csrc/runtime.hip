@@ -117,11 +117,15 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
     return fail("no persistent forward is compiled for this shape");
-  // the attention split-combine's weight of every (split, query column) of one
-  // (sequence, kv head) lives in the 4 x 16 x (hd+1) floats of LDS (the
-  // persistent forward keeps the split maxima and sums there, two per pair)
-  const size_t combine = (size_t)Lo.max_splits * SPEC_MAX_SPAN * Lo.G * ((d.flags & SPEC_FLAG_PERSISTENT) ? 2 : 1);
-  if (combine > (size_t)4 * 16 * (Lo.hd + 1)) return fail("max_ctx too long for this head geometry");
+  // the persistent forward's attention split-combine keeps the split maxima
+  // and sums of one (sequence, kv head) in 4 x 16 x (hd+1) floats of LDS; the
+  // per-kernel combine holds up to 256 split weights per query column
+  if (d.flags & SPEC_FLAG_PERSISTENT) {
+    if ((size_t)2 * Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
+      return fail("max_ctx too long for this head geometry");
+  } else if (Lo.max_splits > 256) {
+    return fail("max_ctx must be at most 65536");
+  }
   // the split-K partial sums of a column pair are reduced from registers
   if (d.flags & SPEC_FLAG_PERSISTENT)
     for (int K : {Lo.H, Lo.DQ, Lo.F})
