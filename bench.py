@@ -16,8 +16,11 @@ timed rounds; `value` is committed tokens per second over those K rounds.
 Also on the JSON line: the same rounds with drafting off (spec-off tok/s), the
 256-token end-to-end A/B of the page's protocol with the perfect- and
 all-wrong-draft bounds, the verify-cost sweep c_v(S) for S = 1..16 at an
-848-token context, the roofline of the dominant kernel (the gate/up GEMM:
-99.6 MB of bf16 weights per launch) and the CPU oracle timed on this host.
+848-token context, the 16-sequence paged batched verify (K = 7, 128 rows,
+contexts U[512, 4096]) against its spec-off batched step, the int4 32B-class
+model at an 8192-token context (c_v sweep and a 256-token adaptive-K run),
+the roofline of the dominant kernel (the gate/up GEMM: 99.6 MB of bf16
+weights per launch) and the CPU oracle timed on this host.
 """
 import argparse
 import hashlib
@@ -194,6 +197,56 @@ def batched_bench(steps, warmup, log_every=8):
             "on": on, "off": off, "ratio": round(on["tok_s"] / off["tok_s"], 3)}
 
 
+INT4_CTX = 8192
+
+
+def int4_bench(cv_iters=15, gen_tokens=256):
+    """The 32B-class dense shape (64 layers, hidden 5120, 64q/8kv heads x 128,
+    FFN 25600, vocab 151936) with int4 group-128 weights (seeded), batch 1 at
+    an 8192-token uniform context: the verify-cost sweep c_v(S) for S = 1..16,
+    and one spec-off / spec-on (adaptive K, cap 7) generation of 256 tokens
+    from the same context."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["dense_32b"]
+    t = time.time()
+    sess = specv.Session(shape, specv.synth_weights(shape, seed=0, device="cuda", fmt="int4"),
+                         max_ctx=INT4_CTX + gen_tokens + 64, fmt="int4")
+    torch.cuda.empty_cache()
+    c, d = sess.ctx, sess.desc
+    prompt = synth.uniform_prompt(5, shape["vocab"], INT4_CTX)
+    specv.spec_prefill(c, prompt)
+    log(f"int4: session + {INT4_CTX}-token prefill in {time.time() - t:.1f}s")
+    rng = np.random.default_rng(6)
+    ms = []
+    for S in range(1, 17):
+        m = specv.spec_time_verify(c, rng.integers(0, shape["vocab"], (cv_iters + 5, S)).astype(np.int32))
+        ms.append(float(np.median(m[5:])))
+    byts = []
+    for S in range(1, 17):
+        b = specv.spec_op_bytes(d, "lm", S, INT4_CTX) + specv.spec_op_bytes(d, "embed", S, INT4_CTX)
+        b += shape["n_layers"] * sum(specv.spec_op_bytes(d, op, S, INT4_CTX)
+                                     for op in ("qkv", "attn", "o", "gateup", "down"))
+        byts.append(b)
+    per_op = {op: round(specv.spec_time_op(c, op, 1, 3), 2) for op in specv.OPS}
+    off, s_off = specv.spec_generate(c, prompt, gen_tokens, spec=False)
+    on, s_on = specv.spec_generate(c, prompt, gen_tokens, spec=True, fixed_k=0, k_cap=7)
+    sess.close()
+    del sess
+    torch.cuda.empty_cache()
+    return {"workload": f"32B-class dense int4 group-128, batch 1, {INT4_CTX}-token uniform context",
+            "ctx": INT4_CTX, "ms": [round(x, 4) for x in ms], "c_v": [round(x / ms[0], 3) for x in ms],
+            "gbps": [round(b / (x * 1e-3) / 1e9, 1) for b, x in zip(byts, ms)],
+            "bytes_S1": round(byts[0]), "hbm_frac_S1": round(byts[0] / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_op_us_S1": per_op,
+            "gen": {"tokens": gen_tokens, "off_tok_s": round((gen_tokens - 1) / s_off["decode_s"], 2),
+                    "on_tok_s": round((gen_tokens - 1) / s_on["decode_s"], 2),
+                    "ratio": round(s_off["decode_s"] / s_on["decode_s"], 3),
+                    "streams_equal": bool(np.array_equal(off, on)), "forwards_on": s_on["forwards"],
+                    "accept_hist_on": s_on["accept_hist"][:8]}}
+
+
 def counters_workload():
     """Short workload for the rocprofv3 --pmc passes: ten S=1 verify forwards at
     the 848-token context, then one device copy of exactly 1 GiB, whose
@@ -293,6 +346,7 @@ def main():
     ap.add_argument("--batch-steps", type=int, default=32)
     ap.add_argument("--batch-warmup", type=int, default=5)
     ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-int4", action="store_true")
     ap.add_argument("--counters", action="store_true", help="short workload for rocprofv3 --pmc passes")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
@@ -414,6 +468,11 @@ def main():
         batched = batched_bench(args.batch_steps, args.batch_warmup)
         log(f"batched: {batched}")
 
+    int4 = None
+    if not args.no_int4:
+        int4 = int4_bench()
+        log(f"int4: {int4}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, prompt)
@@ -432,7 +491,7 @@ def main():
                        "batch": 1, "prompt_tokens": PROMPT_TOKENS, "parallelism": "single GPU"},
             "spec_off_tok_s": round(off_tok_s, 3), "speedup": round(on_tok_s / off_tok_s, 4),
             "tok_per_forward": round((on_st["accepted"] + on_st["forwards"]) / on_st["forwards"], 3),
-            "e2e_256": e2e_256, "cv": cv, "batched_paged": batched, "roofline": roofline,
+            "e2e_256": e2e_256, "cv": cv, "batched_paged": batched, "int4_32b": int4, "roofline": roofline,
             "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
