@@ -111,6 +111,20 @@ struct EmbedParams {
   int H;
 };
 
+// One GEMM unit of a workgroup's walk in the persistent forward: the 64-column
+// block nb of GEMM phase g (4l + {QKV, O, gate/up, down}, 4L = LM head) and
+// the K slice sl of nk 32-input steps.  woff is the byte offset, in the
+// weight arena, of the unit's first fragment for streamer wave 0; wave w
+// adds w * tile_stride.  Built on the host once per context.
+struct FwdUnit {  // 32-bit fields only: scalar loads read whole dwords
+  uint64_t woff;
+  uint32_t tile_stride;
+  int32_t g, nk, nb, sl, pad;
+};
+static_assert(sizeof(FwdUnit) == 32, "unit table entries are 32 bytes");
+constexpr int kFwdMaxGrid = 1024;  // workgroups the unit table is sized for
+constexpr int kFwdMaxWalk = 640;   // units one workgroup walks (its LDS copy)
+
 // Everything one persistent forward launch needs (forward.hip).
 struct FwdParams {
   // shape
@@ -136,6 +150,10 @@ struct FwdParams {
   unsigned long long* argkey;
   int32_t *status, *err;
   unsigned long long* clock;  // per-phase start stamps of workgroup 0, or null
+  // unit table: workgroup wg's units of GEMM phase g are
+  // units[unit_first[wg * (4L + 2) + g] .. unit_first[wg * (4L + 2) + g + 1])
+  const FwdUnit* units;
+  const int32_t* unit_first;
   // step
   const StepDev* step;
   const int32_t *tokens, *seq_ids;

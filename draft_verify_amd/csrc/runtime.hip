@@ -65,7 +65,8 @@ struct Layout {
   size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
   // workspace
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
-      logits, done, exit_cnt, err, clock, workspace_bytes;
+      logits, done, exit_cnt, err, clock, units, unit_first, workspace_bytes;
+  size_t n_units;  // GEMM units of one forward over all workgroups (persistent forward)
   int n_phases;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
@@ -117,6 +118,8 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
     return fail("no persistent forward is compiled for this shape");
+  if ((d.flags & SPEC_FLAG_PERSISTENT) && d.max_rows > 16)
+    return fail("the persistent forward takes at most 16 rows per forward");
   // the persistent forward's attention split-combine keeps the split maxima
   // and sums of one (sequence, kv head) in 4 x 16 x (hd+1) floats of LDS; the
   // per-kernel combine holds up to 256 split weights per query column
@@ -187,6 +190,17 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.exit_cnt = take(4);
   Lo.err = take(4);
   Lo.clock = take((size_t)(Lo.n_phases + 2) * 8);
+  Lo.n_units = 0;
+  Lo.units = Lo.unit_first = (size_t)-1;
+  if (d.flags & SPEC_FLAG_PERSISTENT) {
+    // every (64-column block, K slice) pair of every GEMM is one unit
+    auto units_of = [&](int N, int K, int nk) { return (size_t)(N / 64) * (size_t)(K / (32 * nk)); };
+    Lo.n_units = (size_t)Lo.L * (units_of(Lo.Nqkv, Lo.H, Lo.nk_qkv) + units_of(Lo.H, Lo.DQ, Lo.nk_o) +
+                                 units_of(Lo.Ngu, Lo.H, Lo.nk_gu) + units_of(Lo.H, Lo.F, Lo.nk_d)) +
+                 units_of(Lo.V, Lo.H, Lo.nk_lm);
+    Lo.units = take(Lo.n_units * sizeof(FwdUnit));
+    Lo.unit_first = take((size_t)kFwdMaxGrid * (4 * Lo.L + 2) * 4);
+  }
   Lo.workspace_bytes = off;
 
   off = 0;
@@ -501,6 +515,59 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   return SPEC_OK;
 }
 
+// The persistent forward's unit table for a grid of G workgroups.  Workgroup
+// wg keeps K slice wg % ns of a GEMM and walks its 64-column blocks
+// wg / ns + k * (G / ns), k = 0, 1, ... (workgroups past (G / ns) * ns idle).
+int build_unit_table(spec_ctx* c, int G) {
+  const Layout& L = c->lo;
+  if (G < 1 || G > kFwdMaxGrid) return set_err(c, SPEC_EINVAL, "persistent grid out of range");
+  const int NP = 4 * L.L + 2;
+  std::vector<FwdUnit> units;
+  units.reserve(L.n_units);
+  std::vector<int32_t> first((size_t)kFwdMaxGrid * NP, 0);
+  struct Gm { size_t w; int N, K, nk; };
+  auto gemm_of = [&](int g) -> Gm {
+    if (g == 4 * L.L) return {L.wlm, L.V, L.H, L.nk_lm};
+    const LayerOff& lw = L.lay[(size_t)(g / 4)];
+    switch (g & 3) {
+      case 0: return {lw.wqkv, L.Nqkv, L.H, L.nk_qkv};
+      case 1: return {lw.wo, L.H, L.DQ, L.nk_o};
+      case 2: return {lw.wgu, L.Ngu, L.H, L.nk_gu};
+      default: return {lw.wd, L.H, L.F, L.nk_d};
+    }
+  };
+  for (int wg = 0; wg < G; ++wg) {
+    for (int g = 0; g <= 4 * L.L; ++g) {
+      first[(size_t)wg * NP + g] = (int32_t)units.size();
+      const Gm m = gemm_of(g);
+      const int ns = m.K / (32 * m.nk), Gs = G / ns, NB = m.N / 64;
+      if (Gs < 1) return set_err(c, SPEC_EINVAL, "persistent grid smaller than a GEMM's K slices");
+      if (wg >= Gs * ns) continue;
+      const int sl = wg % ns;
+      for (int nb = wg / ns; nb < NB; nb += Gs) {
+        FwdUnit u;
+        memset(&u, 0, sizeof(u));
+        const size_t tile0 = (size_t)nb * 4;
+        u.woff = m.w + (tile0 * (size_t)(m.K / 32) + (size_t)sl * m.nk) * 1024;
+        u.tile_stride = (uint32_t)((size_t)(m.K / 32) * 1024);
+        u.g = g;
+        u.nk = m.nk;
+        u.nb = nb;
+        u.sl = sl;
+        units.push_back(u);
+      }
+    }
+    first[(size_t)wg * NP + 4 * L.L + 1] = (int32_t)units.size();
+    if (units.size() - (size_t)first[(size_t)wg * NP] > (size_t)kFwdMaxWalk)
+      return set_err(c, SPEC_EINVAL, "a workgroup's walk exceeds the persistent forward's LDS unit table");
+  }
+  if (units.size() > L.n_units) return set_err(c, SPEC_EINVAL, "unit table overflow");
+  HIPCHK(c, hipMemcpyAsync(c->WS + L.units, units.data(), units.size() * sizeof(FwdUnit), hipMemcpyHostToDevice, c->st));
+  HIPCHK(c, hipMemcpyAsync(c->WS + L.unit_first, first.data(), first.size() * 4, hipMemcpyHostToDevice, c->st));
+  HIPCHK(c, hipStreamSynchronize(c->st));
+  return SPEC_OK;
+}
+
 FwdParams fwd_params(spec_ctx* c, int n_seq, int S, bool with_clock) {
   const Layout& L = c->lo;
   FwdParams p;
@@ -528,6 +595,8 @@ FwdParams fwd_params(spec_ctx* c, int n_seq, int S, bool with_clock) {
   p.argkey = c->ws<unsigned long long>(L.argkey);
   p.status = c->ws<int32_t>(L.status); p.err = c->ws<int32_t>(L.err);
   p.clock = with_clock ? c->ws<unsigned long long>(L.clock) : nullptr;
+  p.units = c->ws<FwdUnit>(L.units);
+  p.unit_first = c->ws<int32_t>(L.unit_first);
   const StepDev* sd = c->ws<StepDev>(L.step);
   p.step = sd;
   p.tokens = (const int32_t*)(sd + 1);
@@ -686,7 +755,12 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
       delete c;
       return SPEC_EHIP;
     }
-    c->fwd_grid = std::min(occ, 2) * cus;
+    c->fwd_grid = std::min(cus, kFwdMaxGrid);  // one 512-thread workgroup per CU
+    if (build_unit_table(c, c->fwd_grid) != SPEC_OK) {
+      g_create_error = c->err;
+      delete c;
+      return SPEC_EINVAL;
+    }
   }
   *out = c;
   return SPEC_OK;
