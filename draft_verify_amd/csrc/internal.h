@@ -99,9 +99,16 @@ struct AttnParams {
   float scale;
   int max_splits;        // grid.x: 256-key splits of the longest context
   float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
-  unsigned* cnt;         // [n_seq][n_kv]
+  unsigned* cnt;         // [n_seq][n_kv] arrival counters of the fused combine, zero between launches
   float* out;            // [R][n_q*hd]
+  int fuse;              // short contexts, few query columns: the last split combines in k_attn
 };
+// The attention combines its splits in one kernel when every context of the
+// step (cache + span) holds at most kAttnFuseKeys keys and a sequence has at
+// most kAttnFuseCols query columns (span rows x heads per kv head): the last
+// split's workgroup then combines every column itself.
+constexpr int kAttnFuseKeys = 8 * 256;
+constexpr int kAttnFuseCols = 4;
 
 struct EmbedParams {
   const uint16_t* emb;   // [V][H] bf16
@@ -168,6 +175,14 @@ hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
 
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
+// One-pass GEMM for R <= 16 (kernels.hip: k_mm): nw waves split K into nw
+// parts of spw 32-input steps, blocks of ct 16-column tiles, nbuf weight
+// buffers in registers, at most max_grid workgroups (each walks every
+// max_grid-th block).  Numerically identical to launch_gemm with nk = spw
+// (nslices = nw).
+bool mm_supported(int epi, int nw, int spw, int ct, int nbuf);
+hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int max_grid, int epi,
+                     hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
 // Repack canonical bf16 [rows][cols] into fragments of a fused matrix whose

@@ -120,11 +120,11 @@ __global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t value, size_t co
 // -------------------------------------------------------------- embedding
 
 // One workgroup per row: x = E[token] in fp32, plus the sum of squares of
-// every 64-column block (the format the RMSNorm prologues consume).
+// every 16-column group (the format the RMSNorm prologues consume).
 __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
   const int r = blockIdx.x;
   const int tok = P.tokens[r];
-  const int H = P.H, nb = H / 64;
+  const int H = P.H, ng = H / 16;
   const uint16_t* e = P.emb + (size_t)tok * H;
   for (int c0 = 0; c0 < H; c0 += 256) {
     const int c = c0 + threadIdx.x;
@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
       P.x[(size_t)r * H + c] = v;
       float t = v * v;
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-      if ((threadIdx.x & 63) == 0) P.ss[(size_t)r * nb + c / 64] = t;
+      for (int o = 8; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+      if ((threadIdx.x & 15) == 0) P.ss[(size_t)r * ng + c / 16] = t;
     }
   }
 }
@@ -162,7 +162,32 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
 // to stream as many weight bytes per staged activation tile.
 constexpr int gemm_tiles_per_wave(int fmt) { return fmt == FMT_INT4 ? 4 : 1; }
 
-constexpr int kMaxSsIter = 8;  // RMSNorm partial sums per row / 16 (hidden <= 8192, host-checked)
+// RMSNorm statistics: the producer of a residual row writes the sum of
+// squares of every 16-column group; a consumer sums them with 16 lanes per
+// row, lane j taking groups j, j + 16, ... in increasing order, then a fixed
+// xor tree -- the same order for every kernel and any number of rows.
+constexpr int kSsChunk = 8;  // partial-sum loads in flight per lane
+__device__ __forceinline__ float rstd_finish(float acc, float inv_dim, float eps) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  return 1.0f / sqrtf(acc * inv_dim + eps);
+}
+__device__ __forceinline__ float rstd16(const float* ss, int ss_n, int r, int R, int j, float inv_dim, float eps) {
+#pragma clang fp contract(off)
+  float acc = 0.0f;
+  for (int i0 = 0; i0 * 16 < ss_n; i0 += kSsChunk) {
+    float v[kSsChunk];
+#pragma unroll
+    for (int i = 0; i < kSsChunk; ++i) {
+      const int q = j + 16 * (i0 + i);
+      v[i] = (r < R && q < ss_n) ? ss[(size_t)r * ss_n + q] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kSsChunk; ++i) acc += v[i];
+  }
+  return rstd_finish(acc, inv_dim, eps);
+}
 
 // Offset nibbles -> exact fp16 q: (1024 + u) - 1032 in packed fp16.
 __device__ __forceinline__ f16x8 dequant8(uint32_t x) {
@@ -250,22 +275,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   }
 
   if (P.ss) {
-    // rstd of every row: 16 lanes per row sum the partials strided by 16 in
-    // increasing order, then a fixed xor tree -- the same order for any R.
+    // rstd of every row, 16 lanes per row (rstd16)
     for (int pass = 0; pass * 16 < P.R; ++pass) {
       const int r = pass * 16 + ss_row;
-      float v[kMaxSsIter];
-#pragma unroll
-      for (int i = 0; i < kMaxSsIter; ++i) {
-        const int q = ss_part + 16 * i;
-        v[i] = (r < P.R && q < P.ss_n) ? P.ss[(size_t)r * P.ss_n + q] : 0.0f;
-      }
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kMaxSsIter; ++i) acc += v[i];
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-      if (ss_part == 0) sR[r] = r < P.R ? 1.0f / sqrtf(acc * P.inv_dim + P.eps) : 0.0f;
+      const float rs = rstd16(P.ss, P.ss_n, r, P.R, ss_part, P.inv_dim, P.eps);
+      if (ss_part == 0) sR[r] = r < P.R ? rs : 0.0f;
     }
     __syncthreads();
   }
@@ -390,11 +404,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 // idx/(32CT), columns nb*64CT + 2*(idx%(32CT)) + {0,1}), summed over the K
 // slices in slice order; pairs past N (a ragged last block) are skipped, 64
 // columns at a time.  Each thread takes two pairs at a time and issues every
-// slice load of them (up to 8 slices per round) before the first add, so the
-// gather costs one memory round trip per two pairs and per 8 slices.  Every
+// slice load of them (up to SB slices per round) before the first add, so the
+// gather costs one memory round trip per two pairs and per SB slices.  Every
 // 32 consecutive pairs are 64 columns of one row (the shuffle groups of the
 // epilogues).
-template <int CT, class F>
+template <int CT, int SB = 16, class F>
 __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
   constexpr int U = 2, PR = 32 * CT;
   const int n = P.R * PR, ns = P.nslices;
@@ -411,17 +425,17 @@ __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
       ok[u] = idx < n && c < P.N;
       off[u] = (unsigned)(idx / PR) * (unsigned)P.N + (unsigned)c;
     }
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float2 t[U][8];
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      float2 t[U][SB];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < SB; ++i)
           if (ok[u] && s0 + i < ns) t[u][i] = ld_dev2(P.part + (off[u] + (unsigned)(s0 + i) * stride));
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < SB; ++i)
           if (ok[u] && s0 + i < ns) {
             v0[u] += t[u][i].x;
             v1[u] += t[u][i].y;
@@ -442,66 +456,92 @@ __device__ __forceinline__ void row_pos(const GemmParams& P, int r, int& seq, in
   pos = P.kv_len[seq] + i;
 }
 
-template <int CT>
-__device__ void epi_qkv(const GemmParams& P, int nb) {
+// Per column-pair epilogue arithmetic, shared by the split-K and the
+// one-pass GEMMs so that both give bit-identical results (contraction off:
+// every product and sum rounds on its own, whatever the surrounding code).
+
+// RoPE on the pair (d, d + hd/2) stored interleaved, then q (fp32) or the
+// K / V cache rows (fp16) at the row's position.
+__device__ __forceinline__ void qkv_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+#pragma clang fp contract(off)
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
-  for_pairs<CT>(P, nb, [&](int, int r, int c, float v0, float v1) {
-    int seq, pos;
-    row_pos(P, r, seq, pos);
-    const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
-    if (c < DQ + DK) {  // rotate the pair (d, d + hd/2) stored interleaved
-      const int local = c < DQ ? c : c - DQ;
-      const int head = local / hd, j = (local % hd) >> 1;
-      const float cs = P.rope[((size_t)pos * half + j) * 2], sn = P.rope[((size_t)pos * half + j) * 2 + 1];
-      const float o0 = v0 * cs - v1 * sn, o1 = v0 * sn + v1 * cs;
-      if (c < DQ) {
-        float* qr = P.q + (size_t)r * DQ + head * hd;
-        qr[j] = o0;
-        qr[j + half] = o1;
-      } else {
-        _Float16* kr = P.kpool + (((size_t)blk * P.n_kv + head) * 16 + slot) * hd;
-        kr[j] = (_Float16)o0;
-        kr[j + half] = (_Float16)o1;
-      }
+  int seq, pos;
+  row_pos(P, r, seq, pos);
+  const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
+  if (c < DQ + DK) {
+    const int local = c < DQ ? c : c - DQ;
+    const int head = local / hd, j = (local % hd) >> 1;
+    const float cs = P.rope[((size_t)pos * half + j) * 2], sn = P.rope[((size_t)pos * half + j) * 2 + 1];
+    const float o0 = v0 * cs - v1 * sn, o1 = v0 * sn + v1 * cs;
+    if (c < DQ) {
+      float* qr = P.q + (size_t)r * DQ + head * hd;
+      qr[j] = o0;
+      qr[j + half] = o1;
     } else {
-      const int local = c - DQ - DK;
-      const int head = local / hd, d = local % hd;
-      _Float16* vb = P.vpool + ((size_t)blk * P.n_kv + head) * hd * 16;
-      vb[(size_t)d * 16 + slot] = (_Float16)v0;
-      vb[(size_t)(d + 1) * 16 + slot] = (_Float16)v1;
+      _Float16* kr = P.kpool + (((size_t)blk * P.n_kv + head) * 16 + slot) * hd;
+      kr[j] = (_Float16)o0;
+      kr[j + half] = (_Float16)o1;
     }
-  });
+  } else {
+    const int local = c - DQ - DK;
+    const int head = local / hd, d = local % hd;
+    _Float16* vb = P.vpool + ((size_t)blk * P.n_kv + head) * hd * 16;
+    vb[(size_t)d * 16 + slot] = (_Float16)v0;
+    vb[(size_t)(d + 1) * 16 + slot] = (_Float16)v1;
+  }
+}
+
+// x += (v0, v1); returns the pair's sum of squares of the new residual.
+__device__ __forceinline__ float resid_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+#pragma clang fp contract(off)
+  float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
+  float2 x = *xp;
+  x.x = x.x + v0;
+  x.y = x.y + v1;
+  *xp = x;
+  return x.x * x.x + x.y * x.y;
+}
+
+// Sum over the 8 pairs (16 columns) held by an aligned group of 8 lanes;
+// every lane of the group must be active.
+__device__ __forceinline__ float sum8(float t) {
+#pragma clang fp contract(off)
+  t += __shfl_xor(t, 4);
+  t += __shfl_xor(t, 2);
+  t += __shfl_xor(t, 1);
+  return t;
+}
+
+__device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, float g, float u) {
+#pragma clang fp contract(off)
+  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
+}
+
+template <int CT>
+__device__ void epi_qkv(const GemmParams& P, int nb) {
+  for_pairs<CT>(P, nb, [&](int, int r, int c, float v0, float v1) { qkv_pair(P, r, c, v0, v1); });
 }
 
 template <int CT>
 __device__ void epi_resid(const GemmParams& P, int nb) {
-  const int NB = P.N >> 6;  // RMSNorm partial sums: one per 64 columns
+  const int NG = P.N >> 4;  // RMSNorm partial sums: one per 16 columns
   for_pairs<CT>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
-    float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
-    float2 x = *xp;
-    x.x = x.x + v0;
-    x.y = x.y + v1;
-    *xp = x;
-    float t = x.x * x.x + x.y * x.y;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-    if ((idx & 31) == 0) P.ss_out[(size_t)r * NB + (c >> 6)] = t;
+    const float t = sum8(resid_pair(P, r, c, v0, v1));
+    if ((idx & 7) == 0) P.ss_out[(size_t)r * NG + (c >> 4)] = t;
   });
 }
 
 template <int CT>
 __device__ void epi_swiglu(const GemmParams& P, int nb) {
-  const int F = P.N >> 1;
-  for_pairs<CT>(P, nb, [&](int, int r, int c, float g, float u) {
-    P.h[(size_t)r * F + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
-  });
+  for_pairs<CT>(P, nb, [&](int, int r, int c, float g, float u) { swiglu_pair(P, r, c, g, u); });
 }
 
 template <int CT>
 __device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
   __shared__ int sFinal;
-  for_pairs<CT>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
+  // 8 slices per round keeps the LM head's registers (and occupancy) low
+  for_pairs<CT, 8>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     if (P.logits) {
       float2* lp = (float2*)(P.logits + (size_t)r * P.N + c);
       *lp = make_float2(v0, v1);
@@ -562,6 +602,325 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
   else epi_lm<CT>(P, nb, sbuf);
 }
 
+// ------------------------------------------------------- one-pass GEMM
+//
+// For R <= 16 rows.  A workgroup of NW waves walks column blocks of CT
+// 16-column tiles, blockIdx.x, blockIdx.x + gridDim.x, ..., over the whole
+// K; wave w owns the K part of steps [w*SPW, (w+1)*SPW).  The prologue loads
+// the wave's A rows once, straight into the MFMA A-operand layout (lane l:
+// row l%16, inputs 8*(l/16)..+8 of every step) and applies the RMSNorm;
+// they then serve every block of the walk (split into bf16 hi + lo per
+// step as the MFMAs need them).
+// Weights stream through NBUF register buffers: the fragments of the block
+// NBUF walk steps ahead are issued as soon as the current block's MFMAs have
+// read theirs, so NBUF blocks are in flight while one is reduced.  Per block each wave runs
+// 2*CT*SPW MFMA and leaves its partial tiles in LDS; the workgroup adds the
+// parts in wave order and runs the epilogue.  No partial buffer, arrival
+// counter or second pass.  The K parts, the MFMA order within a part and the
+// order of the final additions are those of the split-K kernel with
+// NK = SPW and NW slices, so the two agree bit for bit (the split-K kernel
+// serves R > 16).
+template <int EPI, int NW, int SPW, int CT, int NBUF>
+__global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
+  static_assert(NBUF == 1 || NBUF == 2, "one or two weight buffers");
+  constexpr int NT = NW * 64, KS = NW * SPW;
+  constexpr bool NORM = EPI != EPI_RESID;
+  constexpr int SSN = KS * 2;                  // RMSNorm partials per row (K = hidden, one per 16 columns)
+  constexpr int SSI = (SSN + 15) / 16;         // of them per lane
+  constexpr int GPT = (KS * 32 + NT - 1) / NT; // gain values per thread
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int s0 = wave * SPW;
+  const int row = lane & 15, kg = lane >> 4;
+  const int nblk = (P.N + 16 * CT - 1) / (16 * CT), G = (int)gridDim.x;
+
+  __shared__ f32x4 sAcc[NW * CT * 64];
+  __shared__ float sG[NORM ? KS * 32 : 1];
+  __shared__ float sR[16];
+
+  auto fetch = [&](u32x4 (&bw)[CT][SPW], int blk) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int tile = blk * CT + c;
+      if (tile * 16 < P.N) {
+        const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) bw[c][j] = __builtin_nontemporal_load(wp + j * 64);
+      } else {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) bw[c][j] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // Issue order: the small RMSNorm inputs first, then the first block's
+  // weights, then A, so that waiting for the former never waits for the
+  // weights.
+  float gv[NORM ? GPT : 1], sv[NORM ? SSI : 1];
+  const int ss_r = tid >> 4, ss_j = tid & 15;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int e = tid + i * NT;
+      gv[i] = e < KS * 32 ? P.gain[e] : 0.0f;
+    }
+    if constexpr (NT >= 256) {
+#pragma unroll
+      for (int i = 0; i < SSI; ++i) {
+        const int q = ss_j + 16 * i;
+        sv[i] = (tid < 256 && ss_r < P.R && q < SSN) ? P.ss[(size_t)ss_r * SSN + q] : 0.0f;
+      }
+    }
+  }
+  u32x4 b0[CT][SPW], b1[NBUF == 2 ? CT : 1][NBUF == 2 ? SPW : 1];
+  int blk = blockIdx.x;
+  fetch(b0, blk);
+  f32x4 a[SPW][2];
+  if (row < P.R) {
+    const f32x4* ap = (const f32x4*)(P.A + (size_t)row * P.lda + s0 * 32 + kg * 8);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      a[j][0] = ap[j * 8];
+      a[j][1] = ap[j * 8 + 1];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) a[j][0] = a[j][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int e = tid + i * NT;
+      if (e < KS * 32) sG[e] = gv[i];
+    }
+    if constexpr (NT >= 256) {
+      if (tid < 256) {
+        float acc = 0.0f;  // the order of rstd16: partials j, j + 16, ... then the xor tree
+#pragma unroll
+        for (int i = 0; i < SSI; ++i) acc += sv[i];
+        const float rs = rstd_finish(acc, P.inv_dim, P.eps);
+        if (ss_j == 0) sR[ss_r] = ss_r < P.R ? rs : 0.0f;
+      }
+    } else {
+      for (int t = tid; t < 256; t += NT) {
+        const int r = t >> 4, j = t & 15;
+        const float rs = rstd16(P.ss, SSN, r, P.R, j, P.inv_dim, P.eps);
+        if (j == 0) sR[r] = r < P.R ? rs : 0.0f;
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (NORM) {  // normalised in place; the bf16 split happens per block
+    const float rs = sR[row];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const float* g = sG + (s0 + j) * 32 + kg * 8;
+      a[j][0] = (f32x4){(a[j][0].x * rs) * g[0], (a[j][0].y * rs) * g[1], (a[j][0].z * rs) * g[2], (a[j][0].w * rs) * g[3]};
+      a[j][1] = (f32x4){(a[j][1].x * rs) * g[4], (a[j][1].y * rs) * g[5], (a[j][1].z * rs) * g[6], (a[j][1].w * rs) * g[7]};
+    }
+  }
+
+  // One block: MFMA on bw, then (bw free) issue the block NBUF steps ahead
+  // into it, then the reduction and the epilogue.
+  auto pass = [&](u32x4 (&bw)[CT][SPW], int cur, int refill) {
+    f32x4 acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(v[e] - (float)h);
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const bf16x8 w = __builtin_bit_cast(bf16x8, bw[c][j]);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w, acc[c], 0, 0, 0);
+      }
+    }
+    if (refill < nblk) fetch(bw, refill);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) sAcc[(wave * CT + c) * 64 + lane] = acc[c];
+    __syncthreads();
+    // Column pairs: p = (row * CT + tile) * 8 + pair; an aligned group of 8
+    // pairs is 16 columns of one row (the RMSNorm partial-sum group).  The
+    // D layout keeps element (row r, column cc) of a tile in component r%4
+    // of lane 16*(r/4) + cc.
+    const int npairs = P.R * 8 * CT;
+    for (int p = tid; p < npairs; p += NT) {
+      const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+      const int col = (cur * CT + ct) * 16 + 2 * pp;
+      const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+      float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float* t = (const float*)(sAcc + (w * CT + ct) * 64);
+        v0 += t[e0];
+        v1 += t[e0 + 4];
+      }
+      if (col < P.N) {
+        if constexpr (EPI == EPI_QKV) {
+          qkv_pair(P, r, col, v0, v1);
+        } else if constexpr (EPI == EPI_RESID) {
+          const float t = sum8(resid_pair(P, r, col, v0, v1));
+          if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+        } else {
+          swiglu_pair(P, r, col, v0, v1);
+        }
+      }
+    }
+    __syncthreads();  // sAcc is rewritten by the next block
+  };
+
+  // blocks blk, blk + G, ...; with two buffers b0 and b1 alternate without
+  // register copies
+  if constexpr (NBUF == 2) {
+    if (blk + G < nblk) fetch(b1, blk + G);
+    while (blk < nblk) {
+      pass(b0, blk, blk + 2 * G);
+      blk += G;
+      if (blk >= nblk) break;
+      pass(b1, blk, blk + 2 * G);
+      blk += G;
+    }
+  } else {
+    for (; blk < nblk; blk += G) pass(b0, blk, blk + G);
+  }
+}
+
+// The same arithmetic for one 16-column tile per workgroup (grid = tiles)
+// with the wave's SPW steps loaded and multiplied in PH phases of up to
+// SPP steps: phase p+1's weights and A rows are issued once phase p's MFMAs
+// have read theirs, so a K part too long for the registers still runs in
+// one pass (each phase adds one memory latency, not a second kernel).
+template <int EPI, int NW, int SPW, int PH>
+__global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
+  constexpr int NT = NW * 64, KS = NW * SPW, SPP = (SPW + PH - 1) / PH;
+  constexpr bool NORM = EPI != EPI_RESID;
+  constexpr int SSN = KS * 2, SSI = (SSN + 15) / 16, GPT = (KS * 32 + NT - 1) / NT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tile = blockIdx.x, s0 = wave * SPW;
+  const int row = lane & 15, kg = lane >> 4;
+
+  __shared__ f32x4 sAcc[NW * 64];
+  __shared__ float sG[NORM ? KS * 32 : 1];
+  __shared__ float sR[16];
+
+  float gv[NORM ? GPT : 1], sv[NORM ? SSI : 1];
+  const int ss_r = tid >> 4, ss_j = tid & 15;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int e = tid + i * NT;
+      gv[i] = e < KS * 32 ? P.gain[e] : 0.0f;
+    }
+    if constexpr (NT >= 256) {
+#pragma unroll
+      for (int i = 0; i < SSI; ++i) {
+        const int q = ss_j + 16 * i;
+        sv[i] = (tid < 256 && ss_r < P.R && q < SSN) ? P.ss[(size_t)ss_r * SSN + q] : 0.0f;
+      }
+    }
+  }
+  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
+  const f32x4* ap = (const f32x4*)(P.A + (size_t)row * P.lda + s0 * 32 + kg * 8);
+  const bool arow = row < P.R;
+  u32x4 b[SPP];
+  f32x4 a[SPP][2];
+#define SPECV_MM1_LOAD(J0)                                                  \
+  _Pragma("unroll") for (int j = 0; j < SPP; ++j) if ((J0) + j < SPW) b[j] = \
+      __builtin_nontemporal_load(wp + ((J0) + j) * 64);                       \
+  _Pragma("unroll") for (int j = 0; j < SPP; ++j) {                          \
+    if (arow && (J0) + j < SPW) {                                            \
+      a[j][0] = ap[((J0) + j) * 8];                                          \
+      a[j][1] = ap[((J0) + j) * 8 + 1];                                      \
+    } else {                                                                 \
+      a[j][0] = a[j][1] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};                   \
+    }                                                                        \
+  }
+  SPECV_MM1_LOAD(0)
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int e = tid + i * NT;
+      if (e < KS * 32) sG[e] = gv[i];
+    }
+    if constexpr (NT >= 256) {
+      if (tid < 256) {
+        float acc = 0.0f;  // the order of rstd16
+#pragma unroll
+        for (int i = 0; i < SSI; ++i) acc += sv[i];
+        const float rs = rstd_finish(acc, P.inv_dim, P.eps);
+        if (ss_j == 0) sR[ss_r] = ss_r < P.R ? rs : 0.0f;
+      }
+    } else {
+      for (int t = tid; t < 256; t += NT) {
+        const int r = t >> 4, j = t & 15;
+        const float rs = rstd16(P.ss, SSN, r, P.R, j, P.inv_dim, P.eps);
+        if (j == 0) sR[r] = r < P.R ? rs : 0.0f;
+      }
+    }
+    __syncthreads();
+  }
+  const float rs = NORM ? sR[row] : 1.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ph = 0; ph < PH; ++ph) {
+    if (ph > 0) {
+      SPECV_MM1_LOAD(ph * SPP)
+    }
+#pragma unroll
+    for (int j = 0; j < SPP; ++j) {
+      if (ph * SPP + j < SPW) {
+        float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
+        if constexpr (NORM) {
+          const float* g = sG + (s0 + ph * SPP + j) * 32 + kg * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * g[e];
+        }
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 h = (__bf16)v[e];
+          hi[e] = h;
+          lo[e] = (__bf16)(v[e] - (float)h);
+        }
+        const bf16x8 w = __builtin_bit_cast(bf16x8, b[j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w, acc, 0, 0, 0);
+      }
+    }
+  }
+#undef SPECV_MM1_LOAD
+  sAcc[wave * 64 + lane] = acc;
+  __syncthreads();
+  const int npairs = P.R * 8;
+  for (int p = tid; p < npairs; p += NT) {
+    const int r = p >> 3, pp = p & 7;
+    const int col = tile * 16 + 2 * pp;
+    const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+    float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float* t = (const float*)(sAcc + w * 64);
+      v0 += t[e0];
+      v1 += t[e0 + 4];
+    }
+    if constexpr (EPI == EPI_QKV) {
+      qkv_pair(P, r, col, v0, v1);
+    } else if constexpr (EPI == EPI_RESID) {
+      const float t = sum8(resid_pair(P, r, col, v0, v1));
+      if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+    } else {
+      swiglu_pair(P, r, col, v0, v1);
+    }
+  }
+}
+
 // -------------------------------------------------------------- attention
 //
 // Grid (split, kv head, sequence); a split is 256 keys at absolute positions
@@ -575,6 +934,10 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
 // goes to memory, and k_attn_combine merges the splits of every query
 // column.  Row i attends keys [0, p+i]; a chunk or split lying wholly past a
 // row's position contributes exactly nothing.
+
+template <int HD, bool COH>
+__device__ void combine_col(const AttnParams& P, int b, int kvh, int qcol, int lane, float* sW);
+constexpr int kFuseSplitsMax = 16;  // the fused combine keeps 16 split weights per wave in LDS
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
@@ -721,25 +1084,47 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
     }
     __syncthreads();
   }
-
+  if (!P.fuse) return;
+  // Short contexts: the last split of this (sequence, kv head) to finish
+  // combines every query column, as k_attn_combine would.
+  __shared__ int sLast;
+  wait_mem();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = atomicAdd(&P.cnt[b * P.n_kv + kvh], 1u);
+    sLast = old == (unsigned)(n_act - 1);
+  }
+  __syncthreads();
+  if (!sLast) return;
+  if (tid == 0) P.cnt[b * P.n_kv + kvh] = 0u;  // ready for the next launch
+  float* sW = &sM[0][0] + wave * 16;            // kFuseSplits <= 16 weights per wave
+  for (int qcol = wave; qcol < QC; qcol += 4) combine_col<HD, true>(P, b, kvh, qcol, lane, sW);
 }
 
-// Split combine: grid (ceil(QC/4), kv head, sequence); wave w combines query
-// column 4*blockIdx.x + w over the splits holding keys at or before its
-// row's position.  Lane i reduces splits i, i+64, ...: the maximum and the
-// sum of l_s exp(m_s - M) by fixed xor trees, then every lane takes output
-// pairs and sums w_s o_s in split order with eight split loads in flight.
-// The order depends only on the row's position, never on the other rows.
+// Split combine of one query column (one wave): lane i reduces splits i,
+// i+64, ...: the maximum and the sum of l_s exp(m_s - M) by fixed xor trees,
+// then every lane takes output pairs and sums w_s o_s in split order with
+// eight split loads in flight.  The order depends only on the row's
+// position, never on the other rows.  COH: the partials were written by
+// other workgroups of the same kernel (device-coherent loads).
 constexpr int kMaxCombineSplits = 256;  // host-checked: max_ctx <= 65536
+constexpr int kFuseSplits = 8;          // contexts of at most 8 splits may combine in the attention kernel
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <bool COH>
+__device__ __forceinline__ float ld_part(const float* p) {
+  if constexpr (COH) return ld_dev(p);
+  else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float2 ld_part2(const float* p) {
+  if constexpr (COH) return ld_dev2(p);
+  else return *(const float2*)p;
+}
+
+template <int HD, bool COH>
+__device__ void combine_col(const AttnParams& P, int b, int kvh, int qcol, int lane, float* sW) {
+#pragma clang fp contract(off)
   const int G = P.n_q / P.n_kv, S = P.S, QC = S * G;
-  const int qcol = blockIdx.x * 4 + wave;
-  __shared__ float sW[4][kMaxCombineSplits];
-  if (qcol >= QC) return;  // whole waves; no barrier below
   const int seq = P.seq_ids[b];
   const int p = P.kv_len[seq];
   const int iq = qcol / G, head = kvh * G + qcol % G;
@@ -747,20 +1132,20 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
   const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
   const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
   float M = -INFINITY;
-  for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, base[sp * stride]);
+  for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, ld_part<COH>(base + sp * stride));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.0f;
   for (int sp = lane; sp < nsp; sp += 64) {
-    const float2 ml = *(const float2*)(base + sp * stride);
+    const float2 ml = ld_part2<COH>(base + sp * stride);
     const float f = expf(ml.x - M);
-    sW[wave][sp] = f;
+    sW[sp] = f;
     L += ml.y * f;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
   const float inv = 1.0f / L;
-  for (int sp = lane; sp < nsp; sp += 64) sW[wave][sp] *= inv;
+  for (int sp = lane; sp < nsp; sp += 64) sW[sp] *= inv;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   const int DQ = P.n_q * HD;
@@ -771,17 +1156,31 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
       float2 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) v[i] = *(const float2*)(src + (size_t)(s0 + i) * stride);
+        if (s0 + i < nsp) v[i] = ld_part2<COH>(src + (size_t)(s0 + i) * stride);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (s0 + i < nsp) {
-          const float w = sW[wave][s0 + i];
+          const float w = sW[s0 + i];
           o0 += v[i].x * w;
           o1 += v[i].y * w;
         }
     }
     *(float2*)(P.out + (size_t)(b * S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0, o1);
   }
+  __builtin_amdgcn_wave_barrier();  // sW is reused by this wave's next column
+}
+
+// Split combine kernel: grid (ceil(QC/4), kv head, sequence); wave w
+// combines query column 4*blockIdx.x + w.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int QC = P.S * (P.n_q / P.n_kv);
+  const int qcol = blockIdx.x * 4 + wave;
+  __shared__ float sW[4][kMaxCombineSplits];
+  if (qcol >= QC) return;  // whole waves; no barrier below
+  combine_col<HD, false>(P, b, kvh, qcol, lane, sW[wave]);
 }
 
 // -------------------------------------------------------------- launchers
@@ -803,8 +1202,11 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
   }
   if (fmt != FMT_BF16) return hipErrorInvalidValue;
   switch (nk) {
+    case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 10: hipLaunchKernelGGL((k_gemm<10, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 5: hipLaunchKernelGGL((k_gemm<5, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
@@ -822,26 +1224,76 @@ hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_
   return hipErrorInvalidValue;
 }
 
+// The compiled one-pass configurations (waves = K parts, steps per part,
+// tiles per workgroup) of each epilogue class.
+// nbuf 1 or 2: the walking k_mm with ct-tile blocks; nbuf 0: k_mm1, one tile
+// per workgroup, loaded in ct phases.
+#define SPECV_MM_H(X) X(16, 5, 1, 1) X(8, 10, 1, 1) X(16, 5, 1, 0) X(1, 2, 1, 1) X(2, 1, 1, 1)
+#define SPECV_MM_R(X) X(16, 8, 1, 0) X(8, 16, 2, 0) X(16, 19, 4, 0) X(1, 2, 1, 1) X(2, 1, 1, 1) X(1, 4, 1, 1) X(2, 2, 1, 1) X(4, 1, 1, 1)
+
+bool mm_supported(int epi, int nw, int spw, int ct, int nbuf) {
+#define SPECV_MM_HAS(a, b, c, d) if (nw == a && spw == b && ct == c && nbuf == d) return true;
+  if (epi == EPI_QKV || epi == EPI_SWIGLU) {
+    SPECV_MM_H(SPECV_MM_HAS)
+  } else if (epi == EPI_RESID) {
+    SPECV_MM_R(SPECV_MM_HAS)
+  }
+#undef SPECV_MM_HAS
+  return false;
+}
+
+hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int max_grid, int epi, hipStream_t st) {
+  if (p.R < 1 || p.R > 16 || p.K != nw * spw * 32 || max_grid < 1 || p.N % 16) return hipErrorInvalidValue;
+  // the RMSNorm prologue reads K/16 partial sums per row (K = hidden)
+  if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
+  const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
+  const int grid = nblk < max_grid ? nblk : max_grid;
+#define SPECV_MM_GO(E, a, b, c, d)                                                       \
+  if (nw == a && spw == b && ct == c && nbuf == d) {                                     \
+    if constexpr (d == 0)                                                                \
+      hipLaunchKernelGGL((k_mm1<E, a, b, c>), dim3(nblk1), dim3(a * 64), 0, st, p);      \
+    else                                                                                 \
+      hipLaunchKernelGGL((k_mm<E, a, b, c, d>), dim3(grid), dim3(a * 64), 0, st, p);    \
+    return hipGetLastError();                                                            \
+  }
+#define SPECV_MM_GO_Q(a, b, c, d) SPECV_MM_GO(EPI_QKV, a, b, c, d)
+#define SPECV_MM_GO_S(a, b, c, d) SPECV_MM_GO(EPI_SWIGLU, a, b, c, d)
+#define SPECV_MM_GO_R(a, b, c, d) SPECV_MM_GO(EPI_RESID, a, b, c, d)
+  if (epi == EPI_QKV) {
+    SPECV_MM_H(SPECV_MM_GO_Q)
+  } else if (epi == EPI_SWIGLU) {
+    SPECV_MM_H(SPECV_MM_GO_S)
+  } else if (epi == EPI_RESID) {
+    SPECV_MM_R(SPECV_MM_GO_R)
+  }
+#undef SPECV_MM_GO_Q
+#undef SPECV_MM_GO_S
+#undef SPECV_MM_GO_R
+#undef SPECV_MM_GO
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
   if (p.max_splits > kMaxCombineSplits) return hipErrorInvalidValue;
+  static_assert(kFuseSplits <= kFuseSplitsMax, "fused combine weights fit the LDS scratch");
   const dim3 grid(p.max_splits, p.n_kv, p.n_seq);
   const dim3 cgrid((p.S * (p.n_q / p.n_kv) + 3) / 4, p.n_kv, p.n_seq);
   switch (hd) {
     case 128:
       hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p);
-      hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, st, p);
+      if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, st, p);
       break;
     case 64:
       hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, p);
-      hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, st, p);
+      if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, st, p);
       break;
     case 32:
       hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, st, p);
-      hipLaunchKernelGGL(k_attn_combine<32>, cgrid, dim3(256), 0, st, p);
+      if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<32>, cgrid, dim3(256), 0, st, p);
       break;
     case 16:
       hipLaunchKernelGGL(k_attn<16>, grid, dim3(256), 0, st, p);
-      hipLaunchKernelGGL(k_attn_combine<16>, cgrid, dim3(256), 0, st, p);
+      if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<16>, cgrid, dim3(256), 0, st, p);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -52,12 +52,45 @@ struct LayerOff {
   size_t wqkv, wo, wgu, wd, g_attn, g_ffn;
 };
 
+// One-pass GEMM plan of one projection (launch_mm): nw K parts of spw steps;
+// nbuf 1 or 2: walking blocks of ct tiles with nbuf weight buffers; nbuf 0:
+// one tile per workgroup loaded in ct phases; used for R <= rmax.  nw == 0
+// means the split-K kernel serves every R.
+struct MmPlan {
+  int nw, spw, ct, nbuf, rmax;
+};
+
+// Preference lists, first match on K = nw * spw * 32 wins.
+#ifndef SPECV_MM_QKV
+#define SPECV_MM_QKV {16, 5, 1, 1, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}
+#endif
+#ifndef SPECV_MM_GU
+#define SPECV_MM_GU {16, 5, 1, 1, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}
+#endif
+#ifndef SPECV_MM_O
+#define SPECV_MM_O {8, 16, 2, 0, 8}, {16, 8, 1, 0, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}, {4, 1, 1, 1, 16}
+#endif
+#ifndef SPECV_MM_D
+#define SPECV_MM_D {16, 19, 4, 0, 2}, {16, 8, 1, 0, 16}, {1, 4, 1, 1, 16}, {2, 2, 1, 1, 16}, {1, 2, 1, 1, 16}, {4, 1, 1, 1, 16}
+#endif
+
+#ifndef SPECV_MM_WG_PER_CU
+#define SPECV_MM_WG_PER_CU 1
+#endif
+
+MmPlan pick_mm(int epi, int K, std::initializer_list<MmPlan> prefs) {
+  for (const MmPlan& m : prefs)
+    if (m.nw * m.spw * 32 == K && mm_supported(epi, m.nw, m.spw, m.ct, m.nbuf)) return m;
+  return MmPlan{0, 0, 0, 0, 0};
+}
+
 // Byte layout of the three device buffers for one description.
 struct Layout {
   int fmt;  // FMT_BF16 or FMT_INT4 (GEMM weights; the embedding is bf16)
   int H, nq, nkv, hd, F, V, L, DQ, DK, Nqkv, Ngu;
   int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
   int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
+  MmPlan mm_qkv, mm_o, mm_gu, mm_d;  // per-kernel path, bf16: the one-pass GEMMs for R <= 16
   // weights
   std::vector<LayerOff> lay;
   size_t emb, wlm, g_final, weights_bytes;
@@ -115,6 +148,19 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
+  Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = MmPlan{0, 0, 0, 0, 0};
+  if (Lo.fmt == FMT_BF16 && !(d.flags & SPEC_FLAG_PERSISTENT)) {
+    // one-pass GEMMs for R <= 16; the split-K kernel (R > 16) then takes the
+    // same K parts (nk = spw), so both give identical results
+    Lo.mm_qkv = pick_mm(EPI_QKV, Lo.H, {SPECV_MM_QKV});
+    Lo.mm_gu = pick_mm(EPI_SWIGLU, Lo.H, {SPECV_MM_GU});
+    Lo.mm_o = pick_mm(EPI_RESID, Lo.DQ, {SPECV_MM_O});
+    Lo.mm_d = pick_mm(EPI_RESID, Lo.F, {SPECV_MM_D});
+    if (Lo.mm_qkv.nw) Lo.nk_qkv = Lo.mm_qkv.spw;
+    if (Lo.mm_gu.nw) Lo.nk_gu = Lo.mm_gu.spw;
+    if (Lo.mm_o.nw) Lo.nk_o = Lo.mm_o.spw;
+    if (Lo.mm_d.nw) Lo.nk_d = Lo.mm_d.spw;
+  }
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
     return fail("no persistent forward is compiled for this shape");
@@ -161,7 +207,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   const size_t R = (size_t)Lo.max_rows;
   off = 0;
   Lo.x = take(R * Lo.H * 4);
-  Lo.ss = take(R * (Lo.H / 64) * 4);
+  Lo.ss = take(R * (Lo.H / 16) * 4);
   Lo.q = take(R * Lo.DQ * 4);
   Lo.o = take(R * Lo.DQ * 4);
   Lo.h = take(R * Lo.F * 4);
@@ -229,6 +275,8 @@ struct spec_ctx {
   std::string err;
   int last_rows = 0;
   int fwd_grid = 0;      // workgroups of the persistent forward (all co-resident)
+  int mm_grid = 1;       // most workgroups of a one-pass GEMM (they walk the column blocks)
+  int attn_fuse = 0;     // the current step's contexts are short: attention combines in one kernel
   bool per_op = true;    // the per-kernel launch sequence (else the persistent forward)
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
@@ -317,6 +365,12 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
   return p;
 }
 
+// R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K.
+hipError_t gemm_or_mm(const GemmParams& p, const MmPlan& m, int nk, int epi, int fmt, int max_grid, hipStream_t st) {
+  if (m.nw && p.R <= m.rmax && p.R <= 16) return launch_mm(p, m.nw, m.spw, m.ct, m.nbuf, max_grid, epi, st);
+  return launch_gemm(p, nk, epi, fmt, st);
+}
+
 // Per-op event hook for spec_profile_ops (null in the normal path).
 struct OpTimer {
   std::vector<hipEvent_t>* ev;
@@ -363,7 +417,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.A = c->ws<float>(L.x);
     gl.lda = L.H;
     gl.ss = c->ws<float>(L.ss);
-    gl.ss_n = L.H / 64;
+    gl.ss_n = L.H / 16;
     gl.gain = (const float*)(c->W + L.g_final);
     gl.argkey = c->ws<unsigned long long>(L.argkey);
     gl.lm_cnt = c->ws<unsigned>(L.lm_cnt);
@@ -386,7 +440,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.A = c->ws<float>(L.x);
       g.lda = L.H;
       g.ss = c->ws<float>(L.ss);
-      g.ss_n = L.H / 64;
+      g.ss_n = L.H / 16;
       g.gain = (const float*)(c->W + lw.g_attn);
       g.q = c->ws<float>(L.q);
       g.kpool = c->kpool(l);
@@ -400,7 +454,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.n_kv = L.nkv;
       g.hd = L.hd;
       g.rope = c->ws<float>(L.rope);
-      HIPCHK(c, launch_gemm(g, L.nk_qkv, EPI_QKV, L.fmt, st));
+      HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, st));
       return SPEC_OK;
     }
     case SPEC_OP_ATTN: {
@@ -421,6 +475,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.part = c->ws<float>(L.apart);
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
+      a.fuse = c->attn_fuse;
       HIPCHK(c, launch_attn(a, L.hd, st));
       return SPEC_OK;
     }
@@ -430,7 +485,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, launch_gemm(go, L.nk_o, EPI_RESID, L.fmt, st));
+      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, st));
       return SPEC_OK;
     }
     case SPEC_OP_GATEUP: {
@@ -438,10 +493,10 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.A = c->ws<float>(L.x);
       gu.lda = L.H;
       gu.ss = c->ws<float>(L.ss);
-      gu.ss_n = L.H / 64;
+      gu.ss_n = L.H / 16;
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
-      HIPCHK(c, launch_gemm(gu, L.nk_gu, EPI_SWIGLU, L.fmt, st));
+      HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, st));
       return SPEC_OK;
     }
     case SPEC_OP_DOWN: {
@@ -450,7 +505,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.lda = L.F;
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, launch_gemm(gd, L.nk_d, EPI_RESID, L.fmt, st));
+      HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, st));
       return SPEC_OK;
     }
   }
@@ -473,7 +528,7 @@ int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
 }
 
 int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
-  auto key = std::make_pair(n_seq, S);
+  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16));
   auto it = c->graphs.find(key);
   if (it != c->graphs.end()) {
     *out = it->second;
@@ -498,9 +553,13 @@ int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
   return SPEC_OK;
 }
 
-// Stage the step block (mode, shape, tokens, sequence ids) and copy it.
+// Stage the step block (mode, shape, tokens, sequence ids) and copy it; pick
+// the attention variant of the step from the host's cache lengths.
 int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
   const Layout& L = c->lo;
+  int longest = 0;
+  for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
+  c->attn_fuse = (longest <= kAttnFuseKeys && S * L.G <= kAttnFuseCols) ? 1 : 0;
   StepDev* sd = (StepDev*)c->h_step();
   sd->mode = mode;
   sd->n_seq = n_seq;
@@ -746,6 +805,16 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
     return SPEC_EHIP;
   }
   c->per_op = (desc->flags & SPEC_FLAG_PERSISTENT) == 0;
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      g_create_error = "cannot read the device's compute unit count";
+      delete c;
+      return SPEC_EHIP;
+    }
+    c->mm_grid = cus * SPECV_MM_WG_PER_CU;  // one resident workgroup per CU walks the blocks
+  }
   if (!c->per_op) {
     int dev = 0, cus = 0;
     const int occ = forward_occupancy(L.nk_qkv, L.nk_o, L.nk_d, L.hd);
