@@ -175,13 +175,14 @@ hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
 
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
-// One-pass GEMM for R <= 16 (kernels.hip: k_mm): nw waves split K into nw
-// parts of spw 32-input steps, blocks of ct 16-column tiles, nbuf weight
-// buffers in registers, at most max_grid workgroups (each walks every
-// max_grid-th block).  Numerically identical to launch_gemm with nk = spw
-// (nslices = nw).
-bool mm_supported(int epi, int nw, int spw, int ct, int nbuf);
-hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int max_grid, int epi,
+// One-pass GEMM for R <= 16 (kernels.hip: k_mm, k_mm1): nw waves split K
+// into nw parts of spw 32-input steps, summed in groups of gp parts (gp = 1
+// or nw: the plain part order); nbuf 1 or 2: blocks of ct 16-column tiles
+// walked by at most max_grid workgroups with nbuf weight buffers; nbuf 0:
+// one tile per workgroup in ct phases.  With gp = 1 or nw numerically
+// identical to launch_gemm with nk = spw (nslices = nw).
+bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp);
+hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
                      hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);

@@ -154,7 +154,9 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
 // XCD (ids are dealt round-robin over the 8 XCDs), keeping the partial sums
 // in one L2.
 
-template <int EPI, int CT>
+// SB slices per gather round and U pairs per thread (eight and two keep the
+// split-K kernel's registers, and so its occupancy, low).
+template <int EPI, int CT, int SB = 8, int U = 2>
 __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf);
 
 // 16-column tiles per wave: int4 fragments are a quarter the bytes of bf16
@@ -403,14 +405,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 // The epilogue's column pairs of block nb (64*CT columns): pair idx = (row
 // idx/(32CT), columns nb*64CT + 2*(idx%(32CT)) + {0,1}), summed over the K
 // slices in slice order; pairs past N (a ragged last block) are skipped, 64
-// columns at a time.  Each thread takes two pairs at a time and issues every
+// columns at a time.  Each thread takes U pairs at a time and issues every
 // slice load of them (up to SB slices per round) before the first add, so the
-// gather costs one memory round trip per two pairs and per SB slices.  Every
+// gather costs one memory round trip per U pairs and per SB slices.  Every
 // 32 consecutive pairs are 64 columns of one row (the shuffle groups of the
 // epilogues).
-template <int CT, int SB = 16, class F>
+template <int CT, int SB = 8, int U = 2, class F>
 __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
-  constexpr int U = 2, PR = 32 * CT;
+#pragma clang fp contract(off)
+  constexpr int PR = 32 * CT;
   const int n = P.R * PR, ns = P.nslices;
   const unsigned stride = (unsigned)P.R * (unsigned)P.N;  // floats; the partial buffer is < 4 GiB
   for (int base = 0; base < n; base += U * 256) {
@@ -518,61 +521,52 @@ __device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, f
   P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
 }
 
-template <int CT>
+template <int CT, int SB, int U>
 __device__ void epi_qkv(const GemmParams& P, int nb) {
-  for_pairs<CT>(P, nb, [&](int, int r, int c, float v0, float v1) { qkv_pair(P, r, c, v0, v1); });
+  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float v0, float v1) { qkv_pair(P, r, c, v0, v1); });
 }
 
-template <int CT>
+template <int CT, int SB, int U>
 __device__ void epi_resid(const GemmParams& P, int nb) {
   const int NG = P.N >> 4;  // RMSNorm partial sums: one per 16 columns
-  for_pairs<CT>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
+  for_pairs<CT, SB, U>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
     const float t = sum8(resid_pair(P, r, c, v0, v1));
     if ((idx & 7) == 0) P.ss_out[(size_t)r * NG + (c >> 4)] = t;
   });
 }
 
-template <int CT>
+template <int CT, int SB, int U>
 __device__ void epi_swiglu(const GemmParams& P, int nb) {
-  for_pairs<CT>(P, nb, [&](int, int r, int c, float g, float u) { swiglu_pair(P, r, c, g, u); });
+  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float g, float u) { swiglu_pair(P, r, c, g, u); });
 }
 
-template <int CT>
-__device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
+// One logit (row r, column c): optional copy-out, NaN flag, argmax key.
+__device__ __forceinline__ unsigned long long lm_value(const GemmParams& P, int r, int c, float v) {
+  if (P.logits) P.logits[(size_t)r * P.N + c] = v;
+  if (v != v) atomicOr(P.status, 1);
+  return argmax_key(v, c);
+}
+
+// After a workgroup's row maxima are in: the last of nblk workgroups reads
+// them, runs accept_greedy per sequence and advances the cache lengths.
+__device__ void lm_finish(const GemmParams& P, int nblk, float* sbuf) {
   __shared__ int sFinal;
-  // 8 slices per round keeps the LM head's registers (and occupancy) low
-  for_pairs<CT, 8>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
-    if (P.logits) {
-      float2* lp = (float2*)(P.logits + (size_t)r * P.N + c);
-      *lp = make_float2(v0, v1);
-    }
-    if (v0 != v0 || v1 != v1) atomicOr(P.status, 1);
-    unsigned long long k0 = argmax_key(v0, c), k1 = argmax_key(v1, c + 1);
-    unsigned long long k = k0 > k1 ? k0 : k1;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      const unsigned long long t = __shfl_xor(k, o);
-      k = t > k ? t : k;
-    }
-    if ((idx & 31) == 0) atomicMax(&P.argkey[r], k);
-  });
-  // Last column block to finish: read the row maxima, accept, advance the cache.
   wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old = atomicAdd(P.lm_cnt, 1u);
-    sFinal = (old == (unsigned)((P.N + 64 * CT - 1) / (64 * CT) - 1));
+    sFinal = (old == (unsigned)(nblk - 1));
   }
   __syncthreads();
   if (!sFinal) return;
   int* arg = (int*)sbuf;
-  for (int r = threadIdx.x; r < P.R; r += 256) {
+  for (int r = threadIdx.x; r < P.R; r += blockDim.x) {
     const unsigned long long k = atomicExch(&P.argkey[r], 0ull);
     arg[r] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
   }
   __syncthreads();
   const int mode = *P.mode, S = P.S;
-  for (int b = threadIdx.x; b < P.n_seq; b += 256) {
+  for (int b = threadIdx.x; b < P.n_seq; b += blockDim.x) {
     const int row0 = b * S;
     int m;
     if (mode == MODE_COMMIT_ALL) {
@@ -594,12 +588,50 @@ __device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
   }
 }
 
-template <int EPI, int CT>
+template <int CT, int SB, int U>
+__device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
+  for_pairs<CT, SB, U>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
+    const unsigned long long k0 = lm_value(P, r, c, v0), k1 = lm_value(P, r, c + 1, v1);
+    unsigned long long k = k0 > k1 ? k0 : k1;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      const unsigned long long t = __shfl_xor(k, o);
+      k = t > k ? t : k;
+    }
+    if ((idx & 31) == 0) atomicMax(&P.argkey[r], k);
+  });
+  lm_finish(P, (P.N + 64 * CT - 1) / (64 * CT), sbuf);
+}
+
+template <int EPI, int CT, int SB, int U>
 __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
-  if constexpr (EPI == EPI_QKV) epi_qkv<CT>(P, nb);
-  else if constexpr (EPI == EPI_RESID) epi_resid<CT>(P, nb);
-  else if constexpr (EPI == EPI_SWIGLU) epi_swiglu<CT>(P, nb);
-  else epi_lm<CT>(P, nb, sbuf);
+  if constexpr (EPI == EPI_QKV) epi_qkv<CT, SB, U>(P, nb);
+  else if constexpr (EPI == EPI_RESID) epi_resid<CT, SB, U>(P, nb);
+  else if constexpr (EPI == EPI_SWIGLU) epi_swiglu<CT, SB, U>(P, nb);
+  else epi_lm<CT, SB, U>(P, nb, sbuf);
+}
+
+// Sum of the NW K parts' partial tiles (part w at sAcc[(w*CT + ct)*64]) in
+// groups of GP: the parts of each group in order, then the group sums in
+// order, each sum from zero.  With GP = 1 or GP = NW this is the plain
+// part-order sum of the split-K gather.
+template <int NW, int GP, int CT>
+__device__ __forceinline__ void group_sum(const f32x4* sAcc, int ct, int e0, float& v0, float& v1) {
+#pragma clang fp contract(off)
+  v0 = 0.0f;
+  v1 = 0.0f;
+#pragma unroll
+  for (int gi = 0; gi < NW / GP; ++gi) {
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int p = 0; p < GP; ++p) {
+      const float* t = (const float*)(sAcc + ((gi * GP + p) * CT + ct) * 64);
+      a0 += t[e0];
+      a1 += t[e0 + 4];
+    }
+    v0 += a0;
+    v1 += a1;
+  }
 }
 
 // ------------------------------------------------------- one-pass GEMM
@@ -620,9 +652,10 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
 // order of the final additions are those of the split-K kernel with
 // NK = SPW and NW slices, so the two agree bit for bit (the split-K kernel
 // serves R > 16).
-template <int EPI, int NW, int SPW, int CT, int NBUF>
+template <int EPI, int NW, int SPW, int CT, int NBUF, int GP>
 __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
   static_assert(NBUF == 1 || NBUF == 2, "one or two weight buffers");
+  static_assert(NW % GP == 0, "parts form whole groups");
   constexpr int NT = NW * 64, KS = NW * SPW;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int SSN = KS * 2;                  // RMSNorm partials per row (K = hidden, one per 16 columns)
@@ -755,13 +788,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
       const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
       const int col = (cur * CT + ct) * 16 + 2 * pp;
       const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
-      float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float* t = (const float*)(sAcc + (w * CT + ct) * 64);
-        v0 += t[e0];
-        v1 += t[e0 + 4];
-      }
+      float v0, v1;
+      group_sum<NW, GP, CT>(sAcc, ct, e0, v0, v1);
       if (col < P.N) {
         if constexpr (EPI == EPI_QKV) {
           qkv_pair(P, r, col, v0, v1);
@@ -797,8 +825,9 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
 // SPP steps: phase p+1's weights and A rows are issued once phase p's MFMAs
 // have read theirs, so a K part too long for the registers still runs in
 // one pass (each phase adds one memory latency, not a second kernel).
-template <int EPI, int NW, int SPW, int PH>
+template <int EPI, int NW, int SPW, int PH, int GP>
 __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
+  static_assert(NW % GP == 0, "parts form whole groups");
   constexpr int NT = NW * 64, KS = NW * SPW, SPP = (SPW + PH - 1) / PH;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int SSN = KS * 2, SSI = (SSN + 15) / 16, GPT = (KS * 32 + NT - 1) / NT;
@@ -903,13 +932,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
     const int r = p >> 3, pp = p & 7;
     const int col = tile * 16 + 2 * pp;
     const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
-    float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float* t = (const float*)(sAcc + w * 64);
-      v0 += t[e0];
-      v1 += t[e0 + 4];
-    }
+    float v0, v1;
+    group_sum<NW, GP, 1>(sAcc, 0, e0, v0, v1);
     if constexpr (EPI == EPI_QKV) {
       qkv_pair(P, r, col, v0, v1);
     } else if constexpr (EPI == EPI_RESID) {
@@ -1228,11 +1252,13 @@ hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_
 // tiles per workgroup) of each epilogue class.
 // nbuf 1 or 2: the walking k_mm with ct-tile blocks; nbuf 0: k_mm1, one tile
 // per workgroup, loaded in ct phases.
-#define SPECV_MM_H(X) X(16, 5, 1, 1) X(8, 10, 1, 1) X(16, 5, 1, 0) X(1, 2, 1, 1) X(2, 1, 1, 1)
-#define SPECV_MM_R(X) X(16, 8, 1, 0) X(8, 16, 2, 0) X(16, 19, 4, 0) X(1, 2, 1, 1) X(2, 1, 1, 1) X(1, 4, 1, 1) X(2, 2, 1, 1) X(4, 1, 1, 1)
+// (nw, spw, ct, nbuf, gp): gp parts per group of the final sum.
+#define SPECV_MM_H(X) X(16, 5, 1, 1, 16) X(1, 2, 1, 1, 1) X(2, 1, 1, 1, 2)
+#define SPECV_MM_R(X) X(8, 16, 2, 0, 1) X(16, 8, 1, 0, 1) X(16, 19, 4, 0, 1) X(1, 2, 1, 1, 1) X(2, 1, 1, 1, 2) \
+  X(1, 4, 1, 1, 1) X(2, 2, 1, 1, 2) X(4, 1, 1, 1, 4)
 
-bool mm_supported(int epi, int nw, int spw, int ct, int nbuf) {
-#define SPECV_MM_HAS(a, b, c, d) if (nw == a && spw == b && ct == c && nbuf == d) return true;
+bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
+#define SPECV_MM_HAS(a, b, c, d, e) if (nw == a && spw == b && ct == c && nbuf == d && gp == e) return true;
   if (epi == EPI_QKV || epi == EPI_SWIGLU) {
     SPECV_MM_H(SPECV_MM_HAS)
   } else if (epi == EPI_RESID) {
@@ -1242,23 +1268,24 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf) {
   return false;
 }
 
-hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int max_grid, int epi, hipStream_t st) {
+hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
+                     hipStream_t st) {
   if (p.R < 1 || p.R > 16 || p.K != nw * spw * 32 || max_grid < 1 || p.N % 16) return hipErrorInvalidValue;
   // the RMSNorm prologue reads K/16 partial sums per row (K = hidden)
   if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
   const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
   const int grid = nblk < max_grid ? nblk : max_grid;
-#define SPECV_MM_GO(E, a, b, c, d)                                                       \
-  if (nw == a && spw == b && ct == c && nbuf == d) {                                     \
+#define SPECV_MM_GO(E, a, b, c, d, e)                                                    \
+  if (nw == a && spw == b && ct == c && nbuf == d && gp == e) {                          \
     if constexpr (d == 0)                                                                \
-      hipLaunchKernelGGL((k_mm1<E, a, b, c>), dim3(nblk1), dim3(a * 64), 0, st, p);      \
+      hipLaunchKernelGGL((k_mm1<E, a, b, c, e>), dim3(nblk1), dim3(a * 64), 0, st, p);   \
     else                                                                                 \
-      hipLaunchKernelGGL((k_mm<E, a, b, c, d>), dim3(grid), dim3(a * 64), 0, st, p);    \
+      hipLaunchKernelGGL((k_mm<E, a, b, c, d, e>), dim3(grid), dim3(a * 64), 0, st, p); \
     return hipGetLastError();                                                            \
   }
-#define SPECV_MM_GO_Q(a, b, c, d) SPECV_MM_GO(EPI_QKV, a, b, c, d)
-#define SPECV_MM_GO_S(a, b, c, d) SPECV_MM_GO(EPI_SWIGLU, a, b, c, d)
-#define SPECV_MM_GO_R(a, b, c, d) SPECV_MM_GO(EPI_RESID, a, b, c, d)
+#define SPECV_MM_GO_Q(a, b, c, d, e) SPECV_MM_GO(EPI_QKV, a, b, c, d, e)
+#define SPECV_MM_GO_S(a, b, c, d, e) SPECV_MM_GO(EPI_SWIGLU, a, b, c, d, e)
+#define SPECV_MM_GO_R(a, b, c, d, e) SPECV_MM_GO(EPI_RESID, a, b, c, d, e)
   if (epi == EPI_QKV) {
     SPECV_MM_H(SPECV_MM_GO_Q)
   } else if (epi == EPI_SWIGLU) {

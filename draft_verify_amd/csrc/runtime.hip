@@ -54,24 +54,27 @@ struct LayerOff {
 
 // One-pass GEMM plan of one projection (launch_mm): nw K parts of spw steps;
 // nbuf 1 or 2: walking blocks of ct tiles with nbuf weight buffers; nbuf 0:
-// one tile per workgroup loaded in ct phases; used for R <= rmax.  nw == 0
-// means the split-K kernel serves every R.
+// one tile per workgroup loaded in ct phases; used for R <= rmax, so one
+// kernel serves every R <= rmax and a row's result does not depend on the
+// other rows (the rows gate).  Above rmax the split-K kernel runs with the
+// depth that suits many rows; its results agree to rounding, not bit for bit.
+// nw == 0 means the split-K kernel serves every R.
 struct MmPlan {
-  int nw, spw, ct, nbuf, rmax;
+  int nw, spw, ct, nbuf, gp, rmax;
 };
 
 // Preference lists, first match on K = nw * spw * 32 wins.
 #ifndef SPECV_MM_QKV
-#define SPECV_MM_QKV {16, 5, 1, 1, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}
+#define SPECV_MM_QKV {16, 5, 1, 1, 16, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}
 #endif
 #ifndef SPECV_MM_GU
-#define SPECV_MM_GU {16, 5, 1, 1, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}
+#define SPECV_MM_GU {16, 5, 1, 1, 16, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}
 #endif
 #ifndef SPECV_MM_O
-#define SPECV_MM_O {8, 16, 2, 0, 8}, {16, 8, 1, 0, 16}, {1, 2, 1, 1, 16}, {2, 1, 1, 1, 16}, {4, 1, 1, 1, 16}
+#define SPECV_MM_O {8, 16, 2, 0, 1, 8}, {16, 8, 1, 0, 1, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}, {4, 1, 1, 1, 4, 16}
 #endif
 #ifndef SPECV_MM_D
-#define SPECV_MM_D {16, 19, 4, 0, 2}, {16, 8, 1, 0, 16}, {1, 4, 1, 1, 16}, {2, 2, 1, 1, 16}, {1, 2, 1, 1, 16}, {4, 1, 1, 1, 16}
+#define SPECV_MM_D {16, 8, 1, 0, 1, 16}, {1, 4, 1, 1, 1, 16}, {2, 2, 1, 1, 2, 16}, {1, 2, 1, 1, 1, 16}, {4, 1, 1, 1, 4, 16}
 #endif
 
 #ifndef SPECV_MM_WG_PER_CU
@@ -80,8 +83,8 @@ struct MmPlan {
 
 MmPlan pick_mm(int epi, int K, std::initializer_list<MmPlan> prefs) {
   for (const MmPlan& m : prefs)
-    if (m.nw * m.spw * 32 == K && mm_supported(epi, m.nw, m.spw, m.ct, m.nbuf)) return m;
-  return MmPlan{0, 0, 0, 0, 0};
+    if (m.nw * m.spw * 32 == K && mm_supported(epi, m.nw, m.spw, m.ct, m.nbuf, m.gp)) return m;
+  return MmPlan{0, 0, 0, 0, 0, 0};
 }
 
 // Byte layout of the three device buffers for one description.
@@ -90,7 +93,7 @@ struct Layout {
   int H, nq, nkv, hd, F, V, L, DQ, DK, Nqkv, Ngu;
   int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
   int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
-  MmPlan mm_qkv, mm_o, mm_gu, mm_d;  // per-kernel path, bf16: the one-pass GEMMs for R <= 16
+  MmPlan mm_qkv, mm_o, mm_gu, mm_d;  // per-kernel path, bf16: the one-pass GEMMs for R <= rmax
   // weights
   std::vector<LayerOff> lay;
   size_t emb, wlm, g_final, weights_bytes;
@@ -148,7 +151,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
-  Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = MmPlan{0, 0, 0, 0, 0};
+  Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = MmPlan{0, 0, 0, 0, 0, 0};
   if (Lo.fmt == FMT_BF16 && !(d.flags & SPEC_FLAG_PERSISTENT)) {
     // one-pass GEMMs for R <= 16; the split-K kernel (R > 16) then takes the
     // same K parts (nk = spw), so both give identical results
@@ -156,10 +159,12 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     Lo.mm_gu = pick_mm(EPI_SWIGLU, Lo.H, {SPECV_MM_GU});
     Lo.mm_o = pick_mm(EPI_RESID, Lo.DQ, {SPECV_MM_O});
     Lo.mm_d = pick_mm(EPI_RESID, Lo.F, {SPECV_MM_D});
-    if (Lo.mm_qkv.nw) Lo.nk_qkv = Lo.mm_qkv.spw;
-    if (Lo.mm_gu.nw) Lo.nk_gu = Lo.mm_gu.spw;
-    if (Lo.mm_o.nw) Lo.nk_o = Lo.mm_o.spw;
-    if (Lo.mm_d.nw) Lo.nk_d = Lo.mm_d.spw;
+    // one-pass plans of R up to 16 that the split-K kernel cannot take at its
+    // own depth keep their parts there too (rmax < 16: both serve R <= 16)
+    if (Lo.mm_qkv.nw && Lo.mm_qkv.rmax < 16) Lo.nk_qkv = Lo.mm_qkv.spw;
+    if (Lo.mm_gu.nw && Lo.mm_gu.rmax < 16) Lo.nk_gu = Lo.mm_gu.spw;
+    if (Lo.mm_o.nw && Lo.mm_o.rmax < 16) Lo.nk_o = Lo.mm_o.spw;
+    if (Lo.mm_d.nw && Lo.mm_d.rmax < 16) Lo.nk_d = Lo.mm_d.spw;
   }
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
@@ -366,9 +371,9 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
 }
 
 // R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K.
-hipError_t gemm_or_mm(const GemmParams& p, const MmPlan& m, int nk, int epi, int fmt, int max_grid, hipStream_t st) {
-  if (m.nw && p.R <= m.rmax && p.R <= 16) return launch_mm(p, m.nw, m.spw, m.ct, m.nbuf, max_grid, epi, st);
-  return launch_gemm(p, nk, epi, fmt, st);
+hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, hipStream_t st) {
+  if (m.nw && p0.R <= m.rmax && p0.R <= 16) return launch_mm(p0, m.nw, m.spw, m.ct, m.nbuf, m.gp, max_grid, epi, st);
+  return launch_gemm(p0, nk, epi, fmt, st);
 }
 
 // Per-op event hook for spec_profile_ops (null in the normal path).
