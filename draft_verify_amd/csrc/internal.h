@@ -182,6 +182,9 @@ hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_
 // one tile per workgroup in ct phases.  With gp = 1 or nw numerically
 // identical to launch_gemm with nk = spw (nslices = nw).
 bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp);
+// The residual one-pass GEMM for at most rl rows with A staged in LDS
+// (kernels.hip: k_mm1l); compiled for nw = 16, spw = 19, rl = 4.
+hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st);
 hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
                      hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);

@@ -945,6 +945,87 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
   }
 }
 
+// The same arithmetic as k_mm1 (one tile per workgroup, NW K parts of SPW
+// steps, parts summed in order) for at most RL rows with A staged in LDS:
+// for up to four rows the whole A (split into bf16 hi + lo) fits the LDS
+// even at K = 9728, so each wave keeps all of its SPW weight fragments in
+// flight at once, however long its K part (the residual epilogue only).
+// The A rows are loaded first, the weights second, so the staging waits for
+// the A rows alone and runs while the weights stream.
+template <int NW, int SPW, int RL>
+__global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
+  constexpr int NT = NW * 64, KS = NW * SPW;
+  constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tile = blockIdx.x, s0 = wave * SPW;
+  const int row = lane & 15, kg = lane >> 4;
+
+  __shared__ u32x4 sA[KS * 2 * 4 * RL];  // [step][hi, lo][lane group][row]; then the partial tiles
+  static_assert(NW * 64 <= KS * 2 * 4 * RL, "the partial tiles fit the A buffer");
+  f32x4* sAcc = (f32x4*)sA;
+
+  f32x4 pa[UPT][2];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+    const bool ok = u < UNITS && r < P.R;
+    const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
+    pa[i][0] = src[0];
+    pa[i][1] = src[1];
+  }
+  const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
+  u32x4 b[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u < UNITS) {
+      const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+      const bool ok = r < P.R;
+      float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = ok ? v[e] : 0.0f;
+        const __bf16 h = (__bf16)x;
+        hi[e] = h;
+        lo[e] = (__bf16)(x - (float)h);
+      }
+      sA[((j * 2) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
+      sA[((j * 2 + 1) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, lo);
+    }
+  }
+  __syncthreads();
+  const bool rok = row < P.R && row < RL;
+  const int rc = row < RL ? row : RL - 1;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 h = sA[(((s0 + j) * 2) * 4 + kg) * RL + rc];
+    const u32x4 l = sA[(((s0 + j) * 2 + 1) * 4 + kg) * RL + rc];
+    const bf16x8 ah = __builtin_bit_cast(bf16x8, rok ? h : z), al = __builtin_bit_cast(bf16x8, rok ? l : z);
+    const bf16x8 w = __builtin_bit_cast(bf16x8, b[j]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, w, acc, 0, 0, 0);
+  }
+  __syncthreads();  // every wave is done with A
+  sAcc[wave * 64 + lane] = acc;
+  __syncthreads();
+  const int npairs = P.R * 8;
+  for (int p = tid; p < npairs; p += NT) {
+    const int r = p >> 3, pp = p & 7;
+    const int col = tile * 16 + 2 * pp;
+    const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+    float v0, v1;
+    group_sum<NW, 1, 1>(sAcc, 0, e0, v0, v1);
+    const float t = sum8(resid_pair(P, r, col, v0, v1));
+    if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+  }
+}
+
 // -------------------------------------------------------------- attention
 //
 // Grid (split, kv head, sequence); a split is 256 keys at absolute positions
@@ -1266,6 +1347,16 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
   }
 #undef SPECV_MM_HAS
   return false;
+}
+
+hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st) {
+  if (p.R < 1 || p.R > rl || p.K != nw * spw * 32 || p.N % 16) return hipErrorInvalidValue;
+  if (nw == 16 && spw == 19 && rl == 4) {  // the smallest staging that holds the rows
+    if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<16, 19, 2>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+    else hipLaunchKernelGGL((k_mm1l<16, 19, 4>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,

@@ -63,6 +63,10 @@ struct MmPlan {
   int nw, spw, ct, nbuf, gp, rmax;
 };
 
+// The down projection at K = 9728 for up to four rows: one tile per
+// workgroup, 16 K parts of 19 steps, A staged in LDS (launch_mm1l); the
+// split-K kernel takes the same parts (nk = 19) for more rows.
+
 // Preference lists, first match on K = nw * spw * 32 wins.
 #ifndef SPECV_MM_QKV
 #define SPECV_MM_QKV {16, 5, 1, 1, 16, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}
@@ -77,6 +81,9 @@ struct MmPlan {
 #define SPECV_MM_D {16, 8, 1, 0, 1, 16}, {1, 4, 1, 1, 1, 16}, {2, 2, 1, 1, 2, 16}, {1, 2, 1, 1, 1, 16}, {4, 1, 1, 1, 4, 16}
 #endif
 
+#ifndef SPECV_DOWN_LDS
+#define SPECV_DOWN_LDS 1
+#endif
 #ifndef SPECV_MM_WG_PER_CU
 #define SPECV_MM_WG_PER_CU 1
 #endif
@@ -94,6 +101,7 @@ struct Layout {
   int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
   int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
   MmPlan mm_qkv, mm_o, mm_gu, mm_d;  // per-kernel path, bf16: the one-pass GEMMs for R <= rmax
+  bool d_lds;                        // down: the LDS-staged one-pass GEMM for R <= 4
   // weights
   std::vector<LayerOff> lay;
   size_t emb, wlm, g_final, weights_bytes;
@@ -152,6 +160,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = MmPlan{0, 0, 0, 0, 0, 0};
+  Lo.d_lds = false;
   if (Lo.fmt == FMT_BF16 && !(d.flags & SPEC_FLAG_PERSISTENT)) {
     // one-pass GEMMs for R <= 16; the split-K kernel (R > 16) then takes the
     // same K parts (nk = spw), so both give identical results
@@ -161,6 +170,10 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     Lo.mm_d = pick_mm(EPI_RESID, Lo.F, {SPECV_MM_D});
     // one-pass plans of R up to 16 that the split-K kernel cannot take at its
     // own depth keep their parts there too (rmax < 16: both serve R <= 16)
+    if (SPECV_DOWN_LDS && !Lo.mm_d.nw && Lo.F == 16 * 19 * 32) {
+      Lo.d_lds = true;
+      Lo.nk_d = 19;
+    }
     if (Lo.mm_qkv.nw && Lo.mm_qkv.rmax < 16) Lo.nk_qkv = Lo.mm_qkv.spw;
     if (Lo.mm_gu.nw && Lo.mm_gu.rmax < 16) Lo.nk_gu = Lo.mm_gu.spw;
     if (Lo.mm_o.nw && Lo.mm_o.rmax < 16) Lo.nk_o = Lo.mm_o.spw;
@@ -510,7 +523,8 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.lda = L.F;
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, st));
+      if (L.d_lds && R <= 4) HIPCHK(c, launch_mm1l(gd, 16, 19, 4, st));
+      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, st));
       return SPEC_OK;
     }
   }
