@@ -279,7 +279,7 @@ def _csv_rows(path):
 
 # the gate/up GEMM at S=1: the walking one-pass kernel (SwiGLU epilogue,
 # 16 K parts of 5 steps, one 16-column tile per block, one weight buffer)
-GU_KERNEL = "k_mm<2, 16, 5, 1, 1>"
+GU_KERNEL = "k_mm<2, 16, 5, 1, 1, 16>"
 
 
 def summarize_counters(fetch_csv, write_csv, out_dir):

@@ -648,7 +648,10 @@ __device__ __forceinline__ void group_sum(const f32x4* sAcc, int ct, int e0, flo
 // read theirs, so NBUF blocks are in flight while one is reduced.  Per block each wave runs
 // 2*CT*SPW MFMA and leaves its partial tiles in LDS; the workgroup adds the
 // parts in wave order and runs the epilogue.  No partial buffer, arrival
-// counter or second pass.  The K parts, the MFMA order within a part and the
+// counter or second pass, except for the LM head: its threads keep the
+// largest argmax key of their (row, 16 columns) over the walk, each group
+// makes one atomic max per row, and the last workgroup to arrive runs the
+// accept stage.  The K parts, the MFMA order within a part and the
 // order of the final additions are those of the split-K kernel with
 // NK = SPW and NW slices, so the two agree bit for bit (the split-K kernel
 // serves R > 16).
@@ -704,6 +707,12 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
       }
     }
   }
+  // LM head: a pair of each thread's (row, 16 columns) group keeps the
+  // largest argmax key over the walk; one atomic per group at the end.
+  constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // pairs per thread at 16 rows
+  unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
+#pragma unroll
+  for (int it = 0; it < (EPI == EPI_LM ? PPT : 1); ++it) kmax[it] = 0ull;
   u32x4 b0[CT][SPW], b1[NBUF == 2 ? CT : 1][NBUF == 2 ? SPW : 1];
   int blk = blockIdx.x;
   fetch(b0, blk);
@@ -784,20 +793,28 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
     // D layout keeps element (row r, column cc) of a tile in component r%4
     // of lane 16*(r/4) + cc.
     const int npairs = P.R * 8 * CT;
-    for (int p = tid; p < npairs; p += NT) {
-      const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
-      const int col = (cur * CT + ct) * 16 + 2 * pp;
-      const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
-      float v0, v1;
-      group_sum<NW, GP, CT>(sAcc, ct, e0, v0, v1);
-      if (col < P.N) {
-        if constexpr (EPI == EPI_QKV) {
-          qkv_pair(P, r, col, v0, v1);
-        } else if constexpr (EPI == EPI_RESID) {
-          const float t = sum8(resid_pair(P, r, col, v0, v1));
-          if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
-        } else {
-          swiglu_pair(P, r, col, v0, v1);
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + it * NT;
+      if (p < npairs) {
+        const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+        const int col = (cur * CT + ct) * 16 + 2 * pp;
+        const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+        float v0, v1;
+        group_sum<NW, GP, CT>(sAcc, ct, e0, v0, v1);
+        if (col < P.N) {
+          if constexpr (EPI == EPI_QKV) {
+            qkv_pair(P, r, col, v0, v1);
+          } else if constexpr (EPI == EPI_RESID) {
+            const float t = sum8(resid_pair(P, r, col, v0, v1));
+            if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+          } else if constexpr (EPI == EPI_SWIGLU) {
+            swiglu_pair(P, r, col, v0, v1);
+          } else {
+            const unsigned long long k0 = lm_value(P, r, col, v0), k1 = lm_value(P, r, col + 1, v1);
+            const unsigned long long k = k0 > k1 ? k0 : k1;
+            kmax[it] = k > kmax[it] ? k : kmax[it];
+          }
         }
       }
     }
@@ -817,6 +834,20 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
     }
   } else {
     for (; blk < nblk; blk += G) pass(b0, blk, blk + G);
+  }
+  if constexpr (EPI == EPI_LM) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      unsigned long long k = kmax[it];
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(k, o);
+        k = t > k ? t : k;
+      }
+      const int p = tid + it * NT;
+      if (p < P.R * 8 * CT && (p & 7) == 0) atomicMax(&P.argkey[p / (8 * CT)], k);
+    }
+    lm_finish(P, G, (float*)sAcc);
   }
 }
 
@@ -1340,7 +1371,7 @@ hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_
 
 bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
 #define SPECV_MM_HAS(a, b, c, d, e) if (nw == a && spw == b && ct == c && nbuf == d && gp == e) return true;
-  if (epi == EPI_QKV || epi == EPI_SWIGLU) {
+  if (epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LM) {
     SPECV_MM_H(SPECV_MM_HAS)
   } else if (epi == EPI_RESID) {
     SPECV_MM_R(SPECV_MM_HAS)
@@ -1363,7 +1394,10 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
                      hipStream_t st) {
   if (p.R < 1 || p.R > 16 || p.K != nw * spw * 32 || max_grid < 1 || p.N % 16) return hipErrorInvalidValue;
   // the RMSNorm prologue reads K/16 partial sums per row (K = hidden)
-  if ((epi == EPI_QKV || epi == EPI_SWIGLU) && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
+  if ((epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LM) && (!p.ss || !p.gain || p.ss_n * 16 != p.K))
+    return hipErrorInvalidValue;
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
+    return hipErrorInvalidValue;
   const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
   const int grid = nblk < max_grid ? nblk : max_grid;
 #define SPECV_MM_GO(E, a, b, c, d, e)                                                    \
@@ -1377,13 +1411,17 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
 #define SPECV_MM_GO_Q(a, b, c, d, e) SPECV_MM_GO(EPI_QKV, a, b, c, d, e)
 #define SPECV_MM_GO_S(a, b, c, d, e) SPECV_MM_GO(EPI_SWIGLU, a, b, c, d, e)
 #define SPECV_MM_GO_R(a, b, c, d, e) SPECV_MM_GO(EPI_RESID, a, b, c, d, e)
+#define SPECV_MM_GO_L(a, b, c, d, e) SPECV_MM_GO(EPI_LM, a, b, c, d, e)
   if (epi == EPI_QKV) {
     SPECV_MM_H(SPECV_MM_GO_Q)
   } else if (epi == EPI_SWIGLU) {
     SPECV_MM_H(SPECV_MM_GO_S)
   } else if (epi == EPI_RESID) {
     SPECV_MM_R(SPECV_MM_GO_R)
+  } else if (epi == EPI_LM) {
+    SPECV_MM_H(SPECV_MM_GO_L)
   }
+#undef SPECV_MM_GO_L
 #undef SPECV_MM_GO_Q
 #undef SPECV_MM_GO_S
 #undef SPECV_MM_GO_R

@@ -77,6 +77,9 @@ struct MmPlan {
 #ifndef SPECV_MM_O
 #define SPECV_MM_O {8, 16, 2, 0, 1, 8}, {16, 8, 1, 0, 1, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}, {4, 1, 1, 1, 4, 16}
 #endif
+#ifndef SPECV_MM_LM
+#define SPECV_MM_LM {16, 5, 1, 1, 16, 16}, {1, 2, 1, 1, 1, 16}, {2, 1, 1, 1, 2, 16}
+#endif
 #ifndef SPECV_MM_D
 #define SPECV_MM_D {16, 8, 1, 0, 1, 16}, {1, 4, 1, 1, 1, 16}, {2, 2, 1, 1, 2, 16}, {1, 2, 1, 1, 1, 16}, {4, 1, 1, 1, 4, 16}
 #endif
@@ -100,7 +103,7 @@ struct Layout {
   int H, nq, nkv, hd, F, V, L, DQ, DK, Nqkv, Ngu;
   int max_rows, max_seqs, max_ctx, bt_stride, n_blocks, max_splits, G;
   int nk_qkv, nk_o, nk_gu, nk_d, nk_lm;
-  MmPlan mm_qkv, mm_o, mm_gu, mm_d;  // per-kernel path, bf16: the one-pass GEMMs for R <= rmax
+  MmPlan mm_qkv, mm_o, mm_gu, mm_d, mm_lm;  // per-kernel path, bf16: the one-pass GEMMs for R <= rmax
   bool d_lds;                        // down: the LDS-staged one-pass GEMM for R <= 4
   // weights
   std::vector<LayerOff> lay;
@@ -159,7 +162,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
-  Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = MmPlan{0, 0, 0, 0, 0, 0};
+  Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = Lo.mm_lm = MmPlan{0, 0, 0, 0, 0, 0};
   Lo.d_lds = false;
   if (Lo.fmt == FMT_BF16 && !(d.flags & SPEC_FLAG_PERSISTENT)) {
     // one-pass GEMMs for R <= 16; the split-K kernel (R > 16) then takes the
@@ -168,6 +171,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     Lo.mm_gu = pick_mm(EPI_SWIGLU, Lo.H, {SPECV_MM_GU});
     Lo.mm_o = pick_mm(EPI_RESID, Lo.DQ, {SPECV_MM_O});
     Lo.mm_d = pick_mm(EPI_RESID, Lo.F, {SPECV_MM_D});
+    Lo.mm_lm = pick_mm(EPI_LM, Lo.H, {SPECV_MM_LM});
     // one-pass plans of R up to 16 that the split-K kernel cannot take at its
     // own depth keep their parts there too (rmax < 16: both serve R <= 16)
     if (SPECV_DOWN_LDS && !Lo.mm_d.nw && Lo.F == 16 * 19 * 32) {
@@ -178,6 +182,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     if (Lo.mm_gu.nw && Lo.mm_gu.rmax < 16) Lo.nk_gu = Lo.mm_gu.spw;
     if (Lo.mm_o.nw && Lo.mm_o.rmax < 16) Lo.nk_o = Lo.mm_o.spw;
     if (Lo.mm_d.nw && Lo.mm_d.rmax < 16) Lo.nk_d = Lo.mm_d.spw;
+    if (Lo.mm_lm.nw && Lo.mm_lm.rmax < 16) Lo.nk_lm = Lo.mm_lm.spw;
   }
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
   if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
@@ -448,7 +453,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.seq_ids = seq_ids;
     gl.S = S;
     gl.n_seq = n_seq;
-    HIPCHK(c, launch_gemm(gl, L.nk_lm, EPI_LM, L.fmt, st));
+    HIPCHK(c, gemm_or_mm(gl, L.mm_lm, L.nk_lm, EPI_LM, L.fmt, c->mm_grid, st));
     return SPEC_OK;
   }
   const LayerOff& lw = L.lay[(size_t)l];
