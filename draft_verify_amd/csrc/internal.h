@@ -99,16 +99,16 @@ struct AttnParams {
   float scale;
   int max_splits;        // grid.x: 256-key splits of the longest context
   float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
-  unsigned* cnt;         // [n_seq][n_kv] arrival counters of the fused combine, zero between launches
+  unsigned* cnt;         // [n_seq][n_kv][n_qt] arrival counters of the fused merge, zero between launches
   float* out;            // [R][n_q*hd]
-  int fuse;              // short contexts, few query columns: the last split combines in k_attn
+  int n_qt;              // query tiles per sequence: ceil(S * n_q / n_kv / 16)
+  int fuse;              // short contexts: the last split of a tile merges it in k_attn
 };
-// The attention combines its splits in one kernel when every context of the
-// step (cache + span) holds at most kAttnFuseKeys keys and a sequence has at
-// most kAttnFuseCols query columns (span rows x heads per kv head): the last
-// split's workgroup then combines every column itself.
-constexpr int kAttnFuseKeys = 8 * 256;
-constexpr int kAttnFuseCols = 4;
+// The attention merges its splits in the same kernel when every context of
+// the step (cache + span) spans at most attn_fuse_splits(hd) splits of 256
+// keys: the last split of each query tile to finish then merges the tile's
+// columns itself, keeping the splits' (max, sum) in its LDS.
+constexpr int attn_fuse_splits(int hd) { return hd >= 32 ? 64 : 32; }
 
 struct EmbedParams {
   const uint16_t* emb;   // [V][H] bf16

@@ -1059,264 +1059,313 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 
 // -------------------------------------------------------------- attention
 //
-// Grid (split, kv head, sequence); a split is 256 keys at absolute positions
-// [256*split, 256*split + 256), one 64-key chunk (four 16-token blocks) per
-// wave.  Scores are computed transposed, S^T = K Q^T, so the probabilities
-// come out of the MFMA already in the B-operand layout of O^T = V^T P^T and
-// never leave registers; V blocks are stored d-major ([hd][16 tokens]) so
-// the V^T operand is read straight from memory.  Query columns are
-// (span row, head of the GQA group).  Each wave's chunk softmax is combined
-// across the four waves in LDS in wave order, each split's (max, sum, o)
-// goes to memory, and k_attn_combine merges the splits of every query
-// column.  Row i attends keys [0, p+i]; a chunk or split lying wholly past a
-// row's position contributes exactly nothing.
+// Grid (split, kv head, sequence x query tile).  A split is 256 keys at
+// absolute positions [256*split, 256*split + 256), one 64-key chunk (four
+// 16-token blocks) per wave; a query tile is 16 query columns (span row,
+// head of the GQA group) of one sequence and kv head, so the tiles of a long
+// span run side by side.  Scores are computed transposed, S^T = K Q^T, so the
+// probabilities come out of the MFMA already in the B-operand layout of
+// O^T = V^T P^T and never leave registers; V blocks are stored d-major
+// ([hd][16 tokens]) so the V^T operand is read straight from memory.  The
+// prologue issues every load unconditionally from clamped addresses (block
+// ids, then K, V and the queries) and zeroes what lies past the context
+// afterwards, so a workgroup waits for two memory latencies, not one per
+// block.  Each wave's chunk softmax is combined across the four waves in LDS
+// in wave order and each split's (max, sum, o) goes to memory; the splits of
+// a column are merged by combine_tile, run by the tile's last split to
+// finish when every context of the step is short, else by k_attn_combine.
+// Row i attends keys [0, p+i]; a chunk or split lying wholly past a row's
+// position contributes exactly nothing.
 
-template <int HD, bool COH>
-__device__ void combine_col(const AttnParams& P, int b, int kvh, int qcol, int lane, float* sW);
-constexpr int kFuseSplitsMax = 16;  // the fused combine keeps 16 split weights per wave in LDS
+template <int HD, bool COH, int MS>
+__device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p, float* sML);
+constexpr int kMaxCombineSplits = 256;  // host-checked: max_ctx <= 65536
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   constexpr int KST = (HD + 31) / 32;  // 32-wide steps over the head dim (zero padded)
   constexpr int DT = HD / 16;          // 16-row tiles of O^T
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int seq = P.seq_ids[b];
-  const int p = P.kv_len[seq];
-  const int S = P.S, G = P.n_q / P.n_kv, QC = S * G;
-  const int total = p + S;
-  const int n_act = (total + 255) >> 8;
-  if (split >= n_act) return;
+  constexpr int FS = attn_fuse_splits(HD);
+  static_assert(16 * FS * 2 <= 4 * 16 * (HD + 1), "the fused merge's split table fits sO");
+  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int b = blockIdx.z / P.n_qt, qt = blockIdx.z - b * P.n_qt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int DQ = P.n_q * HD;
+  const int S = P.S, G = P.n_q / P.n_kv, QC = S * G;
+  // The context length and this wave's four block ids load together (ids
+  // clamped to the table row; blocks past the context take the sequence's
+  // block 0 and are zeroed below), then K, V and the queries.
+  const int seq = P.seq_ids[b];
+  const int32_t* btrow = P.bt + (size_t)seq * P.bt_stride;
+  const int kb0 = split * 16 + wave * 4;
+  int bv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bv[t] = btrow[kb0 + t < P.bt_stride ? kb0 + t : 0];
+  const int bz = btrow[0];
+  // every id is loaded before anything branches on the context length
+  asm volatile("" ::"v"(bv[0]), "v"(bv[1]), "v"(bv[2]), "v"(bv[3]), "v"(bz));
+  const int p = P.kv_len[seq];
+  const int total = p + S;
+  const int n_act = (total + 255) >> 8;
+  if (split >= n_act) return;
 
   __shared__ float sO[4][16][HD + 1];
   __shared__ float sM[4][16], sL[4][16], sF[4][16];
 
-  // This wave's four blocks, loaded once and reused for every query tile.
-  const int kb0 = split * 16 + wave * 4;
+  int blk[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) blk[t] = (kb0 + t) * 16 < total ? bv[t] : bz;
+  const int col = qt * 16 + c16;
+  const bool qok = col < QC;
+  const int colc = qok ? col : 0;
+  const int iq = colc / G, head = kvh * G + colc % G;
+  const int pos_q = p + iq;
+  const float* qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
+  f32x4 qa[KST][2];
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) {
+    const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
+    qa[ks][0] = *(const f32x4*)(qrow + dc);
+    qa[ks][1] = *(const f32x4*)(qrow + dc + 4);
+  }
   f16x8 kf[4][KST];
   f16x4 vf[4][DT];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int kb = kb0 + t;
-    const bool ok = kb * 16 < total;
-    const int blk = ok ? P.bt[(size_t)seq * P.bt_stride + kb] : 0;
-    const _Float16* kbase = P.kpool + ((size_t)blk * P.n_kv + kvh) * 16 * HD;
-    const _Float16* vbase = P.vpool + ((size_t)blk * P.n_kv + kvh) * HD * 16;
+    const _Float16* kbase = P.kpool + ((size_t)blk[t] * P.n_kv + kvh) * 16 * HD;
+    const _Float16* vbase = P.vpool + ((size_t)blk[t] * P.n_kv + kvh) * HD * 16;
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
-      const int d = ks * 32 + g4 * 8;
-      if (ok && d < HD) kf[t][ks] = *(const f16x8*)(kbase + c16 * HD + d);
-      else kf[t][ks] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
+      kf[t][ks] = *(const f16x8*)(kbase + c16 * HD + dc);
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      if (ok) vf[t][dt] = *(const f16x4*)(vbase + (dt * 16 + c16) * 16 + g4 * 4);
-      else vf[t][dt] = (f16x4){0, 0, 0, 0};
+    for (int dt = 0; dt < DT; ++dt) vf[t][dt] = *(const f16x4*)(vbase + (dt * 16 + c16) * 16 + g4 * 4);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bool ok = (kb0 + t) * 16 < total;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const bool dok = ks * 32 + g4 * 8 < HD;
+      kf[t][ks] = (ok && dok) ? kf[t][ks] : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[t][dt] = ok ? vf[t][dt] : (f16x4){0, 0, 0, 0};
+  }
+  f16x8 qf[KST];
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) {
+    const bool use = qok && ks * 32 + g4 * 8 < HD;
+    const float v[8] = {qa[ks][0].x, qa[ks][0].y, qa[ks][0].z, qa[ks][0].w,
+                        qa[ks][1].x, qa[ks][1].y, qa[ks][1].z, qa[ks][1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[ks][e] = use ? (_Float16)v[e] : (_Float16)0.0f;
   }
 
-  const int n_qt = (QC + 15) >> 4;
-  for (int qt = 0; qt < n_qt; ++qt) {
-    const int col = qt * 16 + c16;
-    const bool qok = col < QC;
-    const int iq = qok ? col / G : 0, hh = qok ? col % G : 0;
-    const int head = kvh * G + hh;
-    const int pos_q = p + iq;
-    const float* qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
-    f16x8 qf[KST];
+  float s[4][4];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) {
-      const int d = ks * 32 + g4 * 8;
-      f16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (qok && d < HD) {
-        const f32x4 a0 = *(const f32x4*)(qrow + d), a1 = *(const f32x4*)(qrow + d + 4);
-        v[0] = (_Float16)a0.x; v[1] = (_Float16)a0.y; v[2] = (_Float16)a0.z; v[3] = (_Float16)a0.w;
-        v[4] = (_Float16)a1.x; v[5] = (_Float16)a1.y; v[6] = (_Float16)a1.z; v[7] = (_Float16)a1.w;
-      }
-      qf[ks] = v;
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ks], qf[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = (kb0 + t) * 16 + g4 * 4 + i;
+      s[t][i] = (qok && key <= pos_q) ? acc[i] * P.scale : -INFINITY;
+      mx = fmaxf(mx, s[t][i]);
     }
-    float s[4][4];
-    float mx = -INFINITY;
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float l = 0.0f;
+  f16x8 pf[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ks], qf[ks], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = (kb0 + t) * 16 + g4 * 4 + i;
-        s[t][i] = (qok && key <= pos_q) ? acc[i] * P.scale : -INFINITY;
-        mx = fmaxf(mx, s[t][i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float e = (mx == -INFINITY) ? 0.0f : expf(s[t][i] - mx);
+      l += e;
+      pf[t >> 1][(t & 1) * 4 + i] = (_Float16)e;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float l = 0.0f;
-    f16x8 pf[2];
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = (mx == -INFINITY) ? 0.0f : expf(s[t][i] - mx);
-        l += e;
-        pf[t >> 1][(t & 1) * 4 + i] = (_Float16)e;
-      }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const f16x4 v0 = vf[2 * s2][dt], v1 = vf[2 * s2 + 1][dt];
-        const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[s2], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sO[wave][c16][dt * 16 + g4 * 4 + i] = acc[i];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const f16x4 v0 = vf[2 * s2][dt], v1 = vf[2 * s2 + 1][dt];
+      const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[s2], acc, 0, 0, 0);
     }
-    if (g4 == 0) {
-      sM[wave][c16] = mx;
-      sL[wave][c16] = l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sO[wave][c16][dt * 16 + g4 * 4 + i] = acc[i];
+  }
+  if (g4 == 0) {
+    sM[wave][c16] = mx;
+    sL[wave][c16] = l;
+  }
+  __syncthreads();
+  // Combine the four chunks of this split, in wave order: the weight of
+  // each (wave, column) once, then the values.
+  if (tid < 16) {
+    const int c = tid;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][c]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (M == -INFINITY) ? 0.0f : expf(sM[w][c] - M);
+      sF[w][c] = f;
+      L += sL[w][c] * f;
     }
-    __syncthreads();
-    // Combine the four chunks of this split, in wave order: the weight of
-    // each (wave, column) once, then the values.
-    if (tid < 16) {
-      const int c = tid;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][c]);
-      float L = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = (M == -INFINITY) ? 0.0f : expf(sM[w][c] - M);
-        sF[w][c] = f;
-        L += sL[w][c] * f;
-      }
-      const int qcol = qt * 16 + c;
-      if (qcol < QC) {
-        float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-        st_dev(dst, M);
-        st_dev(dst + 1, L);
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < 16 * (HD / 2); e += 256) {
-      const int c = e / (HD / 2), d = 2 * (e % (HD / 2));
-      const int qcol = qt * 16 + c;
-      if (qcol >= QC) continue;
-      float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = sF[w][c];
-        o0 += sO[w][c][d] * f;
-        o1 += sO[w][c][d + 1] * f;
-      }
+    const int qcol = qt * 16 + c;
+    if (qcol < QC) {
       float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-      st_dev2(dst + 2 + d, o0, o1);
+      st_dev(dst, M);
+      st_dev(dst + 1, L);
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int e = tid; e < 16 * (HD / 2); e += 256) {
+    const int c = e / (HD / 2), d = 2 * (e % (HD / 2));
+    const int qcol = qt * 16 + c;
+    if (qcol >= QC) continue;
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = sF[w][c];
+      o0 += sO[w][c][d] * f;
+      o1 += sO[w][c][d + 1] * f;
+    }
+    float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+    st_dev2(dst + 2 + d, o0, o1);
   }
   if (!P.fuse) return;
-  // Short contexts: the last split of this (sequence, kv head) to finish
-  // combines every query column, as k_attn_combine would.
+  // Short contexts: the last split of this (sequence, kv head, tile) to
+  // finish merges the tile's columns, as k_attn_combine would.
   __shared__ int sLast;
   wait_mem();
   __syncthreads();
+  unsigned* cnt = P.cnt + ((size_t)b * P.n_kv + kvh) * P.n_qt + qt;
   if (tid == 0) {
-    const unsigned old = atomicAdd(&P.cnt[b * P.n_kv + kvh], 1u);
+    const unsigned old = atomicAdd(cnt, 1u);
     sLast = old == (unsigned)(n_act - 1);
   }
   __syncthreads();
   if (!sLast) return;
-  if (tid == 0) P.cnt[b * P.n_kv + kvh] = 0u;  // ready for the next launch
-  float* sW = &sM[0][0] + wave * 16;            // kFuseSplits <= 16 weights per wave
-  for (int qcol = wave; qcol < QC; qcol += 4) combine_col<HD, true>(P, b, kvh, qcol, lane, sW);
+  if (tid == 0) *cnt = 0u;  // ready for the next launch
+  combine_tile<HD, true, FS>(P, b, kvh, qt, p, &sO[0][0][0]);
 }
 
-// Split combine of one query column (one wave): lane i reduces splits i,
-// i+64, ...: the maximum and the sum of l_s exp(m_s - M) by fixed xor trees,
-// then every lane takes output pairs and sums w_s o_s in split order with
-// eight split loads in flight.  The order depends only on the row's
-// position, never on the other rows.  COH: the partials were written by
-// other workgroups of the same kernel (device-coherent loads).
-constexpr int kMaxCombineSplits = 256;  // host-checked: max_ctx <= 65536
-constexpr int kFuseSplits = 8;          // contexts of at most 8 splits may combine in the attention kernel
-
-template <bool COH>
-__device__ __forceinline__ float ld_part(const float* p) {
-  if constexpr (COH) return ld_dev(p);
-  else return *p;
-}
 template <bool COH>
 __device__ __forceinline__ float2 ld_part2(const float* p) {
   if constexpr (COH) return ld_dev2(p);
   else return *(const float2*)p;
 }
 
-template <int HD, bool COH>
-__device__ void combine_col(const AttnParams& P, int b, int kvh, int qcol, int lane, float* sW) {
+// Split merge of the 16 query columns of tile qt (sequence b, kv head kvh)
+// by 256 threads: column c = tid / 16 belongs to 16 threads of one wave,
+// which hold its splits j, j + 16, ... for the maxima and its output pairs
+// j, j + 16, ... for the sums.  Per column: M = the largest split maximum;
+// f_s = exp(m_s - M); L = the sum of l_s f_s in split order; o = the sum
+// of o_s (f_s (1/L)) in split order.  Every order depends only on the
+// column's own row position, never on the other rows.  p is the sequence's
+// cache length; sML holds 16 x MS (f, l) pairs of LDS (MS >= the column's
+// splits).  The maxima, then the first 16 splits' outputs, are loaded
+// before anything waits.  COH: the partials were written by other
+// workgroups of the same kernel (device-coherent loads).
+template <int HD, bool COH, int MS>
+__device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p, float* sML) {
 #pragma clang fp contract(off)
-  const int G = P.n_q / P.n_kv, S = P.S, QC = S * G;
-  const int seq = P.seq_ids[b];
-  const int p = P.kv_len[seq];
-  const int iq = qcol / G, head = kvh * G + qcol % G;
-  const int nsp = ((p + iq) >> 8) + 1;
+  static_assert(MS % 16 == 0, "whole rounds of 16 splits");
+  constexpr int PP = HD >= 32 ? HD / 32 : 1;  // output pairs per thread
+  constexpr int CH = 16;                      // splits of output loads in flight
+  const int tid = threadIdx.x, c = tid >> 4, j = tid & 15;
+  const int G = P.n_q / P.n_kv, QC = P.S * G;
+  const int qcol = qt * 16 + c;
+  const bool cok = qcol < QC;
+  const int qc = cok ? qcol : 0;
+  const int iq = qc / G, head = kvh * G + qc % G;
+  int nsp = cok ? ((p + iq) >> 8) + 1 : 0;
+  nsp = nsp < MS ? nsp : MS;
   const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
-  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
+  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qc) * (HD + 2);
+  float* ml = sML + (size_t)c * MS * 2;
+
+  float2 mlv[MS / 16];
+#pragma unroll
+  for (int it = 0; it < MS / 16; ++it) {
+    const int sp = j + 16 * it;
+    mlv[it] = ld_part2<COH>(base + (size_t)(sp < nsp ? sp : 0) * stride);
+  }
+  float2 v[PP][CH];
+#define SPECV_COMBINE_LOADS(s0)                                                  \
+  _Pragma("unroll") for (int i = 0; i < PP; ++i) {                               \
+    const int dp = j + 16 * i, dpc = dp < HD / 2 ? dp : 0;                       \
+    _Pragma("unroll") for (int k = 0; k < CH; ++k) {                             \
+      const int sp = (s0) + k < nsp ? (s0) + k : 0;                              \
+      v[i][k] = ld_part2<COH>(base + (size_t)sp * stride + 2 + 2 * dpc);         \
+    }                                                                            \
+  }
+  SPECV_COMBINE_LOADS(0)
   float M = -INFINITY;
-  for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, ld_part<COH>(base + sp * stride));
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float L = 0.0f;
-  for (int sp = lane; sp < nsp; sp += 64) {
-    const float2 ml = ld_part2<COH>(base + sp * stride);
-    const float f = expf(ml.x - M);
-    sW[sp] = f;
-    L += ml.y * f;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-  const float inv = 1.0f / L;
-  for (int sp = lane; sp < nsp; sp += 64) sW[sp] *= inv;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  const int DQ = P.n_q * HD;
-  for (int dp = lane; dp < HD / 2; dp += 64) {
-    const float* src = base + 2 + 2 * dp;
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int s0 = 0; s0 < nsp; s0 += 8) {
-      float2 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) v[i] = ld_part2<COH>(src + (size_t)(s0 + i) * stride);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsp) {
-          const float w = sW[s0 + i];
-          o0 += v[i].x * w;
-          o1 += v[i].y * w;
-        }
+  for (int it = 0; it < MS / 16; ++it) {
+    const int sp = j + 16 * it;
+    if (sp < nsp) {
+      ml[2 * sp] = mlv[it].x;
+      ml[2 * sp + 1] = mlv[it].y;
+      M = fmaxf(M, mlv[it].x);
     }
-    *(float2*)(P.out + (size_t)(b * S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0, o1);
   }
-  __builtin_amdgcn_wave_barrier();  // sW is reused by this wave's next column
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the column's maxima and sums are in LDS
+  for (int sp = j; sp < nsp; sp += 16) ml[2 * sp] = expf(ml[2 * sp] - M);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  float L = 0.0f;
+  for (int sp = 0; sp < nsp; ++sp) L += ml[2 * sp + 1] * ml[2 * sp];
+  const float inv = 1.0f / L;
+  float o0[PP], o1[PP];
+#pragma unroll
+  for (int i = 0; i < PP; ++i) o0[i] = o1[i] = 0.0f;
+  for (int s0 = 0; s0 < nsp; s0 += CH) {
+    if (s0 > 0) { SPECV_COMBINE_LOADS(s0) }
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+      if (s0 + k < nsp) {
+        const float w = ml[2 * (s0 + k)] * inv;
+#pragma unroll
+        for (int i = 0; i < PP; ++i) {
+          o0[i] += v[i][k].x * w;
+          o1[i] += v[i][k].y * w;
+        }
+      }
+  }
+#undef SPECV_COMBINE_LOADS
+  const int DQ = P.n_q * HD;
+#pragma unroll
+  for (int i = 0; i < PP; ++i) {
+    const int dp = j + 16 * i;
+    if (cok && dp < HD / 2)
+      *(float2*)(P.out + (size_t)(b * P.S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0[i], o1[i]);
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
-// Split combine kernel: grid (ceil(QC/4), kv head, sequence); wave w
-// combines query column 4*blockIdx.x + w.
+// Split merge kernel for long contexts: grid (query tile, kv head, sequence).
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int QC = P.S * (P.n_q / P.n_kv);
-  const int qcol = blockIdx.x * 4 + wave;
-  __shared__ float sW[4][kMaxCombineSplits];
-  if (qcol >= QC) return;  // whole waves; no barrier below
-  combine_col<HD, false>(P, b, kvh, qcol, lane, sW[wave]);
+  __shared__ float sML[16 * kMaxCombineSplits * 2];
+  const int b = blockIdx.z;
+  combine_tile<HD, false, kMaxCombineSplits>(P, b, blockIdx.y, blockIdx.x, P.kv_len[P.seq_ids[b]], sML);
 }
 
 // -------------------------------------------------------------- launchers
@@ -1430,10 +1479,11 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
 }
 
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
-  if (p.max_splits > kMaxCombineSplits) return hipErrorInvalidValue;
-  static_assert(kFuseSplits <= kFuseSplitsMax, "fused combine weights fit the LDS scratch");
-  const dim3 grid(p.max_splits, p.n_kv, p.n_seq);
-  const dim3 cgrid((p.S * (p.n_q / p.n_kv) + 3) / 4, p.n_kv, p.n_seq);
+  if (p.max_splits > kMaxCombineSplits || p.n_kv < 1 || p.n_q % p.n_kv) return hipErrorInvalidValue;
+  const int n_qt = (p.S * (p.n_q / p.n_kv) + 15) / 16;
+  if (p.n_qt != n_qt || p.n_seq < 1 || p.n_seq * n_qt > 65535) return hipErrorInvalidValue;
+  const dim3 grid(p.max_splits, p.n_kv, p.n_seq * n_qt);
+  const dim3 cgrid(n_qt, p.n_kv, p.n_seq);
   switch (hd) {
     case 128:
       hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p);

@@ -243,7 +243,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.part = take(part * R * 4);
   Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
   Lo.cnt = take((size_t)Lo.cnt_n * 4);
-  Lo.attn_cnt = take(R * Lo.nkv * 4);
+  Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
   Lo.argkey = take(R * 8);
   Lo.status = take(4);
@@ -498,6 +498,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.part = c->ws<float>(L.apart);
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
+      a.n_qt = (S * L.G + 15) / 16;
       a.fuse = c->attn_fuse;
       HIPCHK(c, launch_attn(a, L.hd, st));
       return SPEC_OK;
@@ -583,7 +584,7 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   const Layout& L = c->lo;
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
-  c->attn_fuse = (longest <= kAttnFuseKeys && S * L.G <= kAttnFuseCols) ? 1 : 0;
+  c->attn_fuse = longest <= attn_fuse_splits(L.hd) * 256 ? 1 : 0;
   StepDev* sd = (StepDev*)c->h_step();
   sd->mode = mode;
   sd->n_seq = n_seq;
@@ -716,7 +717,7 @@ int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
     // a timed-out launch leaves counters mid-count: clear every counter,
     // key and flag before the context is used again
     const Layout& L = c->lo;
-    const size_t spans[][2] = {{L.cnt, (size_t)L.cnt_n * 4}, {L.attn_cnt, (size_t)L.max_rows * L.nkv * 4},
+    const size_t spans[][2] = {{L.cnt, (size_t)L.cnt_n * 4}, {L.attn_cnt, (size_t)L.max_rows * L.nq * 4},
                                {L.lm_cnt, 4}, {L.argkey, (size_t)L.max_rows * 8}, {L.status, 4},
                                {L.done, (size_t)L.n_phases * 4}, {L.exit_cnt, 4}, {L.err, 4}};
     for (const auto& sp : spans) HIPCHK(c, launch_fill_u32(c->WS + sp[0], 0u, sp[1] / 4, c->st));
