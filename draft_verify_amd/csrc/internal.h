@@ -54,6 +54,7 @@ struct GemmParams {
   int nslices;           // K split into nslices slices of NK*32 inputs
   const float* A;        // activation rows [R][lda] (fp32)
   int lda;
+  const void* Af;        // or, bf16 only: A prepared by k_prep (hi/lo fragments), else null
   const float* ss;       // RMSNorm: per-row partial sums of squares [R][ss_n], or null
   int ss_n;
   const float* gain;     // RMSNorm gain [K]
@@ -175,6 +176,12 @@ hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
 
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
+// Prepare A for the split-K GEMM (kernels.hip: k_prep): the RMSNorm (when
+// p.ss is set) and the bf16 hi/lo split of every row once, in the MFMA
+// A-operand order, into af: ceil(R/16) * 16 * K * 4 bytes.
+hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st);
+// Slice depths whose split-K kernel is compiled to read prepared A.
+inline bool gemm_prep_supported(int nk, int fmt) { return fmt == FMT_BF16 && (nk == 19 || nk == 16 || nk == 8); }
 // One-pass GEMM for R <= 16 (kernels.hip: k_mm, k_mm1): nw waves split K
 // into nw parts of spw 32-input steps, summed in groups of gp parts (gp = 1
 // or nw: the plain part order); nbuf 1 or 2: blocks of ct 16-column tiles

@@ -206,9 +206,12 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t x) {
   return r;
 }
 
-template <int NK, int EPI, int FMT>
+template <int NK, int EPI, int FMT, bool PREP>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   static_assert(FMT == FMT_BF16 || NK % 4 == 0, "int4 slices hold whole 128-input groups");
+  static_assert(!PREP || FMT == FMT_BF16, "prepared A is bf16 hi + lo");
+  constexpr int PU = NK * 2 * 64;             // prepared A: fragment lanes of a 16-row chunk
+  constexpr int PUT = (PU + 255) / 256;
   constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per tile per slice
   constexpr int CT = gemm_tiles_per_wave(FMT);       // 16-column tiles per wave
   constexpr int UNITS = 16 * NK * 4;          // (row, step, lane group) units of 8 inputs per 16-row chunk
@@ -230,10 +233,23 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   // and gain, then A of the first 16 rows, and the weights last, so the
   // prologue's arithmetic overlaps the weights' DRAM latency.
   const int ss_row = tid >> 4, ss_part = tid & 15;
-  if (P.ss)
+  if (!PREP && P.ss)
     for (int e = tid; e < NK * 32; e += 256) sG[e] = P.gain[k0 + e];
-  f32x4 pa[UPT][2];
+  f32x4 pa[PREP ? 1 : UPT][2];
+  u32x4 pf[PREP ? PUT : 1];
+  const int nch = (P.R + 15) >> 4;
   auto load_a = [&](int m0) {
+    if constexpr (PREP) {
+      // lane u of the chunk's fragments is LDS entry u: (step j, hi/lo, lane)
+      const u32x4* af = (const u32x4*)P.Af;
+#pragma unroll
+      for (int i = 0; i < PUT; ++i) {
+        const int u = tid + i * 256, uc = u < PU ? u : 0;
+        const int j = uc >> 7, hl = (uc >> 6) & 1, l = uc & 63;
+        pf[i] = af[(((size_t)(sl * NK + j) * nch + (m0 >> 4)) * 2 + hl) * 64 + l];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * 256;
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     }
   }
 
-  if (P.ss) {
+  if (!PREP && P.ss) {
     // rstd of every row, 16 lanes per row (rstd16)
     for (int pass = 0; pass * 16 < P.R; ++pass) {
       const int r = pass * 16 + ss_row;
@@ -288,8 +304,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 
   for (int m0 = 0; m0 < P.R; m0 += 16) {
     // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo.
+    if constexpr (PREP) {
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
+      for (int i = 0; i < PUT; ++i) {
+        const int u = tid + i * 256;
+        if (u < PU) sA[u] = pf[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (PREP ? 0 : UPT); ++i) {
       const int u = tid + i * 256;
       if (u >= UNITS) continue;
       const int g = u & 3, j = (u >> 2) % NK, row = u / (4 * NK);
@@ -1378,24 +1401,88 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
   if (fmt == FMT_INT4) {
     if (!p.scales) return hipErrorInvalidValue;
     switch (nk) {
-      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
-      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
-      case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
+      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
+      case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   if (fmt != FMT_BF16) return hipErrorInvalidValue;
+  if (p.Af) {
+    switch (nk) {
+      case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
+      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
+      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (nk) {
-    case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 10: hipLaunchKernelGGL((k_gemm<10, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 5: hipLaunchKernelGGL((k_gemm<5, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 10: hipLaunchKernelGGL((k_gemm<10, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 5: hipLaunchKernelGGL((k_gemm<5, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// Activation rows once in the split-K kernel's A-operand order, for GEMMs of
+// many rows: entry ((ks * nch + ch) * 2 + hl) * 64 + l (16 bytes) holds, for
+// lane l, row 16 ch + l % 16 and inputs 32 ks + 8 (l / 16) .. +8 as bf16 hi
+// (hl = 0) or lo (hl = 1); rows past R are zero.  The RMSNorm is the split-K
+// kernel's own (rstd16, then (x * rstd) * gain), so either path gives the
+// same operands.  Grid (ceil(K/512), ceil(R/16)): 16 steps of one 16-row
+// chunk per workgroup.
+__global__ __launch_bounds__(256) void k_prep(GemmParams P, u32x4* af) {
+  const int ch = blockIdx.y, nch = gridDim.y, ks0 = blockIdx.x * 16, KS = P.K / 32;
+  const int tid = threadIdx.x;
+  __shared__ float sR[16];
+  if (P.ss) {
+    const int r = ch * 16 + (tid >> 4);
+    const float rs = rstd16(P.ss, P.ss_n, r, P.R, tid & 15, P.inv_dim, P.eps);
+    if ((tid & 15) == 0) sR[tid >> 4] = r < P.R ? rs : 0.0f;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + i * 256, l = u & 63, ks = ks0 + (u >> 6);
+    const int row = l & 15, g = l >> 4, r = ch * 16 + row;
+    if (ks < KS) {
+      float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      if (r < P.R) {
+        const f32x4* src = (const f32x4*)(P.A + (size_t)r * P.lda + ks * 32 + g * 8);
+        const f32x4 a0 = src[0], a1 = src[1];
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+      }
+      if (P.ss) {
+        const float rs = sR[row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * P.gain[ks * 32 + g * 8 + e];
+      }
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(v[e] - (float)h);
+      }
+      u32x4* dst = af + ((size_t)ks * nch + ch) * 2 * 64 + l;
+      dst[0] = __builtin_bit_cast(u32x4, hi);
+      dst[64] = __builtin_bit_cast(u32x4, lo);
+    }
+  }
+}
+
+hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
+  if (!af || !p.A || p.R < 1 || p.K % 32 || p.lda % 4 || (p.ss && !p.gain)) return hipErrorInvalidValue;
+  const dim3 grid((p.K / 32 + 15) / 16, (p.R + 15) / 16);
+  hipLaunchKernelGGL(k_prep, grid, dim3(256), 0, st, p, (u32x4*)af);
   return hipGetLastError();
 }
 

@@ -111,6 +111,7 @@ struct Layout {
   // kv
   size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
   // workspace
+  size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, done, exit_cnt, err, clock, units, unit_first, workspace_bytes;
   size_t n_units;  // GEMM units of one forward over all workgroups (persistent forward)
@@ -254,6 +255,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.rope = take((size_t)Lo.max_ctx * (Lo.hd / 2) * 2 * 4);
   Lo.apart = take((size_t)Lo.nkv * Lo.max_splits * R * Lo.G * (Lo.hd + 2) * 4);
   Lo.logits = (d.flags & SPEC_FLAG_KEEP_LOGITS) ? take(R * Lo.V * 4) : (size_t)-1;
+  Lo.af = (Lo.fmt == FMT_BF16 && R > 16 && !(d.flags & SPEC_FLAG_PERSISTENT))
+              ? take((R + 15) / 16 * 16 * (size_t)std::max({Lo.H, Lo.DQ, Lo.F}) * 4)
+              : (size_t)-1;
   Lo.n_phases = 2 + 5 * Lo.L;
   Lo.done = take((size_t)Lo.n_phases * 4);
   Lo.exit_cnt = take(4);
@@ -303,6 +307,7 @@ struct spec_ctx {
   bool per_op = true;    // the per-kernel launch sequence (else the persistent forward)
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
+  void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
   int32_t* h_step() { return (int32_t*)(HB + lo.host_step); }
   int32_t* h_result() { return (int32_t*)(HB + lo.host_result); }
   int32_t* h_kvlen() { return (int32_t*)(HB + lo.host_kvlen); }
@@ -388,9 +393,19 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
   return p;
 }
 
-// R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K.
-hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, hipStream_t st) {
+// R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K, whose
+// A above 16 rows (bf16, af set) is prepared once by k_prep rather than by
+// every workgroup.
+hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, void* af,
+                      hipStream_t st) {
   if (m.nw && p0.R <= m.rmax && p0.R <= 16) return launch_mm(p0, m.nw, m.spw, m.ct, m.nbuf, m.gp, max_grid, epi, st);
+  if (af && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
+    hipError_t e = launch_prep_a(p0, af, st);
+    if (e != hipSuccess) return e;
+    GemmParams p = p0;
+    p.Af = af;
+    return launch_gemm(p, nk, epi, fmt, st);
+  }
   return launch_gemm(p0, nk, epi, fmt, st);
 }
 
@@ -453,7 +468,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.seq_ids = seq_ids;
     gl.S = S;
     gl.n_seq = n_seq;
-    HIPCHK(c, gemm_or_mm(gl, L.mm_lm, L.nk_lm, EPI_LM, L.fmt, c->mm_grid, st));
+    HIPCHK(c, gemm_or_mm(gl, L.mm_lm, L.nk_lm, EPI_LM, L.fmt, c->mm_grid, c->af(), st));
     return SPEC_OK;
   }
   const LayerOff& lw = L.lay[(size_t)l];
@@ -477,7 +492,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.n_kv = L.nkv;
       g.hd = L.hd;
       g.rope = c->ws<float>(L.rope);
-      HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, st));
+      HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
     case SPEC_OP_ATTN: {
@@ -509,7 +524,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, st));
+      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
     case SPEC_OP_GATEUP: {
@@ -520,7 +535,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.ss_n = L.H / 16;
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
-      HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, st));
+      HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
     case SPEC_OP_DOWN: {
@@ -530,7 +545,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
       if (L.d_lds && R <= 4) HIPCHK(c, launch_mm1l(gd, 16, 19, 4, st));
-      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, st));
+      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
   }
