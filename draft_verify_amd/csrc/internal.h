@@ -100,9 +100,10 @@ struct AttnParams {
   float scale;
   int max_splits;        // grid.x: 256-key splits of the longest context
   float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
-  unsigned* cnt;         // [n_seq][n_kv][n_qt] arrival counters of the fused merge, zero between launches
+  unsigned* cnt;         // [n_seq][n_kv][tile groups] arrival counters of the fused merge, zero between launches
   float* out;            // [R][n_q*hd]
   int n_qt;              // query tiles per sequence: ceil(S * n_q / n_kv / 16)
+  int tpw;               // query tiles per workgroup (1..n_qt), taken one after another
   int fuse;              // short contexts: the last split of a tile merges it in k_attn
 };
 // The attention merges its splits in the same kernel when every context of

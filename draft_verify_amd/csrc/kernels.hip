@@ -1082,11 +1082,13 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 
 // -------------------------------------------------------------- attention
 //
-// Grid (split, kv head, sequence x query tile).  A split is 256 keys at
-// absolute positions [256*split, 256*split + 256), one 64-key chunk (four
-// 16-token blocks) per wave; a query tile is 16 query columns (span row,
-// head of the GQA group) of one sequence and kv head, so the tiles of a long
-// span run side by side.  Scores are computed transposed, S^T = K Q^T, so the
+// Grid (split, kv head, sequence x group of tpw query tiles).  A split is
+// 256 keys at absolute positions [256*split, 256*split + 256), one 64-key
+// chunk (four 16-token blocks) per wave; a query tile is 16 query columns
+// (span row, head of the GQA group) of one sequence and kv head.  With
+// tpw = 1 the tiles of a long span run side by side (few workgroups: batch
+// 1); with more, a workgroup takes its tiles one after another on the K and
+// V it loaded once (many workgroups: batched steps).  Scores are computed transposed, S^T = K Q^T, so the
 // probabilities come out of the MFMA already in the B-operand layout of
 // O^T = V^T P^T and never leave registers; V blocks are stored d-major
 // ([hd][16 tokens]) so the V^T operand is read straight from memory.  The
@@ -1111,7 +1113,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   constexpr int FS = attn_fuse_splits(HD);
   static_assert(16 * FS * 2 <= 4 * 16 * (HD + 1), "the fused merge's split table fits sO");
   const int split = blockIdx.x, kvh = blockIdx.y;
-  const int b = blockIdx.z / P.n_qt, qt = blockIdx.z - b * P.n_qt;
+  const int n_tg = (P.n_qt + P.tpw - 1) / P.tpw;  // groups of tpw query tiles
+  const int b = blockIdx.z / n_tg, tg = blockIdx.z - b * n_tg;
+  const int qt0 = tg * P.tpw, qt1 = min(P.n_qt, qt0 + P.tpw);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int DQ = P.n_q * HD;
@@ -1139,11 +1143,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   int blk[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) blk[t] = (kb0 + t) * 16 < total ? bv[t] : bz;
-  const int col = qt * 16 + c16;
-  const bool qok = col < QC;
-  const int colc = qok ? col : 0;
-  const int iq = colc / G, head = kvh * G + colc % G;
-  const int pos_q = p + iq;
+  int qt = qt0;
+  int col = qt * 16 + c16;
+  bool qok = col < QC;
+  int colc = qok ? col : 0;
+  int iq = colc / G, head = kvh * G + colc % G;
+  int pos_q = p + iq;
   const float* qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
   f32x4 qa[KST][2];
 #pragma unroll
@@ -1177,6 +1182,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[t][dt] = ok ? vf[t][dt] : (f16x4){0, 0, 0, 0};
   }
+  // The group's query tiles, one after another on the same K and V.
+  for (;;) {
   f16x8 qf[KST];
 #pragma unroll
   for (int ks = 0; ks < KST; ++ks) {
@@ -1268,13 +1275,29 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
     float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
     st_dev2(dst + 2 + d, o0, o1);
   }
+  if (++qt >= qt1) break;
+  __syncthreads();  // sO, sM, sL and sF are rewritten by the next tile
+  col = qt * 16 + c16;
+  qok = col < QC;
+  colc = qok ? col : 0;
+  iq = colc / G;
+  head = kvh * G + colc % G;
+  pos_q = p + iq;
+  qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
+#pragma unroll
+  for (int ks = 0; ks < KST; ++ks) {
+    const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
+    qa[ks][0] = *(const f32x4*)(qrow + dc);
+    qa[ks][1] = *(const f32x4*)(qrow + dc + 4);
+  }
+  }
   if (!P.fuse) return;
-  // Short contexts: the last split of this (sequence, kv head, tile) to
-  // finish merges the tile's columns, as k_attn_combine would.
+  // Short contexts: the last split of this (sequence, kv head, tile group)
+  // to finish merges the group's columns, as k_attn_combine would.
   __shared__ int sLast;
   wait_mem();
   __syncthreads();
-  unsigned* cnt = P.cnt + ((size_t)b * P.n_kv + kvh) * P.n_qt + qt;
+  unsigned* cnt = P.cnt + ((size_t)b * P.n_kv + kvh) * n_tg + tg;
   if (tid == 0) {
     const unsigned old = atomicAdd(cnt, 1u);
     sLast = old == (unsigned)(n_act - 1);
@@ -1282,7 +1305,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   __syncthreads();
   if (!sLast) return;
   if (tid == 0) *cnt = 0u;  // ready for the next launch
-  combine_tile<HD, true, FS>(P, b, kvh, qt, p, &sO[0][0][0]);
+  for (int t = qt0; t < qt1; ++t) combine_tile<HD, true, FS>(P, b, kvh, t, p, &sO[0][0][0]);
 }
 
 template <bool COH>
@@ -1568,8 +1591,9 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
   if (p.max_splits > kMaxCombineSplits || p.n_kv < 1 || p.n_q % p.n_kv) return hipErrorInvalidValue;
   const int n_qt = (p.S * (p.n_q / p.n_kv) + 15) / 16;
-  if (p.n_qt != n_qt || p.n_seq < 1 || p.n_seq * n_qt > 65535) return hipErrorInvalidValue;
-  const dim3 grid(p.max_splits, p.n_kv, p.n_seq * n_qt);
+  if (p.n_qt != n_qt || p.tpw < 1 || p.tpw > n_qt || p.n_seq < 1 || p.n_seq * n_qt > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid(p.max_splits, p.n_kv, p.n_seq * ((n_qt + p.tpw - 1) / p.tpw));
   const dim3 cgrid(n_qt, p.n_kv, p.n_seq);
   switch (hd) {
     case 128:

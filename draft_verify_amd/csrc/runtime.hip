@@ -304,6 +304,7 @@ struct spec_ctx {
   int fwd_grid = 0;      // workgroups of the persistent forward (all co-resident)
   int mm_grid = 1;       // most workgroups of a one-pass GEMM (they walk the column blocks)
   int attn_fuse = 0;     // the current step's contexts are short: attention combines in one kernel
+  int attn_tpw = 1;      // the current step's query tiles per attention workgroup
   bool per_op = true;    // the per-kernel launch sequence (else the persistent forward)
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
@@ -514,6 +515,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
       a.n_qt = (S * L.G + 15) / 16;
+      a.tpw = std::min(c->attn_tpw, a.n_qt);
       a.fuse = c->attn_fuse;
       HIPCHK(c, launch_attn(a, L.hd, st));
       return SPEC_OK;
@@ -568,7 +570,7 @@ int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
 }
 
 int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
-  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16));
+  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16) | ((c->attn_tpw > 1) << 17));
   auto it = c->graphs.find(key);
   if (it != c->graphs.end()) {
     *out = it->second;
@@ -600,6 +602,9 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
   c->attn_fuse = longest <= attn_fuse_splits(L.hd) * 256 ? 1 : 0;
+  // Enough (sequence, kv head, split) workgroups to fill the chip: each
+  // takes all its query tiles on K and V loaded once; else one tile each.
+  c->attn_tpw = (size_t)n_seq * L.nkv * ((longest + 255) / 256) >= 256 ? 16 : 1;
   StepDev* sd = (StepDev*)c->h_step();
   sd->mode = mode;
   sd->n_seq = n_seq;
