@@ -159,8 +159,11 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   auto steps = [&](int K) { return Lo.fmt == FMT_INT4 ? slice_steps_int4(K) : slice_steps(K); };
   Lo.nk_qkv = steps(Lo.H); Lo.nk_o = steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
   Lo.nk_d = steps(Lo.F);
-  // The LM head runs ~10^4 workgroups; half-depth slices keep more of them resident.
-  Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
+  // The split-K LM head serves int4 and, in bf16, more than 16 rows (the
+  // one-pass kernel takes fewer): int4 runs ~10^4 workgroups, where
+  // half-depth slices keep more of them resident; bf16 rows above 16 take
+  // full-depth slices, halving the split partials (R x vocab x 4 bytes each).
+  Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) || Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = Lo.mm_lm = MmPlan{0, 0, 0, 0, 0, 0};
