@@ -302,6 +302,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     __syncthreads();
   }
 
+  if constexpr (PREP) {
+    // The weights are in before the chunk loop, so inside it only the next
+    // chunk's A copy is outstanding and the MFMAs never wait for it.
+#pragma unroll
+    for (int j = 0; j < NF; ++j) asm volatile("" ::"v"(b[0][j]));
+  }
   for (int m0 = 0; m0 < P.R; m0 += 16) {
     // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo.
     if constexpr (PREP) {
