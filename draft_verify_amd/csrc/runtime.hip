@@ -87,6 +87,10 @@ struct MmPlan {
 #ifndef SPECV_DOWN_LDS
 #define SPECV_DOWN_LDS 1
 #endif
+// Longest context, in 256-key splits, whose attention merges in k_attn.
+#ifndef SPECV_ATTN_FUSE_SPLITS
+#define SPECV_ATTN_FUSE_SPLITS 8
+#endif
 #ifndef SPECV_MM_WG_PER_CU
 #define SPECV_MM_WG_PER_CU 1
 #endif
@@ -604,10 +608,15 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   const Layout& L = c->lo;
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
-  c->attn_fuse = longest <= attn_fuse_splits(L.hd) * 256 ? 1 : 0;
   // Enough (sequence, kv head, split) workgroups to fill the chip: each
   // takes all its query tiles on K and V loaded once; else one tile each.
-  c->attn_tpw = (size_t)n_seq * L.nkv * ((longest + 255) / 256) >= 256 ? 16 : 1;
+  const int splits = (longest + 255) / 256, n_qt = (S * L.G + 15) / 16;
+  c->attn_tpw = (size_t)n_seq * L.nkv * splits >= 256 ? 16 : 1;
+  // The last split merges its tile group itself when that is short work: few
+  // splits per column and at most two tiles; else the merge kernel spreads
+  // the columns over the chip.
+  c->attn_fuse = (splits <= std::min(SPECV_ATTN_FUSE_SPLITS, attn_fuse_splits(L.hd)) &&
+                  std::min(c->attn_tpw, n_qt) <= 2) ? 1 : 0;
   StepDev* sd = (StepDev*)c->h_step();
   sd->mode = mode;
   sd->n_seq = n_seq;
