@@ -27,6 +27,10 @@ SHAPES = {
                  eps=1e-6, rope_theta=1e6),
     "qwen3_4b": dict(n_layers=36, hidden=2560, n_q=32, n_kv=8, head_dim=128, ffn=9728,
                      vocab=151936, eps=1e-6, rope_theta=1e6),
+    # four query heads per kv head: batched spans of 8 rows fill two 16-column
+    # query tiles per (sequence, kv head) in attention
+    "tiny_g4": dict(n_layers=2, hidden=64, n_q=8, n_kv=2, head_dim=16, ffn=128, vocab=256,
+                    eps=1e-6, rope_theta=1e6),
     # the smallest decoder whose GEMM depths hold whole int4 groups of 128
     "tiny_int4": dict(n_layers=2, hidden=128, n_q=4, n_kv=2, head_dim=32, ffn=256, vocab=256,
                       eps=1e-6, rope_theta=1e6),
