@@ -71,6 +71,7 @@ struct GemmParams {
   const int32_t* seq_ids;// [n_seq]
   int S, n_q, n_kv, hd;
   const float* rope;     // [max_ctx][hd/2][2] = cos, sin
+  const int32_t* rowinfo;// [R][2]: each row's absolute position and its KV block (k_embed)
   // EPI_RESID
   float* x;              // residual [R][N]
   float* ss_out;         // [R][N/64] partial sums of squares of the new residual
@@ -116,8 +117,15 @@ struct EmbedParams {
   const uint16_t* emb;   // [V][H] bf16
   const int32_t* tokens; // [R]
   float* x;              // [R][H]
-  float* ss;             // [R][H/64]
+  float* ss;             // [R][H/16]
   int H;
+  // each row's position and KV block, for every layer's QKV epilogue:
+  // rowinfo[2r] = kv_len[seq_ids[r/S]] + r%S, rowinfo[2r+1] = its block
+  const int32_t* seq_ids;
+  const int32_t* kv_len;
+  const int32_t* bt;
+  int bt_stride, S;
+  int32_t* rowinfo;
 };
 
 // One GEMM unit of a workgroup's walk in the persistent forward: the 64-column

@@ -123,6 +123,12 @@ __global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t value, size_t co
 // every 16-column group (the format the RMSNorm prologues consume).
 __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
   const int r = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int b = r / P.S, seq = P.seq_ids[b];
+    const int pos = P.kv_len[seq] + (r - b * P.S);
+    P.rowinfo[2 * r] = pos;
+    P.rowinfo[2 * r + 1] = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)];
+  }
   const int tok = P.tokens[r];
   const int H = P.H, ng = H / 16;
   const uint16_t* e = P.emb + (size_t)tok * H;
@@ -481,26 +487,19 @@ __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
   }
 }
 
-// Position of row r of the forward and its sequence.
-__device__ __forceinline__ void row_pos(const GemmParams& P, int r, int& seq, int& pos) {
-  const int b = r / P.S, i = r - b * P.S;
-  seq = P.seq_ids[b];
-  pos = P.kv_len[seq] + i;
-}
-
 // Per column-pair epilogue arithmetic, shared by the split-K and the
 // one-pass GEMMs so that both give bit-identical results (contraction off:
 // every product and sum rounds on its own, whatever the surrounding code).
 
 // RoPE on the pair (d, d + hd/2) stored interleaved, then q (fp32) or the
 // K / V cache rows (fp16) at the row's position.
-__device__ __forceinline__ void qkv_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+// pos: the row's absolute position; blk: the KV block holding it.
+__device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, float v0, float v1, int pos,
+                                            int blk) {
 #pragma clang fp contract(off)
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
-  int seq, pos;
-  row_pos(P, r, seq, pos);
-  const int blk = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)], slot = pos & 15;
+  const int slot = pos & 15;
   if (c < DQ + DK) {
     const int local = c < DQ ? c : c - DQ;
     const int head = local / hd, j = (local % hd) >> 1;
@@ -522,6 +521,10 @@ __device__ __forceinline__ void qkv_pair(const GemmParams& P, int r, int c, floa
     vb[(size_t)d * 16 + slot] = (_Float16)v0;
     vb[(size_t)(d + 1) * 16 + slot] = (_Float16)v1;
   }
+}
+
+__device__ __forceinline__ void qkv_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+  qkv_pair_at(P, r, c, v0, v1, P.rowinfo[2 * r], P.rowinfo[2 * r + 1]);
 }
 
 // x += (v0, v1); returns the pair's sum of squares of the new residual.
@@ -717,9 +720,19 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
     }
   };
 
-  // Issue order: the small RMSNorm inputs first, then the first block's
-  // weights, then A, so that waiting for the former never waits for the
-  // weights.
+  // Issue order: the QKV rows' positions and blocks, the small RMSNorm
+  // inputs, then the first block's weights, then A, so that waiting for the
+  // former never waits for the weights.
+  constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // epilogue pairs per thread at 16 rows
+  int qpos[EPI == EPI_QKV ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int r = (tid + it * NT) / (8 * CT), rc = r < P.R ? r : 0;
+      qpos[it] = P.rowinfo[2 * rc];
+      qblk[it] = P.rowinfo[2 * rc + 1];
+    }
+  }
   float gv[NORM ? GPT : 1], sv[NORM ? SSI : 1];
   const int ss_r = tid >> 4, ss_j = tid & 15;
   if constexpr (NORM) {
@@ -738,7 +751,6 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
   }
   // LM head: a pair of each thread's (row, 16 columns) group keeps the
   // largest argmax key over the walk; one atomic per group at the end.
-  constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // pairs per thread at 16 rows
   unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
 #pragma unroll
   for (int it = 0; it < (EPI == EPI_LM ? PPT : 1); ++it) kmax[it] = 0ull;
@@ -833,7 +845,7 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
         group_sum<NW, GP, CT>(sAcc, ct, e0, v0, v1);
         if (col < P.N) {
           if constexpr (EPI == EPI_QKV) {
-            qkv_pair(P, r, col, v0, v1);
+            qkv_pair_at(P, r, col, v0, v1, qpos[it], qblk[it]);
           } else if constexpr (EPI == EPI_RESID) {
             const float t = sum8(resid_pair(P, r, col, v0, v1));
             if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
@@ -1516,6 +1528,7 @@ hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st) {
+  if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, fmt, st);
     case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, fmt, st);
@@ -1561,6 +1574,7 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
   // the RMSNorm prologue reads K/16 partial sums per row (K = hidden)
   if ((epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LM) && (!p.ss || !p.gain || p.ss_n * 16 != p.K))
     return hipErrorInvalidValue;
+  if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
   if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
@@ -1624,6 +1638,7 @@ hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
 }
 
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st) {
+  if (R < 1 || p.S < 1 || R % p.S || !p.rowinfo || !p.seq_ids || !p.kv_len || !p.bt) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_embed, dim3(R), dim3(256), 0, st, p);
   return hipGetLastError();
 }

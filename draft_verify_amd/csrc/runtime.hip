@@ -116,6 +116,7 @@ struct Layout {
   size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
   // workspace
   size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
+  size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, done, exit_cnt, err, clock, units, unit_first, workspace_bytes;
   size_t n_units;  // GEMM units of one forward over all workgroups (persistent forward)
@@ -253,6 +254,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.cnt = take((size_t)Lo.cnt_n * 4);
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
+  Lo.rowinfo = take(R * 8);
   Lo.argkey = take(R * 8);
   Lo.status = take(4);
   Lo.step = take(sizeof(StepDev) + 2 * R * 4);
@@ -455,6 +457,12 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     ep.x = c->ws<float>(L.x);
     ep.ss = c->ws<float>(L.ss);
     ep.H = L.H;
+    ep.seq_ids = seq_ids;
+    ep.kv_len = c->ws<int32_t>(L.kv_len);
+    ep.bt = c->ws<int32_t>(L.bt);
+    ep.bt_stride = L.bt_stride;
+    ep.S = S;
+    ep.rowinfo = c->ws<int32_t>(L.rowinfo);
     HIPCHK(c, launch_embed(ep, R, st));
     return SPEC_OK;
   }
@@ -500,6 +508,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.n_kv = L.nkv;
       g.hd = L.hd;
       g.rope = c->ws<float>(L.rope);
+      g.rowinfo = c->ws<int32_t>(L.rowinfo);
       HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
@@ -1190,7 +1199,9 @@ int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
   STEP(upload_step(c, MODE_NO_COMMIT, 1, S, span.data(), &sid));
   const bool per_layer = !(op == SPEC_OP_EMBED || op == SPEC_OP_LM);
   const int per_rep = per_layer ? c->lo.L : 1;
-  // one untimed pass, then the timed passes back to back
+  // the embedding (which also resolves the rows' positions for the QKV
+  // epilogue), one untimed pass, then the timed passes back to back
+  if (op != SPEC_OP_EMBED) STEP(launch_op(c, SPEC_OP_EMBED, 0, 1, S));
   for (int l = 0; l < per_rep; ++l) STEP(launch_op(c, op, l, 1, S));
   hipEvent_t e0, e1;
   HIPCHK(c, hipEventCreate(&e0));
