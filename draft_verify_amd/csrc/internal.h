@@ -91,12 +91,11 @@ struct GemmParams {
 
 struct AttnParams {
   const float* q;        // [R][n_q*hd]
+  const int32_t* rowinfo;// [R][2] (k_embed): row b*S's position is sequence b's cache length
+  const int32_t* slotbt; // [n_seq][bt_stride] (k_embed): sequence b's block table row
   const _Float16* kpool; // [n_blocks][n_kv][16][hd]
   const _Float16* vpool; // [n_blocks][n_kv][hd][16]
-  const int32_t* bt;
   int bt_stride;
-  const int32_t* kv_len;
-  const int32_t* seq_ids;
   int S, n_seq, n_q, n_kv;
   float scale;
   int max_splits;        // grid.x: 256-key splits of the longest context
@@ -126,6 +125,7 @@ struct EmbedParams {
   const int32_t* bt;
   int bt_stride, S;
   int32_t* rowinfo;
+  int32_t* slotbt;       // [n_seq][bt_stride]: the block table rows of the step's sequences, by slot
 };
 
 // One GEMM unit of a workgroup's walk in the persistent forward: the 64-column

@@ -123,11 +123,18 @@ __global__ void k_fill_u32(uint32_t* __restrict__ dst, uint32_t value, size_t co
 // every 16-column group (the format the RMSNorm prologues consume).
 __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
   const int r = blockIdx.x;
-  if (threadIdx.x == 0) {
+  {
     const int b = r / P.S, seq = P.seq_ids[b];
-    const int pos = P.kv_len[seq] + (r - b * P.S);
-    P.rowinfo[2 * r] = pos;
-    P.rowinfo[2 * r + 1] = P.bt[(size_t)seq * P.bt_stride + (pos >> 4)];
+    const int len = P.kv_len[seq], pos = len + (r - b * P.S);
+    const int32_t* row = P.bt + (size_t)seq * P.bt_stride;
+    if (threadIdx.x == 0) {
+      P.rowinfo[2 * r] = pos;
+      P.rowinfo[2 * r + 1] = row[pos >> 4];
+    }
+    if (r == b * P.S) {  // the sequence's first row copies its blocks, by slot, for attention
+      const int nb = (len + P.S + 15) >> 4;
+      for (int i = threadIdx.x; i < nb; i += blockDim.x) P.slotbt[(size_t)b * P.bt_stride + i] = row[i];
+    }
   }
   const int tok = P.tokens[r];
   const int H = P.H, ng = H / 16;
@@ -1141,8 +1148,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   // The context length and this wave's four block ids load together (ids
   // clamped to the table row; blocks past the context take the sequence's
   // block 0 and are zeroed below), then K, V and the queries.
-  const int seq = P.seq_ids[b];
-  const int32_t* btrow = P.bt + (size_t)seq * P.bt_stride;
+  const int32_t* btrow = P.slotbt + (size_t)b * P.bt_stride;
   const int kb0 = split * 16 + wave * 4;
   int bv[4];
 #pragma unroll
@@ -1150,7 +1156,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   const int bz = btrow[0];
   // every id is loaded before anything branches on the context length
   asm volatile("" ::"v"(bv[0]), "v"(bv[1]), "v"(bv[2]), "v"(bv[3]), "v"(bz));
-  const int p = P.kv_len[seq];
+  const int p = P.rowinfo[2 * b * S];
   const int total = p + S;
   const int n_act = (total + 255) >> 8;
   if (split >= n_act) return;
@@ -1429,7 +1435,7 @@ template <int HD>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
   __shared__ float sML[16 * kMaxCombineSplits * 2];
   const int b = blockIdx.z;
-  combine_tile<HD, false, kMaxCombineSplits>(P, b, blockIdx.y, blockIdx.x, P.kv_len[P.seq_ids[b]], sML);
+  combine_tile<HD, false, kMaxCombineSplits>(P, b, blockIdx.y, blockIdx.x, P.rowinfo[2 * b * P.S], sML);
 }
 
 // -------------------------------------------------------------- launchers
@@ -1638,7 +1644,8 @@ hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
 }
 
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st) {
-  if (R < 1 || p.S < 1 || R % p.S || !p.rowinfo || !p.seq_ids || !p.kv_len || !p.bt) return hipErrorInvalidValue;
+  if (R < 1 || p.S < 1 || R % p.S || !p.rowinfo || !p.slotbt || !p.seq_ids || !p.kv_len || !p.bt)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_embed, dim3(R), dim3(256), 0, st, p);
   return hipGetLastError();
 }

@@ -117,6 +117,7 @@ struct Layout {
   // workspace
   size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
   size_t rowinfo;  // per row: position and KV block, written by k_embed
+  size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, done, exit_cnt, err, clock, units, unit_first, workspace_bytes;
   size_t n_units;  // GEMM units of one forward over all workgroups (persistent forward)
@@ -255,6 +256,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
   Lo.rowinfo = take(R * 8);
+  Lo.slotbt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
   Lo.argkey = take(R * 8);
   Lo.status = take(4);
   Lo.step = take(sizeof(StepDev) + 2 * R * 4);
@@ -463,6 +465,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     ep.bt_stride = L.bt_stride;
     ep.S = S;
     ep.rowinfo = c->ws<int32_t>(L.rowinfo);
+    ep.slotbt = c->ws<int32_t>(L.slotbt);
     HIPCHK(c, launch_embed(ep, R, st));
     return SPEC_OK;
   }
@@ -517,10 +520,9 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.q = c->ws<float>(L.q);
       a.kpool = c->kpool(l);
       a.vpool = c->vpool(l);
-      a.bt = c->ws<int32_t>(L.bt);
+      a.rowinfo = c->ws<int32_t>(L.rowinfo);
+      a.slotbt = c->ws<int32_t>(L.slotbt);
       a.bt_stride = L.bt_stride;
-      a.kv_len = c->ws<int32_t>(L.kv_len);
-      a.seq_ids = seq_ids;
       a.S = S;
       a.n_seq = n_seq;
       a.n_q = L.nq;
