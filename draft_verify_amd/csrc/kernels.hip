@@ -1485,32 +1485,66 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
 // kernel's own (rstd16, then (x * rstd) * gain), so either path gives the
 // same operands.  Grid (ceil(K/512), ceil(R/16)): 16 steps of one 16-row
 // chunk per workgroup.
+constexpr int kPrepSs = 32;  // RMSNorm partial sums per lane in k_prep: hidden <= 16 * 16 * 32
+
 __global__ __launch_bounds__(256) void k_prep(GemmParams P, u32x4* af) {
   const int ch = blockIdx.y, nch = gridDim.y, ks0 = blockIdx.x * 16, KS = P.K / 32;
   const int tid = threadIdx.x;
+  const bool norm = P.ss != nullptr;
   __shared__ float sR[16];
-  if (P.ss) {
-    const int r = ch * 16 + (tid >> 4);
-    const float rs = rstd16(P.ss, P.ss_n, r, P.R, tid & 15, P.inv_dim, P.eps);
-    if ((tid & 15) == 0) sR[tid >> 4] = r < P.R ? rs : 0.0f;
+  // Every load first, from clamped addresses (zeroed after): the chunk's
+  // RMSNorm statistics (16 lanes per row, as rstd16), its rows, the gains.
+  const int sr = ch * 16 + (tid >> 4), sj = tid & 15, src = sr < P.R ? sr : 0;
+  // without the RMSNorm, the statistics and gain loads read A (valid memory, values unused)
+  const float* ssp = norm ? P.ss + (size_t)src * P.ss_n : P.A;
+  const float* gp = norm ? P.gain : P.A;
+  const int ssn = norm ? P.ss_n : 1;
+  float sv[kPrepSs];
+#pragma unroll
+  for (int i = 0; i < kPrepSs; ++i) {
+    const int q = sj + 16 * i;
+    sv[i] = ssp[q < ssn ? q : 0];
+  }
+  f32x4 a[4][2], gg[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + i * 256, l = u & 63, ks = ks0 + (u >> 6);
+    const int r = ch * 16 + (l & 15), g = l >> 4, kc = ks < KS ? ks : 0;
+    const f32x4* src_a = (const f32x4*)(P.A + (size_t)(r < P.R ? r : 0) * P.lda + kc * 32 + g * 8);
+    a[i][0] = src_a[0];
+    a[i][1] = src_a[1];
+    const f32x4* src_g = (const f32x4*)(gp + (norm ? kc * 32 + g * 8 : 0));
+    gg[i][0] = src_g[0];
+    gg[i][1] = src_g[1];
+  }
+  asm volatile("" ::: "memory");  // every load above is issued before any is used
+  if (norm) {
+    float acc = 0.0f;  // rstd16's order: partials j, j + 16, ... (zeros past the row), then the xor tree
+#pragma unroll
+    for (int i = 0; i < kPrepSs; ++i) {
+      const unsigned keep = (sr < P.R && sj + 16 * i < P.ss_n) ? ~0u : 0u;  // a mask, not a branch
+      acc += __uint_as_float(__float_as_uint(sv[i]) & keep);
+    }
+    const float rs = rstd_finish(acc, P.inv_dim, P.eps);
+    if (sj == 0) sR[tid >> 4] = sr < P.R ? rs : 0.0f;
     __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + i * 256, l = u & 63, ks = ks0 + (u >> 6);
-    const int row = l & 15, g = l >> 4, r = ch * 16 + row;
+    const int row = l & 15, r = ch * 16 + row;
     if (ks < KS) {
       float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
       if (r < P.R) {
-        const f32x4* src = (const f32x4*)(P.A + (size_t)r * P.lda + ks * 32 + g * 8);
-        const f32x4 a0 = src[0], a1 = src[1];
-        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+        v[0] = a[i][0].x; v[1] = a[i][0].y; v[2] = a[i][0].z; v[3] = a[i][0].w;
+        v[4] = a[i][1].x; v[5] = a[i][1].y; v[6] = a[i][1].z; v[7] = a[i][1].w;
       }
-      if (P.ss) {
+      if (norm) {
         const float rs = sR[row];
+        const float gv[8] = {gg[i][0].x, gg[i][0].y, gg[i][0].z, gg[i][0].w,
+                             gg[i][1].x, gg[i][1].y, gg[i][1].z, gg[i][1].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * P.gain[ks * 32 + g * 8 + e];
+        for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * gv[e];
       }
       bf16x8 hi, lo;
 #pragma unroll
@@ -1527,7 +1561,8 @@ __global__ __launch_bounds__(256) void k_prep(GemmParams P, u32x4* af) {
 }
 
 hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
-  if (!af || !p.A || p.R < 1 || p.K % 32 || p.lda % 4 || (p.ss && !p.gain)) return hipErrorInvalidValue;
+  if (!af || !p.A || p.R < 1 || p.K % 32 || p.lda % 4 || (p.ss && (!p.gain || p.ss_n > 16 * kPrepSs)))
+    return hipErrorInvalidValue;
   const dim3 grid((p.K / 32 + 15) / 16, (p.R + 15) / 16);
   hipLaunchKernelGGL(k_prep, grid, dim3(256), 0, st, p, (u32x4*)af);
   return hipGetLastError();
