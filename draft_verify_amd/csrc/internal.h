@@ -77,6 +77,7 @@ struct GemmParams {
   float* ss_out;         // [R][N/64] partial sums of squares of the new residual
   // EPI_SWIGLU
   float* h;              // [R][N/2]
+  void* af_out;          // or null: h also as the next GEMM's prepared A (k_prep's layout)
   // EPI_LM
   unsigned long long* argkey; // per-row packed (value, index) maxima, zero between forwards
   unsigned* lm_cnt;           // arrival counter over all column blocks
@@ -102,6 +103,7 @@ struct AttnParams {
   float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
   unsigned* cnt;         // [n_seq][n_kv][tile groups] arrival counters of the fused merge, zero between launches
   float* out;            // [R][n_q*hd]
+  void* af_out;          // or null: out also as the O GEMM's prepared A (k_prep's layout)
   int n_qt;              // query tiles per sequence: ceil(S * n_q / n_kv / 16)
   int tpw;               // query tiles per workgroup (1..n_qt), taken one after another
   int fuse;              // short contexts: the last split of a tile merges it in k_attn

@@ -555,9 +555,37 @@ __device__ __forceinline__ float sum8(float t) {
   return t;
 }
 
+// Prepared A (k_prep's layout, bf16 hi then lo, nch = ceil(R/16) chunks)
+// written by a producer: element (row r, input k) sits at bf16 index
+// (((k/32 * nch + r/16) * 2 + hl) * 64 + r%16 + 16 * (k%32/8)) * 8 + k%8;
+// the split is k_prep's, so the consumer sees the same operands.
+__device__ __forceinline__ size_t prep_index(int nch, int r, int k, int hl) {
+  return ((((size_t)(k >> 5) * nch + (r >> 4)) * 2 + hl) * 64 + (r & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+__device__ __forceinline__ void prep_store1(void* af, int nch, int r, int k, float v) {
+#pragma clang fp contract(off)
+  const __bf16 h = (__bf16)v, l = (__bf16)(v - (float)h);
+  uint16_t* a = (uint16_t*)af;
+  a[prep_index(nch, r, k, 0)] = __builtin_bit_cast(uint16_t, h);
+  a[prep_index(nch, r, k, 1)] = __builtin_bit_cast(uint16_t, l);
+}
+// k even: the pair (k, k + 1) shares one 4-byte word of each half
+__device__ __forceinline__ void prep_store2(void* af, int nch, int r, int k, float v0, float v1) {
+#pragma clang fp contract(off)
+  const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+  const __bf16 l0 = (__bf16)(v0 - (float)h0), l1 = (__bf16)(v1 - (float)h1);
+  uint16_t* a = (uint16_t*)af;
+  *(uint32_t*)(a + prep_index(nch, r, k, 0)) =
+      (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  *(uint32_t*)(a + prep_index(nch, r, k, 1)) =
+      (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
 __device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, float g, float u) {
 #pragma clang fp contract(off)
-  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = (g / (1.0f + expf(-g))) * u;
+  const float v = (g / (1.0f + expf(-g))) * u;
+  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
+  if (P.af_out) prep_store1(P.af_out, (P.R + 15) >> 4, r, c >> 1, v);
 }
 
 template <int CT, int SB, int U>
@@ -1424,8 +1452,10 @@ __device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p,
 #pragma unroll
   for (int i = 0; i < PP; ++i) {
     const int dp = j + 16 * i;
-    if (cok && dp < HD / 2)
+    if (cok && dp < HD / 2) {
       *(float2*)(P.out + (size_t)(b * P.S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0[i], o1[i]);
+      if (P.af_out) prep_store2(P.af_out, (P.n_seq * P.S + 15) >> 4, b * P.S + iq, head * HD + 2 * dp, o0[i], o1[i]);
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }

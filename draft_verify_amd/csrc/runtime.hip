@@ -116,6 +116,7 @@ struct Layout {
   size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
   // workspace
   size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
+  size_t af2; // the same for O and down, written by their producers
   size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
@@ -269,6 +270,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.af = (Lo.fmt == FMT_BF16 && R > 16 && !(d.flags & SPEC_FLAG_PERSISTENT))
               ? take((R + 15) / 16 * 16 * (size_t)std::max({Lo.H, Lo.DQ, Lo.F}) * 4)
               : (size_t)-1;
+  Lo.af2 = Lo.af != (size_t)-1 ? take((R + 15) / 16 * 16 * (size_t)std::max(Lo.DQ, Lo.F) * 4) : (size_t)-1;
   Lo.n_phases = 2 + 5 * Lo.L;
   Lo.done = take((size_t)Lo.n_phases * 4);
   Lo.exit_cnt = take(4);
@@ -320,6 +322,12 @@ struct spec_ctx {
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
+  // the prepared A that a producer writes for the GEMM of depth nk after it
+  // (O after attention, down after gate/up), or null when that GEMM will
+  // not read prepared A
+  void* af_next(int nk, int R) {
+    return lo.af2 != (size_t)-1 && R > 16 && gemm_prep_supported(nk, lo.fmt) ? (void*)(WS + lo.af2) : nullptr;
+  }
   int32_t* h_step() { return (int32_t*)(HB + lo.host_step); }
   int32_t* h_result() { return (int32_t*)(HB + lo.host_result); }
   int32_t* h_kvlen() { return (int32_t*)(HB + lo.host_kvlen); }
@@ -408,9 +416,16 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
 // R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K, whose
 // A above 16 rows (bf16, af set) is prepared once by k_prep rather than by
 // every workgroup.
+// ready: A already in the prepared layout, written by its producer (the
+// SwiGLU epilogue, the attention merge) for this GEMM, or null.
 hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, void* af,
-                      hipStream_t st) {
+                      hipStream_t st, const void* ready = nullptr) {
   if (m.nw && p0.R <= m.rmax && p0.R <= 16) return launch_mm(p0, m.nw, m.spw, m.ct, m.nbuf, m.gp, max_grid, epi, st);
+  if (ready && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
+    GemmParams p = p0;
+    p.Af = ready;
+    return launch_gemm(p, nk, epi, fmt, st);
+  }
   if (af && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
     hipError_t e = launch_prep_a(p0, af, st);
     if (e != hipSuccess) return e;
@@ -532,6 +547,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.part = c->ws<float>(L.apart);
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
+      a.af_out = c->af_next(L.nk_o, R);
       a.n_qt = (S * L.G + 15) / 16;
       a.tpw = std::min(c->attn_tpw, a.n_qt);
       a.fuse = c->attn_fuse;
@@ -544,7 +560,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
-      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st));
+      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_o, R)));
       return SPEC_OK;
     }
     case SPEC_OP_GATEUP: {
@@ -555,6 +571,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.ss_n = L.H / 16;
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
+      gu.af_out = c->af_next(L.nk_d, R);
       HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
@@ -565,7 +582,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
       if (L.d_lds && R <= 4) HIPCHK(c, launch_mm1l(gd, 16, 19, 4, st));
-      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st));
+      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_d, R)));
       return SPEC_OK;
     }
   }
