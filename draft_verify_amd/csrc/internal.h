@@ -203,6 +203,12 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp);
 // The residual one-pass GEMM for at most rl rows with A staged in LDS
 // (kernels.hip: k_mm1l); compiled for nw = 16, spw = 19, rl = 4.
 hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st);
+// The int4 one-pass GEMM for at most four rows (kernels.hip: k_mmq): waves
+// own the K parts of the int4 split-K kernel with nk-step slices, so the two
+// agree bit for bit; compiled for K / (32 nk) waves of nk / 4 groups in
+// {10 x 4, 16 x 4, 1 x 1}.
+bool mmq_supported(int K, int nk);
+hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStream_t st);
 hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
                      hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);

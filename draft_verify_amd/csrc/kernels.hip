@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[c][i] += t[c][i] * gs[c][gi];
+          for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(t[c][i], gs[c][gi], acc[c][i]);  // one rounding
       }
     } else {
 #pragma unroll
@@ -1133,6 +1133,181 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   }
 }
 
+// The int4 one-pass GEMM for at most four rows (K = hidden or n_q * hd):
+// every workgroup stages the whole normalised activation once in LDS as fp16
+// hi + lo in the MFMA A-operand order ([step][hi, lo][lane group][row]),
+// then walks 16-column tiles (blockIdx.x, + gridDim.x, ...).  Wave w owns
+// the K part of groups [w*GPW, (w+1)*GPW) of 128 inputs: per group the four
+// steps' MFMAs on the exact integer weights, then one fused multiply-add by
+// the column's group scale -- the arithmetic of the int4 split-K kernel with
+// 4*GPW-step slices -- and the parts are added in wave order, so both agree
+// bit for bit.  The next tile's fragments are issued as soon as the MFMAs
+// have read the current ones.
+template <int EPI, int NW, int GPW>
+__global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
+  constexpr int NT = NW * 64, KG = NW * GPW, KS = KG * 4, RL = 4;
+  constexpr bool NORM = EPI != EPI_RESID;
+  constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
+  constexpr int PPT = (RL * 8 + NT - 1) / NT;                      // epilogue pairs per thread
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g0 = wave * GPW, row = lane & 15, kg = lane >> 4;
+  const int nblk = P.N >> 4, G = (int)gridDim.x;
+
+  __shared__ u32x4 sA[KS * 2 * 4 * RL];
+  __shared__ f32x4 sAcc[NW * 64];
+  __shared__ float sR[RL];
+
+  // Issue order: the QKV rows' positions, A and the gains (needed first),
+  // then the first tile's weights and scales, then the RMSNorm row
+  // statistics (one wave).
+  int qpos[EPI == EPI_QKV ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int r = (tid + it * NT) >> 3, rc = r < P.R ? r : 0;
+      qpos[it] = P.rowinfo[2 * rc];
+      qblk[it] = P.rowinfo[2 * rc + 1];
+    }
+  }
+  f32x4 pa[UPT][2], pg[NORM ? UPT : 1][2];
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+    const bool ok = u < UNITS && r < P.R;
+    const int jc = u < UNITS ? j : 0;
+    const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
+    pa[i][0] = src[0];
+    pa[i][1] = src[1];
+    if constexpr (NORM) {
+      const f32x4* gsrc = (const f32x4*)(P.gain + (size_t)jc * 32 + g * 8);
+      pg[i][0] = gsrc[0];
+      pg[i][1] = gsrc[1];
+    }
+  }
+  // one weight buffer: the next tile is issued once the MFMAs have read it
+  u32x4 b0[GPW];
+  uint32_t s0[GPW];  // raw bf16 scale bits, converted at use (no wait on arrival)
+  auto fetch = [&](u32x4 (&bw)[GPW], uint32_t (&sw)[GPW], int tile) {
+    const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KG + g0) * 64 + lane;
+    const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * KG + g0;
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      bw[gi] = __builtin_nontemporal_load(wp + gi * 64);
+      sw[gi] = sp[gi];
+    }
+  };
+  int blk = blockIdx.x;
+  if (blk < nblk) fetch(b0, s0, blk);
+  if constexpr (NORM) {  // rstd of the rows (rstd16; one wave), after every load is out
+    if (tid < 16 * RL) {
+      const float rs = rstd16(P.ss, P.ss_n, tid >> 4, P.R, tid & 15, P.inv_dim, P.eps);
+      if ((tid & 15) == 0) sR[tid >> 4] = (tid >> 4) < P.R ? rs : 0.0f;
+    }
+    __syncthreads();
+  }
+  // A into LDS as fp16 hi + lo (the int4 split-K kernel's conversion)
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = tid + i * NT;
+    if (u < UNITS) {
+      const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+      float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+      if (r >= P.R) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+      }
+      if constexpr (NORM) {
+        const float sc = r < P.R ? sR[r] : 0.0f;
+        const float gv[8] = {pg[i][0].x, pg[i][0].y, pg[i][0].z, pg[i][0].w, pg[i][1].x, pg[i][1].y, pg[i][1].z, pg[i][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
+      }
+      f16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 h = (_Float16)v[e];
+        hi[e] = h;
+        lo[e] = (_Float16)(v[e] - (float)h);
+      }
+      sA[((j * 2) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
+      sA[((j * 2 + 1) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, lo);
+    }
+  }
+  __syncthreads();
+  const bool rok = row < P.R && row < RL;
+  const int rc = row < RL ? row : RL - 1;
+  unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
+#pragma unroll
+  for (int it = 0; it < (EPI == EPI_LM ? PPT : 1); ++it) kmax[it] = 0ull;
+
+  // One tile on the weights in bw, then (bw free) the tile refill into it,
+  // then the reduction and the epilogue.
+  auto pass = [&](u32x4 (&bw)[GPW], uint32_t (&sw)[GPW], int cur, int refill) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int j = (g0 + gi) * 4 + d;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 h = sA[((j * 2) * 4 + kg) * RL + rc], l = sA[((j * 2 + 1) * 4 + kg) * RL + rc];
+        const f16x8 ah = __builtin_bit_cast(f16x8, rok ? h : z), al = __builtin_bit_cast(f16x8, rok ? l : z);
+        const f16x8 bq = dequant8(bw[gi][d]);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
+      }
+      const float sc = bf16_bits_to_f32((uint16_t)sw[gi]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], sc, acc[i]);
+    }
+    if (refill < nblk) fetch(bw, sw, refill);
+    sAcc[wave * 64 + lane] = acc;
+    __syncthreads();
+    const int npairs = P.R * 8;
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + it * NT;
+      if (p < npairs) {
+        const int r = p >> 3, pp = p & 7;
+        const int col = cur * 16 + 2 * pp;
+        const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+        float v0, v1;
+        group_sum<NW, 1, 1>(sAcc, 0, e0, v0, v1);
+        if constexpr (EPI == EPI_QKV) {
+          qkv_pair_at(P, r, col, v0, v1, qpos[it], qblk[it]);
+        } else if constexpr (EPI == EPI_RESID) {
+          const float s8 = sum8(resid_pair(P, r, col, v0, v1));
+          if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = s8;
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          swiglu_pair(P, r, col, v0, v1);
+        } else {
+          const unsigned long long k0 = lm_value(P, r, col, v0), k1 = lm_value(P, r, col + 1, v1);
+          const unsigned long long k = k0 > k1 ? k0 : k1;
+          kmax[it] = k > kmax[it] ? k : kmax[it];
+        }
+      }
+    }
+    __syncthreads();  // sAcc is rewritten by the next tile
+  };
+  for (; blk < nblk; blk += G) pass(b0, s0, blk, blk + G);
+  if constexpr (EPI == EPI_LM) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      unsigned long long k = kmax[it];
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(k, o);
+        k = t > k ? t : k;
+      }
+      const int p = tid + it * NT;
+      if (p < P.R * 8 && (p & 7) == 0) atomicMax(&P.argkey[p >> 3], k);
+    }
+    lm_finish(P, G, (float*)sAcc);
+  }
+}
+
 // -------------------------------------------------------------- attention
 //
 // Grid (split, kv head, sequence x group of tpw query tiles).  A split is
@@ -1627,6 +1802,43 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
   }
 #undef SPECV_MM_HAS
   return false;
+}
+
+// int4 one-pass (k_mmq) configurations: (waves, groups per wave).
+#define SPECV_MMQ(X) X(10, 4) X(16, 4) X(1, 1)
+
+bool mmq_supported(int K, int nk) {
+  if (nk % 4 || K % (32 * nk)) return false;
+  const int gpw = nk / 4, nw = K / (32 * nk);
+#define SPECV_MMQ_HAS(a, b) if (nw == a && gpw == b) return true;
+  SPECV_MMQ(SPECV_MMQ_HAS)
+#undef SPECV_MMQ_HAS
+  return false;
+}
+
+hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStream_t st) {
+  if (p.R < 1 || p.R > 4 || !p.scales || p.N % 16 || max_grid < 1 || !mmq_supported(p.K, nk))
+    return hipErrorInvalidValue;
+  if (epi != EPI_RESID && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
+    return hipErrorInvalidValue;
+  const int gpw = nk / 4, nw = p.K / (32 * nk), nblk = p.N / 16;
+  const dim3 grid(nblk < max_grid ? nblk : max_grid);
+#define SPECV_MMQ_GO(a, b)                                                                          \
+  if (nw == a && gpw == b) {                                                                        \
+    switch (epi) {                                                                                  \
+      case EPI_QKV: hipLaunchKernelGGL((k_mmq<EPI_QKV, a, b>), grid, dim3(a * 64), 0, st, p); break;   \
+      case EPI_RESID: hipLaunchKernelGGL((k_mmq<EPI_RESID, a, b>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_mmq<EPI_SWIGLU, a, b>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_LM: hipLaunchKernelGGL((k_mmq<EPI_LM, a, b>), grid, dim3(a * 64), 0, st, p); break;     \
+      default: return hipErrorInvalidValue;                                                         \
+    }                                                                                               \
+    return hipGetLastError();                                                                       \
+  }
+  SPECV_MMQ(SPECV_MMQ_GO)
+#undef SPECV_MMQ_GO
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st) {

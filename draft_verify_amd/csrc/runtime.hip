@@ -172,6 +172,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   // full-depth slices, halving the split partials (R x vocab x 4 bytes each).
   Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) || Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
+  // int4 rows up to four take the one-pass kernel at the QKV depth; more rows
+  // keep the same K parts
+  if (Lo.fmt == FMT_INT4 && !(d.flags & SPEC_FLAG_PERSISTENT) && mmq_supported(Lo.H, Lo.nk_qkv)) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = Lo.mm_lm = MmPlan{0, 0, 0, 0, 0, 0};
   Lo.d_lds = false;
@@ -421,6 +424,8 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
 hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, void* af,
                       hipStream_t st, const void* ready = nullptr) {
   if (m.nw && p0.R <= m.rmax && p0.R <= 16) return launch_mm(p0, m.nw, m.spw, m.ct, m.nbuf, m.gp, max_grid, epi, st);
+  // int4, up to four rows: the one-pass kernel with the split-K kernel's K parts
+  if (fmt == FMT_INT4 && p0.R <= 4 && mmq_supported(p0.K, nk)) return launch_mmq(p0, nk, epi, max_grid, st);
   if (ready && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
     GemmParams p = p0;
     p.Af = ready;
