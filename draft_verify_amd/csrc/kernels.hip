@@ -581,11 +581,12 @@ __device__ __forceinline__ void prep_store2(void* af, int nch, int r, int k, flo
       (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
 }
 
-__device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, float g, float u) {
+__device__ __forceinline__ float swiglu_val(float g, float u) {
 #pragma clang fp contract(off)
-  const float v = (g / (1.0f + expf(-g))) * u;
-  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
-  if (P.af_out) prep_store1(P.af_out, (P.R + 15) >> 4, r, c >> 1, v);
+  return (g / (1.0f + expf(-g))) * u;
+}
+__device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, float g, float u) {
+  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = swiglu_val(g, u);
 }
 
 template <int CT, int SB, int U>
@@ -602,9 +603,15 @@ __device__ void epi_resid(const GemmParams& P, int nb) {
   });
 }
 
+// The split-K kernel serves the rows above 16, whose down GEMM reads the
+// prepared layout: h is also written there (af_out), only on this path.
 template <int CT, int SB, int U>
 __device__ void epi_swiglu(const GemmParams& P, int nb) {
-  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float g, float u) { swiglu_pair(P, r, c, g, u); });
+  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float g, float u) {
+    const float v = swiglu_val(g, u);
+    P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
+    if (P.af_out) prep_store1(P.af_out, (P.R + 15) >> 4, r, c >> 1, v);
+  });
 }
 
 // One logit (row r, column c): optional copy-out, NaN flag, argmax key.
