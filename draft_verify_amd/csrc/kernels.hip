@@ -441,7 +441,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   __syncthreads();
   if (!sLast) return;
   if (tid == 0) P.cnt[nb] = 0u;  // ready for the next launch
-  gemm_epilogue<EPI, CT>(P, nb, (float*)sA);
+  // int4 down runs 50 slices: 16 per gather round (four rounds, not seven)
+  gemm_epilogue<EPI, CT, FMT == FMT_INT4 ? 16 : 8>(P, nb, (float*)sA);
 }
 
 // The epilogue's column pairs of block nb (64*CT columns): pair idx = (row
