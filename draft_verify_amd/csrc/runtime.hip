@@ -64,8 +64,9 @@ struct MmPlan {
 };
 
 // The down projection at K = 9728 for up to four rows: one tile per
-// workgroup, 16 K parts of 19 steps, A staged in LDS (launch_mm1l); the
-// split-K kernel takes the same parts (nk = 19) for more rows.
+// workgroup, 16 K parts of 19 steps, A staged in LDS (launch_mm1l); k_mm1
+// with the same parts for up to SPECV_DOWN_MM1_ROWS rows, and the split-K
+// kernel with the same parts (nk = 19) for more.
 
 // Preference lists, first match on K = nw * spw * 32 wins.
 #ifndef SPECV_MM_QKV
@@ -86,6 +87,12 @@ struct MmPlan {
 
 #ifndef SPECV_DOWN_LDS
 #define SPECV_DOWN_LDS 1
+#endif
+// Rows above four and up to this many take the down projection's one-pass
+// kernel with A read from global memory (the same K parts, summed in the same
+// order as the LDS-staged kernel); more rows take split-K.
+#ifndef SPECV_DOWN_MM1_ROWS
+#define SPECV_DOWN_MM1_ROWS 8
 #endif
 // Longest context, in 256-key splits, whose attention merges in k_attn.
 #ifndef SPECV_ATTN_FUSE_SPLITS
@@ -587,6 +594,8 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
       if (L.d_lds && R <= 4) HIPCHK(c, launch_mm1l(gd, 16, 19, 4, st));
+      else if (L.d_lds && R <= SPECV_DOWN_MM1_ROWS)
+        HIPCHK(c, launch_mm(gd, 16, 19, 4, 0, 1, c->mm_grid, EPI_RESID, st));
       else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_d, R)));
       return SPEC_OK;
     }
