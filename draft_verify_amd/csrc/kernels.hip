@@ -1144,25 +1144,27 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 // The int4 one-pass GEMM for at most four rows (K = hidden or n_q * hd):
 // every workgroup stages the whole normalised activation once in LDS as fp16
 // hi + lo in the MFMA A-operand order ([step][hi, lo][lane group][row]),
-// then walks 16-column tiles (blockIdx.x, + gridDim.x, ...).  Wave w owns
+// then walks blocks of CT 16-column tiles (blockIdx.x, + gridDim.x, ...),
+// reading each A fragment from LDS once for the CT tiles.  Wave w owns
 // the K part of groups [w*GPW, (w+1)*GPW) of 128 inputs: per group the four
 // steps' MFMAs on the exact integer weights, then one fused multiply-add by
 // the column's group scale -- the arithmetic of the int4 split-K kernel with
 // 4*GPW-step slices -- and the parts are added in wave order, so both agree
-// bit for bit.  The next tile's fragments are issued as soon as the MFMAs
-// have read the current ones.
-template <int EPI, int NW, int GPW>
+// bit for bit (each tile's sums keep their order whatever CT is).  The next
+// block's fragments are issued as soon as the MFMAs have read the current
+// ones.
+template <int EPI, int NW, int GPW, int CT>
 __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   constexpr int NT = NW * 64, KG = NW * GPW, KS = KG * 4, RL = 4;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
-  constexpr int PPT = (RL * 8 + NT - 1) / NT;                      // epilogue pairs per thread
+  constexpr int PPT = (RL * 8 * CT + NT - 1) / NT;                 // epilogue pairs per thread
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g0 = wave * GPW, row = lane & 15, kg = lane >> 4;
-  const int nblk = P.N >> 4, G = (int)gridDim.x;
+  const int ntile = P.N >> 4, nblk = (ntile + CT - 1) / CT, G = (int)gridDim.x;
 
   __shared__ u32x4 sA[KS * 2 * 4 * RL];
-  __shared__ f32x4 sAcc[NW * 64];
+  __shared__ f32x4 sAcc[NW * 64 * CT];
   __shared__ float sR[RL];
 
   // Issue order: the QKV rows' positions, A and the gains (needed first),
@@ -1172,7 +1174,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
-      const int r = (tid + it * NT) >> 3, rc = r < P.R ? r : 0;
+      const int r = (tid + it * NT) / (8 * CT), rc = r < P.R ? r : 0;
       qpos[it] = P.rowinfo[2 * rc];
       qblk[it] = P.rowinfo[2 * rc + 1];
     }
@@ -1193,16 +1195,22 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
       pg[i][1] = gsrc[1];
     }
   }
-  // one weight buffer: the next tile is issued once the MFMAs have read it
-  u32x4 b0[GPW];
-  uint32_t s0[GPW];  // raw bf16 scale bits, converted at use (no wait on arrival)
-  auto fetch = [&](u32x4 (&bw)[GPW], uint32_t (&sw)[GPW], int tile) {
-    const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KG + g0) * 64 + lane;
-    const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * KG + g0;
+  // one weight buffer (CT tiles): the next block is issued once the MFMAs
+  // have read it; a block's tiles past the last (odd tile counts) reload the
+  // last tile, and their columns are not stored
+  u32x4 b0[CT][GPW];
+  uint32_t s0[CT][GPW];  // raw bf16 scale bits, converted at use (no wait on arrival)
+  auto fetch = [&](u32x4 (&bw)[CT][GPW], uint32_t (&sw)[CT][GPW], int blk_) {
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      bw[gi] = __builtin_nontemporal_load(wp + gi * 64);
-      sw[gi] = sp[gi];
+    for (int c = 0; c < CT; ++c) {
+      const int tile = min(blk_ * CT + c, ntile - 1);
+      const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KG + g0) * 64 + lane;
+      const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * KG + g0;
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        bw[c][gi] = __builtin_nontemporal_load(wp + gi * 64);
+        sw[c][gi] = sp[gi];
+      }
     }
   };
   int blk = blockIdx.x;
@@ -1249,40 +1257,53 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 #pragma unroll
   for (int it = 0; it < (EPI == EPI_LM ? PPT : 1); ++it) kmax[it] = 0ull;
 
-  // One tile on the weights in bw, then (bw free) the tile refill into it,
-  // then the reduction and the epilogue.
-  auto pass = [&](u32x4 (&bw)[GPW], uint32_t (&sw)[GPW], int cur, int refill) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // One block of CT tiles on the weights in bw, then (bw free) the block
+  // refill into it, then the reduction and the epilogue.
+  auto pass = [&](u32x4 (&bw)[CT][GPW], uint32_t (&sw)[CT][GPW], int cur, int refill) {
+    f32x4 acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
-      f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 t[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) t[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int j = (g0 + gi) * 4 + d;
         const u32x4 z = {0u, 0u, 0u, 0u};
         const u32x4 h = sA[((j * 2) * 4 + kg) * RL + rc], l = sA[((j * 2 + 1) * 4 + kg) * RL + rc];
         const f16x8 ah = __builtin_bit_cast(f16x8, rok ? h : z), al = __builtin_bit_cast(f16x8, rok ? l : z);
-        const f16x8 bq = dequant8(bw[gi][d]);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
-      }
-      const float sc = bf16_bits_to_f32((uint16_t)sw[gi]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(t[i], sc, acc[i]);
+        for (int c = 0; c < CT; ++c) {
+          const f16x8 bq = dequant8(bw[c][gi][d]);
+          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t[c], 0, 0, 0);
+          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t[c], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const float sc = bf16_bits_to_f32((uint16_t)sw[c][gi]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(t[c][i], sc, acc[c][i]);
+      }
     }
     if (refill < nblk) fetch(bw, sw, refill);
-    sAcc[wave * 64 + lane] = acc;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) sAcc[(wave * CT + c) * 64 + lane] = acc[c];
     __syncthreads();
-    const int npairs = P.R * 8;
+    // p = (row * CT + tile) * 8 + pair: an aligned group of 8 pairs is 16
+    // columns of one row
+    const int npairs = P.R * 8 * CT;
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
       const int p = tid + it * NT;
-      if (p < npairs) {
-        const int r = p >> 3, pp = p & 7;
-        const int col = cur * 16 + 2 * pp;
+      const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+      const int col = (cur * CT + ct) * 16 + 2 * pp;
+      if (p < npairs && col < P.N) {
         const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
         float v0, v1;
-        group_sum<NW, 1, 1>(sAcc, 0, e0, v0, v1);
+        group_sum<NW, 1, CT>(sAcc, ct, e0, v0, v1);
         if constexpr (EPI == EPI_QKV) {
           qkv_pair_at(P, r, col, v0, v1, qpos[it], qblk[it]);
         } else if constexpr (EPI == EPI_RESID) {
@@ -1310,7 +1331,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
         k = t > k ? t : k;
       }
       const int p = tid + it * NT;
-      if (p < P.R * 8 && (p & 7) == 0) atomicMax(&P.argkey[p >> 3], k);
+      if (p < P.R * 8 * CT && (p & 7) == 0) atomicMax(&P.argkey[p / (8 * CT)], k);
     }
     lm_finish(P, G, (float*)sAcc);
   }
@@ -1812,13 +1833,22 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
   return false;
 }
 
-// int4 one-pass (k_mmq) configurations: (waves, groups per wave).
-#define SPECV_MMQ(X) X(10, 4) X(16, 4) X(1, 1)
+// int4 one-pass (k_mmq) configurations: (waves, groups per wave, 16-column
+// tiles per pass).  Two tiles per pass share each read of the A slice from
+// LDS where the LDS holds the second partial tile (K = 5120: 80 KiB of A +
+// 20 KiB of partials; K = 8192 would need 160 KiB); they are taken when
+// every workgroup walks at least four such blocks (gate/up 46.9 -> 42.6 us,
+// LM head 129 -> 110 us at the 32B shape), since with fewer the blocks split
+// unevenly over the workgroups (QKV's 640 tiles: 16.4 -> 18.0 us).
+#ifndef SPECV_MMQ_CT
+#define SPECV_MMQ_CT 2
+#endif
+#define SPECV_MMQ(X) X(10, 4, 1) X(10, 4, SPECV_MMQ_CT) X(16, 4, 1) X(1, 1, 1)
 
 bool mmq_supported(int K, int nk) {
   if (nk % 4 || K % (32 * nk)) return false;
   const int gpw = nk / 4, nw = K / (32 * nk);
-#define SPECV_MMQ_HAS(a, b) if (nw == a && gpw == b) return true;
+#define SPECV_MMQ_HAS(a, b, c) if (nw == a && gpw == b) return true;
   SPECV_MMQ(SPECV_MMQ_HAS)
 #undef SPECV_MMQ_HAS
   return false;
@@ -1831,15 +1861,17 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
   if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
-  const int gpw = nk / 4, nw = p.K / (32 * nk), nblk = p.N / 16;
-  const dim3 grid(nblk < max_grid ? nblk : max_grid);
-#define SPECV_MMQ_GO(a, b)                                                                          \
-  if (nw == a && gpw == b) {                                                                        \
+  const int gpw = nk / 4, nw = p.K / (32 * nk), ntile = p.N / 16;
+  const int ct = (nw == 10 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
+#define SPECV_MMQ_GO(a, b, c)                                                                       \
+  if (nw == a && gpw == b && ct == (c)) {                                                           \
+    const int nblk = (ntile + (c) - 1) / (c);                                                       \
+    const dim3 grid(nblk < max_grid ? nblk : max_grid);                                             \
     switch (epi) {                                                                                  \
-      case EPI_QKV: hipLaunchKernelGGL((k_mmq<EPI_QKV, a, b>), grid, dim3(a * 64), 0, st, p); break;   \
-      case EPI_RESID: hipLaunchKernelGGL((k_mmq<EPI_RESID, a, b>), grid, dim3(a * 64), 0, st, p); break; \
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_mmq<EPI_SWIGLU, a, b>), grid, dim3(a * 64), 0, st, p); break; \
-      case EPI_LM: hipLaunchKernelGGL((k_mmq<EPI_LM, a, b>), grid, dim3(a * 64), 0, st, p); break;     \
+      case EPI_QKV: hipLaunchKernelGGL((k_mmq<EPI_QKV, a, b, c>), grid, dim3(a * 64), 0, st, p); break;   \
+      case EPI_RESID: hipLaunchKernelGGL((k_mmq<EPI_RESID, a, b, c>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_mmq<EPI_SWIGLU, a, b, c>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_LM: hipLaunchKernelGGL((k_mmq<EPI_LM, a, b, c>), grid, dim3(a * 64), 0, st, p); break;     \
       default: return hipErrorInvalidValue;                                                         \
     }                                                                                               \
     return hipGetLastError();                                                                       \
