@@ -1251,7 +1251,9 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
     }
   }
   __syncthreads();
-  const bool rok = row < P.R && row < RL;
+  // Lanes of rows past RL read row RL - 1 (rows R..RL-1 were staged as
+  // zeros): an MFMA output row depends on its own A row alone, and rows past
+  // R are never stored, so no per-lane select is needed on the A fragments.
   const int rc = row < RL ? row : RL - 1;
   unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
 #pragma unroll
@@ -1271,9 +1273,8 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int j = (g0 + gi) * 4 + d;
-        const u32x4 z = {0u, 0u, 0u, 0u};
         const u32x4 h = sA[((j * 2) * 4 + kg) * RL + rc], l = sA[((j * 2 + 1) * 4 + kg) * RL + rc];
-        const f16x8 ah = __builtin_bit_cast(f16x8, rok ? h : z), al = __builtin_bit_cast(f16x8, rok ? l : z);
+        const f16x8 ah = __builtin_bit_cast(f16x8, h), al = __builtin_bit_cast(f16x8, l);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
           const f16x8 bq = dequant8(bw[c][gi][d]);
