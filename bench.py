@@ -271,6 +271,45 @@ def counters_workload():
     print("counters workload done", flush=True)
 
 
+def counters_int4_workload():
+    """Short workload for SQ counter passes over the int4 GEMMs: the 32B-class
+    int4 model (64 layers, hidden 5120), a 64-token prefill, then four S=1
+    verify forwards."""
+    import numpy as np
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["dense_32b"]
+    sess = specv.Session(shape, specv.synth_weights(shape, seed=0, device="cuda", fmt="int4"),
+                         max_ctx=512, fmt="int4")
+    specv.spec_prefill(sess.ctx, synth.uniform_prompt(5, shape["vocab"], 64))
+    rng = np.random.default_rng(6)
+    specv.spec_time_verify(sess.ctx, rng.integers(0, shape["vocab"], (4, 1)).astype(np.int32))
+    sess.close()
+    print("int4 counters workload done", flush=True)
+
+
+def summarize_sq(csv_path, out_md, command):
+    """Per-kernel medians (over dispatches) of the SQ counters of one
+    rocprofv3 --pmc run, for the GEMM and attention kernels."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(csv_path):
+        vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for d in vals.values() for c in d})
+    lines = ["# SQ counters per dispatch (median over dispatches)", "", f"Command: `{command}`", "",
+             "| kernel | dispatches | " + " | ".join(names) + " | VALU / wave |",
+             "|---|---|" + "---|" * len(names) + "---|"]
+    for k, d in sorted(vals.items()):
+        if "specv::k_" not in k or "k_embed" in k:
+            continue
+        med = {c: sorted(v)[len(v) // 2] for c, v in d.items()}
+        per_wave = med.get("SQ_INSTS_VALU", 0) / max(med.get("SQ_WAVES", 1), 1)
+        lines.append(f"| `{k[:60]}` | {len(next(iter(d.values())))} | "
+                     + " | ".join(f"{med.get(c, 0):.0f}" for c in names) + f" | {per_wave:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _csv_rows(path):
     import csv
     with open(path) as f:
@@ -359,6 +398,8 @@ def main():
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-int4", action="store_true")
     ap.add_argument("--counters", action="store_true", help="short workload for rocprofv3 --pmc passes")
+    ap.add_argument("--counters-int4", action="store_true", help="short int4 workload for SQ counter passes")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
     args = ap.parse_args()
@@ -368,6 +409,10 @@ def main():
         return summarize_trace(*args.summarize_trace)
     if args.counters:
         return counters_workload()
+    if args.counters_int4:
+        return counters_int4_workload()
+    if args.summarize_sq:
+        return summarize_sq(*args.summarize_sq)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout "
               f"is a design note, not a measured path.", file=sys.stderr)
