@@ -205,18 +205,37 @@ __device__ __forceinline__ float rstd16(const float* ss, int ss_n, int r, int R,
 }
 
 // Offset nibbles -> exact fp16 q: (1024 + u) - 1032 in packed fp16.
+// Eight int4 weights of a fragment dword as fp16 q = u - 8 (u the stored
+// nibble; the low halves hold nibbles 0-3, the high halves 4-7).  SHIFTLESS:
+// the sequence of dequant8_ao below with the AND-OR left to the compiler
+// (two instructions with literal operands, no register for the constants);
+// otherwise one shift, AND-OR and add per nibble pair, for the split-K QKV
+// kernel, which the other sequence takes past 256 registers.  Both give the
+// same values.
+template <bool SHIFTLESS>
 __device__ __forceinline__ f16x8 dequant8(uint32_t x) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  f16x8 r;
+  if constexpr (SHIFTLESS) {
+    const uint32_t x8 = x >> 8;
+    const uint32_t m0 = (x & 0x000F000Fu) | 0x64006400u, m1 = (x & 0x00F000F0u) | 0x64006400u;
+    const uint32_t m2 = (x8 & 0x000F000Fu) | 0x64006400u, m3 = (x8 & 0x00F000F0u) | 0x64006400u;
+    const h2 sc = {(_Float16)0.0625f, (_Float16)0.0625f}, off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const h2 v0 = __builtin_bit_cast(h2, m0) - off, v2 = __builtin_bit_cast(h2, m2) - off;
+    const h2 v1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, m1), sc, off16);
+    const h2 v3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, m3), sc, off16);
+    return (f16x8){v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+  } else {
+    f16x8 r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t o = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-    const h2 v = __builtin_bit_cast(h2, o) - off;
-    r[2 * j] = v[0];
-    r[2 * j + 1] = v[1];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t o = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+      const h2 v = __builtin_bit_cast(h2, o) - off;
+      r[2 * j] = v[0];
+      r[2 * j + 1] = v[1];
+    }
+    return r;
   }
-  return r;
 }
 
 // (x & mask) | 0x64006400 in one VOP3 instruction (which takes no literal:
@@ -237,7 +256,7 @@ __device__ __forceinline__ f16x8 dequant8_ao(uint32_t x) {
   // (j, j + 4) of x at bits 4j, 16 + 4j take one AND-OR each, with one shift
   // by 8 for j = 2, 3, and one packed add or fma per pair.  The exponent
   // pattern takes a vector register, which the split-K kernel, at the
-  // register limit of two waves per SIMD, cannot spare: it keeps dequant8.
+  // register limit of two waves per SIMD, cannot spare: it takes dequant8.
   const uint32_t x8 = x >> 8;
   const uint32_t m0 = and_or(x, 0x000F000Fu), m1 = and_or(x, 0x00F000F0u);
   const uint32_t m2 = and_or(x8, 0x000F000Fu), m3 = and_or(x8, 0x00F000F0u);
@@ -425,7 +444,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
             // of the chunk loop into 4x the registers.
             uint32_t w = b[c][gi][d];
             asm volatile("" : "+v"(w));
-            const f16x8 bq = dequant8(w);
+            const f16x8 bq = dequant8<EPI != EPI_QKV>(w);
             t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t[c], 0, 0, 0);
             t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t[c], 0, 0, 0);
           }
