@@ -130,61 +130,6 @@ struct EmbedParams {
   int32_t* slotbt;       // [n_seq][bt_stride]: the block table rows of the step's sequences, by slot
 };
 
-// One GEMM unit of a workgroup's walk in the persistent forward: the 64-column
-// block nb of GEMM phase g (4l + {QKV, O, gate/up, down}, 4L = LM head) and
-// the K slice sl of nk 32-input steps.  woff is the byte offset, in the
-// weight arena, of the unit's first fragment for streamer wave 0; wave w
-// adds w * tile_stride.  Built on the host once per context.
-struct FwdUnit {  // 32-bit fields only: scalar loads read whole dwords
-  uint64_t woff;
-  uint32_t tile_stride;
-  int32_t g, nk, nb, sl, pad;
-};
-static_assert(sizeof(FwdUnit) == 32, "unit table entries are 32 bytes");
-constexpr int kFwdMaxGrid = 1024;  // workgroups the unit table is sized for
-constexpr int kFwdMaxWalk = 640;   // units one workgroup walks (its LDS copy)
-
-// Everything one persistent forward launch needs (forward.hip).
-struct FwdParams {
-  // shape
-  int L, H, nq, nkv, hd, F, V, DQ, DK, Nqkv, Ngu;
-  int R, S, n_seq;       // rows of this forward, rows per sequence, sequences
-  int nk_h, nk_o, nk_d;  // 32-input steps per K slice for K = H, n_q*hd, F
-  float eps, inv_dim, scale;
-  int max_splits, bt_stride;
-  // weights: one arena, layers at a fixed stride
-  const uint8_t* W;
-  size_t lay_stride, off_wqkv, off_wo, off_wgu, off_wd, off_gattn, off_gffn;
-  const uint16_t* emb;
-  const void* wlm;
-  const float* g_final;
-  // KV pool: per layer K blocks then V blocks
-  uint8_t* KV;
-  size_t kv_layer_bytes, kv_half_bytes;
-  // activations and scratch (workspace)
-  float *x, *ss, *q, *o, *h, *part, *apart, *logits;
-  const float* rope;
-  unsigned *cnt, *attn_cnt, *lm_cnt, *done, *exit_cnt;
-  int n_phases;
-  unsigned long long* argkey;
-  int32_t *status, *err;
-  unsigned long long* clock;  // per-phase start stamps of workgroup 0, or null
-  // unit table: workgroup wg's units of GEMM phase g are
-  // units[unit_first[wg * (4L + 2) + g] .. unit_first[wg * (4L + 2) + g + 1])
-  const FwdUnit* units;
-  const int32_t* unit_first;
-  // step
-  const StepDev* step;
-  const int32_t *tokens, *seq_ids;
-  int32_t* kv_len;
-  const int32_t* bt;
-  int32_t* result;
-};
-
-bool forward_supported(int nk_h, int nk_o, int nk_d, int hd);
-int forward_occupancy(int nk_h, int nk_o, int nk_d, int hd);
-hipError_t launch_forward_kernel(const FwdParams& p, int grid, hipStream_t st);
-
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
 // Prepare A for the split-K GEMM (kernels.hip: k_prep): the RMSNorm (when

@@ -684,12 +684,17 @@ __device__ void lm_finish(const GemmParams& P, int nblk, float* sbuf) {
   __syncthreads();
   if (!sFinal) return;
   int* arg = (int*)sbuf;
+  __shared__ int sNan;
   for (int r = threadIdx.x; r < P.R; r += blockDim.x) {
     const unsigned long long k = atomicExch(&P.argkey[r], 0ull);
     arg[r] = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
   }
+  // every workgroup's NaN flag is in (they arrived after their stores landed)
+  if (threadIdx.x == 0) sNan = __hip_atomic_load(P.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1;
   __syncthreads();
-  const int mode = *P.mode, S = P.S;
+  // A NaN row leaves every cache length where it was: the forward failed, and
+  // the host keeps its mirror of the lengths unchanged too.
+  const int mode = sNan ? (int)MODE_NO_COMMIT : *P.mode, S = P.S;
   for (int b = threadIdx.x; b < P.n_seq; b += blockDim.x) {
     const int row0 = b * S;
     int m;

@@ -127,9 +127,7 @@ struct Layout {
   size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
-      logits, done, exit_cnt, err, clock, units, unit_first, workspace_bytes;
-  size_t n_units;  // GEMM units of one forward over all workgroups (persistent forward)
-  int n_phases;
+      logits, workspace_bytes;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
 };
@@ -148,8 +146,6 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (d.weight_format != SPEC_WFMT_BF16 && d.weight_format != SPEC_WFMT_INT4G128)
     return fail("weight_format must be SPEC_WFMT_BF16 or SPEC_WFMT_INT4G128");
   Lo.fmt = d.weight_format == SPEC_WFMT_INT4G128 ? FMT_INT4 : FMT_BF16;
-  if (Lo.fmt == FMT_INT4 && (d.flags & SPEC_FLAG_PERSISTENT))
-    return fail("the persistent forward is compiled for bf16 weights only");
   if (Lo.fmt == FMT_INT4 && (d.hidden % 128 || d.ffn % 128 || (d.n_q_heads * d.head_dim) % 128))
     return fail("int4 group-128 weights need hidden, ffn and n_q_heads*head_dim multiples of 128");
   if (!(d.head_dim == 16 || d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128))
@@ -177,15 +173,15 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   // one-pass kernel takes fewer): int4 runs ~10^4 workgroups, where
   // half-depth slices keep more of them resident; bf16 rows above 16 take
   // full-depth slices, halving the split partials (R x vocab x 4 bytes each).
-  Lo.nk_lm = (d.flags & SPEC_FLAG_PERSISTENT) || Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
+  Lo.nk_lm = Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   // int4 rows up to four take the one-pass kernel at the QKV depth; more rows
   // keep the same K parts
-  if (Lo.fmt == FMT_INT4 && !(d.flags & SPEC_FLAG_PERSISTENT) && mmq_supported(Lo.H, Lo.nk_qkv)) Lo.nk_lm = Lo.nk_qkv;
+  if (Lo.fmt == FMT_INT4 && mmq_supported(Lo.H, Lo.nk_qkv)) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = Lo.mm_lm = MmPlan{0, 0, 0, 0, 0, 0};
   Lo.d_lds = false;
-  if (Lo.fmt == FMT_BF16 && !(d.flags & SPEC_FLAG_PERSISTENT)) {
+  if (Lo.fmt == FMT_BF16) {
     // one-pass GEMMs for R <= 16; the split-K kernel (R > 16) then takes the
     // same K parts (nk = spw), so both give identical results
     Lo.mm_qkv = pick_mm(EPI_QKV, Lo.H, {SPECV_MM_QKV});
@@ -206,23 +202,8 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     if (Lo.mm_lm.nw && Lo.mm_lm.rmax < 16) Lo.nk_lm = Lo.mm_lm.spw;
   }
   if (Lo.F % 64) return fail("ffn must be a multiple of 64");
-  if ((d.flags & SPEC_FLAG_PERSISTENT) && !forward_supported(Lo.nk_qkv, Lo.nk_o, Lo.nk_d, Lo.hd))
-    return fail("no persistent forward is compiled for this shape");
-  if ((d.flags & SPEC_FLAG_PERSISTENT) && d.max_rows > 16)
-    return fail("the persistent forward takes at most 16 rows per forward");
-  // the persistent forward's attention split-combine keeps the split maxima
-  // and sums of one (sequence, kv head) in 4 x 16 x (hd+1) floats of LDS; the
-  // per-kernel combine holds up to 256 split weights per query column
-  if (d.flags & SPEC_FLAG_PERSISTENT) {
-    if ((size_t)2 * Lo.max_splits * SPEC_MAX_SPAN * Lo.G > (size_t)4 * 16 * (Lo.hd + 1))
-      return fail("max_ctx too long for this head geometry");
-  } else if (Lo.max_splits > 256) {
-    return fail("max_ctx must be at most 65536");
-  }
-  // the split-K partial sums of a column pair are reduced from registers
-  if (d.flags & SPEC_FLAG_PERSISTENT)
-    for (int K : {Lo.H, Lo.DQ, Lo.F})
-      if (K / (slice_steps(K) * 32) > 32) return fail("a GEMM depth needs more than 32 K slices");
+  // the split merge holds up to 256 split weights per query column
+  if (Lo.max_splits > 256) return fail("max_ctx must be at most 65536");
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -277,26 +258,10 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.rope = take((size_t)Lo.max_ctx * (Lo.hd / 2) * 2 * 4);
   Lo.apart = take((size_t)Lo.nkv * Lo.max_splits * R * Lo.G * (Lo.hd + 2) * 4);
   Lo.logits = (d.flags & SPEC_FLAG_KEEP_LOGITS) ? take(R * Lo.V * 4) : (size_t)-1;
-  Lo.af = (Lo.fmt == FMT_BF16 && R > 16 && !(d.flags & SPEC_FLAG_PERSISTENT))
+  Lo.af = (Lo.fmt == FMT_BF16 && R > 16)
               ? take((R + 15) / 16 * 16 * (size_t)std::max({Lo.H, Lo.DQ, Lo.F}) * 4)
               : (size_t)-1;
   Lo.af2 = Lo.af != (size_t)-1 ? take((R + 15) / 16 * 16 * (size_t)std::max(Lo.DQ, Lo.F) * 4) : (size_t)-1;
-  Lo.n_phases = 2 + 5 * Lo.L;
-  Lo.done = take((size_t)Lo.n_phases * 4);
-  Lo.exit_cnt = take(4);
-  Lo.err = take(4);
-  Lo.clock = take((size_t)(Lo.n_phases + 2) * 8);
-  Lo.n_units = 0;
-  Lo.units = Lo.unit_first = (size_t)-1;
-  if (d.flags & SPEC_FLAG_PERSISTENT) {
-    // every (64-column block, K slice) pair of every GEMM is one unit
-    auto units_of = [&](int N, int K, int nk) { return (size_t)(N / 64) * (size_t)(K / (32 * nk)); };
-    Lo.n_units = (size_t)Lo.L * (units_of(Lo.Nqkv, Lo.H, Lo.nk_qkv) + units_of(Lo.H, Lo.DQ, Lo.nk_o) +
-                                 units_of(Lo.Ngu, Lo.H, Lo.nk_gu) + units_of(Lo.H, Lo.F, Lo.nk_d)) +
-                 units_of(Lo.V, Lo.H, Lo.nk_lm);
-    Lo.units = take(Lo.n_units * sizeof(FwdUnit));
-    Lo.unit_first = take((size_t)kFwdMaxGrid * (4 * Lo.L + 2) * 4);
-  }
   Lo.workspace_bytes = off;
 
   off = 0;
@@ -324,11 +289,10 @@ struct spec_ctx {
   spec_stats stats;
   std::string err;
   int last_rows = 0;
-  int fwd_grid = 0;      // workgroups of the persistent forward (all co-resident)
   int mm_grid = 1;       // most workgroups of a one-pass GEMM (they walk the column blocks)
   int attn_fuse = 0;     // the current step's contexts are short: attention combines in one kernel
   int attn_tpw = 1;      // the current step's query tiles per attention workgroup
-  bool per_op = true;    // the per-kernel launch sequence (else the persistent forward)
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;  // verify forward timing (spec_get_stats)
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
@@ -673,104 +637,7 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   return SPEC_OK;
 }
 
-// The persistent forward's unit table for a grid of G workgroups.  Workgroup
-// wg keeps K slice wg % ns of a GEMM and walks its 64-column blocks
-// wg / ns + k * (G / ns), k = 0, 1, ... (workgroups past (G / ns) * ns idle).
-int build_unit_table(spec_ctx* c, int G) {
-  const Layout& L = c->lo;
-  if (G < 1 || G > kFwdMaxGrid) return set_err(c, SPEC_EINVAL, "persistent grid out of range");
-  const int NP = 4 * L.L + 2;
-  std::vector<FwdUnit> units;
-  units.reserve(L.n_units);
-  std::vector<int32_t> first((size_t)kFwdMaxGrid * NP, 0);
-  struct Gm { size_t w; int N, K, nk; };
-  auto gemm_of = [&](int g) -> Gm {
-    if (g == 4 * L.L) return {L.wlm, L.V, L.H, L.nk_lm};
-    const LayerOff& lw = L.lay[(size_t)(g / 4)];
-    switch (g & 3) {
-      case 0: return {lw.wqkv, L.Nqkv, L.H, L.nk_qkv};
-      case 1: return {lw.wo, L.H, L.DQ, L.nk_o};
-      case 2: return {lw.wgu, L.Ngu, L.H, L.nk_gu};
-      default: return {lw.wd, L.H, L.F, L.nk_d};
-    }
-  };
-  for (int wg = 0; wg < G; ++wg) {
-    for (int g = 0; g <= 4 * L.L; ++g) {
-      first[(size_t)wg * NP + g] = (int32_t)units.size();
-      const Gm m = gemm_of(g);
-      const int ns = m.K / (32 * m.nk), Gs = G / ns, NB = m.N / 64;
-      if (Gs < 1) return set_err(c, SPEC_EINVAL, "persistent grid smaller than a GEMM's K slices");
-      if (wg >= Gs * ns) continue;
-      const int sl = wg % ns;
-      for (int nb = wg / ns; nb < NB; nb += Gs) {
-        FwdUnit u;
-        memset(&u, 0, sizeof(u));
-        const size_t tile0 = (size_t)nb * 4;
-        u.woff = m.w + (tile0 * (size_t)(m.K / 32) + (size_t)sl * m.nk) * 1024;
-        u.tile_stride = (uint32_t)((size_t)(m.K / 32) * 1024);
-        u.g = g;
-        u.nk = m.nk;
-        u.nb = nb;
-        u.sl = sl;
-        units.push_back(u);
-      }
-    }
-    first[(size_t)wg * NP + 4 * L.L + 1] = (int32_t)units.size();
-    if (units.size() - (size_t)first[(size_t)wg * NP] > (size_t)kFwdMaxWalk)
-      return set_err(c, SPEC_EINVAL, "a workgroup's walk exceeds the persistent forward's LDS unit table");
-  }
-  if (units.size() > L.n_units) return set_err(c, SPEC_EINVAL, "unit table overflow");
-  HIPCHK(c, hipMemcpyAsync(c->WS + L.units, units.data(), units.size() * sizeof(FwdUnit), hipMemcpyHostToDevice, c->st));
-  HIPCHK(c, hipMemcpyAsync(c->WS + L.unit_first, first.data(), first.size() * 4, hipMemcpyHostToDevice, c->st));
-  HIPCHK(c, hipStreamSynchronize(c->st));
-  return SPEC_OK;
-}
-
-FwdParams fwd_params(spec_ctx* c, int n_seq, int S, bool with_clock) {
-  const Layout& L = c->lo;
-  FwdParams p;
-  memset(&p, 0, sizeof(p));
-  p.L = L.L; p.H = L.H; p.nq = L.nq; p.nkv = L.nkv; p.hd = L.hd; p.F = L.F; p.V = L.V;
-  p.DQ = L.DQ; p.DK = L.DK; p.Nqkv = L.Nqkv; p.Ngu = L.Ngu;
-  p.R = n_seq * S; p.S = S; p.n_seq = n_seq;
-  p.nk_h = L.nk_qkv; p.nk_o = L.nk_o; p.nk_d = L.nk_d;
-  p.eps = c->d.rms_eps; p.inv_dim = 1.0f / (float)L.H; p.scale = (float)(1.0 / sqrt((double)L.hd));
-  p.max_splits = L.max_splits; p.bt_stride = L.bt_stride;
-  p.W = c->W;
-  p.lay_stride = L.L > 1 ? L.lay[1].wqkv - L.lay[0].wqkv : 0;
-  p.off_wqkv = L.lay[0].wqkv; p.off_wo = L.lay[0].wo; p.off_wgu = L.lay[0].wgu; p.off_wd = L.lay[0].wd;
-  p.off_gattn = L.lay[0].g_attn; p.off_gffn = L.lay[0].g_ffn;
-  p.emb = (const uint16_t*)(c->W + L.emb);
-  p.wlm = c->W + L.wlm;
-  p.g_final = (const float*)(c->W + L.g_final);
-  p.KV = c->KV; p.kv_layer_bytes = L.kv_layer_bytes; p.kv_half_bytes = L.kv_half_bytes;
-  p.x = c->ws<float>(L.x); p.ss = c->ws<float>(L.ss); p.q = c->ws<float>(L.q); p.o = c->ws<float>(L.o);
-  p.h = c->ws<float>(L.h); p.part = c->ws<float>(L.part); p.apart = c->ws<float>(L.apart);
-  p.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
-  p.rope = c->ws<float>(L.rope);
-  p.cnt = c->ws<unsigned>(L.cnt); p.attn_cnt = c->ws<unsigned>(L.attn_cnt); p.lm_cnt = c->ws<unsigned>(L.lm_cnt);
-  p.done = c->ws<unsigned>(L.done); p.exit_cnt = c->ws<unsigned>(L.exit_cnt); p.n_phases = L.n_phases;
-  p.argkey = c->ws<unsigned long long>(L.argkey);
-  p.status = c->ws<int32_t>(L.status); p.err = c->ws<int32_t>(L.err);
-  p.clock = with_clock ? c->ws<unsigned long long>(L.clock) : nullptr;
-  p.units = c->ws<FwdUnit>(L.units);
-  p.unit_first = c->ws<int32_t>(L.unit_first);
-  const StepDev* sd = c->ws<StepDev>(L.step);
-  p.step = sd;
-  p.tokens = (const int32_t*)(sd + 1);
-  p.seq_ids = p.tokens + L.max_rows;
-  p.kv_len = c->ws<int32_t>(L.kv_len);
-  p.bt = c->ws<int32_t>(L.bt);
-  p.result = c->ws<int32_t>(L.result);
-  return p;
-}
-
-int launch_forward(spec_ctx* c, int n_seq, int S, bool with_clock = false) {
-  if (!c->per_op) {
-    const FwdParams p = fwd_params(c, n_seq, S, with_clock);
-    HIPCHK(c, launch_forward_kernel(p, c->fwd_grid, c->st));
-    return SPEC_OK;
-  }
+int launch_forward(spec_ctx* c, int n_seq, int S) {
   if (c->d.flags & SPEC_FLAG_NO_GRAPH) return enqueue_forward(c, n_seq, S, nullptr);
   hipGraphExec_t ge;
   STEP(get_graph(c, n_seq, S, &ge));
@@ -778,26 +645,24 @@ int launch_forward(spec_ctx* c, int n_seq, int S, bool with_clock = false) {
   return SPEC_OK;
 }
 
-// One forward and its result copy; synchronous.
+// One forward and its result copy; synchronous.  Verify forwards are timed
+// with the context's two events (forward launch to accept done) into the
+// per-span totals of spec_get_stats.
 int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
   STEP(upload_step(c, mode, n_seq, S, tokens, seq_ids));
+  const bool timed = mode == MODE_VERIFY && c->ev0 && c->ev1;
+  if (timed) HIPCHK(c, hipEventRecord(c->ev0, c->st));
   STEP(launch_forward(c, n_seq, S));
+  if (timed) HIPCHK(c, hipEventRecord(c->ev1, c->st));
   HIPCHK(c, hipMemcpyAsync(c->h_result(), c->ws<int32_t>(c->lo.result), (size_t)(1 + n_seq * (S + 1)) * 4,
                            hipMemcpyDeviceToHost, c->st));
   HIPCHK(c, hipStreamSynchronize(c->st));
+  if (timed) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, c->ev0, c->ev1) == hipSuccess) c->stats.forward_ms_by_span[S] += ms;
+  }
   c->stats.forwards++;
   c->last_rows = n_seq * S;
-  if (c->h_result()[0] & 2) {
-    // a timed-out launch leaves counters mid-count: clear every counter,
-    // key and flag before the context is used again
-    const Layout& L = c->lo;
-    const size_t spans[][2] = {{L.cnt, (size_t)L.cnt_n * 4}, {L.attn_cnt, (size_t)L.max_rows * L.nq * 4},
-                               {L.lm_cnt, 4}, {L.argkey, (size_t)L.max_rows * 8}, {L.status, 4},
-                               {L.done, (size_t)L.n_phases * 4}, {L.exit_cnt, 4}, {L.err, 4}};
-    for (const auto& sp : spans) HIPCHK(c, launch_fill_u32(c->WS + sp[0], 0u, sp[1] / 4, c->st));
-    HIPCHK(c, hipStreamSynchronize(c->st));
-    return set_err(c, SPEC_EHIP, "forward watchdog: a phase wait timed out (counters cleared)");
-  }
   if (c->h_result()[0] & 1) return set_err(c, SPEC_ENAN, "a logit row held NaN");
   return SPEC_OK;
 }
@@ -903,7 +768,6 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
     delete c;
     return SPEC_EHIP;
   }
-  c->per_op = (desc->flags & SPEC_FLAG_PERSISTENT) == 0;
   {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -914,21 +778,11 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
     }
     c->mm_grid = cus * SPECV_MM_WG_PER_CU;  // one resident workgroup per CU walks the blocks
   }
-  if (!c->per_op) {
-    int dev = 0, cus = 0;
-    const int occ = forward_occupancy(L.nk_qkv, L.nk_o, L.nk_d, L.hd);
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || occ <= 0 || cus <= 0) {
-      g_create_error = "cannot size the persistent forward grid";
-      delete c;
-      return SPEC_EHIP;
-    }
-    c->fwd_grid = std::min(cus, kFwdMaxGrid);  // one 512-thread workgroup per CU
-    if (build_unit_table(c, c->fwd_grid) != SPEC_OK) {
-      g_create_error = c->err;
-      delete c;
-      return SPEC_EINVAL;
-    }
+  if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
+    g_create_error = "cannot create the forward timing events";
+    if (c->ev0) (void)hipEventDestroy(c->ev0);
+    delete c;
+    return SPEC_EHIP;
   }
   *out = c;
   return SPEC_OK;
@@ -937,6 +791,8 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
 int spec_destroy(spec_ctx* c) {
   if (!c) return SPEC_EINVAL;
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (c->ev0) (void)hipEventDestroy(c->ev0);
+  if (c->ev1) (void)hipEventDestroy(c->ev1);
   delete c;
   return SPEC_OK;
 }
@@ -1023,10 +879,19 @@ int spec_prefill_seq(spec_ctx* c, int seq, const int32_t* tokens, int n, int32_t
   for (int off = 0; off < n; off += chunk) {
     const int S = std::min(chunk, n - off);
     bool dirty = false;
-    STEP(ensure_blocks(c, seq, off + S, &dirty));
-    if (dirty) STEP(upload_bt_row(c, seq));
+    int rc = ensure_blocks(c, seq, off + S, &dirty);
+    if (rc == SPEC_OK && dirty) rc = upload_bt_row(c, seq);
     const int32_t sid = seq;
-    STEP(run_forward(c, MODE_COMMIT_ALL, 1, S, tokens + off, &sid));
+    if (rc == SPEC_OK) rc = run_forward(c, MODE_COMMIT_ALL, 1, S, tokens + off, &sid);
+    if (rc != SPEC_OK) {
+      // a failed chunk leaves the sequence empty (not half prefilled) on
+      // both sides
+      c->len[(size_t)seq] = 0;
+      trim_blocks(c, seq, 0);
+      (void)upload_kv_len(c, seq);
+      (void)hipStreamSynchronize(c->st);
+      return rc;
+    }
     c->len[(size_t)seq] += S;
     g = c->h_result()[1 + 1 + (S - 1)];
   }
@@ -1067,7 +932,19 @@ int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int3
     }
     if (dirty) STEP(upload_bt_row(c, seq));
   }
-  STEP(run_forward(c, MODE_VERIFY, n_seq, S, spans, seq_ids));
+  const int frc = run_forward(c, MODE_VERIFY, n_seq, S, spans, seq_ids);
+  if (frc != SPEC_OK) {
+    // The accept stage does not advance a cache on a NaN row; after any
+    // failure the device lengths are set back to the host's (unchanged)
+    // mirror and the blocks this call took are returned, so host and device
+    // agree on every sequence's length and blocks.
+    for (int b = 0; b < n_seq; ++b) {
+      trim_blocks(c, seq_ids[b], c->len[(size_t)seq_ids[b]]);
+      (void)upload_kv_len(c, seq_ids[b]);
+    }
+    (void)hipStreamSynchronize(c->st);
+    return frc;
+  }
   const int32_t* res = c->h_result() + 1;
   for (int b = 0; b < n_seq; ++b) {
     const int m = res[b * (S + 1)];
@@ -1253,59 +1130,6 @@ int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
   if (rc != SPEC_OK) return rc;
   if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("timing: ") + hipGetErrorString(e));
   *us_out = ms * 1000.0f / (float)(reps * per_rep);
-  return SPEC_OK;
-}
-
-int spec_profile_phases(spec_ctx* c, int S, int iters, const int32_t* spans, float* us_out, int32_t* count_out) {
-  if (!c || !spans || !us_out || !count_out || iters <= 0)
-    return c ? set_err(c, SPEC_EINVAL, "bad profiling arguments") : SPEC_EINVAL;
-  if (c->per_op) return set_err(c, SPEC_ESTATE, "phase profiling needs the persistent forward");
-  if (S < 1 || S > SPEC_MAX_SPAN || S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "S must be in [1, 16]");
-  STEP(check_ready(c));
-  STEP(check_tokens(c, spans, S * iters));
-  if (!c->live[0]) return set_err(c, SPEC_ESTATE, "profiling before prefill");
-  if (c->len[0] + S > c->lo.max_ctx) return set_err(c, SPEC_ECAPACITY, "cache length + span exceeds max_ctx");
-  bool dirty = false;
-  STEP(ensure_blocks(c, 0, c->len[0] + S, &dirty));
-  if (dirty) STEP(upload_bt_row(c, 0));
-  const Layout& L = c->lo;
-  const int np = L.n_phases;
-  std::vector<unsigned long long> clk((size_t)np + 2);
-  double tot[SPEC_OP_COUNT] = {0};
-  int cnt[SPEC_OP_COUNT] = {0};
-  const int32_t sid = 0;
-  for (int it = 0; it < iters; ++it) {
-    STEP(upload_step(c, MODE_NO_COMMIT, 1, S, spans + (size_t)it * S, &sid));
-    STEP(launch_forward(c, 1, S, true));
-    HIPCHK(c, hipMemcpyAsync(clk.data(), c->WS + L.clock, clk.size() * 8, hipMemcpyDeviceToHost, c->st));
-    HIPCHK(c, hipStreamSynchronize(c->st));
-    // clock[ph] = when workgroup 0 finished waiting on phase ph, i.e. the start
-    // of the phase after it; 100 MHz constant clock.
-    auto us = [&](unsigned long long a, unsigned long long b) { return (double)(b - a) / 100.0; };
-    for (int l = 0; l < L.L; ++l) {
-      const unsigned long long q0 = clk[(size_t)(5 * l)];
-      const int ops[5] = {SPEC_OP_QKV, SPEC_OP_ATTN, SPEC_OP_O, SPEC_OP_GATEUP, SPEC_OP_DOWN};
-      unsigned long long prev = q0;
-      for (int k = 0; k < 5; ++k) {
-        const unsigned long long nx = clk[(size_t)(5 * l + 1 + k)];
-        tot[ops[k]] += us(prev, nx);
-        if (it == 0) cnt[ops[k]]++;
-        prev = nx;
-      }
-    }
-    tot[SPEC_OP_EMBED] += us(clk[(size_t)np], clk[0]);
-    tot[SPEC_OP_LM] += us(clk[(size_t)(5 * L.L)], clk[(size_t)np + 1]);
-    if (it == 0) {
-      cnt[SPEC_OP_EMBED]++;
-      cnt[SPEC_OP_LM]++;
-    }
-  }
-  trim_blocks(c, 0, c->len[0]);
-  c->last_rows = S;
-  for (int op = 0; op < SPEC_OP_COUNT; ++op) {
-    count_out[op] = cnt[op];
-    us_out[op] = cnt[op] ? (float)(tot[op] / ((double)cnt[op] * iters)) : 0.0f;
-  }
   return SPEC_OK;
 }
 

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "specv.h")
 
 SPEC_OK, SPEC_EINVAL, SPEC_ECAPACITY, SPEC_ESTATE, SPEC_EHIP, SPEC_ENAN = 0, -1, -2, -3, -4, -5
 SPEC_WFMT_BF16, SPEC_WFMT_INT4G128 = 0, 1
-SPEC_FLAG_KEEP_LOGITS, SPEC_FLAG_NO_GRAPH, SPEC_FLAG_PERSISTENT = 1, 2, 4
+SPEC_FLAG_KEEP_LOGITS, SPEC_FLAG_NO_GRAPH = 1, 2
 SPEC_MAX_SPAN, SPEC_MAX_ROWS, SPEC_BLOCK_TOKENS = 16, 128, 16
 (SPEC_MAT_Q, SPEC_MAT_K, SPEC_MAT_V, SPEC_MAT_O, SPEC_MAT_GATE, SPEC_MAT_UP, SPEC_MAT_DOWN,
  SPEC_MAT_EMB, SPEC_MAT_LM) = range(9)
@@ -60,7 +60,7 @@ class spec_device_buffers(C.Structure):
 class spec_stats(C.Structure):
     _fields_ = [("forwards", C.c_int64), ("verify_calls", C.c_int64), ("drafted", C.c_int64),
                 ("accepted", C.c_int64), ("forwards_by_span", C.c_int64 * (SPEC_MAX_SPAN + 1)),
-                ("graphs", C.c_int64)]
+                ("graphs", C.c_int64), ("forward_ms_by_span", C.c_double * (SPEC_MAX_SPAN + 1))]
 
 
 class spec_gen_params(C.Structure):
@@ -112,7 +112,6 @@ def lib():
         "spec_profile_ops": [P, I, I, i32p, f32p, i32p],
         "spec_op_bytes": [C.POINTER(spec_model_desc), I, I, I, dp],
         "spec_time_op": [P, I, I, I, f32p],
-        "spec_profile_phases": [P, I, I, i32p, f32p, i32p],
         "spec_ngram_create": [I, I, I, C.POINTER(P)],
         "spec_ngram_destroy": [P],
         "spec_ngram_append": [P, i32p, I],
@@ -250,7 +249,8 @@ def spec_get_stats(ctx):
     s = spec_stats()
     _check(lib().spec_get_stats(ctx, C.byref(s)), ctx)
     return {"forwards": s.forwards, "verify_calls": s.verify_calls, "drafted": s.drafted,
-            "accepted": s.accepted, "forwards_by_span": list(s.forwards_by_span), "graphs": s.graphs}
+            "accepted": s.accepted, "forwards_by_span": list(s.forwards_by_span), "graphs": s.graphs,
+            "forward_ms_by_span": list(s.forward_ms_by_span)}
 
 
 def spec_time_verify(ctx, spans):
@@ -269,16 +269,6 @@ def spec_profile_ops(ctx, spans):
     us = np.zeros(SPEC_OP_COUNT, np.float32)
     n, npp = _i32(np.zeros(SPEC_OP_COUNT, np.int32))
     _check(lib().spec_profile_ops(ctx, S, iters, sp, us.ctypes.data_as(C.POINTER(C.c_float)), npp), ctx)
-    return {OPS[i]: (float(us[i]), int(n[i])) for i in range(SPEC_OP_COUNT)}
-
-
-def spec_profile_phases(ctx, spans):
-    sp2 = np.ascontiguousarray(np.asarray(spans, np.int32))
-    iters, S = sp2.shape
-    s, sp = _i32(sp2.reshape(-1))
-    us = np.zeros(SPEC_OP_COUNT, np.float32)
-    n, npp = _i32(np.zeros(SPEC_OP_COUNT, np.int32))
-    _check(lib().spec_profile_phases(ctx, S, iters, sp, us.ctypes.data_as(C.POINTER(C.c_float)), npp), ctx)
     return {OPS[i]: (float(us[i]), int(n[i])) for i in range(SPEC_OP_COUNT)}
 
 

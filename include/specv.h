@@ -53,8 +53,6 @@ extern "C" {
 
 #define SPEC_FLAG_KEEP_LOGITS 1u /* also store every row's logits (fp32) for spec_debug_logits */
 #define SPEC_FLAG_NO_GRAPH 2u    /* launch each kernel eagerly instead of replaying a HIP graph */
-#define SPEC_FLAG_PERSISTENT 4u  /* run each forward as one persistent cooperative kernel (only the
-                                  * shapes it is compiled for; spec_create fails on others) */
 
 #define SPEC_MAX_SPAN 16    /* rows per sequence per forward (K <= 15)      */
 #define SPEC_MAX_ROWS 128   /* rows per forward over all sequences           */
@@ -103,7 +101,11 @@ typedef struct spec_ctx spec_ctx;
 #define SPEC_NORM_FFN 1
 #define SPEC_NORM_FINAL 2
 
-/* Buffer sizes for `desc`.  EINVAL for an unsupported description. */
+/* Buffer sizes for `desc`: the caller allocates all four (the library never
+ * allocates device memory).  Sizing everything up front is how an admission
+ * that cannot fit is refused cleanly before any work starts (pegainfer page,
+ * memory section: a request that does not fit is rejected at admission).
+ * EINVAL for an unsupported description. */
 SPEC_API int spec_query_buffers(const spec_model_desc* desc, spec_buffer_sizes* out);
 
 /* Create a context over caller-owned buffers (each at least the size
@@ -130,7 +132,11 @@ SPEC_API int spec_load_norm(spec_ctx* ctx, int layer, int which, const float* sr
  * spec_prefill: empty the sequence, forward the prompt (rows 0..n-1, in
  * chunks of up to SPEC_MAX_SPAN rows, each committing all its rows) and
  * return g0 = argmax of the last prompt row.  g0 is not cached; it is span[0]
- * of the first verify. */
+ * of the first verify, which writes its KV row (pegainfer page, draft-seed
+ * alignment paragraph: the first verify after prefill starts from the token
+ * prefill produced).  Prefill itself is the plain forward: speculation only
+ * changes decoding (TensorSharp page, benchmarks paragraph).  On any failure
+ * (ENAN, EHIP) the sequence is left empty on the host and the device. */
 SPEC_API int spec_prefill(spec_ctx* ctx, const int32_t* tokens, int n, int32_t* next_token);
 
 /* spec_verify: span = [last, d1..dK], K in [0, SPEC_MAX_SPAN-1]; span[0] is
@@ -140,7 +146,13 @@ SPEC_API int spec_prefill(spec_ctx* ctx, const int32_t* tokens, int n, int32_t* 
  * (set on the device by the accept kernel).  K = 0 is a plain decode step. */
 SPEC_API int spec_verify(spec_ctx* ctx, const int32_t* span, int K, int32_t* argmax, int32_t* accept_len);
 
-/* spec_rewind: shorten the cache to len (0 <= len <= cache length). */
+/* spec_rewind: shorten the cache to len (0 <= len <= cache length); rows past
+ * len stay in memory and are overwritten by later forwards (TensorSharp page,
+ * interfaces section: SpecRewindCache(length); coreai note, KV-only rollback
+ * paragraph: rolling back is not advancing the position).  Used for budget or
+ * stop truncation and by the verify-cost sweep.  ESTATE outside [0, length].
+ * spec_cache_len: the current cache length (TensorSharp page, interfaces
+ * section: CacheSeqLen). */
 SPEC_API int spec_rewind(spec_ctx* ctx, int len);
 SPEC_API int spec_cache_len(spec_ctx* ctx, int* len);
 
@@ -158,7 +170,12 @@ SPEC_API int spec_cache_len_seq(spec_ctx* ctx, int seq, int* len);
 SPEC_API int spec_release_seq(spec_ctx* ctx, int seq);
 
 /* Logits of the rows of the last forward, fp32 [rows][vocab]; only for a
- * context created with SPEC_FLAG_KEEP_LOGITS.  rows <= rows of that forward. */
+ * context created with SPEC_FLAG_KEEP_LOGITS.  rows <= rows of that forward.
+ * For checking only: the per-row logits of the multi-row forward (TensorSharp
+ * page, interfaces section, SpecForward with every row's logits), compared
+ * row by row with a reference under teacher forcing (TensorSharp page, parity
+ * section).  host_out: caller-owned [rows][vocab] floats.  ESTATE without the
+ * flag, EINVAL for rows outside [0, rows of the last forward]. */
 SPEC_API int spec_debug_logits(spec_ctx* ctx, float* host_out, int rows);
 
 /* --------------------------------------------------------- measurement */
@@ -169,6 +186,8 @@ typedef struct spec_stats {
   int64_t drafted, accepted;      /* drafts submitted / accepted over verify calls */
   int64_t forwards_by_span[SPEC_MAX_SPAN + 1]; /* verify forwards by rows per sequence */
   int64_t graphs;                 /* HIP graphs instantiated */
+  double forward_ms_by_span[SPEC_MAX_SPAN + 1]; /* summed device time of those forwards (HIP events
+                                                  * on the context stream around each forward) */
 } spec_stats;
 SPEC_API int spec_get_stats(spec_ctx* ctx, spec_stats* out);
 
@@ -200,13 +219,6 @@ SPEC_API int spec_profile_ops(spec_ctx* ctx, int S, int iters, const int32_t* sp
  * context stream (no commit).  The KV rows of positions p..p+S-1 are
  * rewritten, as a verify would. */
 SPEC_API int spec_time_op(spec_ctx* ctx, int op, int S, int reps, float* us_per_launch);
-
-/* Per-phase timing of the persistent forward: `iters` forwards of span S at
- * sequence 0's current cache (no commit) with device timestamps taken by
- * workgroup 0 as each phase begins (100 MHz clock).  us_out[SPEC_OP_COUNT] =
- * mean microseconds per phase of each class, count_out = phases per forward. */
-SPEC_API int spec_profile_phases(spec_ctx* ctx, int S, int iters, const int32_t* spans, float* us_out,
-                                 int32_t* count_out);
 
 /* Algorithmic bytes one launch of an op class streams at span S and cache
  * length ctx_len (weights, KV reads and writes; activations excluded). */

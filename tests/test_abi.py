@@ -48,15 +48,12 @@ def test_unsupported_shapes_are_rejected(bad):
 def test_int4_needs_whole_groups():
     """int4 group-128 weights need every GEMM depth to hold whole groups: the
     tiny decoder (hidden 64) is refused, its group-aligned sibling and the
-    32B-class shape are accepted, and the persistent forward is bf16 only."""
+    32B-class shape are accepted."""
     i4 = specv.SPEC_WFMT_INT4G128
     with pytest.raises(specv.SpecError):
         specv.spec_query_buffers(specv.make_desc(synth.SHAPES["tiny"], max_ctx=64, weight_format=i4))
     for name in ("tiny_int4", "dense_32b"):
         specv.spec_query_buffers(specv.make_desc(synth.SHAPES[name], max_ctx=64, weight_format=i4))
-    with pytest.raises(specv.SpecError):
-        specv.spec_query_buffers(specv.make_desc(synth.SHAPES["tiny_int4"], max_ctx=64, weight_format=i4,
-                                                 flags=specv.SPEC_FLAG_PERSISTENT))
 
 
 def test_int4_op_bytes_match_the_32b_stream():

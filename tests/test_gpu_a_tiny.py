@@ -16,8 +16,8 @@ def weights():
     return synth.weights(SHAPE, seed=0)
 
 
-PATHS = {"per_op": specv.SPEC_FLAG_KEEP_LOGITS,
-         "persistent": specv.SPEC_FLAG_KEEP_LOGITS | specv.SPEC_FLAG_PERSISTENT}
+PATHS = {"graph": specv.SPEC_FLAG_KEEP_LOGITS,
+         "eager": specv.SPEC_FLAG_KEEP_LOGITS | specv.SPEC_FLAG_NO_GRAPH}
 
 
 @pytest.fixture(params=list(PATHS))
@@ -54,6 +54,8 @@ def test_planted_drafts_accept_exactly(twin):
         assert m == j
         assert list(am[: m + 1]) == [int(t) for t in stream[1:m + 2]]
         assert specv.spec_cache_len(twin.ctx) == len(prompt) + m + 1
+    st = specv.spec_get_stats(twin.ctx)
+    assert st["forwards_by_span"][K + 1] >= K + 1 and st["forward_ms_by_span"][K + 1] > 0.0
 
 
 def test_rows_gate_bit_exact(twin):
@@ -142,3 +144,45 @@ def test_error_codes(weights):
     assert specv.spec_cache_len(s.ctx) == n           # refused, nothing changed
     specv.spec_verify(s.ctx, [g])                     # still usable
     s.close()
+
+
+def test_nan_row_leaves_the_cache_unchanged(weights):
+    """A NaN logit row fails the verify with SPEC_ENAN and moves no cache
+    length, on the device or the host: with the final norm gain set to NaN,
+    the verify is refused, the cache length stays p, and after the gain is
+    restored the next verify matches the oracle at that same p.  The same
+    holds for a prefill, which leaves the sequence empty."""
+    import torch
+    t = Twin(SHAPE, weights, max_ctx=256)
+    try:
+        prompt = synth.motif_prompt(1, SHAPE["vocab"])
+        t.prefill(prompt)
+        ctx = t.ctx
+        p = specv.spec_cache_len(ctx)
+        nan = torch.full((SHAPE["hidden"],), float("nan"), dtype=torch.float32, device="cuda")
+        one = torch.ones(SHAPE["hidden"], dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        specv.spec_load_norm(ctx, 0, specv.SPEC_NORM_FINAL, nan.data_ptr())
+        for K in (0, 3, 7):
+            with pytest.raises(specv.SpecError) as e:
+                specv.spec_verify(ctx, [t.history[-1]] + [5] * K)
+            assert e.value.code == specv.SPEC_ENAN
+            assert specv.spec_cache_len(ctx) == p
+        specv.spec_load_norm(ctx, 0, specv.SPEC_NORM_FINAL, one.data_ptr())
+        rng = np.random.default_rng(3)
+        for K in (3, 0, 7):
+            t.verify_checked(rng.integers(0, SHAPE["vocab"], K))
+        # a prefill that hits NaN leaves the sequence empty and unusable
+        specv.spec_load_norm(ctx, 0, specv.SPEC_NORM_FINAL, nan.data_ptr())
+        with pytest.raises(specv.SpecError) as e:
+            specv.spec_prefill(ctx, prompt)
+        assert e.value.code == specv.SPEC_ENAN
+        assert specv.spec_cache_len(ctx) == 0
+        specv.spec_load_norm(ctx, 0, specv.SPEC_NORM_FINAL, one.data_ptr())
+        with pytest.raises(specv.SpecError) as e:
+            specv.spec_verify(ctx, [1, 2])
+        assert e.value.code == specv.SPEC_ESTATE
+        t.prefill(prompt)
+        t.verify_checked([3, 4])
+    finally:
+        t.close()

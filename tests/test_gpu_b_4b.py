@@ -78,22 +78,6 @@ def test_spec_on_equals_off_repetition_prompt(twin):
     log(f"  48 tokens: spec-off {s_off['forwards']} forwards, adaptive {s_on['forwards']}")
 
 
-def test_persistent_forward(twin):
-    """The persistent single-kernel forward against the same oracle: every
-    span length class on a short context."""
-    w = synth.weights(SHAPE, seed=0, device="cuda")
-    t = Twin(SHAPE, w, max_ctx=1024, flags=specv.SPEC_FLAG_KEEP_LOGITS | specv.SPEC_FLAG_PERSISTENT, orc=twin.orc)
-    del w
-    try:
-        t.prefill(synth.uniform_prompt(7, SHAPE["vocab"], 40))
-        rng = np.random.default_rng(7)
-        for K in (0, 3, 7, 15):
-            _, m, err = t.verify_checked(rng.integers(0, SHAPE["vocab"], K))
-            log(f"  persistent K={K:2d} m={m} max|dlogit|={err:.2e}")
-    finally:
-        t.close()
-
-
 def test_full_848_context(twin):
     """The verify-cost sweep's context: 848 uniform tokens, then spans of 1,
     8 and 16 rows, checked against the oracle."""
