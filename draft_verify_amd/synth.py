@@ -36,6 +36,14 @@ SHAPES = {
                       eps=1e-6, rope_theta=1e6),
     "dense_32b": dict(n_layers=64, hidden=5120, n_q=64, n_kv=8, head_dim=128, ffn=25600,
                       vocab=151936, eps=1e-6, rope_theta=1e6),
+    # the attention geometry of the Qwen3-4B shape (32q/8kv heads of 128) and
+    # of the 32B-class shape (64q/8kv heads of 128) on a narrow trunk (hidden
+    # 512): long contexts at the real head layout, with projections small
+    # enough for the CPU oracle to prefill thousands of tokens
+    "attn_4b": dict(n_layers=2, hidden=512, n_q=32, n_kv=8, head_dim=128, ffn=512, vocab=1024,
+                    eps=1e-6, rope_theta=1e6),
+    "attn_32b": dict(n_layers=2, hidden=512, n_q=64, n_kv=8, head_dim=128, ffn=512, vocab=1024,
+                     eps=1e-6, rope_theta=1e6),
 }
 
 LAYER_MATS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")

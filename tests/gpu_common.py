@@ -12,6 +12,7 @@ After a step whose accept lengths legitimately differ, the oracle is re-synced
 to the GPU's committed history.
 """
 import sys
+import time
 
 import numpy as np
 
@@ -25,6 +26,52 @@ MARGIN = 0.05
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def oracle_prefill(orc, prompt, seq=0, chunk=0):
+    """The oracle's prefill of `prompt` on `seq`: one call, or chunk-row
+    forwards with a progress line each; returns (g0, margin)."""
+    n = len(prompt)
+    if chunk <= 0 or chunk >= n:
+        return orc.prefill(prompt, seq)
+    orc.rewind(0, seq)
+    t0 = time.time()
+    for off in range(0, n, chunk):
+        end = min(n, off + chunk)
+        am, mg, _ = orc.forward(prompt[off:end], seq, lm_from=(end - off - 1) if end == n else (end - off))
+        log(f"    oracle prefill {end}/{n} rows ({time.time() - t0:.0f}s)")
+    return int(am[0]), float(mg[0])
+
+
+def check_batch_step(sess, orc, ids, spans, am, acc, hist, V, tag=""):
+    """The comparison protocol for one batched verify step, per sequence,
+    against the oracle replaying each sequence's span on its own prefix;
+    commits to `hist` and re-syncs the oracle after a legitimate difference.
+    Returns the worst logit difference."""
+    n_seq, S = spans.shape
+    K = S - 1
+    lg = specv.spec_debug_logits(sess.ctx, n_seq * S, V).reshape(n_seq, S, V)
+    worst = 0.0
+    for b, sid in enumerate(ids):
+        p = len(hist[sid]) - 1
+        amo, mo, mgo, lgo = orc.verify(spans[b], sid, want_logits=True)
+        err = float(np.abs(lg[b] - lgo).max())
+        worst = max(worst, err)
+        assert err < LOGIT_TOL, f"{tag} seq {sid}: logits differ by {err:.3e}"
+        sure = mgo >= MARGIN
+        assert np.array_equal(am[b][sure], amo[sure]), f"{tag} seq {sid}: argmax differs on a sure row"
+        m = int(acc[b])
+        decide = min(m, mo, K - 1)
+        if K == 0 or bool(np.all(sure[: decide + 1])):
+            assert m == mo, f"{tag} seq {sid}: accept {m} != oracle {mo}"
+        assert m == O.accept_greedy(spans[b], am[b]), f"{tag} seq {sid}: device accept != accept_greedy"
+        assert 0 <= m <= K
+        assert specv.spec_cache_len_seq(sess.ctx, sid) == p + m + 1
+        commit = [int(x) for x in am[b][: m + 1]]
+        hist[sid] += commit
+        if m != mo or list(amo[: mo + 1]) != commit:
+            orc.prefill(hist[sid][:-1], sid)  # re-sync to the GPU's stream
+    return worst
 
 
 class Twin:
@@ -44,9 +91,12 @@ class Twin:
         self.ctx = self.sess.ctx
         self.history = []
 
-    def prefill(self, prompt, seq=0):
+    def prefill(self, prompt, seq=0, chunk=0):
+        """Prefill both sides; chunk > 0 runs the oracle's prefill in chunks of
+        that many rows with a progress line each (the oracle's rows are
+        independent of how they are grouped, so the cache is the same)."""
         g = specv.spec_prefill_seq(self.ctx, seq, prompt)
-        go, mg = self.orc.prefill(prompt, seq)
+        go, mg = oracle_prefill(self.orc, prompt, seq, chunk)
         assert g == go or mg < MARGIN, f"prefill token {g} != oracle {go} (margin {mg:.3f})"
         self.history = [int(t) for t in prompt] + [g]
         return g
@@ -69,6 +119,9 @@ class Twin:
         decide = min(m, mo, K - 1) if K > 0 else -1
         if decide < 0 or bool(np.all(sure[: decide + 1])):
             assert m == mo, f"accept length {m} != oracle {mo}"
+        # on every step, near-ties included: the device's accept length is
+        # accept_greedy of the span against the device's own argmax rows
+        assert m == O.accept_greedy(span, am), f"device accept {m} != accept_greedy(span, device argmax)"
         assert 0 <= m <= K
         assert specv.spec_cache_len_seq(self.ctx, seq) == p + m + 1
         commit = [int(x) for x in am[: m + 1]]

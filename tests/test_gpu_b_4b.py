@@ -54,19 +54,23 @@ def test_planted_drafts_accept(twin):
         log(f"  planted mismatch at {j}: accepted {m}, max|dlogit|={err:.2e}")
 
 
-def test_rows_gate_bit_exact(twin):
+@pytest.mark.parametrize("S", [5, 8, 9, 12, 16])
+def test_rows_gate_bit_exact(twin, S):
+    """One S-row forward == S one-row decodes, bit for bit, across the row
+    counts where the O and down projections change kernels (one-pass below
+    nine rows, split-K with the same K parts above)."""
     prompt = synth.uniform_prompt(5, SHAPE["vocab"], 33)
     g = specv.spec_prefill(twin.ctx, prompt)
     p = specv.spec_cache_len(twin.ctx)
-    span = [g] + [int(t) for t in synth.uniform_prompt(6, SHAPE["vocab"], 7)]
+    span = [g] + [int(t) for t in synth.uniform_prompt(6, SHAPE["vocab"], S - 1)]
     specv.spec_verify(twin.ctx, span)
-    multi = specv.spec_debug_logits(twin.ctx, 8, SHAPE["vocab"])
+    multi = specv.spec_debug_logits(twin.ctx, S, SHAPE["vocab"])
     specv.spec_rewind(twin.ctx, p)
     rows = []
     for t in span:
         specv.spec_verify(twin.ctx, [t])
         rows.append(specv.spec_debug_logits(twin.ctx, 1, SHAPE["vocab"])[0])
-    assert np.array_equal(multi, np.stack(rows)), "8-row forward differs from 8 one-row decodes"
+    assert np.array_equal(multi, np.stack(rows)), f"{S}-row forward differs from {S} one-row decodes"
 
 
 def test_spec_on_equals_off_repetition_prompt(twin):
@@ -75,7 +79,26 @@ def test_spec_on_equals_off_repetition_prompt(twin):
     on, s_on = specv.spec_generate(twin.ctx, prompt, 48, spec=True, fixed_k=0, k_cap=7)
     assert np.array_equal(off, on)
     assert s_on["forwards"] <= s_off["forwards"]
-    log(f"  48 tokens: spec-off {s_off['forwards']} forwards, adaptive {s_on['forwards']}")
+    log(f"  48 tokens: spec-off {s_off['forwards']} forwards, adaptive {s_on['forwards']} "
+        f"({s_on['drafted']} drafted)")
+
+
+def test_spec_on_equals_off_with_accepts_and_rejections(twin):
+    """Drafts that are mostly right and sometimes wrong: the spec-off stream
+    with every fifth token changed, fed as drafts at adaptive K.  Full
+    accepts, partial accepts and rejections all occur, and the committed
+    stream still equals the spec-off stream token for token."""
+    prompt = synth.repetition_prompt(3, SHAPE["vocab"], 512)
+    off, _ = specv.spec_generate(twin.ctx, prompt, 64, spec=False)
+    ref = np.array(off, np.int32)
+    ref[5::5] = (ref[5::5] + 1) % SHAPE["vocab"]
+    on, st = specv.spec_generate(twin.ctx, prompt, 64, spec=True, fixed_k=0, k_cap=7,
+                                 draft_source=specv.SPEC_DRAFT_STREAM, ref_stream=ref)
+    assert np.array_equal(off, on)
+    assert st["drafted"] > 0 and 0 < st["accepted"] < st["drafted"]
+    assert st["accept_hist"][0] > 0 and sum(st["accept_hist"][1:]) > 0
+    log(f"  64 tokens, corrupted-stream drafts: {st['forwards']} forwards, {st['drafted']} drafted, "
+        f"{st['accepted']} accepted, accept histogram {st['accept_hist'][:8]}")
 
 
 def test_full_848_context(twin):
