@@ -22,7 +22,8 @@ struct StepDev {
   int32_t n_seq;
   int32_t span;      // rows per sequence (S)
   int32_t pad;
-  // followed by tokens[max_rows] and seq_ids[max_rows]
+  // followed by tokens[max_rows], seq_ids[max_rows] and kd[max_rows] (the
+  // drafts each sequence really proposed; its span rows past 1 + kd are padding)
 };
 
 // Packed bf16 weights: fragments of 16 output rows x 32 inputs, 1 KiB each,
@@ -84,6 +85,7 @@ struct GemmParams {
   int32_t* status;            // bit 0: NaN logit seen
   float* logits;              // [R][N] or null
   const int32_t* tokens;      // [R] span tokens
+  const int32_t* kd;          // [n_seq] drafts per sequence (rows past 1 + kd[b] are padding)
   const int32_t* mode;        // StepDev::mode
   int32_t* result;            // [1 + n_seq*(S+1)]: status, then (m, a0..a(S-1)) per sequence
   int32_t* kv_len_w;          // cache lengths, advanced by the accept stage

@@ -701,8 +701,10 @@ __device__ void lm_finish(const GemmParams& P, int nblk, float* sbuf) {
     if (mode == MODE_COMMIT_ALL) {
       m = S - 1;
     } else {
+      // accept_greedy over the sequence's own drafts; padding rows never count
+      const int kb = min(S - 1, max(0, P.kd[b]));
       m = 0;
-      while (m < S - 1 && P.tokens[row0 + m + 1] == arg[row0 + m]) ++m;
+      while (m < kb && P.tokens[row0 + m + 1] == arg[row0 + m]) ++m;
     }
     const int seq = P.seq_ids[b];
     if (mode == MODE_COMMIT_ALL) P.kv_len_w[seq] += S;
@@ -1859,6 +1861,7 @@ hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st) {
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
+  if (epi == EPI_LM && !p.kd) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, fmt, st);
     case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, fmt, st);
@@ -1914,7 +1917,7 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
     return hipErrorInvalidValue;
   if (epi != EPI_RESID && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
-  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int gpw = nk / 4, nw = p.K / (32 * nk), ntile = p.N / 16;
   const int ct = (nw == 10 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
@@ -1953,7 +1956,7 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
   if ((epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LM) && (!p.ss || !p.gain || p.ss_n * 16 != p.K))
     return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
-  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || p.R != p.n_seq * p.S))
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
   const int grid = nblk < max_grid ? nblk : max_grid;

@@ -251,7 +251,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.slotbt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
   Lo.argkey = take(R * 8);
   Lo.status = take(4);
-  Lo.step = take(sizeof(StepDev) + 2 * R * 4);
+  Lo.step = take(sizeof(StepDev) + 3 * R * 4);
   Lo.result = take((1 + 2 * R) * 4);
   Lo.kv_len = take((size_t)Lo.max_seqs * 4);
   Lo.bt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
@@ -265,7 +265,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.workspace_bytes = off;
 
   off = 0;
-  Lo.host_step = take(sizeof(StepDev) + 2 * R * 4);
+  Lo.host_step = take(sizeof(StepDev) + 3 * R * 4);
   Lo.host_result = take((1 + 2 * R) * 4);
   Lo.host_kvlen = take((size_t)Lo.max_seqs * 4);
   Lo.host_bt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
@@ -472,6 +472,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.status = c->ws<int32_t>(L.status);
     gl.logits = (c->d.flags & SPEC_FLAG_KEEP_LOGITS) ? c->ws<float>(L.logits) : nullptr;
     gl.tokens = tokens;
+    gl.kd = seq_ids + L.max_rows;
     gl.mode = &sd->mode;
     gl.result = c->ws<int32_t>(L.result);
     gl.kv_len_w = c->ws<int32_t>(L.kv_len);
@@ -608,9 +609,11 @@ int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
   return SPEC_OK;
 }
 
-// Stage the step block (mode, shape, tokens, sequence ids) and copy it; pick
-// the attention variant of the step from the host's cache lengths.
-int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
+// Stage the step block (mode, shape, tokens, sequence ids, drafts per
+// sequence) and copy it; pick the attention variant of the step from the
+// host's cache lengths.  kd: drafts per sequence, or null for S - 1 each.
+int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids,
+                const int32_t* kd = nullptr) {
   const Layout& L = c->lo;
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
@@ -631,7 +634,9 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   int32_t* tk = (int32_t*)(sd + 1);
   memcpy(tk, tokens, sizeof(int32_t) * (size_t)n_seq * S);
   memcpy(tk + L.max_rows, seq_ids, sizeof(int32_t) * (size_t)n_seq);
-  const size_t bytes = sizeof(StepDev) + (size_t)L.max_rows * 4 + (size_t)n_seq * 4;
+  int32_t* kdev = tk + 2 * L.max_rows;
+  for (int b = 0; b < n_seq; ++b) kdev[b] = kd ? kd[b] : S - 1;
+  const size_t bytes = sizeof(StepDev) + (size_t)L.max_rows * 8 + (size_t)n_seq * 4;
   // tokens of the whole row range and the used sequence ids, in one copy
   HIPCHK(c, hipMemcpyAsync(c->ws<uint8_t>(L.step), c->h_step(), bytes, hipMemcpyHostToDevice, c->st));
   return SPEC_OK;
@@ -648,8 +653,9 @@ int launch_forward(spec_ctx* c, int n_seq, int S) {
 // One forward and its result copy; synchronous.  Verify forwards are timed
 // with the context's two events (forward launch to accept done) into the
 // per-span totals of spec_get_stats.
-int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids) {
-  STEP(upload_step(c, mode, n_seq, S, tokens, seq_ids));
+int run_forward(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, const int32_t* seq_ids,
+                const int32_t* kd = nullptr) {
+  STEP(upload_step(c, mode, n_seq, S, tokens, seq_ids, kd));
   const bool timed = mode == MODE_VERIFY && c->ev0 && c->ev1;
   if (timed) HIPCHK(c, hipEventRecord(c->ev0, c->st));
   STEP(launch_forward(c, n_seq, S));
@@ -904,13 +910,16 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int n, int32_t* next_token)
   return spec_prefill_seq(c, 0, tokens, n, next_token);
 }
 
-int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
-                      int32_t* argmax, int32_t* accept_len) {
+int spec_verify_batch_k(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
+                        const int32_t* drafts, int32_t* argmax, int32_t* accept_len) {
   if (!c) return SPEC_EINVAL;
   if (!seq_ids || !spans || !argmax || !accept_len || n_seq <= 0)
     return set_err(c, SPEC_EINVAL, "null argument or n_seq < 1");
   const int S = K + 1;
   if (K < 0 || S > SPEC_MAX_SPAN) return set_err(c, SPEC_EINVAL, "K must be in [0, 15]");
+  if (drafts)
+    for (int b = 0; b < n_seq; ++b)
+      if (drafts[b] < 0 || drafts[b] > K) return set_err(c, SPEC_EINVAL, "drafts per sequence must be in [0, K]");
   if (n_seq * S > c->lo.max_rows) return set_err(c, SPEC_EINVAL, "n_seq*(K+1) exceeds max_rows");
   STEP(check_ready(c));
   STEP(check_tokens(c, spans, n_seq * S));
@@ -932,7 +941,7 @@ int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int3
     }
     if (dirty) STEP(upload_bt_row(c, seq));
   }
-  const int frc = run_forward(c, MODE_VERIFY, n_seq, S, spans, seq_ids);
+  const int frc = run_forward(c, MODE_VERIFY, n_seq, S, spans, seq_ids, drafts);
   if (frc != SPEC_OK) {
     // The accept stage does not advance a cache on a NaN row; after any
     // failure the device lengths are set back to the host's (unchanged)
@@ -953,12 +962,17 @@ int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int3
     const int seq = seq_ids[b];
     c->len[(size_t)seq] += m + 1;
     trim_blocks(c, seq, c->len[(size_t)seq]);
-    c->stats.drafted += K;
+    c->stats.drafted += drafts ? drafts[b] : K;
     c->stats.accepted += m;
   }
   c->stats.verify_calls++;
   c->stats.forwards_by_span[S]++;
   return SPEC_OK;
+}
+
+int spec_verify_batch(spec_ctx* c, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
+                      int32_t* argmax, int32_t* accept_len) {
+  return spec_verify_batch_k(c, n_seq, seq_ids, spans, K, nullptr, argmax, accept_len);
 }
 
 int spec_verify(spec_ctx* c, const int32_t* span, int K, int32_t* argmax, int32_t* accept_len) {
@@ -1161,8 +1175,12 @@ struct spec_gen {
   spec_gen_params gp;
   int capacity, kcap, k;
   spec_ngram* ng;
+  spec_governor* gov;  // governed loops only
   std::vector<int32_t> out;
-  ~spec_gen() { spec_ngram_destroy(ng); }
+  ~spec_gen() {
+    spec_ngram_destroy(ng);
+    spec_governor_destroy(gov);
+  }
 };
 
 extern "C" {
@@ -1182,9 +1200,11 @@ int spec_gen_begin(spec_ctx* c, const int32_t* prompt, int n_prompt, int capacit
   g->kcap = std::max(1, std::min(gp->fixed_k > 0 ? gp->fixed_k : gp->k_cap, SPEC_MAX_SPAN - 1));
   g->k = gp->fixed_k > 0 ? std::min(gp->fixed_k, SPEC_MAX_SPAN - 1) : 1;
   g->ng = nullptr;
+  g->gov = nullptr;
   int rc = SPEC_OK;
   if (gp->spec && gp->draft_source == SPEC_DRAFT_NGRAM)
     rc = spec_ngram_create(gp->n_min, gp->n_max, n_prompt + capacity + 1, &g->ng);
+  if (rc == SPEC_OK && gp->spec && gp->governed) rc = spec_governor_create(nullptr, &g->gov);
   int32_t g0 = 0;
   if (rc == SPEC_OK) rc = spec_prefill(c, prompt, n_prompt, &g0);
   if (rc == SPEC_OK && g->ng) rc = spec_ngram_append(g->ng, prompt, n_prompt);
@@ -1209,9 +1229,12 @@ int spec_gen_step(spec_gen* g, int rounds, spec_gen_stats* gs) {
   double in_verify = 0.0;
   int done = 0;
   while (done < rounds && (int)g->out.size() < g->capacity) {
+    const auto tr = clk::now();
     const int n = (int)g->out.size();
     int kd = 0;
-    if (gp.spec) {
+    // a governed loop drafts only when its governor says so
+    const bool draft = gp.spec && (!g->gov || spec_governor_should_draft(g->gov) == 1);
+    if (draft) {
       const int want = std::max(0, std::min(g->k, g->capacity - n - 1));
       if (gp.draft_source == SPEC_DRAFT_NGRAM) {
         kd = spec_ngram_propose(g->ng, want, span + 1);
@@ -1242,7 +1265,12 @@ int spec_gen_step(spec_gen* g, int rounds, spec_gen_stats* gs) {
     }
     for (int i = 0; i < commit; ++i) g->out.push_back(am[i]);
     if (g->ng) STEP(spec_ngram_append(g->ng, am, commit));
-    if (gp.spec && gp.fixed_k <= 0) g->k = spec_adapt_k(g->k, kd, m, g->kcap);
+    if (draft && gp.fixed_k <= 0) g->k = spec_adapt_k(g->k, kd, m, g->kcap);
+    if (g->gov) {
+      if (!draft) gs->plain_steps++;
+      const double sec = std::chrono::duration<double>(clk::now() - tr).count();
+      STEP(spec_governor_record(g->gov, draft ? 1 : 0, commit, m, sec));
+    }
     ++done;
   }
   const double dt = std::chrono::duration<double>(clk::now() - t0).count();
@@ -1256,6 +1284,11 @@ int spec_gen_tokens(spec_gen* g, int32_t* out, int cap) {
   const int n = std::min(cap, (int)g->out.size());
   if (n > 0) memcpy(out, g->out.data(), sizeof(int32_t) * (size_t)n);
   return (int)g->out.size();
+}
+
+int spec_gen_governor_stats(spec_gen* g, spec_governor_stats* out) {
+  if (!g || !out || !g->gov) return SPEC_EINVAL;
+  return spec_governor_get_stats(g->gov, out);
 }
 
 int spec_gen_end(spec_gen* g) {

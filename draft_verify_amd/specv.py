@@ -66,14 +66,27 @@ class spec_stats(C.Structure):
 class spec_gen_params(C.Structure):
     _fields_ = [("spec", C.c_int32), ("fixed_k", C.c_int32), ("k_cap", C.c_int32),
                 ("n_min", C.c_int32), ("n_max", C.c_int32), ("draft_source", C.c_int32),
-                ("ref_stream", C.POINTER(C.c_int32))]
+                ("ref_stream", C.POINTER(C.c_int32)), ("governed", C.c_int32)]
 
 
 class spec_gen_stats(C.Structure):
     _fields_ = [("forwards", C.c_int64), ("drafted", C.c_int64), ("accepted", C.c_int64),
                 ("accept_hist", C.c_int64 * SPEC_MAX_SPAN),
                 ("forwards_by_span", C.c_int64 * (SPEC_MAX_SPAN + 1)),
-                ("decode_s", C.c_double), ("host_s", C.c_double), ("prefill_s", C.c_double)]
+                ("decode_s", C.c_double), ("host_s", C.c_double), ("prefill_s", C.c_double),
+                ("plain_steps", C.c_int64)]
+
+
+class spec_governor_params(C.Structure):
+    _fields_ = [("probe_spec", C.c_int32), ("probe_spec_short", C.c_int32), ("probe_plain", C.c_int32),
+                ("park_first", C.c_int32), ("park_max", C.c_int32), ("zero_accept_exit", C.c_int32),
+                ("hold_window", C.c_int32), ("hold_refresh", C.c_int32)]
+
+
+class spec_governor_stats(C.Structure):
+    _fields_ = [("wins", C.c_int64), ("losses", C.c_int64), ("probes", C.c_int64),
+                ("spec_steps", C.c_int64), ("plain_samples", C.c_int64), ("parked_steps", C.c_int64),
+                ("state", C.c_int32), ("plain_ms_per_token", C.c_double), ("spec_ms_per_token", C.c_double)]
 
 
 _lib = None
@@ -103,6 +116,7 @@ def lib():
         "spec_cache_len": [P, i32p],
         "spec_prefill_seq": [P, I, i32p, I, i32p],
         "spec_verify_batch": [P, I, i32p, i32p, I, i32p, i32p],
+        "spec_verify_batch_k": [P, I, i32p, i32p, I, i32p, i32p, i32p],
         "spec_rewind_seq": [P, I, I],
         "spec_cache_len_seq": [P, I, i32p],
         "spec_release_seq": [P, I],
@@ -124,6 +138,13 @@ def lib():
         "spec_gen_step": [P, I, C.POINTER(spec_gen_stats)],
         "spec_gen_tokens": [P, i32p, I],
         "spec_gen_end": [P],
+        "spec_gen_governor_stats": [P, C.POINTER(spec_governor_stats)],
+        "spec_governor_create": [C.POINTER(spec_governor_params), C.POINTER(P)],
+        "spec_governor_destroy": [P],
+        "spec_governor_should_draft": [P],
+        "spec_governor_record": [P, I, I, I, C.c_double],
+        "spec_governor_new_request": [P],
+        "spec_governor_get_stats": [P, C.POINTER(spec_governor_stats)],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -212,6 +233,19 @@ def spec_verify_batch(ctx, seq_ids, spans):
     am, ap = _i32(np.zeros(n * S, np.int32))
     acc, accp = _i32(np.zeros(n, np.int32))
     _check(lib().spec_verify_batch(ctx, n, idp, sp, S - 1, ap, accp), ctx)
+    return am.reshape(n, S).copy(), acc.copy()
+
+
+def spec_verify_batch_k(ctx, seq_ids, spans, drafts):
+    """spans [n_seq, K+1] (rows past 1 + drafts[b] are padding), drafts [n_seq]."""
+    ids, idp = _i32(seq_ids)
+    sp2 = np.ascontiguousarray(np.asarray(spans, np.int32))
+    n, S = sp2.shape
+    s, sp = _i32(sp2.reshape(-1))
+    kd, kdp = _i32(drafts)
+    am, ap = _i32(np.zeros(n * S, np.int32))
+    acc, accp = _i32(np.zeros(n, np.int32))
+    _check(lib().spec_verify_batch_k(ctx, n, idp, sp, S - 1, kdp, ap, accp), ctx)
     return am.reshape(n, S).copy(), acc.copy()
 
 
@@ -319,14 +353,14 @@ def spec_adapt_k(k, drafted, accepted, k_cap):
 
 
 def spec_generate(ctx, prompt, n_tokens, spec=True, fixed_k=0, k_cap=7, n_min=2, n_max=4,
-                  draft_source=SPEC_DRAFT_NGRAM, ref_stream=None):
+                  draft_source=SPEC_DRAFT_NGRAM, ref_stream=None, governed=False):
     p, pp = _i32(prompt)
     out, op = _i32(np.zeros(n_tokens, np.int32))
     ref = None
     if ref_stream is not None:
         ref, refp = _i32(ref_stream)
     params = spec_gen_params(int(spec), fixed_k, k_cap, n_min, n_max, draft_source,
-                             refp if ref is not None else None)
+                             refp if ref is not None else None, int(governed))
     st = spec_gen_stats()
     _check(lib().spec_generate(ctx, pp, len(p), n_tokens, C.byref(params), op, C.byref(st)), ctx)
     return out.copy(), _gen_stats_dict(st)
@@ -335,21 +369,65 @@ def spec_generate(ctx, prompt, n_tokens, spec=True, fixed_k=0, k_cap=7, n_min=2,
 def _gen_stats_dict(st):
     return {"forwards": st.forwards, "drafted": st.drafted, "accepted": st.accepted,
             "accept_hist": list(st.accept_hist), "forwards_by_span": list(st.forwards_by_span),
-            "decode_s": st.decode_s, "host_s": st.host_s, "prefill_s": st.prefill_s}
+            "decode_s": st.decode_s, "host_s": st.host_s, "prefill_s": st.prefill_s,
+            "plain_steps": st.plain_steps}
+
+
+GOV_FIELDS = ("wins", "losses", "probes", "spec_steps", "plain_samples", "parked_steps", "state",
+              "plain_ms_per_token", "spec_ms_per_token")
+
+
+def _gov_stats_dict(st):
+    return {f: getattr(st, f) for f in GOV_FIELDS}
+
+
+class Governor:
+    """spec_governor_create / should_draft / record / new_request / get_stats."""
+
+    def __init__(self, params=None):
+        h = C.c_void_p()
+        _check(lib().spec_governor_create(C.byref(params) if params is not None else None, C.byref(h)))
+        self.h = h.value
+
+    def should_draft(self):
+        return bool(_check(lib().spec_governor_should_draft(self.h)))
+
+    def record(self, speculative, committed, accepted, seconds):
+        return _check(lib().spec_governor_record(self.h, int(speculative), int(committed), int(accepted),
+                                                 float(seconds)))
+
+    def new_request(self):
+        return _check(lib().spec_governor_new_request(self.h))
+
+    def stats(self):
+        st = spec_governor_stats()
+        _check(lib().spec_governor_get_stats(self.h, C.byref(st)))
+        return _gov_stats_dict(st)
+
+    def close(self):
+        if self.h:
+            lib().spec_governor_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class spec_gen_handle:
     """spec_gen_begin / spec_gen_step / spec_gen_tokens / spec_gen_end."""
 
     def __init__(self, ctx, prompt, capacity, spec=True, fixed_k=0, k_cap=7, n_min=2, n_max=4,
-                 draft_source=SPEC_DRAFT_NGRAM, ref_stream=None):
+                 draft_source=SPEC_DRAFT_NGRAM, ref_stream=None, governed=False):
         self.ctx = ctx
         self._p, pp = _i32(prompt)
         self._ref = None
         refp = None
         if ref_stream is not None:
             self._ref, refp = _i32(ref_stream)
-        self.params = spec_gen_params(int(spec), fixed_k, k_cap, n_min, n_max, draft_source, refp)
+        self.params = spec_gen_params(int(spec), fixed_k, k_cap, n_min, n_max, draft_source, refp, int(governed))
         h = C.c_void_p()
         _check(lib().spec_gen_begin(ctx, pp, len(self._p), capacity, C.byref(self.params), C.byref(h)), ctx)
         self.h = h.value
@@ -361,6 +439,11 @@ class spec_gen_handle:
 
     def stats(self):
         return _gen_stats_dict(self.st)
+
+    def governor_stats(self):
+        st = spec_governor_stats()
+        _check(lib().spec_gen_governor_stats(self.h, C.byref(st)), self.ctx)
+        return _gov_stats_dict(st)
 
     def tokens(self):
         out, op = _i32(np.zeros(self.capacity, np.int32))

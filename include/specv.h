@@ -164,6 +164,19 @@ SPEC_API int spec_cache_len(spec_ctx* ctx, int* len);
 SPEC_API int spec_prefill_seq(spec_ctx* ctx, int seq, const int32_t* tokens, int n, int32_t* next_token);
 SPEC_API int spec_verify_batch(spec_ctx* ctx, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
                       int32_t* argmax, int32_t* accept_len);
+/* spec_verify_batch_k: the same step where each sequence b proposed its own
+ * drafts[b] in [0, K] drafts (spans[b][1..drafts[b]]); the rest of its span
+ * row, spans[b][drafts[b]+1..K], is padding (any valid token).  Every
+ * sequence runs the full K+1 rows, so the step keeps one shape and one
+ * captured graph whatever the mix (pegainfer page, CUDA-graph section: a
+ * graph captured at a short span and replayed at a longer one under-computes
+ * the tail; here padding plus a per-sequence draft count replaces shorter
+ * spans).  The accept stage counts only a sequence's real drafts: m[b] <=
+ * drafts[b], the cache advances by m[b]+1, and argmax rows past drafts[b] are
+ * computed on padding and carry no meaning.  drafts == NULL is
+ * spec_verify_batch (K drafts each).  EINVAL for a count outside [0, K]. */
+SPEC_API int spec_verify_batch_k(spec_ctx* ctx, int n_seq, const int32_t* seq_ids, const int32_t* spans, int K,
+                                 const int32_t* drafts, int32_t* argmax, int32_t* accept_len);
 SPEC_API int spec_rewind_seq(spec_ctx* ctx, int seq, int len);
 SPEC_API int spec_cache_len_seq(spec_ctx* ctx, int seq, int* len);
 /* Free every block of a sequence (cache length 0). */
@@ -247,6 +260,50 @@ SPEC_API int spec_ngram_propose(spec_ngram* ng, int K, int32_t* drafts);
  * Pure function. */
 SPEC_API int spec_adapt_k(int k, int drafted, int accepted, int k_cap);
 
+/* ------------------------------------------------------ cost governor */
+
+/* Speculation cost governor (TensorSharp speculative decoding page, protocol
+ * section: speculation must never make decoding slower, so a governor times
+ * speculative against plain steps at run time, parks drafting while it loses
+ * and re-probes with backoff; the governor paragraphs give the numbers).
+ * Host-only policy over the verify loop: before each step the caller asks
+ * spec_governor_should_draft (1: speculate, 0: plain step), runs the step and
+ * reports it with spec_governor_record.  A speculative step that drafted
+ * nothing is still recorded as speculative (a one-token sample).  States:
+ * baseline (plain steps measuring the plain cost), probe (speculative steps
+ * measured against it), hold (speculating after a win, re-checked on the
+ * last hold_window steps, baseline refreshed every hold_refresh steps),
+ * parked (plain steps only).  NULL params give the page's numbers. */
+typedef struct spec_governor spec_governor;
+typedef struct spec_governor_params {
+  int32_t probe_spec;       /* speculative steps of a full probe (8) */
+  int32_t probe_spec_short; /* of a re-probe after a loss (3) */
+  int32_t probe_plain;      /* plain steps measuring or refreshing the baseline (3) */
+  int32_t park_first;       /* first park, in steps (32); doubles per loss ... */
+  int32_t park_max;         /* ... up to this many (256) */
+  int32_t zero_accept_exit; /* this many speculative steps in a row accepting nothing end a probe (4) */
+  int32_t hold_window;      /* speculative steps averaged while a win holds (8) */
+  int32_t hold_refresh;     /* held steps between baseline refreshes (64) */
+} spec_governor_params;
+typedef struct spec_governor_stats {
+  int64_t wins, losses, probes;
+  int64_t spec_steps, plain_samples, parked_steps;
+  int32_t state;            /* 0 baseline, 1 probe, 2 hold, 3 parked */
+  double plain_ms_per_token, spec_ms_per_token;
+} spec_governor_stats;
+SPEC_API int spec_governor_create(const spec_governor_params* params, spec_governor** out);
+SPEC_API int spec_governor_destroy(spec_governor* g);
+/* 1: the next step speculates; 0: it is a plain step (K = 0). */
+SPEC_API int spec_governor_should_draft(spec_governor* g);
+/* Report the step just run: speculative (must match the decision), tokens
+ * committed (>= 1), drafts accepted, wall seconds of the whole step.
+ * ESTATE if the step did not follow the decision. */
+SPEC_API int spec_governor_record(spec_governor* g, int speculative, int committed, int accepted, double seconds);
+/* A new request shares the governor: what is left of a park is capped at the
+ * first park length and the backoff restarts there. */
+SPEC_API int spec_governor_new_request(spec_governor* g);
+SPEC_API int spec_governor_get_stats(spec_governor* g, spec_governor_stats* out);
+
 /* ------------------------------------------------------ generation loop */
 
 #define SPEC_DRAFT_NGRAM 0   /* n-gram proposer over prompt + committed tokens */
@@ -260,6 +317,7 @@ typedef struct spec_gen_params {
   int32_t n_min, n_max;
   int32_t draft_source;        /* SPEC_DRAFT_* */
   const int32_t* ref_stream;   /* [n_tokens] for SPEC_DRAFT_STREAM / WRONG */
+  int32_t governed;            /* 1: a cost governor (default numbers) decides which steps draft */
 } spec_gen_params;
 
 typedef struct spec_gen_stats {
@@ -269,6 +327,7 @@ typedef struct spec_gen_stats {
   double decode_s;  /* wall time from prefill return to the last token committed */
   double host_s;    /* part of decode_s spent outside spec_verify (proposer, bookkeeping) */
   double prefill_s;
+  int64_t plain_steps;  /* steps the governor ran plain (parked or measuring the baseline) */
 } spec_gen_stats;
 
 /* Greedy generation on sequence 0: prefill `prompt`, then commit n_tokens
@@ -289,6 +348,8 @@ SPEC_API int spec_gen_begin(spec_ctx* ctx, const int32_t* prompt, int n_prompt, 
                    const spec_gen_params* params, spec_gen** out);
 SPEC_API int spec_gen_step(spec_gen* gen, int rounds, spec_gen_stats* stats);
 SPEC_API int spec_gen_tokens(spec_gen* gen, int32_t* out, int cap);
+/* The governor's counters of a governed loop (EINVAL if not governed). */
+SPEC_API int spec_gen_governor_stats(spec_gen* gen, spec_governor_stats* out);
 SPEC_API int spec_gen_end(spec_gen* gen);
 
 #ifdef __cplusplus

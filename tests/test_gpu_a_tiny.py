@@ -186,3 +186,30 @@ def test_nan_row_leaves_the_cache_unchanged(weights):
         t.verify_checked([3, 4])
     finally:
         t.close()
+
+
+def test_governed_generation_parks_a_losing_drafter(weights):
+    """A governed loop over all-wrong drafts (every draft rejected, so each
+    speculative step costs a K=4 forward for one token) parks drafting after
+    four zero-accept steps and runs plain steps; with the motif prompt's own
+    n-gram drafts it keeps drafting.  Either way the committed stream equals
+    the spec-off stream token for token."""
+    t = Twin(SHAPE, weights, max_ctx=512)
+    try:
+        prompt = synth.motif_prompt(1, SHAPE["vocab"])
+        off, _ = specv.spec_generate(t.ctx, prompt, 200, spec=False)
+        g = specv.spec_gen_handle(t.ctx, prompt, 200, spec=True, fixed_k=4, draft_source=specv.SPEC_DRAFT_WRONG,
+                                  ref_stream=off, governed=True)
+        g.step(1000)
+        wrong = g.tokens()
+        gs, st = g.governor_stats(), g.stats()
+        g.close()
+        assert np.array_equal(off, wrong)
+        assert gs["losses"] >= 1 and gs["wins"] == 0 and st["plain_steps"] > 100
+        assert st["accepted"] == 0
+        on, st_on = specv.spec_generate(t.ctx, prompt, 200, spec=True, fixed_k=4, governed=True)
+        assert np.array_equal(off, on)
+        log(f"  governed: wrong drafts {st['forwards']} forwards ({st['plain_steps']} plain, governor {gs}); "
+            f"n-gram drafts {st_on['forwards']} forwards ({st_on['plain_steps']} plain)")
+    finally:
+        t.close()
