@@ -16,6 +16,7 @@
 #include <map>
 #include <new>
 #include <string>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -236,13 +237,24 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.q = take(R * Lo.DQ * 4);
   Lo.o = take(R * Lo.DQ * 4);
   Lo.h = take(R * Lo.F * 4);
+  // Split partial sums, for the GEMMs that run the split-K kernel at some row
+  // count up to max_rows (above the row limit of their one-pass kernel).
+  auto onepass_rows = [&](const MmPlan& m, int K, int nk) {
+    if (m.nw) return std::min(m.rmax, 16);
+    if (Lo.fmt == FMT_INT4 && mmq_supported(K, nk)) return 4;
+    return 0;
+  };
+  const int lim_d = Lo.d_lds ? SPECV_DOWN_MM1_ROWS : onepass_rows(Lo.mm_d, Lo.F, Lo.nk_d);
   size_t part = 0;
-  part = std::max(part, (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
-  part = std::max(part, (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
-  part = std::max(part, (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
-  part = std::max(part, (size_t)(Lo.F / (Lo.nk_d * 32)) * Lo.H);
-  part = std::max(part, (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
-  Lo.part = take(part * R * 4);
+  auto need = [&](int lim, size_t floats) {
+    if (Lo.max_rows > lim) part = std::max(part, floats);
+  };
+  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv), (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
+  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o), (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
+  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu), (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
+  need(lim_d, (size_t)(Lo.F / (Lo.nk_d * 32)) * Lo.H);
+  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm), (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
+  Lo.part = take(std::max(part * R * 4, (size_t)256));
   Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
   Lo.cnt = take((size_t)Lo.cnt_n * 4);
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
@@ -293,6 +305,7 @@ struct spec_ctx {
   int attn_fuse = 0;     // the current step's contexts are short: attention combines in one kernel
   int attn_tpw = 1;      // the current step's query tiles per attention workgroup
   hipEvent_t ev0 = nullptr, ev1 = nullptr;  // verify forward timing (spec_get_stats)
+  int static_dev = -1;   // spec_create_static: the device whose scratch is the workspace
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
@@ -708,18 +721,31 @@ int spec_query_buffers(const spec_model_desc* desc, spec_buffer_sizes* out) {
 
 const char* spec_last_error(const spec_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
 
-int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void* hip_stream, spec_ctx** out) {
+}  // extern "C"
+
+namespace {
+
+// no_alloc: the context of spec_create_static -- eager launches (no graph
+// objects) and no timing events, so that nothing beyond host memory is
+// allocated.
+int create_impl(const spec_model_desc* desc, const spec_device_buffers* b, void* hip_stream, spec_ctx** out,
+                bool no_alloc) {
   if (!desc || !b || !out) {
     g_create_error = "null argument";
     return SPEC_EINVAL;
   }
   *out = nullptr;
+  if (desc->flags & ~(SPEC_FLAG_KEEP_LOGITS | SPEC_FLAG_NO_GRAPH)) {
+    g_create_error = "unknown flag bits";
+    return SPEC_EINVAL;
+  }
   spec_ctx* c = new (std::nothrow) spec_ctx;
   if (!c) {
     g_create_error = "out of host memory";
     return SPEC_ECAPACITY;
   }
   c->d = *desc;
+  if (no_alloc) c->d.flags |= SPEC_FLAG_NO_GRAPH;
   if (!build_layout(*desc, c->lo, g_create_error)) {
     delete c;
     return SPEC_EINVAL;
@@ -784,7 +810,7 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
     }
     c->mm_grid = cus * SPECV_MM_WG_PER_CU;  // one resident workgroup per CU walks the blocks
   }
-  if (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess) {
+  if (!no_alloc && (hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess)) {
     g_create_error = "cannot create the forward timing events";
     if (c->ev0) (void)hipEventDestroy(c->ev0);
     delete c;
@@ -794,8 +820,90 @@ int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void*
   return SPEC_OK;
 }
 
+}  // namespace
+
+// Scratch of the allocation-free entry point: the workspace of the one live
+// static context per GPU, in the library's own device memory (each GPU the
+// library runs on holds its copy until the process ends).  Host code never
+// uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, at the device's first
+// spec_create_static.
+static __device__ __align__(256) uint8_t scratch[SPEC_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+struct StaticSlot {
+  void* ptr = nullptr;      // this device's copy of `scratch`
+  spec_ctx* owner = nullptr;  // the live static context on this device, if any
+};
+std::mutex g_static_mu;
+std::vector<StaticSlot> g_static;  // by device ordinal
+
+}  // namespace
+
+extern "C" {
+
+int spec_create(const spec_model_desc* desc, const spec_device_buffers* b, void* hip_stream, spec_ctx** out) {
+  return create_impl(desc, b, hip_stream, out, false);
+}
+
+int spec_create_static(const spec_model_desc* desc, const spec_device_buffers* bufs, void* hip_stream,
+                       spec_ctx** out) {
+  if (!desc || !bufs || !out) {
+    g_create_error = "null argument";
+    return SPEC_EINVAL;
+  }
+  *out = nullptr;
+  if (bufs->workspace || bufs->workspace_bytes) {
+    g_create_error = "spec_create_static takes no workspace: the library's static scratch is the workspace";
+    return SPEC_EINVAL;
+  }
+  Layout L;
+  if (!build_layout(*desc, L, g_create_error)) return SPEC_EINVAL;
+  if (L.workspace_bytes > (size_t)SPEC_STATIC_SCRATCH_BYTES) {
+    g_create_error = "this description needs " + std::to_string(L.workspace_bytes) +
+                     " bytes of workspace, more than the static scratch of " +
+                     std::to_string((size_t)SPEC_STATIC_SCRATCH_BYTES) + " bytes";
+    return SPEC_ECAPACITY;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_create_error = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return SPEC_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if ((size_t)dev >= g_static.size()) g_static.resize((size_t)dev + 1);
+  StaticSlot& slot = g_static[(size_t)dev];
+  if (!slot.ptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_create_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return SPEC_EHIP;
+    }
+    slot.ptr = ptr;
+  }
+  if (slot.owner) {
+    g_create_error = "a static context already lives on this device (they share its scratch)";
+    return SPEC_ESTATE;
+  }
+  spec_device_buffers b = *bufs;
+  b.workspace = slot.ptr;
+  b.workspace_bytes = (size_t)SPEC_STATIC_SCRATCH_BYTES;
+  const int rc = create_impl(desc, &b, hip_stream, out, true);
+  if (rc != SPEC_OK) return rc;
+  (*out)->static_dev = dev;
+  slot.owner = *out;
+  return SPEC_OK;
+}
+
 int spec_destroy(spec_ctx* c) {
   if (!c) return SPEC_EINVAL;
+  if (c->static_dev >= 0) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    g_static[(size_t)c->static_dev].owner = nullptr;
+  }
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
   if (c->ev0) (void)hipEventDestroy(c->ev0);
   if (c->ev1) (void)hipEventDestroy(c->ev1);

@@ -21,6 +21,7 @@ SPEC_OK, SPEC_EINVAL, SPEC_ECAPACITY, SPEC_ESTATE, SPEC_EHIP, SPEC_ENAN = 0, -1,
 SPEC_WFMT_BF16, SPEC_WFMT_INT4G128 = 0, 1
 SPEC_FLAG_KEEP_LOGITS, SPEC_FLAG_NO_GRAPH = 1, 2
 SPEC_MAX_SPAN, SPEC_MAX_ROWS, SPEC_BLOCK_TOKENS = 16, 128, 16
+SPEC_STATIC_SCRATCH_BYTES = 32 << 20
 (SPEC_MAT_Q, SPEC_MAT_K, SPEC_MAT_V, SPEC_MAT_O, SPEC_MAT_GATE, SPEC_MAT_UP, SPEC_MAT_DOWN,
  SPEC_MAT_EMB, SPEC_MAT_LM) = range(9)
 SPEC_NORM_ATTN, SPEC_NORM_FFN, SPEC_NORM_FINAL = 0, 1, 2
@@ -107,6 +108,7 @@ def lib():
     sig = {
         "spec_query_buffers": [C.POINTER(spec_model_desc), C.POINTER(spec_buffer_sizes)],
         "spec_create": [C.POINTER(spec_model_desc), C.POINTER(spec_device_buffers), P, C.POINTER(P)],
+        "spec_create_static": [C.POINTER(spec_model_desc), C.POINTER(spec_device_buffers), P, C.POINTER(P)],
         "spec_destroy": [P],
         "spec_load_matrix": [P, I, I, P, P],
         "spec_load_norm": [P, I, I, P],
@@ -187,6 +189,12 @@ def spec_query_buffers(desc):
 def spec_create(desc, bufs, stream_ptr):
     h = C.c_void_p()
     _check(lib().spec_create(C.byref(desc), C.byref(bufs), C.c_void_p(stream_ptr), C.byref(h)))
+    return h.value
+
+
+def spec_create_static(desc, bufs, stream_ptr):
+    h = C.c_void_p()
+    _check(lib().spec_create_static(C.byref(desc), C.byref(bufs), C.c_void_p(stream_ptr), C.byref(h)))
     return h.value
 
 
@@ -472,7 +480,9 @@ class Session:
     wq..wd, g_attn, g_ffn) or "global" (emb, lm, g_final)."""
 
     def __init__(self, shape: dict, weights, max_ctx: int, max_seqs: int = 1, max_rows: int = 16,
-                 n_blocks: int = 0, flags: int = 0, device: int = 0, fmt: str = "bf16"):
+                 n_blocks: int = 0, flags: int = 0, device: int = 0, fmt: str = "bf16", static: bool = False):
+        """static: the context of spec_create_static (no workspace allocated:
+        the library's static scratch serves as the workspace)."""
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("libspecv needs an MI355X (gfx950) GPU; none is visible")
@@ -486,14 +496,15 @@ class Session:
         u8 = torch.uint8
         self.w_buf = torch.empty(sz.weights_bytes, dtype=u8, device=self.dev)
         self.kv_buf = torch.empty(sz.kv_bytes, dtype=u8, device=self.dev)
-        self.ws_buf = torch.empty(sz.workspace_bytes, dtype=u8, device=self.dev)
+        self.ws_buf = None if static else torch.empty(sz.workspace_bytes, dtype=u8, device=self.dev)
         self.host_buf = torch.empty(sz.host_bytes, dtype=u8, pin_memory=True)
         self.stream = torch.cuda.Stream(device=self.dev)  # default priority
         bufs = spec_device_buffers(self.w_buf.data_ptr(), sz.weights_bytes, self.kv_buf.data_ptr(),
-                                   sz.kv_bytes, self.ws_buf.data_ptr(), sz.workspace_bytes,
-                                   self.host_buf.data_ptr(), sz.host_bytes)
+                                   sz.kv_bytes, None if static else self.ws_buf.data_ptr(),
+                                   0 if static else sz.workspace_bytes, self.host_buf.data_ptr(), sz.host_bytes)
         torch.cuda.synchronize(self.dev)
-        self.ctx = spec_create(self.desc, bufs, self.stream.cuda_stream)
+        create = spec_create_static if static else spec_create
+        self.ctx = create(self.desc, bufs, self.stream.cuda_stream)
         self._load(weights)
 
     def _load_matrix(self, layer, which, t):

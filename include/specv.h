@@ -115,6 +115,22 @@ SPEC_API int spec_query_buffers(const spec_model_desc* desc, spec_buffer_sizes* 
  * with spec_load_matrix / spec_load_norm. */
 SPEC_API int spec_create(const spec_model_desc* desc, const spec_device_buffers* bufs, void* hip_stream,
                 spec_ctx** out);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * context with the library's own static scratch, SPEC_STATIC_SCRATCH_BYTES
+ * per GPU (held until the process ends), as its workspace.  bufs carries the
+ * weights, the KV pool and the pinned host staging as for spec_create; its
+ * workspace must be NULL with size 0.  The context launches its kernels
+ * eagerly (no HIP graph objects) and keeps no timing events, so no call on it
+ * allocates device memory; spec_get_stats leaves forward_ms_by_span at zero.
+ * One static context per GPU at a time: a second spec_create_static on the
+ * same device fails with ESTATE until the first is destroyed (calls on two
+ * would race on the one scratch).  ECAPACITY when the description needs more
+ * workspace than the scratch holds (spec_query_buffers gives the need);
+ * EHIP if the scratch's device address cannot be obtained. */
+#define SPEC_STATIC_SCRATCH_BYTES (32u << 20)
+SPEC_API int spec_create_static(const spec_model_desc* desc, const spec_device_buffers* bufs, void* hip_stream,
+                                spec_ctx** out);
 SPEC_API int spec_destroy(spec_ctx* ctx);
 SPEC_API const char* spec_last_error(const spec_ctx* ctx);
 

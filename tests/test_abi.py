@@ -88,3 +88,21 @@ def test_create_without_buffers_fails_cleanly():
     with pytest.raises(specv.SpecError) as e:
         specv.spec_create(d, bufs, 0)
     assert e.value.code in (specv.SPEC_ECAPACITY, specv.SPEC_EINVAL)
+
+
+def test_static_create_checks_before_touching_the_device():
+    """spec_create_static refuses a workspace (the static scratch is the
+    workspace) and a description that needs more workspace than the scratch
+    holds, before any device call; the 4B shape at up to 16 rows fits."""
+    sh = synth.SHAPES["qwen3_4b"]
+    big = specv.make_desc(sh, max_ctx=4200, max_seqs=16, max_rows=128)
+    assert specv.spec_query_buffers(big).workspace_bytes > specv.SPEC_STATIC_SCRATCH_BYTES
+    with pytest.raises(specv.SpecError) as e:
+        specv.spec_create_static(big, specv.spec_device_buffers(), 0)
+    assert e.value.code == specv.SPEC_ECAPACITY
+    small = specv.make_desc(sh, max_ctx=1024, max_rows=16, flags=specv.SPEC_FLAG_KEEP_LOGITS)
+    assert specv.spec_query_buffers(small).workspace_bytes <= specv.SPEC_STATIC_SCRATCH_BYTES
+    bufs = specv.spec_device_buffers(None, 0, None, 0, 4096, 4096, None, 0)
+    with pytest.raises(specv.SpecError) as e:
+        specv.spec_create_static(small, bufs, 0)
+    assert e.value.code == specv.SPEC_EINVAL
