@@ -29,6 +29,10 @@
  *     off a match of two or more tokens), written as a brute-force search.
  *   - Adaptive K: start at 1, add 2 after a fully accepted round, subtract 1
  *     after any rejection, clamp to [1, cap] (coreai note, adaptive-K section).
+ *   - Sampled verification: each row draws its token (Gumbel-max over the
+ *     logits divided by the temperature, with Philox4x32-10 noise keyed by the
+ *     seed, the sequence and the row's position) and drafts are accepted while
+ *     the drawn token matches (TensorSharp page, protocol section).
  *
  * Row invariance: every dot product below is summed in one fixed sequential
  * order over its reduction index, whatever other rows share the call, so a
@@ -474,6 +478,135 @@ ORC_API int orc_verify(orc_model* m, int seq, const int32_t* span, int K, int32_
   m->len[seq] = p + mm + 1;
 #endif
   return ORC_OK;
+}
+
+/* ------------------------------------------------------- sampled verify */
+
+/* Sampled verification (TensorSharp speculative decoding page, protocol
+ * section, the verify step: the sampler draws a token from every row and
+ * drafts are accepted while the drawn token matches; the draw of the first
+ * mismatching row is the corrected token).  A row draws from softmax(logit/T)
+ * by the Gumbel-max rule: the token is argmax_v (logit_v / T + g_v) with
+ * g_v = -log(-log u_v) and u_v uniform in (0, 1).  The uniforms come from
+ * the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011) keyed by the seed,
+ * with the counter (v / 4, t, seq, 0) for the row at absolute position t of
+ * sequence seq and output word v % 4: a position's draw depends on the seed,
+ * the sequence and the position only, so a draft-free decode of the same
+ * prefix draws exactly the same token. */
+
+/* One Philox4x32-10 block: ten rounds of the two 32x32->64-bit products with
+ * multipliers 0xD2511F53 and 0xCD9E8D57, the key bumped by the Weyl
+ * constants 0x9E3779B9 and 0xBB67AE85 between rounds. */
+ORC_API void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+#if ORC_PLANT == 13
+    c0 = hi1 ^ c1 ^ k1;
+#else
+    c0 = hi1 ^ c1 ^ k0;
+#endif
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* A 32-bit word as a uniform in (0, 1): the top 23 bits plus one half, times
+ * 2^-23 (exact in fp32, never 0 or 1). */
+ORC_API float orc_uniform01(uint32_t x) { return ((float)(x >> 9) + 0.5f) * (1.0f / 8388608.0f); }
+
+/* g = -log(-log u). */
+ORC_API float orc_gumbel(float u) { return -logf(-logf(u)); }
+
+ORC_API float orc_gumbel_noise(uint64_t seed, int seq, int t, int v) {
+  const uint32_t ctr[4] = {(uint32_t)v >> 2, (uint32_t)t, (uint32_t)seq, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return orc_gumbel(orc_uniform01(out[v & 3]));
+}
+
+/* The token drawn from one row of logits at temperature temp > 0 for the
+ * row at position t of sequence seq: the largest logit_v / temp + g_v,
+ * lowest index on ties; margin = the two largest scores' difference.  -1 on
+ * a NaN logit. */
+ORC_API int orc_sample_row(const float* logits, int V, float temp, uint64_t seed, int seq, int t, float* margin) {
+  int best = -1;
+  float b1 = -INFINITY, b2 = -INFINITY;
+  for (int v = 0; v < V; ++v) {
+    if (logits[v] != logits[v]) return -1;
+#if ORC_PLANT == 14
+    const float sc = logits[v] * temp + orc_gumbel_noise(seed, seq, t, v);
+#else
+    const float sc = logits[v] / temp + orc_gumbel_noise(seed, seq, t, v);
+#endif
+    if (best < 0 || sc > b1) {
+      if (best >= 0) b2 = b1;
+      b1 = sc;
+      best = v;
+    } else if (sc > b2) {
+      b2 = sc;
+    }
+  }
+  if (margin) *margin = V > 1 ? b1 - b2 : INFINITY;
+  return best;
+}
+
+/* Sampled verify of span = [last, d1..dK] at p = cache length: forward K+1
+ * rows, draw s_i from row i (position p + i), accept while d(i+1) == s_i,
+ * leave the cache at p + m + 1.  The committed tokens are s_0..s_m.
+ * temp > 0; tokens_out [K+1], margin_out [K+1] (score margins), logits_out
+ * [K+1][V] or NULL. */
+ORC_API int orc_verify_sampled(orc_model* m, int seq, const int32_t* span, int K, float temp, uint64_t seed,
+                               int32_t* tokens_out, int32_t* accept_out, float* logits_out, float* margin_out) {
+  if (!m || !span || !tokens_out || !accept_out || K < 0 || seq < 0 || seq >= m->n_seq || !(temp > 0.0f))
+    return ORC_EINVAL;
+  const int p = m->len[seq], V = m->s.vocab;
+  float* L = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)(K + 1) * V);
+  if (!L) return ORC_ENOMEM;
+  int rc = orc_forward(m, seq, span, K + 1, 0, L, NULL, NULL);
+  for (int i = 0; rc == ORC_OK && i <= K; ++i) {
+    float mg = 0.0f;
+    tokens_out[i] = orc_sample_row(L + (size_t)i * V, V, temp, seed, seq, p + i, &mg);
+    if (tokens_out[i] < 0) rc = ORC_ENAN;
+    if (margin_out) margin_out[i] = mg;
+  }
+  if (!logits_out) free(L);
+  if (rc != ORC_OK) {
+    m->len[seq] = p;
+    return rc;
+  }
+  const int mm = orc_accept_greedy(span, tokens_out, K);  /* the same prefix rule on the drawn tokens */
+  *accept_out = mm;
+  m->len[seq] = p + mm + 1;
+  return ORC_OK;
+}
+
+/* Sampled prefill: the prompt's rows, then g0 drawn from the last row (its
+ * position n - 1) at temperature temp. */
+ORC_API int orc_prefill_sampled(orc_model* m, int seq, const int32_t* toks, int n, float temp, uint64_t seed,
+                                int32_t* g0, float* margin) {
+  if (!m || !toks || !g0 || seq < 0 || seq >= m->n_seq || n <= 0 || !(temp > 0.0f)) return ORC_EINVAL;
+  float* L = (float*)malloc(sizeof(float) * (size_t)m->s.vocab);
+  if (!L) return ORC_ENOMEM;
+  m->len[seq] = 0;
+  int rc = orc_forward(m, seq, toks, n, n - 1, L, NULL, NULL);
+  if (rc == ORC_OK) {
+    *g0 = orc_sample_row(L, m->s.vocab, temp, seed, seq, n - 1, margin);
+    if (*g0 < 0) rc = ORC_ENAN;
+  }
+  free(L);
+  return rc;
 }
 
 /* ---------------------------------------------------------------- proposer */

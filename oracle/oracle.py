@@ -78,6 +78,18 @@ def load_lib(path: str = DEFAULT_LIB):
     lib.orc_silu.restype = F
     lib.orc_argmax.argtypes = [f32p, I, f32p]
     lib.orc_matvec.argtypes = [I, I, I, P, P, f32p, I, f32p]
+    u32p, u64 = C.POINTER(C.c_uint32), C.c_uint64
+    lib.orc_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.orc_philox4x32_10.restype = None
+    lib.orc_uniform01.argtypes = [C.c_uint32]
+    lib.orc_uniform01.restype = F
+    lib.orc_gumbel.argtypes = [F]
+    lib.orc_gumbel.restype = F
+    lib.orc_gumbel_noise.argtypes = [u64, I, I, I]
+    lib.orc_gumbel_noise.restype = F
+    lib.orc_sample_row.argtypes = [f32p, I, F, u64, I, I, f32p]
+    lib.orc_verify_sampled.argtypes = [P, I, i32p, I, F, u64, i32p, i32p, f32p, f32p]
+    lib.orc_prefill_sampled.argtypes = [P, I, i32p, I, F, u64, i32p, f32p]
     lib.orc_plant.restype = I
     _LIBS[path] = lib
     return lib
@@ -169,6 +181,39 @@ def matvec(mat, X, lib=None):
     return Y
 
 
+def philox4x32_10(ctr, key, lib=None):
+    lib = lib or load_lib()
+    c = (C.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (C.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (C.c_uint32 * 4)()
+    lib.orc_philox4x32_10(c, k, out)
+    return [int(x) for x in out]
+
+
+def uniform01(x, lib=None):
+    return float((lib or load_lib()).orc_uniform01(int(x) & 0xFFFFFFFF))
+
+
+def gumbel(u, lib=None):
+    return float((lib or load_lib()).orc_gumbel(float(u)))
+
+
+def gumbel_noise(seed, seq, t, v, lib=None):
+    return float((lib or load_lib()).orc_gumbel_noise(int(seed), seq, t, v))
+
+
+def sample_row(logits, temp, seed, seq, t, lib=None):
+    """The token drawn from one row of logits (Gumbel-max at temperature
+    temp, Philox noise of (seed, seq, position t)) and the score margin."""
+    lib = lib or load_lib()
+    v, vp = _f32(logits)
+    m = C.c_float(0.0)
+    a = lib.orc_sample_row(vp, len(v), float(temp), int(seed), seq, t, C.byref(m))
+    if a < 0:
+        raise OracleError("sampling a row holding NaN")
+    return int(a), float(m.value)
+
+
 def silu(x, lib=None):
     lib = lib or load_lib()
     return float(lib.orc_silu(float(x)))
@@ -258,14 +303,22 @@ class Oracle:
         _check(self.lib.orc_forward(self.h, seq, tp, n, lm_from, lgp, ap, mp), "forward")
         return am[:nl].copy(), mg[:nl].copy(), lg
 
-    def prefill(self, toks, seq=0):
+    def prefill(self, toks, seq=0, temp=0.0, seed=0):
+        """g0 = the argmax of the last prompt row, or (temp > 0) the token
+        drawn from it."""
         t, tp = _i32(toks)
         g, gp = _i32(np.zeros(1, np.int32))
         mg, mp = _f32(np.zeros(1, np.float32))
-        _check(self.lib.orc_prefill(self.h, seq, tp, len(t), gp, mp), "prefill")
+        if temp > 0:
+            _check(self.lib.orc_prefill_sampled(self.h, seq, tp, len(t), float(temp), int(seed), gp, mp),
+                   "prefill_sampled")
+        else:
+            _check(self.lib.orc_prefill(self.h, seq, tp, len(t), gp, mp), "prefill")
         return int(g[0]), float(mg[0])
 
-    def verify(self, span, seq=0, want_logits=False):
+    def verify(self, span, seq=0, want_logits=False, temp=0.0, seed=0):
+        """Greedy verify (argmax rows), or sampled (temp > 0: drawn rows).
+        Returns (tokens per row, accept length, margins, logits or None)."""
         s, sp = _i32(span)
         K = len(s) - 1
         am, ap = _i32(np.zeros(K + 1, np.int32))
@@ -273,12 +326,16 @@ class Oracle:
         mg, mp = _f32(np.zeros(K + 1, np.float32))
         lg = np.zeros((K + 1, self.shape["vocab"]), np.float32) if want_logits else None
         lgp = lg.ctypes.data_as(C.POINTER(C.c_float)) if want_logits else None
-        _check(self.lib.orc_verify(self.h, seq, sp, K, ap, accp, lgp, mp), "verify")
+        if temp > 0:
+            _check(self.lib.orc_verify_sampled(self.h, seq, sp, K, float(temp), int(seed), ap, accp, lgp, mp),
+                   "verify_sampled")
+        else:
+            _check(self.lib.orc_verify(self.h, seq, sp, K, ap, accp, lgp, mp), "verify")
         return am.copy(), int(acc[0]), mg.copy(), lg
 
     # -- generation loop --------------------------------------------------
     def generate(self, prompt, n_tokens, spec=False, fixed_k=None, k_cap=7, n_min=2, n_max=4,
-                 seq=0, drafts_fn=None):
+                 seq=0, drafts_fn=None, temp=0.0, seed=0):
         """Greedy generation of n_tokens tokens counted from g0.
 
         spec=False: one plain step (K=0) per token.  spec=True: propose with the
@@ -288,7 +345,7 @@ class Oracle:
         drafts past the budget; should it commit past it anyway, the commit is
         truncated and the cache rewound to match.
         Returns (tokens, stats)."""
-        g0, _ = self.prefill(prompt, seq)
+        g0, _ = self.prefill(prompt, seq, temp=temp, seed=seed)
         hist = [int(t) for t in prompt] + [g0]
         out = [g0]
         k = fixed_k if fixed_k is not None else 1
@@ -300,7 +357,7 @@ class Oracle:
                 drafts = drafts_fn(hist, kk) if drafts_fn else ngram_propose(hist, n_min, n_max, kk, self.lib)
             span = [hist[-1]] + list(drafts)
             p = self.cache_len(seq)
-            am, m, _, _ = self.verify(span, seq)
+            am, m, _, _ = self.verify(span, seq, temp=temp, seed=seed)
             stats["forwards"] += 1
             stats["drafted"] += len(drafts)
             stats["accepted"] += m

@@ -265,7 +265,94 @@ def pin_multiseq(lib=None):
     assert ga == ga2 and gb == gb2 and np.array_equal(la, lb)
 
 
+def pin_philox_kat(lib=None):
+    """The counter-based generator against its published known-answer vectors."""
+    L = O.load_lib(lib or O.DEFAULT_LIB)
+    for c in _golden("philox_kat.json")["cases"]:
+        got = O.philox4x32_10([int(x, 16) for x in c["ctr"]], [int(x, 16) for x in c["key"]], L)
+        want = [int(x, 16) for x in c["out"]]
+        assert got == want, f"Philox4x32-10 {c['ctr']} / {c['key']}: {[hex(x) for x in got]}"
+
+
+def pin_uniform_gumbel_closed_forms(lib=None):
+    L = O.load_lib(lib or O.DEFAULT_LIB)
+    assert O.uniform01(0, L) == 2.0 ** -24 and O.uniform01(0xFFFFFFFF, L) == 1.0 - 2.0 ** -24
+    assert O.uniform01(1 << 31, L) == 0.5 + 2.0 ** -24
+    assert abs(O.gumbel(float(np.float32(np.exp(-1.0))), L)) < 1e-6  # -log(-log(1/e)) = 0
+    u = np.float32(0.9)
+    assert abs(O.gumbel(float(u), L) - (-np.log(-np.log(np.float64(u))))) < 1e-6
+    assert O.gumbel(0.1, L) < O.gumbel(0.5, L) < O.gumbel(0.9, L)
+
+
+def pin_gumbel_max_is_softmax(lib=None):
+    """Drawing argmax(logit / T + g) over many positions reproduces the
+    softmax(logit / T) distribution (the Gumbel-max rule), for two
+    temperatures: chi-square over 5 tokens and 30000 draws each."""
+    L = O.load_lib(lib or O.DEFAULT_LIB)
+    logits = np.array([1.0, 0.5, -0.3, 2.0, 0.0], np.float32)
+    n = 30000
+    for T, seed in ((0.7, 12345), (1.6, 999)):
+        counts = np.zeros(5)
+        for t in range(n):
+            counts[O.sample_row(logits, T, seed, 0, t, L)[0]] += 1
+        p = np.exp(logits.astype(np.float64) / T)
+        p /= p.sum()
+        chi2 = float(((counts - n * p) ** 2 / (n * p)).sum())
+        assert chi2 < 25.0, f"T={T}: draws do not follow softmax(logit/T) (chi2 {chi2:.1f}, counts {counts})"
+
+
+def pin_sampled_low_temperature_is_greedy(lib=None):
+    """At a tiny temperature the draw is the argmax wherever the row's top-2
+    margin is not itself tiny."""
+    shape = synth.SHAPES["tiny"]
+    _, orc = _model(shape, lib=lib)
+    prompt = synth.motif_prompt(1, shape["vocab"])
+    orc.prefill(prompt)
+    span = [int(x) for x in synth.uniform_prompt(8, shape["vocab"], 8)]
+    p = orc.cache_len()
+    am, _, mg, lg = orc.verify(span, want_logits=True)
+    orc.rewind(p)
+    sm, _, _, lg2 = orc.verify(span, want_logits=True, temp=1e-5, seed=3)
+    assert np.array_equal(lg, lg2)
+    sure = mg > 1e-3
+    assert sure.sum() >= 4 and np.array_equal(am[sure], sm[sure]), "T -> 0 draws must be the argmax"
+
+
+def pin_sampled_planted_and_spec_equals_off(lib=None):
+    """Sampled verification: drafts taken from the sampled plain stream and
+    corrupted at j accept exactly j (the cache grows by m + 1), and a sampled
+    speculative stream (n-gram drafts, fixed and adaptive K) equals the
+    sampled plain stream token for token, because every position's draw
+    depends only on (seed, sequence, position)."""
+    shape = synth.SHAPES["tiny"]
+    V = shape["vocab"]
+    _, orc = _model(shape, gains=False, lib=lib)
+    prompt = synth.motif_prompt(1, V)
+    T, seed = 0.8, 7
+    off, _ = orc.generate(prompt, 48, spec=False, temp=T, seed=seed)
+    greedy, _ = orc.generate(prompt, 48, spec=False)
+    assert off != greedy, "sampling at T = 0.8 should leave the greedy stream"
+    fix, s1 = orc.generate(prompt, 48, spec=True, fixed_k=4, temp=T, seed=seed)
+    ada, _ = orc.generate(prompt, 48, spec=True, temp=T, seed=seed)
+    assert off == fix == ada, "sampled spec-on stream differs from the sampled plain stream"
+    other, _ = orc.generate(prompt, 48, spec=False, temp=T, seed=seed + 1)
+    assert other != off, "the seed must change the draws"
+    K = 5
+    for j in range(K + 1):
+        g0, _ = orc.prefill(prompt, temp=T, seed=seed)
+        assert g0 == off[0]
+        drafts = list(off[1:K + 1])
+        if j < K:
+            drafts[j] = (drafts[j] + 1) % V
+        p = orc.cache_len()
+        tk, m, _, _ = orc.verify([g0] + drafts, temp=T, seed=seed)
+        assert m == j, f"sampled planted mismatch at {j}: accepted {m}"
+        assert list(tk[: m + 1]) == list(off[1:m + 2])
+        assert orc.cache_len() == p + m + 1
+
+
 ALL_PINS = [pin_torch_tiny, pin_torch_wide, pin_torch_int4, pin_closed_forms, pin_argmax,
             pin_rows_gate, pin_accept_golden, pin_verify_planted, pin_rewind_stale,
             pin_spec_equals_off, pin_ngram_golden, pin_adapt_k_golden, pin_int4_nibbles,
-            pin_multiseq]
+            pin_multiseq, pin_philox_kat, pin_uniform_gumbel_closed_forms, pin_gumbel_max_is_softmax,
+            pin_sampled_low_temperature_is_greedy, pin_sampled_planted_and_spec_equals_off]

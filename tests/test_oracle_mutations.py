@@ -19,6 +19,8 @@ PLANTS = {
     10: "argmax ties go to the highest index",
     11: "RoPE uses the row index instead of the position",
     12: "K rows of a span all written at the first position",
+    13: "Philox round mixes the second key word into the first output word",
+    14: "sampling multiplies the logits by the temperature instead of dividing",
 }
 
 
