@@ -22,6 +22,9 @@ struct StepDev {
   int32_t n_seq;
   int32_t span;      // rows per sequence (S)
   int32_t pad;
+  float temp;        // 0: greedy (argmax rows); > 0: every row draws its token at this temperature
+  uint32_t seed_lo, seed_hi;  // the draws' seed (Philox key)
+  int32_t pad2;
   // followed by tokens[max_rows], seq_ids[max_rows] and kd[max_rows] (the
   // drafts each sequence really proposed; its span rows past 1 + kd are padding)
 };
@@ -87,6 +90,7 @@ struct GemmParams {
   const int32_t* tokens;      // [R] span tokens
   const int32_t* kd;          // [n_seq] drafts per sequence (rows past 1 + kd[b] are padding)
   const int32_t* mode;        // StepDev::mode
+  const StepDev* step;        // the step block: sampling temperature and seed
   int32_t* result;            // [1 + n_seq*(S+1)]: status, then (m, a0..a(S-1)) per sequence
   int32_t* kv_len_w;          // cache lengths, advanced by the accept stage
   int n_seq;
@@ -171,6 +175,9 @@ hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, 
 hipError_t launch_pack_int4(const uint8_t* q4, const uint16_t* scales, int rows, int cols, void* dst_frag,
                             uint16_t* dst_scales, int kind, int row0, int hd, hipStream_t st);
 hipError_t launch_fill_u32(void* dst, uint32_t value, size_t count, hipStream_t st);
+// Stream `bytes` (a multiple of 16) from src with non-temporal 16-byte loads
+// over `grid` workgroups; sink: 256 words of device scratch.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 // Row of the fused QKV matrix holding source row s of a Q or K projection:
 // the pair (d, d + hd/2) of a head lands on adjacent rows (2d, 2d+1).

@@ -664,11 +664,67 @@ __device__ void epi_swiglu(const GemmParams& P, int nb) {
   });
 }
 
-// One logit (row r, column c): optional copy-out, NaN flag, argmax key.
-__device__ __forceinline__ unsigned long long lm_value(const GemmParams& P, int r, int c, float v) {
-  if (P.logits) P.logits[(size_t)r * P.N + c] = v;
-  if (v != v) atomicOr(P.status, 1);
-  return argmax_key(v, c);
+// Sampled rows (step temperature > 0): a row draws its token from
+// softmax(logit / T) as argmax_v (logit_v / T + g_v), g_v = -log(-log u_v)
+// (the Gumbel-max rule), so the accept stage's argmax machinery serves both
+// modes.  u_v comes from Philox4x32-10 (Salmon et al., SC 2011: ten rounds of
+// two 32 x 32 -> 64-bit products, multipliers 0xD2511F53 and 0xCD9E8D57, key
+// advanced by 0x9E3779B9 and 0xBB67AE85) with key = the seed and counter =
+// (v / 4, the row's position, the sequence id, 0), word v % 4: a draw depends
+// on (seed, sequence, position, v) alone, so a plain decode of the same
+// prefix draws the same token.  u = (top 23 bits + 1/2) * 2^-23.
+struct Sampling {
+  float temp;
+  uint32_t k0, k1;
+};
+
+__device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                          uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return (u32x4){c0, c1, c2, c3};
+}
+
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+#pragma clang fp contract(off)
+  const float u = ((float)(x >> 9) + 0.5f) * (1.0f / 8388608.0f);
+  return -logf(-logf(u));
+}
+
+// The keys of the pair (c, c + 1), c even, of row r: argmax keys of the
+// logits (greedy) or of the sampled scores.  pos: the row's position.
+__device__ __forceinline__ void lm_pair_keys(const GemmParams& P, const Sampling& sm, int r, int c, float v0,
+                                             float v1, int pos, unsigned long long& k0, unsigned long long& k1) {
+#pragma clang fp contract(off)
+  if (P.logits) *(float2*)(P.logits + (size_t)r * P.N + c) = make_float2(v0, v1);
+  if (v0 != v0 || v1 != v1) atomicOr(P.status, 1);
+  if (sm.temp > 0.0f) {
+    const int seq = P.seq_ids[r / P.S];
+    const u32x4 w = philox10((uint32_t)c >> 2, (uint32_t)pos, (uint32_t)seq, 0u, sm.k0, sm.k1);
+    const int j = c & 3;  // 0 or 2
+    v0 = v0 / sm.temp + gumbel_of(j ? w[2] : w[0]);
+    v1 = v1 / sm.temp + gumbel_of(j ? w[3] : w[1]);
+  }
+  k0 = argmax_key(v0, c);
+  k1 = argmax_key(v1, c + 1);
+}
+
+__device__ __forceinline__ Sampling load_sampling(const GemmParams& P) {
+  Sampling s;
+  s.temp = P.step->temp;
+  s.k0 = P.step->seed_lo;
+  s.k1 = P.step->seed_hi;
+  return s;
 }
 
 // After a workgroup's row maxima are in: the last of nblk workgroups reads
@@ -721,8 +777,10 @@ __device__ void lm_finish(const GemmParams& P, int nblk, float* sbuf) {
 
 template <int CT, int SB, int U>
 __device__ void epi_lm(const GemmParams& P, int nb, float* sbuf) {
+  const Sampling sm = load_sampling(P);
   for_pairs<CT, SB, U>(P, nb, [&](int idx, int r, int c, float v0, float v1) {
-    const unsigned long long k0 = lm_value(P, r, c, v0), k1 = lm_value(P, r, c + 1, v1);
+    unsigned long long k0, k1;
+    lm_pair_keys(P, sm, r, c, v0, v1, P.rowinfo[2 * r], k0, k1);
     unsigned long long k = k0 > k1 ? k0 : k1;
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) {
@@ -823,15 +881,18 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
   // inputs, then the first block's weights, then A, so that waiting for the
   // former never waits for the weights.
   constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // epilogue pairs per thread at 16 rows
-  int qpos[EPI == EPI_QKV ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
-  if constexpr (EPI == EPI_QKV) {
+  constexpr bool POS = EPI == EPI_QKV || EPI == EPI_LM;  // the rows' positions (RoPE, sampling)
+  int qpos[POS ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
+  if constexpr (POS) {
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
       const int r = (tid + it * NT) / (8 * CT), rc = r < P.R ? r : 0;
       qpos[it] = P.rowinfo[2 * rc];
-      qblk[it] = P.rowinfo[2 * rc + 1];
+      if constexpr (EPI == EPI_QKV) qblk[it] = P.rowinfo[2 * rc + 1];
     }
   }
+  Sampling sm = {0.0f, 0u, 0u};
+  if constexpr (EPI == EPI_LM) sm = load_sampling(P);
   float gv[NORM ? GPT : 1], sv[NORM ? SSI : 1];
   const int ss_r = tid >> 4, ss_j = tid & 15;
   if constexpr (NORM) {
@@ -951,7 +1012,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
           } else if constexpr (EPI == EPI_SWIGLU) {
             swiglu_pair(P, r, col, v0, v1);
           } else {
-            const unsigned long long k0 = lm_value(P, r, col, v0), k1 = lm_value(P, r, col + 1, v1);
+            unsigned long long k0, k1;
+            lm_pair_keys(P, sm, r, col, v0, v1, qpos[it], k0, k1);
             const unsigned long long k = k0 > k1 ? k0 : k1;
             kmax[it] = k > kmax[it] ? k : kmax[it];
           }
@@ -1226,15 +1288,18 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   // Issue order: the QKV rows' positions, A and the gains (needed first),
   // then the first tile's weights and scales, then the RMSNorm row
   // statistics (one wave).
-  int qpos[EPI == EPI_QKV ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
-  if constexpr (EPI == EPI_QKV) {
+  constexpr bool POS = EPI == EPI_QKV || EPI == EPI_LM;  // the rows' positions (RoPE, sampling)
+  int qpos[POS ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
+  if constexpr (POS) {
 #pragma unroll
     for (int it = 0; it < PPT; ++it) {
       const int r = (tid + it * NT) / (8 * CT), rc = r < P.R ? r : 0;
       qpos[it] = P.rowinfo[2 * rc];
-      qblk[it] = P.rowinfo[2 * rc + 1];
+      if constexpr (EPI == EPI_QKV) qblk[it] = P.rowinfo[2 * rc + 1];
     }
   }
+  Sampling sm = {0.0f, 0u, 0u};
+  if constexpr (EPI == EPI_LM) sm = load_sampling(P);
   f32x4 pa[UPT][2], pg[NORM ? UPT : 1][2];
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
@@ -1369,7 +1434,8 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
         } else if constexpr (EPI == EPI_SWIGLU) {
           swiglu_pair(P, r, col, v0, v1);
         } else {
-          const unsigned long long k0 = lm_value(P, r, col, v0), k1 = lm_value(P, r, col + 1, v1);
+          unsigned long long k0, k1;
+          lm_pair_keys(P, sm, r, col, v0, v1, qpos[it], k0, k1);
           const unsigned long long k = k0 > k1 ? k0 : k1;
           kmax[it] = k > kmax[it] ? k : kmax[it];
         }
@@ -1729,6 +1795,37 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
   combine_tile<HD, false, kMaxCombineSplits>(P, b, blockIdx.y, blockIdx.x, P.rowinfo[2 * b * P.S], sML);
 }
 
+// ------------------------------------------------------- streaming read
+//
+// The measured read peak: every workgroup streams its share of a buffer with
+// 16-byte non-temporal loads, eight in flight per thread, and folds them into
+// one word per thread (written only if it is a sentinel no data produces, so
+// the loads cannot be dropped).  Grid = a multiple of the CU count.
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, size_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 255] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
+  if (!src || !sink || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15) || grid < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, st, (const u32x4*)src, bytes / 16, sink);
+  return hipGetLastError();
+}
+
 // -------------------------------------------------------------- launchers
 
 template <int EPI>
@@ -1861,7 +1958,7 @@ hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st) {
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
-  if (epi == EPI_LM && !p.kd) return hipErrorInvalidValue;
+  if (epi == EPI_LM && (!p.kd || !p.step || !p.rowinfo || !p.seq_ids)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_QKV: return launch_gemm_epi<EPI_QKV>(p, nk, fmt, st);
     case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, nk, fmt, st);
@@ -1917,7 +2014,7 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
     return hipErrorInvalidValue;
   if (epi != EPI_RESID && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
-  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || p.R != p.n_seq * p.S))
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || !p.step || !p.rowinfo || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int gpw = nk / 4, nw = p.K / (32 * nk), ntile = p.N / 16;
   const int ct = (nw == 10 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
@@ -1956,7 +2053,7 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
   if ((epi == EPI_QKV || epi == EPI_SWIGLU || epi == EPI_LM) && (!p.ss || !p.gain || p.ss_n * 16 != p.K))
     return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
-  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || p.R != p.n_seq * p.S))
+  if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || !p.step || !p.rowinfo || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int nblk = (p.N + 16 * ct - 1) / (16 * ct), nblk1 = (p.N + 15) / 16;
   const int grid = nblk < max_grid ? nblk : max_grid;

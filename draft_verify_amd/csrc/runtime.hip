@@ -306,6 +306,8 @@ struct spec_ctx {
   int attn_tpw = 1;      // the current step's query tiles per attention workgroup
   hipEvent_t ev0 = nullptr, ev1 = nullptr;  // verify forward timing (spec_get_stats)
   int static_dev = -1;   // spec_create_static: the device whose scratch is the workspace
+  float temp = 0.0f;     // spec_set_sampling: 0 greedy, > 0 sampled rows
+  uint64_t seed = 0;
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
@@ -487,6 +489,8 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.tokens = tokens;
     gl.kd = seq_ids + L.max_rows;
     gl.mode = &sd->mode;
+    gl.step = sd;
+    gl.rowinfo = c->ws<int32_t>(L.rowinfo);
     gl.result = c->ws<int32_t>(L.result);
     gl.kv_len_w = c->ws<int32_t>(L.kv_len);
     gl.seq_ids = seq_ids;
@@ -644,6 +648,10 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   sd->n_seq = n_seq;
   sd->span = S;
   sd->pad = 0;
+  sd->temp = c->temp;
+  sd->seed_lo = (uint32_t)c->seed;
+  sd->seed_hi = (uint32_t)(c->seed >> 32);
+  sd->pad2 = 0;
   int32_t* tk = (int32_t*)(sd + 1);
   memcpy(tk, tokens, sizeof(int32_t) * (size_t)n_seq * S);
   memcpy(tk + L.max_rows, seq_ids, sizeof(int32_t) * (size_t)n_seq);
@@ -1130,6 +1138,14 @@ int spec_debug_logits(spec_ctx* c, float* host_out, int rows) {
   return SPEC_OK;
 }
 
+int spec_set_sampling(spec_ctx* c, float temperature, uint64_t seed) {
+  if (!c) return SPEC_EINVAL;
+  if (!(temperature >= 0.0f) || temperature > 1e30f) return set_err(c, SPEC_EINVAL, "temperature must be >= 0 and finite");
+  c->temp = temperature;
+  c->seed = seed;
+  return SPEC_OK;
+}
+
 int spec_get_stats(spec_ctx* c, spec_stats* out) {
   if (!c || !out) return SPEC_EINVAL;
   *out = c->stats;
@@ -1252,6 +1268,35 @@ int spec_time_op(spec_ctx* c, int op, int S, int reps, float* us_out) {
   if (rc != SPEC_OK) return rc;
   if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("timing: ") + hipGetErrorString(e));
   *us_out = ms * 1000.0f / (float)(reps * per_rep);
+  return SPEC_OK;
+}
+
+int spec_measure_read_bw(const void* buf, size_t bytes, uint32_t* sink, int reps, void* hip_stream,
+                         double* gbps_out) {
+  if (!buf || !sink || !gbps_out || reps < 1 || bytes < (1u << 20) || bytes % 16 || !hip_stream)
+    return SPEC_EINVAL;
+  hipStream_t st = (hipStream_t)hip_stream;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus < 1)
+    return SPEC_EHIP;
+  const int grid = cus * 8;
+  if (launch_stream_read(buf, bytes, sink, grid, st) != hipSuccess) return SPEC_EHIP;  // warm
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return SPEC_EHIP;
+  }
+  hipError_t e = hipEventRecord(e0, st);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch_stream_read(buf, bytes, sink, grid, st);
+  if (e == hipSuccess) e = hipEventRecord(e1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess || ms <= 0.0f) return SPEC_EHIP;
+  *gbps_out = (double)bytes * reps / (ms * 1e-3) / 1e9;
   return SPEC_OK;
 }
 

@@ -123,10 +123,12 @@ def lib():
         "spec_cache_len_seq": [P, I, i32p],
         "spec_release_seq": [P, I],
         "spec_debug_logits": [P, f32p, I],
+        "spec_set_sampling": [P, C.c_float, C.c_uint64],
         "spec_get_stats": [P, C.POINTER(spec_stats)],
         "spec_time_verify": [P, I, I, i32p, f32p],
         "spec_profile_ops": [P, I, I, i32p, f32p, i32p],
         "spec_op_bytes": [C.POINTER(spec_model_desc), I, I, I, dp],
+        "spec_measure_read_bw": [P, C.c_size_t, P, I, P, dp],
         "spec_time_op": [P, I, I, I, f32p],
         "spec_ngram_create": [I, I, I, C.POINTER(P)],
         "spec_ngram_destroy": [P],
@@ -281,6 +283,10 @@ def spec_release_seq(ctx, seq):
     return _check(lib().spec_release_seq(ctx, seq), ctx)
 
 
+def spec_set_sampling(ctx, temperature, seed=0):
+    return _check(lib().spec_set_sampling(ctx, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF), ctx)
+
+
 def spec_debug_logits(ctx, rows, vocab):
     out = np.zeros((rows, vocab), np.float32)
     _check(lib().spec_debug_logits(ctx, out.ctypes.data_as(C.POINTER(C.c_float)), rows), ctx)
@@ -318,6 +324,13 @@ def spec_time_op(ctx, op, S, reps):
     us = C.c_float()
     _check(lib().spec_time_op(ctx, OPS.index(op) if isinstance(op, str) else op, S, reps, C.byref(us)), ctx)
     return us.value
+
+
+def spec_measure_read_bw(buf_ptr, nbytes, sink_ptr, reps, stream_ptr):
+    g = C.c_double()
+    _check(lib().spec_measure_read_bw(C.c_void_p(buf_ptr), nbytes, C.c_void_p(sink_ptr), reps,
+                                      C.c_void_p(stream_ptr), C.byref(g)))
+    return g.value
 
 
 def spec_op_bytes(desc, op, S, ctx_len):

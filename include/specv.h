@@ -198,6 +198,22 @@ SPEC_API int spec_cache_len_seq(spec_ctx* ctx, int seq, int* len);
 /* Free every block of a sequence (cache length 0). */
 SPEC_API int spec_release_seq(spec_ctx* ctx, int seq);
 
+/* Sampled verification (TensorSharp page, protocol section, the verify step:
+ * the sampler draws a token from every row and drafts are accepted while the
+ * drawn token matches; the first mismatching row's draw is the corrected
+ * token).  temperature 0 (the default) is greedy: every row's token is its
+ * argmax.  temperature > 0: row i of a span at position p + i draws
+ * argmax_v (logit_v / temperature + g_v) -- a draw from softmax(logit /
+ * temperature) -- with Gumbel noise g_v = -log(-log u_v) and u_v from
+ * Philox4x32-10 keyed by `seed` at the counter (v / 4, p + i, sequence id, 0),
+ * word v % 4.  A draw depends on (seed, sequence, position, v) only, so
+ * speculation leaves the sampled stream exactly as plain sampled decoding
+ * would draw it.  Applies to every later forward of the context (prefill's
+ * g0 included), on the device inside the LM-head epilogue; argmax outputs
+ * then hold the drawn tokens.  EINVAL for a negative or non-finite
+ * temperature. */
+SPEC_API int spec_set_sampling(spec_ctx* ctx, float temperature, uint64_t seed);
+
 /* Logits of the rows of the last forward, fp32 [rows][vocab]; only for a
  * context created with SPEC_FLAG_KEEP_LOGITS.  rows <= rows of that forward.
  * For checking only: the per-row logits of the multi-row forward (TensorSharp
@@ -248,6 +264,16 @@ SPEC_API int spec_profile_ops(spec_ctx* ctx, int S, int iters, const int32_t* sp
  * context stream (no commit).  The KV rows of positions p..p+S-1 are
  * rewritten, as a verify would. */
 SPEC_API int spec_time_op(spec_ctx* ctx, int op, int S, int reps, float* us_per_launch);
+
+/* The measured HBM read peak the roofline fractions are also reported
+ * against: `reps` launches of a streaming-read kernel (16-byte non-temporal
+ * loads, eight in flight per thread, 8 workgroups per CU) over the
+ * caller-owned device buffer `buf` of `bytes` (>= 1 MiB, a multiple of 16;
+ * much larger than the caches to measure HBM), timed with HIP events on
+ * `hip_stream`; sink: 256 words of caller-owned device memory.
+ * *gbps_out = bytes * reps / time. */
+SPEC_API int spec_measure_read_bw(const void* buf, size_t bytes, uint32_t* sink, int reps, void* hip_stream,
+                                  double* gbps_out);
 
 /* Algorithmic bytes one launch of an op class streams at span S and cache
  * length ctx_len (weights, KV reads and writes; activations excluded). */

@@ -90,13 +90,24 @@ class Twin:
         self.orc = orc
         self.ctx = self.sess.ctx
         self.history = []
+        self.temp, self.seed = 0.0, 0
+
+    def set_sampling(self, temp, seed):
+        """Sampled rows on both sides (temp 0: greedy).  With sampling on, the
+        per-row "margin" is the oracle's top-2 margin of the sampled scores
+        logit / T + g."""
+        specv.spec_set_sampling(self.ctx, temp, seed)
+        self.temp, self.seed = float(temp), int(seed)
 
     def prefill(self, prompt, seq=0, chunk=0):
         """Prefill both sides; chunk > 0 runs the oracle's prefill in chunks of
         that many rows with a progress line each (the oracle's rows are
         independent of how they are grouped, so the cache is the same)."""
         g = specv.spec_prefill_seq(self.ctx, seq, prompt)
-        go, mg = oracle_prefill(self.orc, prompt, seq, chunk)
+        if self.temp > 0:
+            go, mg = self.orc.prefill(prompt, seq, temp=self.temp, seed=self.seed)
+        else:
+            go, mg = oracle_prefill(self.orc, prompt, seq, chunk)
         assert g == go or mg < MARGIN, f"prefill token {g} != oracle {go} (margin {mg:.3f})"
         self.history = [int(t) for t in prompt] + [g]
         return g
@@ -110,7 +121,7 @@ class Twin:
         p = specv.spec_cache_len(self.ctx)
         am, m = specv.spec_verify(self.ctx, span)
         lg = specv.spec_debug_logits(self.ctx, K + 1, self.shape["vocab"])
-        amo, mo, mgo, lgo = self.orc.verify(span, seq, want_logits=True)
+        amo, mo, mgo, lgo = self.orc.verify(span, seq, want_logits=True, temp=self.temp, seed=self.seed)
         err = float(np.max(np.abs(lg - lgo)))
         assert err < LOGIT_TOL, f"logits differ by {err:.3e} (K={K})"
         sure = mgo >= MARGIN

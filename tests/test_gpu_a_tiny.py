@@ -189,11 +189,13 @@ def test_nan_row_leaves_the_cache_unchanged(weights):
 
 
 def test_governed_generation_parks_a_losing_drafter(weights):
-    """A governed loop over all-wrong drafts (every draft rejected, so each
-    speculative step costs a K=4 forward for one token) parks drafting after
-    four zero-accept steps and runs plain steps; with the motif prompt's own
-    n-gram drafts it keeps drafting.  Either way the committed stream equals
-    the spec-off stream token for token."""
+    """A governed loop over all-wrong drafts (every draft rejected): whatever
+    the timings, the first full probe ends at its fourth zero-accept step and
+    parks drafting for 32 steps (later verdicts depend on measured times,
+    which at this launch-bound shape are nearly equal for both kinds of
+    step).  With the motif prompt's own n-gram drafts the loop drafts and
+    accepts.  Either way the committed stream equals the spec-off stream
+    token for token."""
     t = Twin(SHAPE, weights, max_ctx=512)
     try:
         prompt = synth.motif_prompt(1, SHAPE["vocab"])
@@ -205,10 +207,10 @@ def test_governed_generation_parks_a_losing_drafter(weights):
         gs, st = g.governor_stats(), g.stats()
         g.close()
         assert np.array_equal(off, wrong)
-        assert gs["losses"] >= 1 and gs["wins"] == 0 and st["plain_steps"] > 100
+        assert gs["losses"] >= 1 and st["plain_steps"] >= 3 + 32 and gs["parked_steps"] >= 32
         assert st["accepted"] == 0
         on, st_on = specv.spec_generate(t.ctx, prompt, 200, spec=True, fixed_k=4, governed=True)
-        assert np.array_equal(off, on)
+        assert np.array_equal(off, on) and st_on["accepted"] > 0
         log(f"  governed: wrong drafts {st['forwards']} forwards ({st['plain_steps']} plain, governor {gs}); "
             f"n-gram drafts {st_on['forwards']} forwards ({st_on['plain_steps']} plain)")
     finally:
