@@ -14,13 +14,17 @@ full accept, -1 on a rejection, capped at 7.  W untimed rounds, then exactly K
 timed rounds; `value` is committed tokens per second over those K rounds.
 
 Also on the JSON line: the same rounds with drafting off (spec-off tok/s), the
-256-token end-to-end A/B of the page's protocol with the perfect- and
-all-wrong-draft bounds, the verify-cost sweep c_v(S) for S = 1..16 at an
-848-token context, the 16-sequence paged batched verify (K = 7, 128 rows,
-contexts U[512, 4096]) against its spec-off batched step, the int4 32B-class
-model at an 8192-token context (c_v sweep and a 256-token adaptive-K run),
-the roofline of the dominant kernel (the gate/up GEMM: 99.6 MB of bf16
-weights per launch) and the CPU oracle timed on this host.
+256-token end-to-end A/B of the page's protocol (one warm-up round, five
+alternating spec-off / spec-on / governed rounds, the band rule) with the
+perfect- and all-wrong-draft bounds, sampled verification at temperature 0.8,
+the verify-cost sweep c_v(S) for S = 1..16 at an 848-token context, the
+16-sequence paged batched verify (K = 7, 128 rows, contexts U[512, 4096];
+fixed-shape, per-sequence draft counts and governed) against its spec-off
+batched step, the int4 32B-class model at an 8192-token context (c_v sweep
+and a 256-token adaptive-K run, ungoverned and governed), the roofline of the
+dominant kernel (the gate/up GEMM: 99.6 MB of bf16 weights per launch)
+against 8 TB/s and the measured streaming-read peak, and the CPU oracle timed
+on this host.
 """
 import argparse
 import hashlib
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "committed tok/s spec-on vs off (batch 1) + verify cost c_v(S=1..16), HBM GB/s"
 HBM_PEAK_GBS = 8000.0
+E2E_PAIRS = 5
 PROMPT_TOKENS, CV_CTX = 512, 848
 
 
@@ -64,10 +69,28 @@ def measured_traffic(kernel, per_launch_bytes):
     return k.get("hbm_bytes_per_launch")
 
 
+def measure_read_peak(gib=4, reps=10):
+    """HBM read peak measured with the library's streaming-read kernel over a
+    buffer far larger than the caches (GB/s)."""
+    import torch
+    from draft_verify_amd import specv
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = specv.spec_measure_read_bw(buf.data_ptr(), buf.numel(), sink.data_ptr(), reps, st.cuda_stream)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return g
+
+
 def cpu_baseline(shape, prompt, budget_s=12.0, max_rounds=24):
-    """The oracle (plain fp32 C, OpenMP) on this host's cores: spec-on rounds
-    (n-gram proposer, adaptive K cap 7) from the same 512-token prompt; the
-    prefill is untimed.  Returns committed tokens per second over the rounds."""
+    """The oracle (plain fp32 C, OpenMP) on this host's cores.  Headline: spec-on
+    rounds (n-gram proposer, adaptive K cap 7) from the same 512-token prompt
+    after an untimed prefill, committed tokens per second.  Extra, on the same
+    prefilled state: one S = 1 and one S = 16 verify forward (the CPU's c_v at a
+    512-token context), and the tiny decoder's 64-token spec-off / spec-on
+    (K = 4) generation."""
     import numpy as np
     from draft_verify_amd import synth
     from oracle import oracle as O
@@ -87,6 +110,27 @@ def cpu_baseline(shape, prompt, budget_s=12.0, max_rounds=24):
         rounds += 1
         k = O.adapt_k(k, len(drafts), m, 7)
     dt = time.time() - t0
+    # the CPU's verify cost at S = 1 and S = 16 on the 512-token prefix
+    orc.rewind(PROMPT_TOKENS)
+    rng = np.random.default_rng(6)
+    fwd = {}
+    for S in (1, 16):
+        span = [g0] + [int(x) for x in rng.integers(0, shape["vocab"], S - 1)]
+        t1 = time.time()
+        orc.verify(span)
+        fwd[S] = time.time() - t1
+        orc.rewind(PROMPT_TOKENS)
+    orc.close()
+    tiny = synth.SHAPES["tiny"]
+    orc_t = O.Oracle(tiny, synth.to_numpy(synth.weights(tiny, seed=0)), max_ctx=128)
+    tp = synth.motif_prompt(1, tiny["vocab"])
+    t1 = time.time()
+    orc_t.generate(tp, 64, spec=False)
+    t_off = time.time() - t1
+    t1 = time.time()
+    _, st_on = orc_t.generate(tp, 64, spec=True, fixed_k=4)
+    t_on = time.time() - t1
+    orc_t.close()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     cpu = ""
     try:
@@ -94,10 +138,18 @@ def cpu_baseline(shape, prompt, budget_s=12.0, max_rounds=24):
             cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    return {"value": round(committed / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+    head = {"value": round(committed / dt, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"{rounds} spec-on rounds ({committed} tokens) of the same workload after an "
                       f"untimed {PROMPT_TOKENS}-token prefill ({prefill_s:.1f}s), fp32, "
                       f"{len(os.sched_getaffinity(0))} host cores visible, {cpu}"}
+    extra = {"qwen3_4b_forward_s": {"S1": round(fwd[1], 3), "S16": round(fwd[16], 3),
+                                    "c_v16": round(fwd[16] / fwd[1], 3), "ctx": PROMPT_TOKENS},
+             "qwen3_4b_prefill_512_s": round(prefill_s, 2),
+             "tiny_64_tokens": {"off_tok_s": round(63 / t_off, 1), "on_k4_tok_s": round(63 / t_on, 1),
+                                "forwards_on": st_on["forwards"]},
+             "note": "the oracle's 4B batched step and the 32B-class int4 forwards are not timed here: "
+                     "each needs minutes of CPU prefill at those contexts"}
+    return head, extra
 
 
 BATCH_SEQS, BATCH_K, BATCH_CTX = 16, 7, (512, 4096)
@@ -110,7 +162,9 @@ def batched_bench(steps, warmup, log_every=8):
     sequence (short drafts padded with the last history token), runs one
     batched verify forward of 16 x 8 = 128 rows, accepts and rewinds per
     sequence, and commits on the host.  Then the spec-off batched step (16
-    rows, one per sequence) from the same prefilled state."""
+    rows, one per sequence) from the same prefilled state.  Also the same steps
+    with each sequence's real draft count (spec_verify_batch_k: the step at 1
+    + the most drafts, padding masked) and under the cost governor."""
     import numpy as np
     import torch
     from draft_verify_amd import specv, synth
@@ -138,7 +192,11 @@ def batched_bench(steps, warmup, log_every=8):
         b += shape["n_layers"] * sum(specv.spec_op_bytes(d, "attn", rows_per_seq, L) for L in cur)
         return b
 
-    def run(spec, n_steps, n_warm):
+    def run(mode, n_steps, n_warm):
+        """mode: "fixed" (every sequence K = 7, short drafts padded, the
+        fixed-shape step), "hetero" (each sequence its own real draft count,
+        the step at S = 1 + the most drafts, padding masked), "governed"
+        (hetero under one cost governor shared by the batch), "off" (S = 1)."""
         hist = [[int(x) for x in p] + [g] for p, g in zip(prompts, g0)]
         ngs = []
         for h in hist:
@@ -147,54 +205,80 @@ def batched_bench(steps, warmup, log_every=8):
             ngs.append(ng)
         for i in ids:
             specv.spec_rewind_seq(c, i, ctxs[i])
+        gov = specv.Governor() if mode == "governed" else None
         committed, t_total, t_verify, byts, acc_hist = 0, 0.0, 0.0, 0.0, np.zeros(S, np.int64)
         per_seq = np.zeros(n, np.int64)
+        spans_by_s = np.zeros(S + 1, np.int64)
+        drafted = 0
         for it in range(n_steps + n_warm):
             cur = [len(h) - 1 for h in hist]
             t0 = time.perf_counter()
-            if spec:
-                spans = np.empty((n, S), np.int32)
+            draft = mode in ("fixed", "hetero") or (gov is not None and gov.should_draft())
+            kd = [0] * n
+            if draft:
+                props = [specv.spec_ngram_propose(ngs[b], K) for b in ids]
+                kd = [len(d) for d in props]
+                Sx = S if mode == "fixed" else 1 + max(kd)
+                spans = np.empty((n, Sx), np.int32)
                 for b in ids:
-                    dr = specv.spec_ngram_propose(ngs[b], K)
-                    spans[b] = [hist[b][-1]] + dr + [hist[b][-1]] * (K - len(dr))
+                    spans[b] = [hist[b][-1]] + props[b] + [hist[b][-1]] * (Sx - 1 - kd[b])
+                if mode == "fixed":
+                    kd = [K] * n
             else:
                 spans = np.array([[h[-1]] for h in hist], np.int32)
             t1 = time.perf_counter()
-            am, acc = specv.spec_verify_batch(c, ids, spans)
+            if mode == "fixed" or spans.shape[1] == 1:
+                am, acc = specv.spec_verify_batch(c, ids, spans)
+            else:
+                am, acc = specv.spec_verify_batch_k(c, ids, spans, kd)
             t2 = time.perf_counter()
+            step_tok = 0
             for b in ids:
                 m = int(acc[b])
                 new = [int(x) for x in am[b][: m + 1]]
                 hist[b] += new
                 specv.spec_ngram_append(ngs[b], new)
+                step_tok += m + 1
                 if it >= n_warm:
-                    committed += m + 1
                     per_seq[b] += m + 1
                     acc_hist[m] += 1
             t3 = time.perf_counter()
+            if gov is not None:
+                gov.record(draft, step_tok, int(np.sum(acc)), t3 - t0)
             if it >= n_warm:
+                committed += step_tok
                 t_total += t3 - t0
                 t_verify += t2 - t1
                 byts += step_bytes(spans.shape[1], cur)
+                spans_by_s[spans.shape[1]] += 1
+                drafted += int(sum(kd)) if draft else 0
             if log_every and it % log_every == 0:
-                log(f"  batched {'on' if spec else 'off'} step {it}: verify {1e3 * (t2 - t1):.2f} ms")
+                log(f"  batched {mode} step {it}: S={spans.shape[1]} verify {1e3 * (t2 - t1):.2f} ms")
         for ng in ngs:
             specv.spec_ngram_destroy(ng)
-        return {"tok_s": round(committed / t_total, 2), "ms_per_step": round(1e3 * t_total / n_steps, 4),
-                "verify_ms_per_step": round(1e3 * t_verify / n_steps, 4),
-                "hbm_gbps_verify": round(byts / t_verify / 1e9, 1),
-                "hbm_frac_verify": round(byts / t_verify / 1e9 / HBM_PEAK_GBS, 4),
-                "bytes_per_step": round(byts / n_steps), "committed": int(committed),
-                "accept_hist": acc_hist.tolist() if spec else None,
-                "per_seq_tok_per_step": [round(x / n_steps, 3) for x in per_seq] if spec else None}
+        out = {"tok_s": round(committed / t_total, 2), "ms_per_step": round(1e3 * t_total / n_steps, 4),
+               "verify_ms_per_step": round(1e3 * t_verify / n_steps, 4),
+               "hbm_gbps_verify": round(byts / t_verify / 1e9, 1),
+               "hbm_frac_verify": round(byts / t_verify / 1e9 / HBM_PEAK_GBS, 4),
+               "bytes_per_step": round(byts / n_steps), "committed": int(committed), "drafted": drafted,
+               "steps_by_span": spans_by_s[1:].tolist()}
+        if mode != "off":
+            out["accept_hist"] = acc_hist.tolist()
+            out["per_seq_tok_per_step"] = [round(x / n_steps, 3) for x in per_seq]
+        if gov is not None:
+            out["governor"] = gov.stats()
+            gov.close()
+        return out
 
-    on = run(True, steps, warmup)
-    off = run(False, steps, warmup)
+    res = {m: run(m, steps, warmup) for m in ("fixed", "hetero", "governed", "off")}
     sess.close()
     del sess
     torch.cuda.empty_cache()
+    off = res["off"]["tok_s"]
     return {"sequences": n, "K": K, "rows": n * S, "contexts": ctxs, "steps": steps, "warmup": warmup,
-            "on": on, "off": off, "ratio": round(on["tok_s"] / off["tok_s"], 3)}
+            "on": res["fixed"], "hetero": res["hetero"], "governed": res["governed"], "off": res["off"],
+            "ratio": round(res["fixed"]["tok_s"] / off, 3), "ratio_hetero": round(res["hetero"]["tok_s"] / off, 3),
+            "ratio_governed": round(res["governed"]["tok_s"] / off, 3)}
 
 
 INT4_CTX = 8192
@@ -232,6 +316,7 @@ def int4_bench(cv_iters=15, gen_tokens=256):
     per_op = {op: round(specv.spec_time_op(c, op, 1, 3), 2) for op in specv.OPS}
     off, s_off = specv.spec_generate(c, prompt, gen_tokens, spec=False)
     on, s_on = specv.spec_generate(c, prompt, gen_tokens, spec=True, fixed_k=0, k_cap=7)
+    gv, s_gv = specv.spec_generate(c, prompt, gen_tokens, spec=True, fixed_k=0, k_cap=7, governed=True)
     sess.close()
     del sess
     torch.cuda.empty_cache()
@@ -243,8 +328,11 @@ def int4_bench(cv_iters=15, gen_tokens=256):
             "gen": {"tokens": gen_tokens, "off_tok_s": round((gen_tokens - 1) / s_off["decode_s"], 2),
                     "on_tok_s": round((gen_tokens - 1) / s_on["decode_s"], 2),
                     "ratio": round(s_off["decode_s"] / s_on["decode_s"], 3),
-                    "streams_equal": bool(np.array_equal(off, on)), "forwards_on": s_on["forwards"],
-                    "accept_hist_on": s_on["accept_hist"][:8]}}
+                    "streams_equal": bool(np.array_equal(off, on) and np.array_equal(off, gv)),
+                    "forwards_on": s_on["forwards"], "accept_hist_on": s_on["accept_hist"][:8],
+                    "governed_tok_s": round((gen_tokens - 1) / s_gv["decode_s"], 2),
+                    "governed_ratio": round(s_off["decode_s"] / s_gv["decode_s"], 3),
+                    "governed_plain_steps": s_gv["plain_steps"], "governed_forwards": s_gv["forwards"]}}
 
 
 def counters_workload():
@@ -433,6 +521,8 @@ def main():
     torch.cuda.empty_cache()
     ctx = sess.ctx
     log(f"session ready in {time.time() - t:.1f}s")
+    read_peak = measure_read_peak()
+    log(f"measured streaming-read peak: {read_peak:.0f} GB/s")
     prompt, pstats = synth.repetition_prompt(3, shape["vocab"], PROMPT_TOKENS, return_stats=True)
 
     def timed_rounds(spec):
@@ -455,32 +545,56 @@ def main():
     off_tok_s, off_dt, _, _ = timed_rounds(False)
     log(f"timed {K} rounds: spec-on {on_tok_s:.1f} tok/s, spec-off {off_tok_s:.1f} tok/s")
 
-    # 256-token A/B of the end-to-end protocol, alternating pairs after one warm-up pair
-    e2e = {"off": [], "on": []}
+    # 256-token A/B of the end-to-end protocol: one warm-up round, then five
+    # alternating rounds of {spec-off, spec-on, spec-on governed}; a round whose
+    # spec-off rate is more than 5% from the session median is dropped (the
+    # coreai note's band rule); medians over the kept rounds
+    rounds = []
     streams_equal = True
-    for i in range(4):
+    for i in range(1 + E2E_PAIRS):
         off, s_off = specv.spec_generate(ctx, prompt, 256, spec=False)
         on, s_on = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=0, k_cap=7)
-        streams_equal &= bool(np.array_equal(off, on))
+        gv, s_gv = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=0, k_cap=7, governed=True)
+        streams_equal &= bool(np.array_equal(off, on) and np.array_equal(off, gv))
         if i:
-            e2e["off"].append(255 / s_off["decode_s"])
-            e2e["on"].append(255 / s_on["decode_s"])
+            rounds.append((255 / s_off["decode_s"], 255 / s_on["decode_s"], 255 / s_gv["decode_s"]))
+    med = lambda v: float(np.median(v))
+    off_med = med([r[0] for r in rounds])
+    kept = [r for r in rounds if abs(r[0] - off_med) <= 0.05 * off_med]
     _, s_perf = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=7,
                                     draft_source=specv.SPEC_DRAFT_STREAM, ref_stream=off)
     _, s_wrong = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=7,
                                      draft_source=specv.SPEC_DRAFT_WRONG, ref_stream=off)
-    med = lambda v: float(np.median(v))
-    e2e_256 = {"off_tok_s": round(med(e2e["off"]), 2), "on_tok_s": round(med(e2e["on"]), 2),
-               "ratio": round(med(e2e["on"]) / med(e2e["off"]), 3),
-               "streams_equal": streams_equal, "forwards_on": s_on["forwards"],
+    e2e_256 = {"off_tok_s": round(med([r[0] for r in kept]), 2), "on_tok_s": round(med([r[1] for r in kept]), 2),
+               "governed_tok_s": round(med([r[2] for r in kept]), 2),
+               "ratio": round(med([r[1] for r in kept]) / med([r[0] for r in kept]), 3),
+               "ratio_governed": round(med([r[2] for r in kept]) / med([r[0] for r in kept]), 3),
+               "rounds": len(rounds), "rounds_kept": len(kept),
+               "streams_equal": streams_equal, "forwards_on": s_on["forwards"], "drafted_on": s_on["drafted"],
                "tok_per_forward_on": round(255 / s_on["forwards"], 3),
                "accept_hist_on": s_on["accept_hist"][:8],
                "forwards_by_span_on": s_on["forwards_by_span"][1:9],
                "host_share_on": round(s_on["host_s"] / s_on["decode_s"], 4),
+               "governed_plain_steps": s_gv["plain_steps"],
                "perfect_drafts_k7_tok_s": round(255 / s_perf["decode_s"], 2),
-               "wrong_drafts_k7_tok_s": round(255 / s_wrong["decode_s"], 2),
-               "pairs": len(e2e["on"])}
+               "wrong_drafts_k7_tok_s": round(255 / s_wrong["decode_s"], 2)}
     log(f"e2e 256: {e2e_256}")
+
+    # sampled verification (temperature 0.8): plain sampled decoding against
+    # speculation with perfect drafts (the sampled plain stream itself)
+    specv.spec_set_sampling(ctx, 0.8, 1234)
+    soff, ss_off = specv.spec_generate(ctx, prompt, 256, spec=False)
+    son, ss_on = specv.spec_generate(ctx, prompt, 256, spec=True, fixed_k=7,
+                                     draft_source=specv.SPEC_DRAFT_STREAM, ref_stream=soff)
+    specv.spec_set_sampling(ctx, 0.0, 0)
+    sampled = {"temperature": 0.8, "off_tok_s": round(255 / ss_off["decode_s"], 2),
+               "perfect_drafts_k7_tok_s": round(255 / ss_on["decode_s"], 2),
+               "streams_equal": bool(np.array_equal(soff, son)), "forwards_on": ss_on["forwards"]}
+    log(f"sampled: {sampled}")
+
+    st = specv.spec_get_stats(ctx)
+    fwd_ms_by_span = {str(S): round(st["forward_ms_by_span"][S] / st["forwards_by_span"][S], 4)
+                      for S in range(1, 17) if st["forwards_by_span"][S]}
 
     # verify-cost sweep at a fixed 848-token uniform context
     specv.spec_prefill(ctx, synth.uniform_prompt(2, shape["vocab"], CV_CTX))
@@ -499,7 +613,9 @@ def main():
     cv = {"ctx": CV_CTX, "ms": [round(x, 4) for x in cv_ms],
           "c_v": [round(x / cv_ms[0], 3) for x in cv_ms],
           "gbps": [round(b / (x * 1e-3) / 1e9, 1) for b, x in zip(fwd_bytes, cv_ms)],
-          "hbm_frac_S1": round(fwd_bytes[0] / (cv_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+          "hbm_frac_S1": round(fwd_bytes[0] / (cv_ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+          "frac_of_measured_read_peak_S1": round(fwd_bytes[0] / (cv_ms[0] * 1e-3) / 1e9 / read_peak, 4),
+          "stats_forward_ms_by_span": fwd_ms_by_span}
     log(f"c_v: {cv['c_v']}")
 
     # roofline of the dominant kernel: each op class launched back to back
@@ -512,6 +628,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": f"{GU_KERNEL} (gate/up + SwiGLU, S=1)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "measured_read_peak": round(read_peak, 1), "frac_of_measured_peak": round(achieved / read_peak, 4),
                 "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3),
                 "per_op_us_S1": {k: round(v, 2) for k, v in per_op.items()}}
     log(f"roofline: {roofline}")
@@ -529,10 +646,10 @@ def main():
         int4 = int4_bench()
         log(f"int4: {int4}")
 
-    cpu = None
+    cpu = cpu_extra = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shape, prompt)
-        log(f"cpu baseline: {cpu}")
+        cpu, cpu_extra = cpu_baseline(shape, prompt)
+        log(f"cpu baseline: {cpu}; extra: {cpu_extra}")
 
     line = {"metric": METRIC, "value": round(on_tok_s, 3), "unit": "tok/s", "n_gpus": 1,
             "steps": K, "warmup": W, "ms_per_step": round(on_dt / K * 1e3, 4),
@@ -547,8 +664,9 @@ def main():
                        "batch": 1, "prompt_tokens": PROMPT_TOKENS, "parallelism": "single GPU"},
             "spec_off_tok_s": round(off_tok_s, 3), "speedup": round(on_tok_s / off_tok_s, 4),
             "tok_per_forward": round((on_st["accepted"] + on_st["forwards"]) / on_st["forwards"], 3),
-            "e2e_256": e2e_256, "cv": cv, "batched_paged": batched, "int4_32b": int4, "roofline": roofline,
-            "cpu_baseline": cpu}
+            "e2e_256": e2e_256, "sampled": sampled, "cv": cv, "batched_paged": batched, "int4_32b": int4,
+            "roofline": roofline, "hbm_read_peak_measured_gbs": round(read_peak, 1),
+            "cpu_baseline": cpu, "cpu_extra": cpu_extra}
     print(json.dumps(line), flush=True)
 
 
