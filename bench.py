@@ -359,6 +359,83 @@ def counters_workload():
     print("counters workload done", flush=True)
 
 
+def gaps_workload(S=1, iters=12):
+    """Short workload for a kernel trace of graph replays: S-row verify
+    forwards at the 848-token context of the Qwen3-4B shape (no commit)."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["qwen3_4b"]
+    wg = synth.weights(shape, seed=0, device="cuda")
+    sess = specv.Session(shape, specv.tree_weights(wg), max_ctx=1024)
+    del wg
+    torch.cuda.empty_cache()
+    specv.spec_prefill(sess.ctx, synth.uniform_prompt(2, shape["vocab"], CV_CTX))
+    rng = np.random.default_rng(6)
+    ms = specv.spec_time_verify(sess.ctx, rng.integers(0, shape["vocab"], (iters, S)).astype(np.int32))
+    sess.close()
+    print(f"gaps workload done: S={S}, median forward {float(np.median(ms[2:])):.4f} ms", flush=True)
+
+
+def summarize_gaps(trace_csv, out_md, command, n_layers=36):
+    """Per-op kernel time and idle gap before each op within the traced
+    forwards (the last forwards of the trace, each starting at k_embed):
+    ops per layer = QKV, attention (+ merge), O, gate/up, down; then the LM
+    head."""
+    rows = sorted(_csv_rows(trace_csv), key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if "specv::" in r["Kernel_Name"]]
+    starts = [i for i, r in enumerate(rows) if "k_embed" in r["Kernel_Name"]]
+    fwds = []
+    for a, b in zip(starts, starts[1:] + [len(rows)]):
+        fwds.append(rows[a:b])
+    fwds = fwds[-10:]  # the workload's last forwards: the timed ones at S rows
+    ops = ["embed", "qkv", "attn", "o", "gateup", "down", "lm"]
+    dur = {o: [] for o in ops}
+    gap = {o: [] for o in ops}
+    walls, busy = [], []
+    for f in fwds:
+        seq = []
+        for r in f:
+            name = r["Kernel_Name"]
+            if "k_attn_combine" in name and seq and seq[-1][0] == "attn":
+                seq[-1][2] = int(r["End_Timestamp"])  # the merge kernel is part of attention
+                seq[-1][3] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                continue
+            seq.append([None, int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), name])
+        if len(seq) != 2 + 5 * n_layers:
+            continue
+        seq[0][0] = "embed"
+        for l in range(n_layers):
+            for k, o in enumerate(ops[1:6]):
+                seq[1 + 5 * l + k][0] = o
+        seq[-1][0] = "lm"
+        walls.append((seq[-1][2] - seq[0][1]) / 1e3)
+        busy.append(sum(x[3] for x in seq) / 1e3)
+        for i, x in enumerate(seq):
+            dur[x[0]].append(x[3] / 1e3)
+            if i:
+                gap[x[0]].append((x[1] - seq[i - 1][2]) / 1e3)
+    import statistics as stt
+    lines = ["# Kernel time and inter-kernel gaps of one verify forward (graph replay)", "",
+             f"Command: `{command}`", "",
+             f"{len(walls)} forwards; wall (first kernel start to last kernel end) median "
+             f"{stt.median(walls):.1f} us, kernel-busy median {stt.median(busy):.1f} us, "
+             f"idle gaps {stt.median(walls) - stt.median(busy):.1f} us "
+             f"({(stt.median(walls) - stt.median(busy)) / stt.median(walls) * 100:.1f}% of the wall).", "",
+             "| op | launches / forward | kernel us (median) | gap before it us (median) | total us / forward |",
+             "|---|---|---|---|---|"]
+    per = {o: len(dur[o]) // max(len(walls), 1) for o in ops}
+    for o in ops:
+        if not dur[o]:
+            continue
+        d, g = stt.median(dur[o]), stt.median(gap[o]) if gap[o] else 0.0
+        lines.append(f"| {o} | {per[o]} | {d:.2f} | {g:.2f} | {(d + g) * per[o]:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def counters_int4_workload():
     """Short workload for SQ counter passes over the int4 GEMMs: the 32B-class
     int4 model (64 layers, hidden 5120), a 64-token prefill, then four S=1
@@ -443,6 +520,46 @@ def summarize_counters(fetch_csv, write_csv, out_dir):
     print(json.dumps(res, indent=1))
 
 
+def summarize_traffic_all(fetch_csv, write_csv, out_md, command, n_fwd=10):
+    """HBM bytes per launch of every kernel of the counters workload's timed
+    S=1 forwards (the last n_fwd of each kernel name's launches), scaled by the
+    1 GiB calibration copy, against the algorithmic bytes of its op."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in _csv_rows(path):
+            if r.get("Counter_Name") == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "copyBuffer" in k)
+    gib_kib = (1 << 30) / 1024.0
+    fs, ws = gib_kib / max(fetch[copy_name]), gib_kib / max(write[copy_name])
+    H, F, DQ, DK, V, hd = 2560, 9728, 4096, 1024, 151936, 128
+    algo = {"k_mm<0,": ("QKV", (DQ + 2 * DK) * H * 2), "k_attn<": ("attention (848 ctx)", 849 * DK * 2 * 2),
+            "k_mm1<1,": ("O", H * DQ * 2), "k_mm<2,": ("gate/up", 2 * F * H * 2),
+            "k_mm1l<": ("down", H * F * 2), "k_mm<3,": ("LM head", V * H * 2)}
+    lines = ["# HBM traffic per launch of the S=1 forward's kernels (Qwen3-4B shape, 848-token context)", "",
+             f"Command: `{command}`", "",
+             f"Calibration: a 1 GiB device copy reads FETCH_SIZE {max(fetch[copy_name]):.0f} KiB and "
+             f"WRITE_SIZE {max(write[copy_name]):.0f} KiB: factors {fs:.3f} (fetch), {ws:.3f} (write).", "",
+             "| op | kernel | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    for key, (op, ab) in algo.items():
+        names = [k for k in fetch if key in k]
+        if not names:
+            continue
+        k = names[0]
+        per = 36 if op not in ("LM head",) else 1
+        f_l = sorted(fetch[k][-n_fwd * per:])
+        w_l = sorted(write.get(k, [0.0])[-n_fwd * per:])
+        f_b, w_b = f_l[len(f_l) // 2] * fs * 1024, w_l[len(w_l) // 2] * ws * 1024
+        lines.append(f"| {op} | `{k[:48]}` | {f_b / 1e6:.2f} | {w_b / 1e6:.2f} | {(f_b + w_b) / 1e6:.2f} | "
+                     f"{ab / 1e6:.2f} | {(f_b + w_b) / ab:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(stats_csv, trace_csv, out_md, command):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
     rows = [r for r in _csv_rows(stats_csv) if "specv::" in r["Name"]]
@@ -490,11 +607,20 @@ def main():
     ap.add_argument("--summarize-sq", nargs=3, metavar=("CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--gaps-workload", type=int, metavar="S", help="short S-row forward workload for a kernel trace")
+    ap.add_argument("--summarize-gaps", nargs=3, metavar=("TRACE_CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
     if args.summarize_trace:
         return summarize_trace(*args.summarize_trace)
+    if args.gaps_workload:
+        return gaps_workload(args.gaps_workload)
+    if args.summarize_gaps:
+        return summarize_gaps(*args.summarize_gaps)
+    if args.summarize_traffic:
+        return summarize_traffic_all(*args.summarize_traffic)
     if args.counters:
         return counters_workload()
     if args.counters_int4:
