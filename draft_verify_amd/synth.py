@@ -36,6 +36,13 @@ SHAPES = {
                       eps=1e-6, rope_theta=1e6),
     "dense_32b": dict(n_layers=64, hidden=5120, n_q=64, n_kv=8, head_dim=128, ffn=25600,
                       vocab=151936, eps=1e-6, rope_theta=1e6),
+    # sliding-window layers: the tiny decoder with layer 0 attending only its
+    # last 24 positions (layer 1 stays global), and a 4-layer variant of the
+    # 4B attention geometry with a 1024-position window on layers 0 and 2
+    "tiny_swa": dict(n_layers=2, hidden=64, n_q=4, n_kv=2, head_dim=16, ffn=128, vocab=256,
+                     eps=1e-6, rope_theta=1e6, swa_window=24, swa_layers=0b01),
+    "attn_4b_swa": dict(n_layers=4, hidden=512, n_q=32, n_kv=8, head_dim=128, ffn=512, vocab=1024,
+                        eps=1e-6, rope_theta=1e6, swa_window=1024, swa_layers=0b0101),
     # the attention geometry of the Qwen3-4B shape (32q/8kv heads of 128) and
     # of the 32B-class shape (64q/8kv heads of 128) on a narrow trunk (hidden
     # 512): long contexts at the real head layout, with projections small

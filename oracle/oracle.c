@@ -29,6 +29,10 @@
  *     off a match of two or more tokens), written as a brute-force search.
  *   - Adaptive K: start at 1, add 2 after a fully accepted round, subtract 1
  *     after any rejection, clamp to [1, cap] (coreai note, adaptive-K section).
+ *   - Sliding-window layers (TensorSharp page, sliding-window section): a
+ *     layer marked local attends, from the row at position t, only the keys
+ *     at positions [t - W + 1, t]; the cache stays a plain linear one here,
+ *     so rewinding it is exact by definition.
  *   - Sampled verification: each row draws its token (Gumbel-max over the
  *     logits divided by the temperature, with Philox4x32-10 noise keyed by the
  *     seed, the sequence and the row's position) and drafts are accepted while
@@ -62,6 +66,8 @@ typedef struct {
   int32_t n_layers, hidden, n_q, n_kv, head_dim, ffn, vocab;
   float eps;
   double rope_theta;
+  int32_t swa_window;  /* > 0: the layers in swa_layers attend only the last swa_window positions */
+  uint64_t swa_layers; /* bit l: layer l is a sliding-window layer */
 } orc_shape;
 
 typedef struct {
@@ -246,7 +252,7 @@ ORC_API int orc_argmax(const float* v, int n, float* margin) {
 
 ORC_API orc_model* orc_new(const orc_shape* s, int max_ctx, int n_seq) {
   if (!s || max_ctx <= 0 || n_seq <= 0) return NULL;
-  if (s->head_dim % 2 || s->n_q % s->n_kv) return NULL;
+  if (s->head_dim % 2 || s->n_q % s->n_kv || s->swa_window < 0) return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
   if (!m) return NULL;
   m->s = *s;
@@ -355,6 +361,7 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
 
   for (int l = 0; l < s->n_layers; ++l) {
     const orc_mat* W = m->lay + (size_t)l * ORC_NW;
+    const int local = s->swa_window > 0 && l < 64 && ((s->swa_layers >> l) & 1u);
     for (int r = 0; r < n; ++r) orc_rmsnorm(X + (size_t)r * H, m->g_attn[l], H, s->eps, U + (size_t)r * H);
     transpose(U, n, H, Ut);
     matmul(&W[ORC_WQ], Ut, n, Q);
@@ -386,8 +393,19 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
 #else
           const int g = h / G;
 #endif
-          orc_attend(Q + (size_t)r * DQ + h * hd, kv_row(m, m->kc, seq, l, 0) + g * hd,
-                     kv_row(m, m->vc, seq, l, 0) + g * hd, p + r, DK, hd, O + (size_t)r * DQ + h * hd,
+          /* keys [lo, p + r]: all earlier positions, or the last W of a
+           * sliding-window layer */
+          int lo = 0;
+          if (local) {
+#if ORC_PLANT == 15
+            lo = p + r - s->swa_window;
+#else
+            lo = p + r - s->swa_window + 1;
+#endif
+            if (lo < 0) lo = 0;
+          }
+          orc_attend(Q + (size_t)r * DQ + h * hd, kv_row(m, m->kc, seq, l, lo) + g * hd,
+                     kv_row(m, m->vc, seq, l, lo) + g * hd, p + r - lo, DK, hd, O + (size_t)r * DQ + h * hd,
                      scratch);
         }
       free(scratch);

@@ -39,7 +39,8 @@ class OracleError(RuntimeError):
 class _Shape(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q", C.c_int32),
                 ("n_kv", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
-                ("vocab", C.c_int32), ("eps", C.c_float), ("rope_theta", C.c_double)]
+                ("vocab", C.c_int32), ("eps", C.c_float), ("rope_theta", C.c_double),
+                ("swa_window", C.c_int32), ("swa_layers", C.c_uint64)]
 
 
 _LIBS = {}
@@ -239,7 +240,7 @@ class Oracle:
         self.shape = dict(shape)
         s = _Shape(shape["n_layers"], shape["hidden"], shape["n_q"], shape["n_kv"],
                    shape["head_dim"], shape["ffn"], shape["vocab"], shape["eps"],
-                   shape["rope_theta"])
+                   shape["rope_theta"], shape.get("swa_window", 0), shape.get("swa_layers", 0))
         self.h = self.lib.orc_new(C.byref(s), max_ctx, n_seq)
         if not self.h:
             raise OracleError("orc_new failed")

@@ -351,8 +351,45 @@ def pin_sampled_planted_and_spec_equals_off(lib=None):
         assert orc.cache_len() == p + m + 1
 
 
+SWA = dict(n_layers=3, hidden=64, n_q=4, n_kv=2, head_dim=16, ffn=128, vocab=256,
+           eps=1e-6, rope_theta=1e6, swa_window=5, swa_layers=0b101)
+
+
+def pin_torch_swa(lib=None):
+    """Sliding-window layers (0 and 2 of 3, window 5) against torch SDPA with
+    a band mask, over 20 positions (the window slides 15 times)."""
+    return _torch_vs_oracle(SWA, "bf16", 20, 1e-4, lib)
+
+
+def pin_swa_window_limits(lib=None):
+    """A window covering the whole context is plain causal attention (bit for
+    bit); the rows gate and spec-on == spec-off hold past the window."""
+    full = dict(SWA, swa_window=64)
+    w, orc_w = _model(full, lib=lib)
+    plain = {k: v for k, v in full.items() if k not in ("swa_window", "swa_layers")}
+    orc_p = O.Oracle(plain, synth.to_numpy(w), max_ctx=128, lib_path=lib)
+    toks = synth.uniform_prompt(12, SWA["vocab"], 40)
+    _, _, a = orc_w.forward(toks, want_logits=True)
+    _, _, b = orc_p.forward(toks, want_logits=True)
+    assert np.array_equal(a, b), "a window wider than the context must change nothing"
+    shape = synth.SHAPES["tiny_swa"]
+    _, orc = _model(shape, lib=lib)
+    prompt = synth.motif_prompt(1, shape["vocab"])
+    orc.prefill(prompt)
+    p = orc.cache_len()
+    span = synth.uniform_prompt(5, shape["vocab"], 9)
+    _, _, multi = orc.forward(span, want_logits=True)
+    orc.rewind(p)
+    rows = [orc.forward(span[i:i + 1], want_logits=True)[2][0] for i in range(9)]
+    assert np.array_equal(multi, np.stack(rows)), "sliding-window rows gate"
+    off, _ = orc.generate(prompt, 48, spec=False)
+    on, st = orc.generate(prompt, 48, spec=True, fixed_k=4)
+    assert off == on and st["accepted"] > 0, "sliding-window spec-on differs from spec-off"
+
+
 ALL_PINS = [pin_torch_tiny, pin_torch_wide, pin_torch_int4, pin_closed_forms, pin_argmax,
             pin_rows_gate, pin_accept_golden, pin_verify_planted, pin_rewind_stale,
             pin_spec_equals_off, pin_ngram_golden, pin_adapt_k_golden, pin_int4_nibbles,
             pin_multiseq, pin_philox_kat, pin_uniform_gumbel_closed_forms, pin_gumbel_max_is_softmax,
-            pin_sampled_low_temperature_is_greedy, pin_sampled_planted_and_spec_equals_off]
+            pin_sampled_low_temperature_is_greedy, pin_sampled_planted_and_spec_equals_off, pin_torch_swa,
+            pin_swa_window_limits]

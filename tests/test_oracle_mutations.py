@@ -21,6 +21,7 @@ PLANTS = {
     12: "K rows of a span all written at the first position",
     13: "Philox round mixes the second key word into the first output word",
     14: "sampling multiplies the logits by the temperature instead of dividing",
+    15: "a sliding-window row sees one key too many (window W + 1)",
 }
 
 

@@ -2,8 +2,8 @@
 
 It pins the CPU oracle against library definitions rather than against a copy
 of its own formulas: RMSNorm is torch.nn.functional.rms_norm, attention is
-scaled_dot_product_attention with its own causal mask and grouped-query
-mapping (enable_gqa), the MLP gate uses F.silu, and the rotary embedding is a
+scaled_dot_product_attention with its own causal (or, for a sliding-window
+layer, band) mask built from torch.tril and grouped-query mapping (enable_gqa), the MLP gate uses F.silu, and the rotary embedding is a
 complex multiplication (torch.polar) instead of the oracle's real-valued
 rotate-half formula.  Only the conventions the pages leave open are shared by
 construction: rotate-half pairing (i, i + d/2), base theta, epsilon, untied
@@ -43,13 +43,19 @@ def logits(shape: dict, w: dict, tokens) -> np.ndarray:
         c = torch.complex(z[..., : hd // 2], z[..., hd // 2:]) * rot[:, None, :]
         return torch.cat([c.real, c.imag], dim=-1)
 
-    for L in w["layers"]:
+    W = shape.get("swa_window", 0)
+    causal = torch.ones(T, T, dtype=torch.bool).tril()
+    # a sliding-window layer: query i sees keys j with i - W < j <= i (a band mask)
+    band = causal & ~torch.ones(T, T, dtype=torch.bool).tril(-W) if W else causal
+    for li, L in enumerate(w["layers"]):
         u = F.rms_norm(x, (H,), weight=_f64(L["g_attn"]), eps=eps)
         q = rope(F.linear(u, _f64(L["wq"])).view(T, nq, hd))
         k = rope(F.linear(u, _f64(L["wk"])).view(T, nkv, hd))
         v = F.linear(u, _f64(L["wv"])).view(T, nkv, hd)
+        local = W and (shape.get("swa_layers", 0) >> li) & 1
         o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
-                                           is_causal=True, scale=1.0 / math.sqrt(hd), enable_gqa=True)
+                                           attn_mask=band if local else causal,
+                                           scale=1.0 / math.sqrt(hd), enable_gqa=True)
         x = x + F.linear(o.transpose(0, 1).reshape(T, nq * hd), _f64(L["wo"]))
         u = F.rms_norm(x, (H,), weight=_f64(L["g_ffn"]), eps=eps)
         x = x + F.linear(F.silu(F.linear(u, _f64(L["wg"]))) * F.linear(u, _f64(L["wu"])), _f64(L["wd"]))
