@@ -76,6 +76,8 @@ struct GemmParams {
   int S, n_q, n_kv, hd;
   const float* rope;     // [max_ctx][hd/2][2] = cos, sin
   const int32_t* rowinfo;// [R][2]: each row's absolute position and its KV block (k_embed)
+  int ring_nb, ring_w;   // sliding-window layer: the KV rows go to the sequence's ring of ring_w
+                         // slots (ring_nb blocks): block seq * ring_nb + (pos % ring_w) / 16; else 0
   // EPI_RESID
   float* x;              // residual [R][N]
   float* ss_out;         // [R][N/64] partial sums of squares of the new residual
@@ -113,6 +115,11 @@ struct AttnParams {
   int n_qt;              // query tiles per sequence: ceil(S * n_q / n_kv / 16)
   int tpw;               // query tiles per workgroup (1..n_qt), taken one after another
   int fuse;              // short contexts: the last split of a tile merges it in k_attn
+  // sliding-window layer (win > 0): row at position t attends keys [t - win + 1, t],
+  // read from the sequence's ring (block seq_ids[b] * ring_nb + (position / 16) % ring_nb);
+  // grid.x covers grid_splits splits from the first one the window touches
+  int win, ring_nb, ring_w, grid_splits;
+  const int32_t* seq_ids;
 };
 // The attention merges its splits in the same kernel when every context of
 // the step (cache + span) spans at most attn_fuse_splits(hd) splits of 256

@@ -557,6 +557,8 @@ __device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, f
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
   const int slot = pos & 15;
+  // a sliding-window layer keeps its KV rows in the sequence's ring
+  if (P.ring_nb && c >= DQ) blk = P.seq_ids[r / P.S] * P.ring_nb + ((pos % P.ring_w) >> 4);
   if (c < DQ + DK) {
     const int local = c < DQ ? c : c - DQ;
     const int head = local / hd, j = (local % hd) >> 1;
@@ -1492,7 +1494,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   constexpr int DT = HD / 16;          // 16-row tiles of O^T
   constexpr int FS = attn_fuse_splits(HD);
   static_assert(16 * FS * 2 <= 4 * 16 * (HD + 1), "the fused merge's split table fits sO");
-  const int split = blockIdx.x, kvh = blockIdx.y;
+  const int kvh = blockIdx.y;
   const int n_tg = (P.n_qt + P.tpw - 1) / P.tpw;  // groups of tpw query tiles
   const int b = blockIdx.z / n_tg, tg = blockIdx.z - b * n_tg;
   const int qt0 = tg * P.tpw, qt1 = min(P.n_qt, qt0 + P.tpw);
@@ -1503,25 +1505,44 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   // The context length and this wave's four block ids load together (ids
   // clamped to the table row; blocks past the context take the sequence's
   // block 0 and are zeroed below), then K, V and the queries.
-  const int32_t* btrow = P.slotbt + (size_t)b * P.bt_stride;
-  const int kb0 = split * 16 + wave * 4;
-  int bv[4];
+  int blk[4];
+  int p, total, n_act, split, kb0, s_lo;
+  if (P.win) {
+    // Sliding window: the ring's block ids follow from the positions, so only
+    // the cache length and the sequence id are loaded; the grid starts at the
+    // first split the window of row 0 touches.
+    p = P.rowinfo[2 * b * S];
+    const int seq = P.seq_ids[b];
+    total = p + S;
+    s_lo = max(0, p - P.win + 1) >> 8;
+    split = blockIdx.x + s_lo;
+    n_act = ((total - 1) >> 8) - s_lo + 1;
+    if ((int)blockIdx.x >= n_act) return;
+    kb0 = split * 16 + wave * 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) bv[t] = btrow[kb0 + t < P.bt_stride ? kb0 + t : 0];
-  const int bz = btrow[0];
-  // every id is loaded before anything branches on the context length
-  asm volatile("" ::"v"(bv[0]), "v"(bv[1]), "v"(bv[2]), "v"(bv[3]), "v"(bz));
-  const int p = P.rowinfo[2 * b * S];
-  const int total = p + S;
-  const int n_act = (total + 255) >> 8;
-  if (split >= n_act) return;
+    for (int t = 0; t < 4; ++t) blk[t] = seq * P.ring_nb + (kb0 + t) % P.ring_nb;
+  } else {
+    split = blockIdx.x;
+    s_lo = 0;
+    const int32_t* btrow = P.slotbt + (size_t)b * P.bt_stride;
+    kb0 = split * 16 + wave * 4;
+    int bv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bv[t] = btrow[kb0 + t < P.bt_stride ? kb0 + t : 0];
+    const int bz = btrow[0];
+    // every id is loaded before anything branches on the context length
+    asm volatile("" ::"v"(bv[0]), "v"(bv[1]), "v"(bv[2]), "v"(bv[3]), "v"(bz));
+    p = P.rowinfo[2 * b * S];
+    total = p + S;
+    n_act = (total + 255) >> 8;
+    if (split >= n_act) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) blk[t] = (kb0 + t) * 16 < total ? bv[t] : bz;
+  }
 
   __shared__ float sO[4][16][HD + 1];
   __shared__ float sM[4][16], sL[4][16], sF[4][16];
 
-  int blk[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) blk[t] = (kb0 + t) * 16 < total ? bv[t] : bz;
   int qt = qt0;
   int col = qt * 16 + c16;
   bool qok = col < QC;
@@ -1583,7 +1604,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = (kb0 + t) * 16 + g4 * 4 + i;
-      s[t][i] = (qok && key <= pos_q) ? acc[i] * P.scale : -INFINITY;
+      const bool vis = qok && key <= pos_q && (P.win == 0 || key > pos_q - P.win);
+      s[t][i] = vis ? acc[i] * P.scale : -INFINITY;
       mx = fmaxf(mx, s[t][i]);
     }
   }
@@ -1716,10 +1738,14 @@ __device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p,
   const bool cok = qcol < QC;
   const int qc = cok ? qcol : 0;
   const int iq = qc / G, head = kvh * G + qc % G;
-  int nsp = cok ? ((p + iq) >> 8) + 1 : 0;
+  // the column's splits: from the first its window touches (0 unless the
+  // layer has a sliding window) to the one holding its own position
+  const int sp0 = P.win ? max(0, p + iq - P.win + 1) >> 8 : 0;
+  int nsp = cok ? ((p + iq) >> 8) + 1 - sp0 : 0;
   nsp = nsp < MS ? nsp : MS;
   const size_t stride = (size_t)(P.n_seq * QC) * (HD + 2);
-  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qc) * (HD + 2);
+  const float* base = P.part + ((size_t)kvh * P.max_splits * (P.n_seq * QC) + b * QC + qc) * (HD + 2) +
+                      (size_t)sp0 * stride;
   float* ml = sML + (size_t)c * MS * 2;
 
   float2 mlv[MS / 16];
@@ -2091,7 +2117,10 @@ hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
   const int n_qt = (p.S * (p.n_q / p.n_kv) + 15) / 16;
   if (p.n_qt != n_qt || p.tpw < 1 || p.tpw > n_qt || p.n_seq < 1 || p.n_seq * n_qt > 65535)
     return hipErrorInvalidValue;
-  const dim3 grid(p.max_splits, p.n_kv, p.n_seq * ((n_qt + p.tpw - 1) / p.tpw));
+  if (p.win && (p.win < 1 || p.ring_nb < 1 || p.ring_w != 16 * p.ring_nb || !p.seq_ids || p.grid_splits < 1 ||
+                p.grid_splits > p.max_splits))
+    return hipErrorInvalidValue;
+  const dim3 grid(p.win ? p.grid_splits : p.max_splits, p.n_kv, p.n_seq * ((n_qt + p.tpw - 1) / p.tpw));
   const dim3 cgrid(n_qt, p.n_kv, p.n_seq);
   switch (hd) {
     case 128:

@@ -121,7 +121,13 @@ struct Layout {
   std::vector<LayerOff> lay;
   size_t emb, wlm, g_final, weights_bytes;
   // kv
-  size_t kv_layer_bytes, kv_half_bytes, kv_bytes;
+  // per layer: its K region at kv_off[l], V at kv_off[l] + kv_half[l]; a
+  // global layer holds the paged pool, a sliding-window layer one ring of
+  // ring_nb blocks per sequence
+  std::vector<size_t> kv_off, kv_half;
+  std::vector<char> local;   // per layer: sliding-window layer
+  int win, ring_nb, ring_w, win_splits;
+  size_t kv_bytes;
   // workspace
   size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
   size_t af2; // the same for O and down, written by their producers
@@ -159,6 +165,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (d.max_rows < 1 || d.max_rows > SPEC_MAX_ROWS) return fail("max_rows must be in [1, 128]");
   if (d.max_ctx < 1 || d.max_seqs < 1) return fail("max_ctx and max_seqs must be positive");
   if (!(d.rms_eps >= 0.0f) || !(d.rope_theta > 0.0)) return fail("rms_eps must be >= 0 and rope_theta > 0");
+  if (d.swa_window < 0 || d.reserved != 0) return fail("swa_window must be >= 0 and reserved 0");
+  if (d.swa_window > 0 && (d.swa_layers == 0 || (d.n_layers < 64 && (d.swa_layers >> d.n_layers) != 0)))
+    return fail("swa_layers must name at least one existing layer when swa_window > 0");
   Lo.H = d.hidden; Lo.nq = d.n_q_heads; Lo.nkv = d.n_kv_heads; Lo.hd = d.head_dim; Lo.F = d.ffn; Lo.V = d.vocab;
   Lo.L = d.n_layers;
   Lo.DQ = Lo.nq * Lo.hd; Lo.DK = Lo.nkv * Lo.hd; Lo.Nqkv = Lo.DQ + 2 * Lo.DK; Lo.Ngu = 2 * Lo.F;
@@ -226,9 +235,28 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.g_final = take((size_t)Lo.H * 4);
   Lo.weights_bytes = off;
 
-  Lo.kv_half_bytes = align_up((size_t)Lo.n_blocks * Lo.nkv * SPEC_BLOCK_TOKENS * Lo.hd * 2);
-  Lo.kv_layer_bytes = 2 * Lo.kv_half_bytes;
-  Lo.kv_bytes = Lo.kv_layer_bytes * Lo.L;
+  // Sliding-window layers keep a ring of ring_w = W + 16 slots (rounded up
+  // to whole blocks) per sequence: a verify of at most 16 rows writes its rows
+  // at their slots (position mod ring_w) without touching any position that
+  // it, or any later query after a partial rejection, still attends to, so no
+  // row ever needs restoring.
+  Lo.win = d.swa_window;
+  Lo.local.assign((size_t)Lo.L, 0);
+  if (Lo.win > 0)
+    for (int l = 0; l < Lo.L && l < 64; ++l) Lo.local[(size_t)l] = (d.swa_layers >> l) & 1u ? 1 : 0;
+  Lo.ring_w = Lo.win > 0 ? (Lo.win + SPEC_MAX_SPAN + 15) / 16 * 16 : 0;
+  Lo.ring_nb = Lo.ring_w / 16;
+  // splits of 256 keys one row group's window can touch
+  Lo.win_splits = Lo.win > 0 ? std::min(Lo.max_splits, (Lo.win + SPEC_MAX_SPAN - 1 + 255) / 256 + 1) : 0;
+  Lo.kv_off.resize((size_t)Lo.L);
+  Lo.kv_half.resize((size_t)Lo.L);
+  Lo.kv_bytes = 0;
+  for (int l = 0; l < Lo.L; ++l) {
+    const size_t blocks = Lo.local[(size_t)l] ? (size_t)Lo.max_seqs * Lo.ring_nb : (size_t)Lo.n_blocks;
+    Lo.kv_off[(size_t)l] = Lo.kv_bytes;
+    Lo.kv_half[(size_t)l] = align_up(blocks * Lo.nkv * SPEC_BLOCK_TOKENS * Lo.hd * 2);
+    Lo.kv_bytes += 2 * Lo.kv_half[(size_t)l];
+  }
 
   const size_t R = (size_t)Lo.max_rows;
   off = 0;
@@ -304,6 +332,7 @@ struct spec_ctx {
   int mm_grid = 1;       // most workgroups of a one-pass GEMM (they walk the column blocks)
   int attn_fuse = 0;     // the current step's contexts are short: attention combines in one kernel
   int attn_tpw = 1;      // the current step's query tiles per attention workgroup
+  int attn_fuse_l = 0, attn_tpw_l = 1;  // the same for the sliding-window layers
   hipEvent_t ev0 = nullptr, ev1 = nullptr;  // verify forward timing (spec_get_stats)
   int static_dev = -1;   // spec_create_static: the device whose scratch is the workspace
   float temp = 0.0f;     // spec_set_sampling: 0 greedy, > 0 sampled rows
@@ -321,8 +350,8 @@ struct spec_ctx {
   int32_t* h_result() { return (int32_t*)(HB + lo.host_result); }
   int32_t* h_kvlen() { return (int32_t*)(HB + lo.host_kvlen); }
   int32_t* h_bt() { return (int32_t*)(HB + lo.host_bt); }
-  _Float16* kpool(int l) { return (_Float16*)(KV + (size_t)l * lo.kv_layer_bytes); }
-  _Float16* vpool(int l) { return (_Float16*)(KV + (size_t)l * lo.kv_layer_bytes + lo.kv_half_bytes); }
+  _Float16* kpool(int l) { return (_Float16*)(KV + lo.kv_off[(size_t)l]); }
+  _Float16* vpool(int l) { return (_Float16*)(KV + lo.kv_off[(size_t)l] + lo.kv_half[(size_t)l]); }
 };
 
 namespace {
@@ -521,6 +550,8 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.hd = L.hd;
       g.rope = c->ws<float>(L.rope);
       g.rowinfo = c->ws<int32_t>(L.rowinfo);
+      g.ring_nb = L.local[(size_t)l] ? L.ring_nb : 0;
+      g.ring_w = L.local[(size_t)l] ? L.ring_w : 0;
       HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
@@ -543,8 +574,14 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.out = c->ws<float>(L.o);
       a.af_out = c->af_next(L.nk_o, R);
       a.n_qt = (S * L.G + 15) / 16;
-      a.tpw = std::min(c->attn_tpw, a.n_qt);
-      a.fuse = c->attn_fuse;
+      const bool loc = L.local[(size_t)l] != 0;
+      a.tpw = std::min(loc ? c->attn_tpw_l : c->attn_tpw, a.n_qt);
+      a.fuse = loc ? c->attn_fuse_l : c->attn_fuse;
+      a.win = loc ? L.win : 0;
+      a.ring_nb = loc ? L.ring_nb : 0;
+      a.ring_w = loc ? L.ring_w : 0;
+      a.grid_splits = loc ? L.win_splits : L.max_splits;
+      a.seq_ids = seq_ids;
       HIPCHK(c, launch_attn(a, L.hd, st));
       return SPEC_OK;
     }
@@ -601,7 +638,8 @@ int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
 }
 
 int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
-  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16) | ((c->attn_tpw > 1) << 17));
+  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16) | ((c->attn_tpw > 1) << 17) | (c->attn_fuse_l << 18) |
+                                       ((c->attn_tpw_l > 1) << 19));
   auto it = c->graphs.find(key);
   if (it != c->graphs.end()) {
     *out = it->second;
@@ -643,6 +681,11 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   // the columns over the chip.
   c->attn_fuse = (splits <= std::min(SPECV_ATTN_FUSE_SPLITS, attn_fuse_splits(L.hd)) &&
                   std::min(c->attn_tpw, n_qt) <= 2) ? 1 : 0;
+  // sliding-window layers: at most the splits a window touches
+  const int splits_l = L.win > 0 ? std::min(splits, L.win_splits) : splits;
+  c->attn_tpw_l = (size_t)n_seq * L.nkv * splits_l >= 256 ? 16 : 1;
+  c->attn_fuse_l = (splits_l <= std::min(SPECV_ATTN_FUSE_SPLITS, attn_fuse_splits(L.hd)) &&
+                    std::min(c->attn_tpw_l, n_qt) <= 2) ? 1 : 0;
   StepDev* sd = (StepDev*)c->h_step();
   sd->mode = mode;
   sd->n_seq = n_seq;

@@ -68,6 +68,17 @@ typedef struct spec_model_desc {
   int32_t max_rows;      /* rows per forward (n_seq * (K+1)), 1..SPEC_MAX_ROWS */
   int32_t n_blocks;      /* 16-token KV blocks in the pool (0: max_seqs*ceil(max_ctx/16)) */
   uint32_t flags;        /* SPEC_FLAG_* */
+  /* Sliding-window layers (TensorSharp page, sliding-window section): each
+   * layer l < 64 with bit l of swa_layers set attends, from a row at position
+   * t, only the keys at positions [t - swa_window + 1, t], and keeps its KV
+   * rows in a ring per sequence of swa_window + 16 slots (rounded up to whole
+   * 16-token blocks).  A verify writes its rows at their true positions; the
+   * ring's 16 spare slots are what keeps every position any row (of this
+   * verify, or after a partial rejection) still attends to, so rewinding a
+   * ring layer is exact and nothing is backed up.  0: no sliding window. */
+  int32_t swa_window;
+  int32_t reserved;      /* 0 */
+  uint64_t swa_layers;
 } spec_model_desc;
 
 /* Sizes of the caller-owned buffers for a description. */
