@@ -43,6 +43,13 @@ SHAPES = {
                      eps=1e-6, rope_theta=1e6, swa_window=24, swa_layers=0b01),
     "attn_4b_swa": dict(n_layers=4, hidden=512, n_q=32, n_kv=8, head_dim=128, ffn=512, vocab=1024,
                         eps=1e-6, rope_theta=1e6, swa_window=1024, swa_layers=0b0101),
+    # recurrent (delta-rule) layers: a 3-layer tiny decoder whose middle layer
+    # is recurrent (write strength 0.5), and a 4-layer variant of the 4B
+    # attention geometry (heads of 128) with recurrent layers 1 and 3
+    "tiny_rec": dict(n_layers=3, hidden=64, n_q=4, n_kv=2, head_dim=16, ffn=128, vocab=256,
+                     eps=1e-6, rope_theta=1e6, rec_layers=0b010, rec_beta=0.5),
+    "attn_4b_rec": dict(n_layers=4, hidden=512, n_q=32, n_kv=8, head_dim=128, ffn=512, vocab=1024,
+                        eps=1e-6, rope_theta=1e6, rec_layers=0b1010, rec_beta=0.5),
     # the attention geometry of the Qwen3-4B shape (32q/8kv heads of 128) and
     # of the 32B-class shape (64q/8kv heads of 128) on a narrow trunk (hidden
     # 512): long contexts at the real head layout, with projections small

@@ -33,6 +33,14 @@
  *     layer marked local attends, from the row at position t, only the keys
  *     at positions [t - W + 1, t]; the cache stays a plain linear one here,
  *     so rewinding it is exact by definition.
+ *   - Recurrent layers (TensorSharp page, recurrent-trunk section: a layer
+ *     whose state a dropped tail cannot roll back): a delta rule per kv head
+ *     with the state S [d_v][d_k], updated row by row with the normalised key
+ *     and value of the row, S <- S + beta (v - S k) k^T, and read by each
+ *     normalised query of the head's group, o = S q (no positional rotation).
+ *     A verify that rejects drafts restores the state from before the verify
+ *     and runs the accepted rows through again -- the slow, plain way the
+ *     page describes before per-row snapshots.
  *   - Sampled verification: each row draws its token (Gumbel-max over the
  *     logits divided by the temperature, with Philox4x32-10 noise keyed by the
  *     seed, the sequence and the row's position) and drafts are accepted while
@@ -68,6 +76,8 @@ typedef struct {
   double rope_theta;
   int32_t swa_window;  /* > 0: the layers in swa_layers attend only the last swa_window positions */
   uint64_t swa_layers; /* bit l: layer l is a sliding-window layer */
+  uint64_t rec_layers; /* bit l: layer l is a recurrent (delta-rule) layer instead of attention */
+  float rec_beta;      /* the delta rule's write strength */
 } orc_shape;
 
 typedef struct {
@@ -88,6 +98,7 @@ typedef struct orc_model {
   float* kc;              /* [n_seq][n_layers][max_ctx][n_kv*head_dim] */
   float* vc;
   int* len;               /* cache length per sequence */
+  float* rs;              /* recurrent states [n_seq][n_layers][n_kv][head_dim (v)][head_dim (k)], or NULL */
 } orc_model;
 
 /* ---------------------------------------------------------------- scalars */
@@ -225,6 +236,39 @@ ORC_API void orc_attend(const float* q, const float* K, const float* V, int t, i
 
 ORC_API float orc_silu(float g) { return g / (1.0f + expf(-g)); }
 
+/* One delta-rule write into the state S [hd (v)][hd (k)]: with k^ = k / |k|,
+ * u = S k^ and S <- S + beta (v - u) k^^T; a later read with key k^ then
+ * returns u + beta (v - u) (exactly v for beta = 1). */
+ORC_API void orc_delta_write(float* S, int hd, const float* k, const float* v, float beta) {
+  float kk = 0.0f;
+  for (int d = 0; d < hd; ++d) kk = kk + k[d] * k[d];
+  const float nrm = sqrtf(kk);
+  float kh[512];
+#if ORC_PLANT == 16
+  for (int d = 0; d < hd; ++d) kh[d] = k[d];
+#else
+  for (int d = 0; d < hd; ++d) kh[d] = k[d] / nrm;
+#endif
+  for (int i = 0; i < hd; ++i) {
+    float u = 0.0f;
+    for (int d = 0; d < hd; ++d) u = u + S[(size_t)i * hd + d] * kh[d];
+    const float c = beta * (v[i] - u);
+    for (int d = 0; d < hd; ++d) S[(size_t)i * hd + d] = S[(size_t)i * hd + d] + c * kh[d];
+  }
+}
+
+/* A read of S with the normalised query: o = S (q / |q|). */
+ORC_API void orc_delta_read(const float* S, int hd, const float* q, float* o) {
+  float qq = 0.0f;
+  for (int d = 0; d < hd; ++d) qq = qq + q[d] * q[d];
+  const float nrm = sqrtf(qq);
+  for (int i = 0; i < hd; ++i) {
+    float a = 0.0f;
+    for (int d = 0; d < hd; ++d) a = a + S[(size_t)i * hd + d] * (q[d] / nrm);
+    o[i] = a;
+  }
+}
+
 /* Largest value, lowest index on ties; NaN is an error (returns -1). */
 ORC_API int orc_argmax(const float* v, int n, float* margin) {
   int best = -1;
@@ -253,6 +297,7 @@ ORC_API int orc_argmax(const float* v, int n, float* margin) {
 ORC_API orc_model* orc_new(const orc_shape* s, int max_ctx, int n_seq) {
   if (!s || max_ctx <= 0 || n_seq <= 0) return NULL;
   if (s->head_dim % 2 || s->n_q % s->n_kv || s->swa_window < 0) return NULL;
+  if (s->rec_layers && (s->head_dim > 512 || !(s->rec_beta > 0.0f))) return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
   if (!m) return NULL;
   m->s = *s;
@@ -265,8 +310,10 @@ ORC_API orc_model* orc_new(const orc_shape* s, int max_ctx, int n_seq) {
   m->kc = (float*)calloc(kv, sizeof(float));
   m->vc = (float*)calloc(kv, sizeof(float));
   m->len = (int*)calloc((size_t)n_seq, sizeof(int));
-  if (!m->lay || !m->g_attn || !m->g_ffn || !m->kc || !m->vc || !m->len) {
-    free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len); free(m);
+  if (s->rec_layers)
+    m->rs = (float*)calloc((size_t)n_seq * s->n_layers * s->n_kv * s->head_dim * s->head_dim, sizeof(float));
+  if (!m->lay || !m->g_attn || !m->g_ffn || !m->kc || !m->vc || !m->len || (s->rec_layers && !m->rs)) {
+    free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len); free(m->rs); free(m);
     return NULL;
   }
   return m;
@@ -274,7 +321,7 @@ ORC_API orc_model* orc_new(const orc_shape* s, int max_ctx, int n_seq) {
 
 ORC_API void orc_free(orc_model* m) {
   if (!m) return;
-  free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len);
+  free(m->lay); free(m->g_attn); free(m->g_ffn); free(m->kc); free(m->vc); free(m->len); free(m->rs);
   free(m);
 }
 
@@ -310,10 +357,20 @@ ORC_API int orc_cache_len(const orc_model* m, int seq) {
   return m->len[seq];
 }
 
-/* Rewind only: the cache can be shortened, never lengthened. */
+/* Rewind only: the cache can be shortened, never lengthened.  A model with
+ * recurrent layers keeps no state for earlier lengths: only its current
+ * length or 0 (which empties the sequence) is accepted. */
+static size_t rec_floats(const orc_model* m) {
+  return (size_t)m->s.n_layers * m->s.n_kv * m->s.head_dim * m->s.head_dim;
+}
+
 ORC_API int orc_rewind(orc_model* m, int seq, int len) {
   if (!m || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
   if (len < 0 || len > m->len[seq]) return ORC_ESTATE;
+  if (m->rs && len != m->len[seq]) {
+    if (len != 0) return ORC_ESTATE;
+    memset(m->rs + (size_t)seq * rec_floats(m), 0, sizeof(float) * rec_floats(m));
+  }
   m->len[seq] = len;
   return ORC_OK;
 }
@@ -338,6 +395,12 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
   if (p + n > m->max_ctx) return ORC_ECAPACITY;
   for (int r = 0; r < n; ++r)
     if (toks[r] < 0 || toks[r] >= V) return ORC_EINVAL;
+  float* rs0 = NULL;  /* a failed forward leaves the recurrent state as it was */
+  if (m->rs) {
+    rs0 = (float*)malloc(sizeof(float) * rec_floats(m));
+    if (!rs0) return ORC_ENOMEM;
+    memcpy(rs0, m->rs + (size_t)seq * rec_floats(m), sizeof(float) * rec_floats(m));
+  }
 
   const size_t big = (size_t)n * (size_t)(F > DQ ? (F > H ? F : H) : (DQ > H ? DQ : H));
   float* X = (float*)malloc(sizeof(float) * (size_t)n * H);
@@ -367,7 +430,18 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
     matmul(&W[ORC_WQ], Ut, n, Q);
     matmul(&W[ORC_WK], Ut, n, Kn);
     matmul(&W[ORC_WV], Ut, n, Vn);
-    for (int r = 0; r < n; ++r) {
+    const int rec = l < 64 && ((s->rec_layers >> l) & 1u);
+    if (rec) {
+      /* the rows in order through the state of each kv head; no cache rows */
+      for (int r = 0; r < n; ++r)
+        for (int g = 0; g < nkv; ++g) {
+          float* S = m->rs + (((size_t)seq * s->n_layers + l) * nkv + g) * hd * hd;
+          orc_delta_write(S, hd, Kn + (size_t)r * DK + g * hd, Vn + (size_t)r * DK + g * hd, s->rec_beta);
+          for (int j = 0; j < G; ++j)
+            orc_delta_read(S, hd, Q + (size_t)r * DQ + (g * G + j) * hd, O + (size_t)r * DQ + (g * G + j) * hd);
+        }
+    }
+    for (int r = 0; !rec && r < n; ++r) {
 #if ORC_PLANT == 11
       const int pos = r;
 #else
@@ -382,6 +456,7 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
 #endif
       memcpy(kv_row(m, m->vc, seq, l, p + r), Vn + (size_t)r * DK, sizeof(float) * DK);
     }
+    if (!rec)
 #pragma omp parallel
     {
       float* scratch = (float*)malloc(sizeof(float) * (size_t)(p + n));
@@ -455,8 +530,40 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
     }
   }
   if (rc == ORC_OK) m->len[seq] = p + n;
+  else if (rs0) memcpy(m->rs + (size_t)seq * rec_floats(m), rs0, sizeof(float) * rec_floats(m));
+  free(rs0);
   free(X); free(U); free(Ut); free(Q); free(Kn); free(Vn); free(O); free(Y); free(Gt); free(Up);
   return rc;
+}
+
+/* After a verify of K+1 rows from length p accepted m drafts: a model with
+ * recurrent layers goes back to the state before the verify (rs0) and runs
+ * rows 0..m again, so its state is the one after row m; the cache rows they
+ * rewrite are the same.  Leaves the length at p + m + 1. */
+static int commit_accepted(orc_model* m, int seq, const int32_t* span, int K, int p, int mm, const float* rs0) {
+#if ORC_PLANT == 17
+  (void)span; (void)K; (void)rs0;
+#else
+  if (m->rs && mm < K) {
+    memcpy(m->rs + (size_t)seq * rec_floats(m), rs0, sizeof(float) * rec_floats(m));
+    m->len[seq] = p;
+    const int rc = orc_forward(m, seq, span, mm + 1, mm + 1, NULL, NULL, NULL);
+    if (rc != ORC_OK) return rc;
+  }
+#endif
+#if ORC_PLANT == 8
+  m->len[seq] = p + mm;
+#else
+  m->len[seq] = p + mm + 1;
+#endif
+  return ORC_OK;
+}
+
+static float* rec_copy(const orc_model* m, int seq) {
+  if (!m->rs) return NULL;
+  float* c = (float*)malloc(sizeof(float) * rec_floats(m));
+  if (c) memcpy(c, m->rs + (size_t)seq * rec_floats(m), sizeof(float) * rec_floats(m));
+  return c;
 }
 
 /* Prefill: reset the sequence, forward the prompt, return g0 = argmax of the
@@ -464,7 +571,7 @@ ORC_API int orc_forward(orc_model* m, int seq, const int32_t* toks, int n, int l
  * verify (pegainfer page, draft-seed alignment paragraph). */
 ORC_API int orc_prefill(orc_model* m, int seq, const int32_t* toks, int n, int32_t* g0, float* margin) {
   if (!m || seq < 0 || seq >= m->n_seq || n <= 0) return ORC_EINVAL;
-  m->len[seq] = 0;
+  orc_rewind(m, seq, 0);
   return orc_forward(m, seq, toks, n, n - 1, NULL, g0, margin);
 }
 
@@ -486,16 +593,16 @@ ORC_API int orc_verify(orc_model* m, int seq, const int32_t* span, int K, int32_
                        int32_t* accept_out, float* logits_out, float* margin_out) {
   if (!m || !span || !argmax_out || !accept_out || K < 0 || seq < 0 || seq >= m->n_seq) return ORC_EINVAL;
   const int p = m->len[seq];
-  const int rc = orc_forward(m, seq, span, K + 1, 0, logits_out, argmax_out, margin_out);
-  if (rc != ORC_OK) return rc;
-  const int mm = orc_accept_greedy(span, argmax_out, K);
-  *accept_out = mm;
-#if ORC_PLANT == 8
-  m->len[seq] = p + mm;
-#else
-  m->len[seq] = p + mm + 1;
-#endif
-  return ORC_OK;
+  float* rs0 = rec_copy(m, seq);
+  if (m->rs && !rs0) return ORC_ENOMEM;
+  int rc = orc_forward(m, seq, span, K + 1, 0, logits_out, argmax_out, margin_out);
+  if (rc == ORC_OK) {
+    const int mm = orc_accept_greedy(span, argmax_out, K);
+    *accept_out = mm;
+    rc = commit_accepted(m, seq, span, K, p, mm, rs0);
+  }
+  free(rs0);
+  return rc;
 }
 
 /* ------------------------------------------------------- sampled verify */
@@ -592,7 +699,8 @@ ORC_API int orc_verify_sampled(orc_model* m, int seq, const int32_t* span, int K
   const int p = m->len[seq], V = m->s.vocab;
   float* L = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)(K + 1) * V);
   if (!L) return ORC_ENOMEM;
-  int rc = orc_forward(m, seq, span, K + 1, 0, L, NULL, NULL);
+  float* rs0 = rec_copy(m, seq);
+  int rc = (m->rs && !rs0) ? ORC_ENOMEM : orc_forward(m, seq, span, K + 1, 0, L, NULL, NULL);
   for (int i = 0; rc == ORC_OK && i <= K; ++i) {
     float mg = 0.0f;
     tokens_out[i] = orc_sample_row(L + (size_t)i * V, V, temp, seed, seq, p + i, &mg);
@@ -601,13 +709,16 @@ ORC_API int orc_verify_sampled(orc_model* m, int seq, const int32_t* span, int K
   }
   if (!logits_out) free(L);
   if (rc != ORC_OK) {
+    if (rs0 && m->len[seq] != p) memcpy(m->rs + (size_t)seq * rec_floats(m), rs0, sizeof(float) * rec_floats(m));
     m->len[seq] = p;
+    free(rs0);
     return rc;
   }
   const int mm = orc_accept_greedy(span, tokens_out, K);  /* the same prefix rule on the drawn tokens */
   *accept_out = mm;
-  m->len[seq] = p + mm + 1;
-  return ORC_OK;
+  rc = commit_accepted(m, seq, span, K, p, mm, rs0);
+  free(rs0);
+  return rc;
 }
 
 /* Sampled prefill: the prompt's rows, then g0 drawn from the last row (its
@@ -617,7 +728,7 @@ ORC_API int orc_prefill_sampled(orc_model* m, int seq, const int32_t* toks, int 
   if (!m || !toks || !g0 || seq < 0 || seq >= m->n_seq || n <= 0 || !(temp > 0.0f)) return ORC_EINVAL;
   float* L = (float*)malloc(sizeof(float) * (size_t)m->s.vocab);
   if (!L) return ORC_ENOMEM;
-  m->len[seq] = 0;
+  orc_rewind(m, seq, 0);
   int rc = orc_forward(m, seq, toks, n, n - 1, L, NULL, NULL);
   if (rc == ORC_OK) {
     *g0 = orc_sample_row(L, m->s.vocab, temp, seed, seq, n - 1, margin);

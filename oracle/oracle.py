@@ -40,7 +40,8 @@ class _Shape(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q", C.c_int32),
                 ("n_kv", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("vocab", C.c_int32), ("eps", C.c_float), ("rope_theta", C.c_double),
-                ("swa_window", C.c_int32), ("swa_layers", C.c_uint64)]
+                ("swa_window", C.c_int32), ("swa_layers", C.c_uint64),
+                ("rec_layers", C.c_uint64), ("rec_beta", C.c_float)]
 
 
 _LIBS = {}
@@ -91,6 +92,10 @@ def load_lib(path: str = DEFAULT_LIB):
     lib.orc_sample_row.argtypes = [f32p, I, F, u64, I, I, f32p]
     lib.orc_verify_sampled.argtypes = [P, I, i32p, I, F, u64, i32p, i32p, f32p, f32p]
     lib.orc_prefill_sampled.argtypes = [P, I, i32p, I, F, u64, i32p, f32p]
+    lib.orc_delta_write.argtypes = [f32p, I, f32p, f32p, F]
+    lib.orc_delta_write.restype = None
+    lib.orc_delta_read.argtypes = [f32p, I, f32p, f32p]
+    lib.orc_delta_read.restype = None
     lib.orc_plant.restype = I
     _LIBS[path] = lib
     return lib
@@ -215,6 +220,25 @@ def sample_row(logits, temp, seed, seq, t, lib=None):
     return int(a), float(m.value)
 
 
+def delta_write(S, k, v, beta, lib=None):
+    """One delta-rule write into a copy of the state S [hd][hd]; returns it."""
+    lib = lib or load_lib()
+    S, sp = _f32(np.array(S, np.float32, copy=True))
+    k, kp = _f32(k)
+    v, vp = _f32(v)
+    lib.orc_delta_write(sp, len(k), kp, vp, float(beta))
+    return S
+
+
+def delta_read(S, q, lib=None):
+    lib = lib or load_lib()
+    S, sp = _f32(S)
+    q, qp = _f32(q)
+    o, op = _f32(np.zeros(len(q), np.float32))
+    lib.orc_delta_read(sp, len(q), qp, op)
+    return o
+
+
 def silu(x, lib=None):
     lib = lib or load_lib()
     return float(lib.orc_silu(float(x)))
@@ -240,7 +264,8 @@ class Oracle:
         self.shape = dict(shape)
         s = _Shape(shape["n_layers"], shape["hidden"], shape["n_q"], shape["n_kv"],
                    shape["head_dim"], shape["ffn"], shape["vocab"], shape["eps"],
-                   shape["rope_theta"], shape.get("swa_window", 0), shape.get("swa_layers", 0))
+                   shape["rope_theta"], shape.get("swa_window", 0), shape.get("swa_layers", 0),
+                   shape.get("rec_layers", 0), shape.get("rec_beta", 0.0))
         self.h = self.lib.orc_new(C.byref(s), max_ctx, n_seq)
         if not self.h:
             raise OracleError("orc_new failed")

@@ -387,9 +387,96 @@ def pin_swa_window_limits(lib=None):
     assert off == on and st["accepted"] > 0, "sliding-window spec-on differs from spec-off"
 
 
+def pin_delta_rule_closed_forms(lib=None):
+    """One write with strength 1 makes the key read back its value exactly
+    (the delta rule replaces the key's old association); strength 1/2 reads
+    back the mean of the old read and the value; writing the current read is
+    a fixed point; reads ignore the query's length."""
+    L = O.load_lib(lib or O.DEFAULT_LIB)
+    rng = np.random.default_rng(17)
+    hd = 16
+    S = (0.3 * rng.standard_normal((hd, hd))).astype(np.float32)
+    k = rng.standard_normal(hd).astype(np.float32)
+    v = rng.standard_normal(hd).astype(np.float32)
+    old = O.delta_read(S, k, L)
+    S1 = O.delta_write(S, k, v, 1.0, L)
+    assert np.allclose(O.delta_read(S1, k, L), v, atol=2e-5), "a full-strength write must store v under k"
+    Sh = O.delta_write(S, k, v, 0.5, L)
+    assert np.allclose(O.delta_read(Sh, k, L), 0.5 * (old + v), atol=2e-5)
+    assert np.allclose(O.delta_write(S, k, old, 0.7, L), S, atol=2e-6), "writing the current read changes S"
+    q = rng.standard_normal(hd).astype(np.float32)
+    assert np.allclose(O.delta_read(S, q, L), O.delta_read(S, 3.0 * q, L), atol=1e-6)
+    # a key orthogonal to k is not disturbed
+    k2 = rng.standard_normal(hd).astype(np.float32)
+    k2 -= k * (np.dot(k2, k) / np.dot(k, k))
+    assert np.allclose(O.delta_read(S1, k2, L), O.delta_read(S, k2, L), atol=2e-5)
+
+
+def pin_delta_rule_unrolled(lib=None):
+    """Twelve writes against the unrolled solution of the recurrence,
+    S_T = S_0 A_1..A_T + sum_t beta v_t k_t^T A_(t+1)..A_T with
+    A_t = I - beta k_t k_t^T (unit keys), evaluated by torch in fp64."""
+    L = O.load_lib(lib or O.DEFAULT_LIB)
+    rng = np.random.default_rng(18)
+    hd, T, beta = 16, 12, 0.5
+    S0 = (0.2 * rng.standard_normal((hd, hd))).astype(np.float32)
+    ks = rng.standard_normal((T, hd)).astype(np.float32)
+    vs = rng.standard_normal((T, hd)).astype(np.float32)
+    S = S0
+    for t in range(T):
+        S = O.delta_write(S, ks[t], vs[t], beta, L)
+    kh = torch.nn.functional.normalize(torch.tensor(ks, dtype=torch.float64), dim=-1)
+    I = torch.eye(hd, dtype=torch.float64)
+    A = [I - beta * torch.outer(kh[t], kh[t]) for t in range(T)]
+    ref = torch.tensor(S0, dtype=torch.float64) @ torch.linalg.multi_dot(A)
+    for t in range(T):
+        tail = torch.linalg.multi_dot(A[t + 1:]) if t + 2 < T else (A[T - 1] if t + 1 < T else I)
+        ref = ref + beta * torch.outer(torch.tensor(vs[t], dtype=torch.float64), kh[t]) @ tail
+    assert float(np.abs(S - ref.numpy()).max()) < 2e-5, "delta rule differs from its unrolled solution"
+
+
+def pin_recurrent_model(lib=None):
+    """A decoder with a recurrent middle layer: logits against the torch
+    reference; one S-row forward equals S one-row decodes; drafts from the
+    greedy stream corrupted at j accept exactly j and the stream continues
+    as plain decoding does (the state after row m, not after the rejected
+    rows); spec-on equals spec-off, greedy and sampled."""
+    shape = synth.SHAPES["tiny_rec"]
+    V = shape["vocab"]
+    w, orc = _model(shape, lib=lib)
+    toks = synth.uniform_prompt(11, V, 20)
+    _, _, lg = orc.forward(toks, want_logits=True)
+    ref = torch_ref.logits(shape, w, toks)
+    assert float(np.max(np.abs(lg.astype(np.float64) - ref))) < 1e-4, "recurrent model vs torch fp64"
+    prompt = synth.motif_prompt(1, V)
+    orc.prefill(prompt)
+    span = synth.uniform_prompt(5, V, 7)
+    _, _, multi = orc.forward(span, want_logits=True)
+    orc.prefill(prompt)
+    rows = [orc.forward(span[i:i + 1], want_logits=True)[2][0] for i in range(7)]
+    assert np.array_equal(multi, np.stack(rows)), "recurrent rows gate"
+    stream, _ = orc.generate(prompt, 24)
+    K = 6
+    for j in range(K + 1):
+        g0, _ = orc.prefill(prompt)
+        drafts = list(stream[1:K + 1])
+        if j < K:
+            drafts[j] = (drafts[j] + 1) % V
+        am, m, _, _ = orc.verify([g0] + drafts)
+        assert m == j
+        am2, m2, _, _ = orc.verify([int(am[m])] + list(stream[m + 2:m + 2 + K]))
+        assert list(am2[: m2 + 1]) == list(stream[m + 2:m + 3 + m2]), "stream after a partial accept"
+    off, _ = orc.generate(prompt, 40)
+    on, st = orc.generate(prompt, 40, spec=True, fixed_k=4)
+    assert off == on and st["accepted"] > 0 and st["accepted"] < st["drafted"]
+    soff, _ = orc.generate(prompt, 40, temp=0.9, seed=5)
+    son, _ = orc.generate(prompt, 40, spec=True, fixed_k=4, temp=0.9, seed=5)
+    assert soff == son
+
+
 ALL_PINS = [pin_torch_tiny, pin_torch_wide, pin_torch_int4, pin_closed_forms, pin_argmax,
             pin_rows_gate, pin_accept_golden, pin_verify_planted, pin_rewind_stale,
             pin_spec_equals_off, pin_ngram_golden, pin_adapt_k_golden, pin_int4_nibbles,
             pin_multiseq, pin_philox_kat, pin_uniform_gumbel_closed_forms, pin_gumbel_max_is_softmax,
             pin_sampled_low_temperature_is_greedy, pin_sampled_planted_and_spec_equals_off, pin_torch_swa,
-            pin_swa_window_limits]
+            pin_swa_window_limits, pin_delta_rule_closed_forms, pin_delta_rule_unrolled, pin_recurrent_model]

@@ -22,6 +22,8 @@ PLANTS = {
     13: "Philox round mixes the second key word into the first output word",
     14: "sampling multiplies the logits by the temperature instead of dividing",
     15: "a sliding-window row sees one key too many (window W + 1)",
+    16: "the delta rule writes with the raw key instead of the unit key",
+    17: "a partial accept keeps the recurrent state of the rejected rows",
 }
 
 

@@ -52,11 +52,24 @@ def logits(shape: dict, w: dict, tokens) -> np.ndarray:
         q = rope(F.linear(u, _f64(L["wq"])).view(T, nq, hd))
         k = rope(F.linear(u, _f64(L["wk"])).view(T, nkv, hd))
         v = F.linear(u, _f64(L["wv"])).view(T, nkv, hd)
-        local = W and (shape.get("swa_layers", 0) >> li) & 1
-        o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
-                                           attn_mask=band if local else causal,
-                                           scale=1.0 / math.sqrt(hd), enable_gqa=True)
-        x = x + F.linear(o.transpose(0, 1).reshape(T, nq * hd), _f64(L["wo"]))
+        if (shape.get("rec_layers", 0) >> li) & 1:
+            # delta rule per kv head on unrotated, unit-normalised keys and queries
+            q0 = F.normalize(F.linear(u, _f64(L["wq"])).view(T, nq, hd), dim=-1)
+            k0 = F.normalize(F.linear(u, _f64(L["wk"])).view(T, nkv, hd), dim=-1)
+            beta, G = shape["rec_beta"], nq // nkv
+            S = torch.zeros(nkv, hd, hd, dtype=torch.float64)
+            o = torch.empty(T, nq, hd, dtype=torch.float64)
+            for t in range(T):
+                err = v[t] - torch.einsum("gij,gj->gi", S, k0[t])
+                S = S + beta * torch.einsum("gi,gj->gij", err, k0[t])
+                o[t] = torch.einsum("gij,ghj->ghi", S, q0[t].view(nkv, G, hd)).reshape(nq, hd)
+            x = x + F.linear(o.reshape(T, nq * hd), _f64(L["wo"]))
+        else:
+            local = W and (shape.get("swa_layers", 0) >> li) & 1
+            o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1),
+                                               attn_mask=band if local else causal,
+                                               scale=1.0 / math.sqrt(hd), enable_gqa=True)
+            x = x + F.linear(o.transpose(0, 1).reshape(T, nq * hd), _f64(L["wo"]))
         u = F.rms_norm(x, (H,), weight=_f64(L["g_ffn"]), eps=eps)
         x = x + F.linear(F.silu(F.linear(u, _f64(L["wg"]))) * F.linear(u, _f64(L["wu"])), _f64(L["wd"]))
     u = F.rms_norm(x, (H,), weight=_f64(w["g_final"]), eps=eps)
