@@ -78,6 +78,8 @@ struct GemmParams {
   const int32_t* rowinfo;// [R][2]: each row's absolute position and its KV block (k_embed)
   int ring_nb, ring_w;   // sliding-window layer: the KV rows go to the sequence's ring of ring_w
                          // slots (ring_nb blocks): block seq * ring_nb + (pos % ring_w) / 16; else 0
+  float* rec_kv;         // recurrent layer: unrotated keys and values [R][2][n_kv*hd] (queries
+                         // unrotated into q), no cache rows; else null
   // EPI_RESID
   float* x;              // residual [R][N]
   float* ss_out;         // [R][N/64] partial sums of squares of the new residual
@@ -93,6 +95,8 @@ struct GemmParams {
   const int32_t* kd;          // [n_seq] drafts per sequence (rows past 1 + kd[b] are padding)
   const int32_t* mode;        // StepDev::mode
   const StepDev* step;        // the step block: sampling temperature and seed
+  int32_t* rec_slot;          // or null: per sequence, the recurrent state slot (set * 16 + row, -1 =
+                              // zero) committed by the accept stage
   int32_t* result;            // [1 + n_seq*(S+1)]: status, then (m, a0..a(S-1)) per sequence
   int32_t* kv_len_w;          // cache lengths, advanced by the accept stage
   int n_seq;
@@ -126,6 +130,19 @@ struct AttnParams {
 // keys: the last split of each query tile to finish then merges the tile's
 // columns itself, keeping the splits' (max, sum) in its LDS.
 constexpr int attn_fuse_splits(int hd) { return hd >= 32 ? 64 : 32; }
+
+// A recurrent (delta-rule) layer's step over the span rows of each sequence.
+struct RecParams {
+  const float* q;        // [R][n_q*hd] unrotated queries
+  const float* kv;       // [R][2][n_kv*hd] unrotated keys, values
+  float* snap;           // [max_seqs][2 sets][16 rows][n_kv][hd (v)][hd (k)]: the state after each row
+  const int32_t* slot;   // [max_seqs]: the committed state (set * 16 + row), or -1 for the zero state
+  const int32_t* seq_ids;
+  float* out;            // [R][n_q*hd]
+  void* af_out;          // or null: out also as the O GEMM's prepared A
+  int S, n_seq, n_q, n_kv;
+  float beta;
+};
 
 struct EmbedParams {
   const uint16_t* emb;   // [V][H] bf16
@@ -170,6 +187,8 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
 hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
                      hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
+// One workgroup per (kv head, sequence); the rows of each span in order.
+hipError_t launch_recur(const RecParams& p, int hd, hipStream_t st);
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
 // Repack canonical bf16 [rows][cols] into fragments of a fused matrix whose
 // row for source row s is map(s): kind 0 identity + row0, kind 1 RoPE pair

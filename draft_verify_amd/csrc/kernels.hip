@@ -557,6 +557,21 @@ __device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, f
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
   const int slot = pos & 15;
+  if (P.rec_kv) {
+    // a recurrent layer: queries, keys and values unrotated, no cache row
+    if (c < DQ + DK) {
+      const int local = c < DQ ? c : c - DQ;
+      const int head = local / hd, j = (local % hd) >> 1;
+      float* dst = c < DQ ? P.q + (size_t)r * DQ : P.rec_kv + (size_t)r * 2 * DK;
+      dst[head * hd + j] = v0;
+      dst[head * hd + j + half] = v1;
+    } else {
+      float* dst = P.rec_kv + (size_t)r * 2 * DK + DK + (c - DQ - DK);
+      dst[0] = v0;
+      dst[1] = v1;
+    }
+    return;
+  }
   // a sliding-window layer keeps its KV rows in the sequence's ring
   if (P.ring_nb && c >= DQ) blk = P.seq_ids[r / P.S] * P.ring_nb + ((pos % P.ring_w) >> 4);
   if (c < DQ + DK) {
@@ -767,6 +782,14 @@ __device__ void lm_finish(const GemmParams& P, int nblk, float* sbuf) {
     const int seq = P.seq_ids[b];
     if (mode == MODE_COMMIT_ALL) P.kv_len_w[seq] += S;
     else if (mode == MODE_VERIFY) P.kv_len_w[seq] += m + 1;
+    if (P.rec_slot && mode != MODE_NO_COMMIT) {
+      // the recurrent layers wrote this forward's per-row states into the set
+      // the committed state is not in; the state after the last kept row
+      // becomes the committed one (no copy, no second forward)
+      const int old = P.rec_slot[seq];
+      const int set = old < 0 ? 0 : 1 - (old >> 4);
+      P.rec_slot[seq] = set * 16 + (mode == MODE_COMMIT_ALL ? S - 1 : m);
+    }
     int32_t* res = P.result + 1 + b * (S + 1);
     res[0] = m;
     for (int i = 0; i < S; ++i) res[1 + i] = arg[row0 + i];
@@ -1819,6 +1842,110 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnParams P) {
   __shared__ float sML[16 * kMaxCombineSplits * 2];
   const int b = blockIdx.z;
   combine_tile<HD, false, kMaxCombineSplits>(P, b, blockIdx.y, blockIdx.x, P.rowinfo[2 * b * P.S], sML);
+}
+
+// ------------------------------------------------------- recurrent layer
+//
+// A delta-rule layer (TensorSharp page, recurrent-trunk section): per kv head
+// a state S [hd (v)][hd (k)] that every row updates, S <- S + beta (v - S k)
+// k^T with the row's unit key k, and every query head of the group reads,
+// o = S q with the unit query q.  One workgroup per (kv head, sequence) holds
+// S in registers (thread t: row t / TPR, columns (t % TPR) * E .. + E) and runs
+// the span's rows in order; after each row it stores S as that row's
+// snapshot, so the accept stage can commit the state after any row by index
+// (the page: keep one snapshot per row, commit it on the device, and the
+// pre-verify state is simply the one not overwritten).  Every sum runs in a
+// fixed order per row, whatever the span, so the rows gate holds.
+template <int HD>
+__global__ __launch_bounds__(256) void k_recur(RecParams P) {
+  constexpr int E = HD * HD / 256, TPR = HD / E;  // state elements per thread, threads per state row
+  constexpr int MAXG = 8;                        // query heads per kv head held in the LDS
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int dv = tid / TPR, dk0 = (tid % TPR) * E;
+  const int G = P.n_q / P.n_kv, DQ = P.n_q * HD, DK = P.n_kv * HD;
+  const int seq = P.seq_ids[b];
+  __shared__ float sX[(2 + MAXG) * HD];  // k, q_0..q_(G-1), then v
+  __shared__ float sN[1 + MAXG];
+  float* sV = sX + (1 + MAXG) * HD;
+  const int old = P.slot[seq];
+  const int set = old < 0 ? 0 : 1 - (old >> 4);
+  float S[E];
+  if (old < 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) S[e] = 0.0f;
+  } else {
+    const float* src = P.snap + ((((size_t)seq * 2 + (old >> 4)) * 16 + (old & 15)) * P.n_kv + g) * HD * HD +
+                       (size_t)dv * HD + dk0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) S[e] = src[e];
+  }
+  for (int i = 0; i < P.S; ++i) {
+    const int r = b * P.S + i;
+    // the row's key, queries and value
+    for (int e = tid; e < (2 + G) * HD; e += 256) {
+      const int v = e / HD, d = e % HD;
+      float x;
+      if (v == 0) x = P.kv[(size_t)r * 2 * DK + g * HD + d];
+      else if (v <= G) x = P.q[(size_t)r * DQ + (g * G + v - 1) * HD + d];
+      else x = P.kv[(size_t)r * 2 * DK + DK + g * HD + d];
+      if (v <= G) sX[v * HD + d] = x;
+      else sV[d] = x;
+    }
+    __syncthreads();
+    // lengths of the key and the queries: one wave each, lanes over d, xor tree
+    for (int v = wave; v <= G; v += 4) {
+      float a = 0.0f;
+      for (int d = lane; d < HD; d += 64) a += sX[v * HD + d] * sX[v * HD + d];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+      if (lane == 0) sN[v] = sqrtf(a);
+    }
+    __syncthreads();
+    for (int e = tid; e < (1 + G) * HD; e += 256) sX[e] = sX[e] / sN[e / HD];
+    __syncthreads();
+    // u = S k (this thread's part, then the TPR threads of the row), the write
+    float u = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) u += S[e] * sX[dk0 + e];
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) u += __shfl_xor(u, o);
+    const float cw = P.beta * (sV[dv] - u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) S[e] = S[e] + cw * sX[dk0 + e];
+    float* dst = P.snap + ((((size_t)seq * 2 + set) * 16 + i) * P.n_kv + g) * HD * HD + (size_t)dv * HD + dk0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = S[e];
+    // the reads of the group's queries
+    for (int h = 0; h < G; ++h) {
+      float o = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o += S[e] * sX[(1 + h) * HD + dk0 + e];
+#pragma unroll
+      for (int x = TPR / 2; x >= 1; x >>= 1) o += __shfl_xor(o, x);
+      if (tid % TPR == 0) {
+        const int col = (g * G + h) * HD + dv;
+        P.out[(size_t)r * DQ + col] = o;
+        if (P.af_out) prep_store1(P.af_out, (P.n_seq * P.S + 15) >> 4, r, col, o);
+      }
+    }
+    __syncthreads();  // the LDS is refilled for the next row
+  }
+}
+
+hipError_t launch_recur(const RecParams& p, int hd, hipStream_t st) {
+  if (!p.q || !p.kv || !p.snap || !p.slot || !p.seq_ids || !p.out || p.n_kv < 1 || p.n_q % p.n_kv ||
+      p.n_q / p.n_kv > 8 || p.S < 1 || p.S > 16 || p.n_seq < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid(p.n_kv, p.n_seq);
+  switch (hd) {
+    case 128: hipLaunchKernelGGL(k_recur<128>, grid, dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL(k_recur<64>, grid, dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL(k_recur<32>, grid, dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL(k_recur<16>, grid, dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------- streaming read

@@ -126,12 +126,15 @@ struct Layout {
   // ring_nb blocks per sequence
   std::vector<size_t> kv_off, kv_half;
   std::vector<char> local;   // per layer: sliding-window layer
+  std::vector<char> rec;     // per layer: recurrent layer (its region holds the state snapshots)
   int win, ring_nb, ring_w, win_splits;
+  bool any_rec;
   size_t kv_bytes;
   // workspace
   size_t af;  // prepared A of the split-K GEMMs above 16 rows (bf16), or (size_t)-1
   size_t af2; // the same for O and down, written by their producers
   size_t rowinfo;  // per row: position and KV block, written by k_embed
+  size_t rec_kv, rec_slot;  // recurrent layers: staged keys and values; committed state slot per sequence
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
   size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, workspace_bytes;
@@ -168,6 +171,13 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   if (d.swa_window < 0 || d.reserved != 0) return fail("swa_window must be >= 0 and reserved 0");
   if (d.swa_window > 0 && (d.swa_layers == 0 || (d.n_layers < 64 && (d.swa_layers >> d.n_layers) != 0)))
     return fail("swa_layers must name at least one existing layer when swa_window > 0");
+  if (d.reserved2 != 0) return fail("reserved2 must be 0");
+  if (d.rec_layers) {
+    if (d.n_layers < 64 && (d.rec_layers >> d.n_layers) != 0) return fail("rec_layers names a layer past n_layers");
+    if (d.swa_window > 0 && (d.rec_layers & d.swa_layers)) return fail("a layer cannot be both recurrent and windowed");
+    if (!(d.rec_beta > 0.0f) || d.rec_beta > 1.0f) return fail("rec_beta must be in (0, 1]");
+    if (d.n_q_heads / d.n_kv_heads > 8) return fail("recurrent layers take at most 8 query heads per kv head");
+  }
   Lo.H = d.hidden; Lo.nq = d.n_q_heads; Lo.nkv = d.n_kv_heads; Lo.hd = d.head_dim; Lo.F = d.ffn; Lo.V = d.vocab;
   Lo.L = d.n_layers;
   Lo.DQ = Lo.nq * Lo.hd; Lo.DK = Lo.nkv * Lo.hd; Lo.Nqkv = Lo.DQ + 2 * Lo.DK; Lo.Ngu = 2 * Lo.F;
@@ -248,12 +258,26 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.ring_nb = Lo.ring_w / 16;
   // splits of 256 keys one row group's window can touch
   Lo.win_splits = Lo.win > 0 ? std::min(Lo.max_splits, (Lo.win + SPEC_MAX_SPAN - 1 + 255) / 256 + 1) : 0;
+  // Recurrent layers keep no cache rows: their region holds, per sequence, two
+  // sets of per-row state snapshots (one committed, one for the next forward).
+  Lo.rec.assign((size_t)Lo.L, 0);
+  Lo.any_rec = false;
+  for (int l = 0; l < Lo.L && l < 64; ++l)
+    if ((d.rec_layers >> l) & 1u) {
+      Lo.rec[(size_t)l] = 1;
+      Lo.any_rec = true;
+    }
   Lo.kv_off.resize((size_t)Lo.L);
   Lo.kv_half.resize((size_t)Lo.L);
   Lo.kv_bytes = 0;
   for (int l = 0; l < Lo.L; ++l) {
-    const size_t blocks = Lo.local[(size_t)l] ? (size_t)Lo.max_seqs * Lo.ring_nb : (size_t)Lo.n_blocks;
     Lo.kv_off[(size_t)l] = Lo.kv_bytes;
+    if (Lo.rec[(size_t)l]) {
+      Lo.kv_half[(size_t)l] = 0;
+      Lo.kv_bytes += align_up((size_t)Lo.max_seqs * 2 * SPEC_MAX_SPAN * Lo.nkv * Lo.hd * Lo.hd * 4);
+      continue;
+    }
+    const size_t blocks = Lo.local[(size_t)l] ? (size_t)Lo.max_seqs * Lo.ring_nb : (size_t)Lo.n_blocks;
     Lo.kv_half[(size_t)l] = align_up(blocks * Lo.nkv * SPEC_BLOCK_TOKENS * Lo.hd * 2);
     Lo.kv_bytes += 2 * Lo.kv_half[(size_t)l];
   }
@@ -288,6 +312,8 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
   Lo.rowinfo = take(R * 8);
+  Lo.rec_kv = Lo.any_rec ? take(R * 2 * Lo.DK * 4) : (size_t)-1;
+  Lo.rec_slot = Lo.any_rec ? take((size_t)Lo.max_seqs * 4) : (size_t)-1;
   Lo.slotbt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
   Lo.argkey = take(R * 8);
   Lo.status = take(4);
@@ -307,7 +333,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   off = 0;
   Lo.host_step = take(sizeof(StepDev) + 3 * R * 4);
   Lo.host_result = take((1 + 2 * R) * 4);
-  Lo.host_kvlen = take((size_t)Lo.max_seqs * 4);
+  Lo.host_kvlen = take((size_t)Lo.max_seqs * 8);  // cache lengths, then recurrent slots
   Lo.host_bt = take((size_t)Lo.max_seqs * Lo.bt_stride * 4);
   Lo.host_bytes = off;
   return true;
@@ -410,6 +436,16 @@ int upload_bt_row(spec_ctx* c, int seq) {
 int upload_kv_len(spec_ctx* c, int seq) {
   c->h_kvlen()[seq] = c->len[(size_t)seq];
   HIPCHK(c, hipMemcpyAsync(c->ws<int32_t>(c->lo.kv_len) + seq, c->h_kvlen() + seq, 4, hipMemcpyHostToDevice, c->st));
+  return SPEC_OK;
+}
+
+// A sequence that starts over (prefill, release) starts from the zero
+// recurrent state.
+int reset_rec_slot(spec_ctx* c, int seq) {
+  if (!c->lo.any_rec) return SPEC_OK;
+  int32_t* h = c->h_kvlen() + c->lo.max_seqs + seq;  // staging word next to the cache lengths
+  *h = -1;
+  HIPCHK(c, hipMemcpyAsync(c->ws<int32_t>(c->lo.rec_slot) + seq, h, 4, hipMemcpyHostToDevice, c->st));
   return SPEC_OK;
 }
 
@@ -520,6 +556,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
     gl.mode = &sd->mode;
     gl.step = sd;
     gl.rowinfo = c->ws<int32_t>(L.rowinfo);
+    gl.rec_slot = L.any_rec ? c->ws<int32_t>(L.rec_slot) : nullptr;
     gl.result = c->ws<int32_t>(L.result);
     gl.kv_len_w = c->ws<int32_t>(L.kv_len);
     gl.seq_ids = seq_ids;
@@ -552,10 +589,28 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.rowinfo = c->ws<int32_t>(L.rowinfo);
       g.ring_nb = L.local[(size_t)l] ? L.ring_nb : 0;
       g.ring_w = L.local[(size_t)l] ? L.ring_w : 0;
+      g.rec_kv = L.rec[(size_t)l] ? c->ws<float>(L.rec_kv) : nullptr;
       HIPCHK(c, gemm_or_mm(g, L.mm_qkv, L.nk_qkv, EPI_QKV, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
     case SPEC_OP_ATTN: {
+      if (L.rec[(size_t)l]) {
+        RecParams rp;
+        rp.q = c->ws<float>(L.q);
+        rp.kv = c->ws<float>(L.rec_kv);
+        rp.snap = (float*)(c->KV + L.kv_off[(size_t)l]);
+        rp.slot = c->ws<int32_t>(L.rec_slot);
+        rp.seq_ids = seq_ids;
+        rp.out = c->ws<float>(L.o);
+        rp.af_out = c->af_next(L.nk_o, R);
+        rp.S = S;
+        rp.n_seq = n_seq;
+        rp.n_q = L.nq;
+        rp.n_kv = L.nkv;
+        rp.beta = c->d.rec_beta;
+        HIPCHK(c, launch_recur(rp, L.hd, st));
+        return SPEC_OK;
+      }
       AttnParams a;
       a.q = c->ws<float>(L.q);
       a.kpool = c->kpool(l);
@@ -1039,6 +1094,7 @@ int spec_prefill_seq(spec_ctx* c, int seq, const int32_t* tokens, int n, int32_t
   c->live[(size_t)seq] = 0;
   trim_blocks(c, seq, 0);
   STEP(upload_kv_len(c, seq));
+  STEP(reset_rec_slot(c, seq));
   const int chunk = std::min(SPEC_MAX_SPAN, c->lo.max_rows);
   int g = -1;
   for (int off = 0; off < n; off += chunk) {
@@ -1054,6 +1110,7 @@ int spec_prefill_seq(spec_ctx* c, int seq, const int32_t* tokens, int n, int32_t
       c->len[(size_t)seq] = 0;
       trim_blocks(c, seq, 0);
       (void)upload_kv_len(c, seq);
+      (void)reset_rec_slot(c, seq);
       (void)hipStreamSynchronize(c->st);
       return rc;
     }
@@ -1143,9 +1200,12 @@ int spec_rewind_seq(spec_ctx* c, int seq, int len) {
   if (!c) return SPEC_EINVAL;
   STEP(check_seq(c, seq));
   if (len < 0 || len > c->len[(size_t)seq]) return set_err(c, SPEC_ESTATE, "rewind length outside [0, cache length]");
+  if (c->lo.any_rec && len != c->len[(size_t)seq] && len != 0)
+    return set_err(c, SPEC_ESTATE, "a model with recurrent layers rewinds only to 0 (its state has no history)");
   c->len[(size_t)seq] = len;
   trim_blocks(c, seq, len);
   STEP(upload_kv_len(c, seq));
+  if (len == 0) STEP(reset_rec_slot(c, seq));
   HIPCHK(c, hipStreamSynchronize(c->st));
   return SPEC_OK;
 }
@@ -1168,6 +1228,7 @@ int spec_release_seq(spec_ctx* c, int seq) {
   c->live[(size_t)seq] = 0;
   trim_blocks(c, seq, 0);
   STEP(upload_kv_len(c, seq));
+  STEP(reset_rec_slot(c, seq));
   HIPCHK(c, hipStreamSynchronize(c->st));
   return SPEC_OK;
 }

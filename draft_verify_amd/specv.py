@@ -44,7 +44,8 @@ class spec_model_desc(C.Structure):
                 ("vocab", C.c_int32), ("weight_format", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_double), ("max_ctx", C.c_int32), ("max_seqs", C.c_int32),
                 ("max_rows", C.c_int32), ("n_blocks", C.c_int32), ("flags", C.c_uint32),
-                ("swa_window", C.c_int32), ("reserved", C.c_int32), ("swa_layers", C.c_uint64)]
+                ("swa_window", C.c_int32), ("reserved", C.c_int32), ("swa_layers", C.c_uint64),
+                ("rec_layers", C.c_uint64), ("rec_beta", C.c_float), ("reserved2", C.c_int32)]
 
 
 class spec_buffer_sizes(C.Structure):
@@ -178,7 +179,8 @@ def make_desc(shape: dict, max_ctx: int, max_seqs: int = 1, max_rows: int = 16, 
     return spec_model_desc(shape["n_layers"], shape["hidden"], shape["n_q"], shape["n_kv"],
                            shape["head_dim"], shape["ffn"], shape["vocab"], weight_format,
                            shape["eps"], shape["rope_theta"], max_ctx, max_seqs, max_rows,
-                           n_blocks, flags, shape.get("swa_window", 0), 0, shape.get("swa_layers", 0))
+                           n_blocks, flags, shape.get("swa_window", 0), 0, shape.get("swa_layers", 0),
+                           shape.get("rec_layers", 0), shape.get("rec_beta", 0.0), 0)
 
 
 # --------------------------------------------------------------- ABI calls

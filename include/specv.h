@@ -79,6 +79,19 @@ typedef struct spec_model_desc {
   int32_t swa_window;
   int32_t reserved;      /* 0 */
   uint64_t swa_layers;
+  /* Recurrent layers (TensorSharp page, recurrent-trunk section): each layer
+   * l < 64 with bit l of rec_layers set is a delta-rule layer instead of
+   * attention -- per kv head a state S [head_dim][head_dim] that every row
+   * updates with its unit key k and value v, S <- S + rec_beta (v - S k) k^T,
+   * and every query head of the group reads with its unit query, o = S q (no
+   * rotary embedding).  A verify stores the state after every span row and
+   * the accept stage commits the one after the last kept row on the device
+   * (no copy, no second forward).  Such a model rewinds only to 0.  Not
+   * combined with a sliding window on the same layer; at most 8 query heads
+   * per kv head; rec_beta in (0, 1]. */
+  uint64_t rec_layers;
+  float rec_beta;
+  int32_t reserved2;     /* 0 */
 } spec_model_desc;
 
 /* Sizes of the caller-owned buffers for a description. */
@@ -173,7 +186,8 @@ SPEC_API int spec_prefill(spec_ctx* ctx, const int32_t* tokens, int n, int32_t* 
  * (set on the device by the accept kernel).  K = 0 is a plain decode step. */
 SPEC_API int spec_verify(spec_ctx* ctx, const int32_t* span, int K, int32_t* argmax, int32_t* accept_len);
 
-/* spec_rewind: shorten the cache to len (0 <= len <= cache length); rows past
+/* spec_rewind: shorten the cache to len (0 <= len <= cache length; a model
+ * with recurrent layers only to 0 or its current length); rows past
  * len stay in memory and are overwritten by later forwards (TensorSharp page,
  * interfaces section: SpecRewindCache(length); coreai note, KV-only rollback
  * paragraph: rolling back is not advancing the position).  Used for budget or
