@@ -184,6 +184,8 @@ hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t
 // {10 x 4, 16 x 4, 1 x 1}.
 bool mmq_supported(int K, int nk);
 hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStream_t st);
+bool mmqr_plan(int K, int* nw, int* gpw, int* parts);
+hipError_t launch_mmqr(const GemmParams& p, int epi, int max_grid, hipStream_t st);
 hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int gp, int max_grid, int epi,
                      hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);

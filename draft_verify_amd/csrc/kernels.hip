@@ -1284,7 +1284,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   }
 }
 
-// The int4 one-pass GEMM for at most four rows (K = hidden or n_q * hd):
+// The int4 one-pass GEMM for at most four rows (K = hidden or n_q * hd),
+// activations staged in LDS:
 // every workgroup stages the whole normalised activation once in LDS as fp16
 // hi + lo in the MFMA A-operand order ([step][hi, lo][lane group][row]),
 // then walks blocks of CT 16-column tiles (blockIdx.x, + gridDim.x, ...),
@@ -1482,6 +1483,237 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
       if (p < P.R * 8 * CT && (p & 7) == 0) atomicMax(&P.argkey[p / (8 * CT)], k);
     }
     lm_finish(P, G, (float*)sAcc);
+  }
+}
+
+// The int4 one-pass GEMM for up to 16 rows, activations in registers.  A
+// workgroup of NW waves owns one K part of KG = NW*GPW groups of 128 inputs
+// (part kp of the K / (KG*128) parts: workgroup blockIdx.x takes part
+// blockIdx.x % parts and walks the column blocks blockIdx.x / parts,
+// + gridDim.x / parts, ...).  Every lane loads its own A values once, straight
+// into the MFMA A-operand layout (lane l: row l%16, inputs 8*(l/16)..+8 of
+// each of the wave's 4*GPW steps), applies the RMSNorm (the gains staged in
+// LDS) and keeps them as fp16 hi + lo for the whole walk, so the row count
+// costs no LDS and no weight is read twice: rows up to 16 run the same
+// instructions as one row.  Per tile and group the four steps' MFMAs on the
+// exact integer weights, then one fused multiply-add by the column's group
+// scale; the wave parts are added in wave order.  With one K part the
+// epilogue follows at once; with several (O, down) each part's tile goes to
+// the split buffer, and after the walk the last part of each tile to arrive
+// (an arrival counter per block) adds the parts in part order and runs the
+// residual epilogue.  Every sum's order depends on the shape of the GEMM
+// alone, never on R, so an S-row forward equals S one-row forwards bit for bit.
+template <int EPI, int NW, int GPW, int CT>
+__global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
+  constexpr int NT = NW * 64, KG = NW * GPW, ST = GPW * 4;
+  constexpr bool NORM = EPI != EPI_RESID;
+  constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // epilogue pairs per thread
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row = lane & 15, kg = lane >> 4;
+  const int parts = P.nslices;  // K parts (host-checked: K = parts * KG * 128, gridDim.x % parts == 0)
+  const int kp = (int)blockIdx.x % parts, wg = (int)blockIdx.x / parts, GW = (int)gridDim.x / parts;
+  const int KGT = P.K >> 7;            // groups over the whole K
+  const int g0 = kp * KG + wave * GPW; // the wave's first group
+  const int ntile = P.N >> 4, nblk = (ntile + CT - 1) / CT;
+
+  __shared__ float sG[NORM ? KG * 128 : 1];
+  __shared__ f32x4 sAcc[NW * 64 * CT];
+  __shared__ float sR[16];
+  __shared__ int sLast;
+
+  constexpr bool POS = EPI == EPI_QKV || EPI == EPI_LM;
+  int qpos[POS ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
+  if constexpr (POS) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int r = (tid + it * NT) / (8 * CT), rc = r < P.R ? r : 0;
+      qpos[it] = P.rowinfo[2 * rc];
+      if constexpr (EPI == EPI_QKV) qblk[it] = P.rowinfo[2 * rc + 1];
+    }
+  }
+  Sampling sm = {0.0f, 0u, 0u};
+  if constexpr (EPI == EPI_LM) sm = load_sampling(P);
+  // the lane's A values: 8 per step, rows past R are zeros
+  float a[ST][8];
+  {
+    const bool live = row < P.R;
+    const float* src = P.A + (size_t)(live ? row : 0) * P.lda + (size_t)g0 * 128 + kg * 8;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      const f32x4 x0 = live ? *(const f32x4*)(src + j * 32) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 x1 = live ? *(const f32x4*)(src + j * 32 + 4) : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      a[j][0] = x0.x; a[j][1] = x0.y; a[j][2] = x0.z; a[j][3] = x0.w;
+      a[j][4] = x1.x; a[j][5] = x1.y; a[j][6] = x1.z; a[j][7] = x1.w;
+    }
+  }
+  if constexpr (NORM) {  // the workgroup's gains, coalesced
+    const f32x4* gsrc = (const f32x4*)(P.gain + (size_t)kp * KG * 128);
+    for (int i = tid; i < KG * 32; i += NT) ((f32x4*)sG)[i] = gsrc[i];
+  }
+  u32x4 b0[CT][GPW];
+  uint32_t s0[CT][GPW];  // raw bf16 scale bits, converted at use
+  auto fetch = [&](u32x4 (&bw)[CT][GPW], uint32_t (&sw)[CT][GPW], int blk_) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int tile = min(blk_ * CT + c, ntile - 1);
+      const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KGT + g0) * 64 + lane;
+      const uint16_t* sp = P.scales + ((size_t)tile * 16 + (lane & 15)) * KGT + g0;
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        bw[c][gi] = __builtin_nontemporal_load(wp + gi * 64);
+        sw[c][gi] = sp[gi];
+      }
+    }
+  };
+  int blk = wg;
+  if (blk < nblk) fetch(b0, s0, blk);
+  if constexpr (NORM) {  // rstd of the 16 rows (16 lanes per row, whole waves), after every load is out
+    for (int t = tid; t < 256; t += NT) {
+      const float rs = rstd16(P.ss, P.ss_n, t >> 4, P.R, t & 15, P.inv_dim, P.eps);
+      if ((t & 15) == 0) sR[t >> 4] = (t >> 4) < P.R ? rs : 0.0f;
+    }
+  }
+  __syncthreads();
+  // normalise and split into fp16 hi + lo, in place
+  f16x8 ah[ST], al[ST];
+  {
+    const float sc = NORM ? sR[row] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = a[j][e];
+      if constexpr (NORM) {
+        const f32x4 g0v = *(const f32x4*)(sG + (wave * GPW * 4 + j) * 32 + kg * 8);
+        const f32x4 g1v = *(const f32x4*)(sG + (wave * GPW * 4 + j) * 32 + kg * 8 + 4);
+        const float gv[8] = {g0v.x, g0v.y, g0v.z, g0v.w, g1v.x, g1v.y, g1v.z, g1v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 h = (_Float16)v[e];
+        ah[j][e] = h;
+        al[j][e] = (_Float16)(v[e] - (float)h);
+      }
+    }
+  }
+  unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
+#pragma unroll
+  for (int it = 0; it < (EPI == EPI_LM ? PPT : 1); ++it) kmax[it] = 0ull;
+
+  auto pass = [&](u32x4 (&bw)[CT][GPW], uint32_t (&sw)[CT][GPW], int cur, int refill) {
+    f32x4 acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      f32x4 t[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c) t[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const f16x8 bq = dequant8_ao(bw[c][gi][d]);
+          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[gi * 4 + d], bq, t[c], 0, 0, 0);
+          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[gi * 4 + d], bq, t[c], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const float sc = bf16_bits_to_f32((uint16_t)sw[c][gi]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(t[c][i], sc, acc[c][i]);
+      }
+    }
+    if (refill < nblk) fetch(bw, sw, refill);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) sAcc[(wave * CT + c) * 64 + lane] = acc[c];
+    __syncthreads();
+    // p = (row * CT + tile) * 8 + pair: an aligned group of 8 pairs is 16
+    // columns of one row
+    const int npairs = P.R * 8 * CT;
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      const int p = tid + it * NT;
+      const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+      const int col = (cur * CT + ct) * 16 + 2 * pp;
+      if (p < npairs && col < P.N) {
+        const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+        float v0, v1;
+        group_sum<NW, 1, CT>(sAcc, ct, e0, v0, v1);
+        if constexpr (EPI == EPI_QKV) {
+          qkv_pair_at(P, r, col, v0, v1, qpos[it], qblk[it]);
+        } else if constexpr (EPI == EPI_RESID) {
+          if (parts > 1) {
+            st_dev2(P.part + ((size_t)kp * P.R + r) * P.N + col, v0, v1);
+          } else {
+            const float s8 = sum8(resid_pair(P, r, col, v0, v1));
+            if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = s8;
+          }
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          swiglu_pair(P, r, col, v0, v1);
+        } else {
+          unsigned long long k0, k1;
+          lm_pair_keys(P, sm, r, col, v0, v1, qpos[it], k0, k1);
+          const unsigned long long k = k0 > k1 ? k0 : k1;
+          kmax[it] = k > kmax[it] ? k : kmax[it];
+        }
+      }
+    }
+    __syncthreads();  // sAcc is rewritten by the next block
+  };
+  for (; blk < nblk; blk += GW) pass(b0, s0, blk, blk + GW);
+  if constexpr (EPI == EPI_LM) {
+#pragma unroll
+    for (int it = 0; it < PPT; ++it) {
+      unsigned long long k = kmax[it];
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(k, o);
+        k = t > k ? t : k;
+      }
+      const int p = tid + it * NT;
+      if (p < P.R * 8 * CT && (p & 7) == 0) atomicMax(&P.argkey[p / (8 * CT)], k);
+    }
+    lm_finish(P, (int)gridDim.x, (float*)sAcc);
+  }
+  if constexpr (EPI == EPI_RESID) {
+    if (parts == 1) return;
+    // the parts of this workgroup's blocks are stored: the last part of a
+    // block to arrive adds them in part order and runs the epilogue
+    wait_mem();
+    __syncthreads();
+    for (int b = wg; b < nblk; b += GW) {
+      if (tid == 0) {
+        const unsigned old = atomicAdd(&P.cnt[b], 1u);
+        sLast = old == (unsigned)(parts - 1);
+        if (sLast) P.cnt[b] = 0u;  // every part has arrived: ready for the next launch
+      }
+      __syncthreads();
+      if (sLast) {
+        const int npairs = P.R * 8 * CT;
+#pragma unroll
+        for (int it = 0; it < PPT; ++it) {
+          const int p = tid + it * NT;
+          const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+          const int col = (b * CT + ct) * 16 + 2 * pp;
+          if (p < npairs && col < P.N) {
+#pragma clang fp contract(off)
+            float v0 = 0.0f, v1 = 0.0f;
+            for (int s = 0; s < parts; ++s) {
+              const float2 t = ld_dev2(P.part + ((size_t)s * P.R + r) * P.N + col);
+              v0 += t.x;
+              v1 += t.y;
+            }
+            const float s8 = sum8(resid_pair(P, r, col, v0, v1));
+            if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = s8;
+          }
+        }
+      }
+      __syncthreads();  // sLast is rewritten for the next block
+    }
   }
 }
 
@@ -2142,16 +2374,19 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
 }
 
 // int4 one-pass (k_mmq) configurations: (waves, groups per wave, 16-column
-// tiles per pass).  Two tiles per pass share each read of the A slice from
+// tiles per pass).  K = 5120 takes eight waves of five groups, the K parts of
+// the register-activation kernel that serves five to sixteen rows, so the
+// two agree bit for bit (ten waves of four ran 1-6 % faster at one row: LM
+// head 93 vs 99 us).  Two tiles per pass share each read of the A slice from
 // LDS where the LDS holds the second partial tile (K = 5120: 80 KiB of A +
-// 20 KiB of partials; K = 8192 would need 160 KiB); they are taken when
+// 16 KiB of partials; K = 8192 would need 160 KiB); they are taken when
 // every workgroup walks at least four such blocks (gate/up 46.9 -> 42.6 us,
 // LM head 129 -> 110 us at the 32B shape), since with fewer the blocks split
 // unevenly over the workgroups (QKV's 640 tiles: 16.4 -> 18.0 us).
 #ifndef SPECV_MMQ_CT
 #define SPECV_MMQ_CT 2
 #endif
-#define SPECV_MMQ(X) X(10, 4, 1) X(10, 4, SPECV_MMQ_CT) X(16, 4, 1) X(1, 1, 1)
+#define SPECV_MMQ(X) X(8, 5, 1) X(8, 5, SPECV_MMQ_CT) X(16, 4, 1) X(1, 1, 1)
 
 bool mmq_supported(int K, int nk) {
   if (nk % 4 || K % (32 * nk)) return false;
@@ -2170,7 +2405,7 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
   if (epi == EPI_LM && (!p.argkey || !p.lm_cnt || !p.status || !p.result || !p.kd || !p.step || !p.rowinfo || p.R != p.n_seq * p.S))
     return hipErrorInvalidValue;
   const int gpw = nk / 4, nw = p.K / (32 * nk), ntile = p.N / 16;
-  const int ct = (nw == 10 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
+  const int ct = (nw == 8 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
 #define SPECV_MMQ_GO(a, b, c)                                                                       \
   if (nw == a && gpw == b && ct == (c)) {                                                           \
     const int nblk = (ntile + (c) - 1) / (c);                                                       \
@@ -2186,6 +2421,66 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
   }
   SPECV_MMQ(SPECV_MMQ_GO)
 #undef SPECV_MMQ_GO
+  return hipErrorInvalidValue;
+}
+
+// int4 register-A one-pass (k_mmqr) configurations: (waves, groups of 128
+// inputs per wave); a wave holds 4 * GPW steps of activations (8 registers
+// each), so GPW <= 5 with eight waves keeps two waves per SIMD.  K is covered
+// by K / (128 * NW * GPW) workgroup parts, at most kMmqrMaxParts.
+#define SPECV_MMQR(X) X(8, 5) X(8, 4) X(4, 1) X(2, 1) X(1, 1)
+constexpr int kMmqrMaxParts = 8;
+
+bool mmqr_plan(int K, int* nw, int* gpw, int* parts) {
+  if (K <= 0 || K % 128) return false;
+  const int groups = K / 128;
+#define SPECV_MMQR_PLAN(a, b)                                      \
+  if (groups % ((a) * (b)) == 0 && groups / ((a) * (b)) <= kMmqrMaxParts) { \
+    *nw = (a);                                                     \
+    *gpw = (b);                                                    \
+    *parts = groups / ((a) * (b));                                 \
+    return true;                                                   \
+  }
+  SPECV_MMQR(SPECV_MMQR_PLAN)
+#undef SPECV_MMQR_PLAN
+  return false;
+}
+
+#ifndef SPECV_MMQR_CT
+#define SPECV_MMQR_CT 1
+#endif
+
+hipError_t launch_mmqr(const GemmParams& p0, int epi, int max_grid, hipStream_t st) {
+  int nw = 0, gpw = 0, parts = 0;
+  if (p0.R < 1 || p0.R > 16 || !p0.scales || p0.N % 16 || max_grid < 1 || !mmqr_plan(p0.K, &nw, &gpw, &parts))
+    return hipErrorInvalidValue;
+  if (parts > 1 && (epi != EPI_RESID || !p0.part || !p0.cnt)) return hipErrorInvalidValue;
+  if (epi != EPI_RESID && (!p0.ss || !p0.gain || p0.ss_n * 16 != p0.K)) return hipErrorInvalidValue;
+  if (epi == EPI_RESID && (!p0.x || !p0.ss_out)) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && !p0.rowinfo) return hipErrorInvalidValue;
+  if (epi == EPI_LM && (!p0.argkey || !p0.lm_cnt || !p0.status || !p0.result || !p0.kd || !p0.step || !p0.rowinfo ||
+                        p0.R != p0.n_seq * p0.S))
+    return hipErrorInvalidValue;
+  GemmParams p = p0;
+  p.nslices = parts;
+  const int ct = SPECV_MMQR_CT;
+  const int nblk = (p.N / 16 + ct - 1) / ct;
+  int gw = max_grid / parts;
+  gw = gw < 1 ? 1 : (gw < nblk ? gw : nblk);
+  const dim3 grid(gw * parts);
+#define SPECV_MMQR_GO(a, b)                                                                                   \
+  if (nw == (a) && gpw == (b)) {                                                                              \
+    switch (epi) {                                                                                            \
+      case EPI_QKV: hipLaunchKernelGGL((k_mmqr<EPI_QKV, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break;     \
+      case EPI_RESID: hipLaunchKernelGGL((k_mmqr<EPI_RESID, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_SWIGLU: hipLaunchKernelGGL((k_mmqr<EPI_SWIGLU, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_LM: hipLaunchKernelGGL((k_mmqr<EPI_LM, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break;       \
+      default: return hipErrorInvalidValue;                                                                   \
+    }                                                                                                         \
+    return hipGetLastError();                                                                                 \
+  }
+  SPECV_MMQR(SPECV_MMQR_GO)
+#undef SPECV_MMQR_GO
   return hipErrorInvalidValue;
 }
 

@@ -49,6 +49,35 @@ inline int slice_steps_int4(int K) {
   return 0;
 }
 
+// Which int4 kernel serves a GEMM of depth K (split-K slices of nk steps) at
+// R rows; both the forward and the workspace sizing ask this one function.
+// Depths whose register-activation plan is one K part run the one-pass LDS
+// kernel with that plan's K parts up to four rows (INT4_MMQ at depth *nk_mmq)
+// and the register kernel from five to sixteen rows (INT4_MMQR): the two add
+// the same parts in the same order, so rows stay bit-exact across the switch.
+// A depth the LDS kernel serves at its own parts (several register parts: O)
+// keeps the LDS kernel up to four rows and the split-K kernel, which adds
+// those parts in that order, above; a depth it cannot serve (down) runs the
+// register kernel for every R up to sixteen (several parts end in the residual
+// epilogue's part sum; other epilogues keep the split-K kernel there).
+enum { INT4_SPLITK = 0, INT4_MMQ = 1, INT4_MMQR = 2 };
+inline int int4_route(int K, int nk, int R, int epi, int* nk_mmq) {
+  int nw = 0, gpw = 0, parts = 0;
+  const bool qr = mmqr_plan(K, &nw, &gpw, &parts);
+  *nk_mmq = nk;
+  if (R > 16) return INT4_SPLITK;
+  if (qr && parts == 1) {
+    if (R <= 4 && mmq_supported(K, 4 * gpw)) {
+      *nk_mmq = 4 * gpw;
+      return INT4_MMQ;
+    }
+    return INT4_MMQR;
+  }
+  if (R <= 4 && mmq_supported(K, nk)) return INT4_MMQ;
+  if (qr && epi == EPI_RESID && !mmq_supported(K, nk)) return INT4_MMQR;
+  return INT4_SPLITK;
+}
+
 struct LayerOff {
   size_t wqkv, wo, wgu, wd, g_attn, g_ffn;
 };
@@ -98,6 +127,11 @@ struct MmPlan {
 // Longest context, in 256-key splits, whose attention merges in k_attn.
 #ifndef SPECV_ATTN_FUSE_SPLITS
 #define SPECV_ATTN_FUSE_SPLITS 8
+#endif
+// Attention workgroups (sequence, kv head, split, query tile) up to which each
+// takes one query tile.
+#ifndef SPECV_ATTN_TPW1_WGS
+#define SPECV_ATTN_TPW1_WGS 2048
 #endif
 #ifndef SPECV_MM_WG_PER_CU
 #define SPECV_MM_WG_PER_CU 1
@@ -291,23 +325,36 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.h = take(R * Lo.F * 4);
   // Split partial sums, for the GEMMs that run the split-K kernel at some row
   // count up to max_rows (above the row limit of their one-pass kernel).
-  auto onepass_rows = [&](const MmPlan& m, int K, int nk) {
-    if (m.nw) return std::min(m.rmax, 16);
-    if (Lo.fmt == FMT_INT4 && mmq_supported(K, nk)) return 4;
-    return 0;
-  };
-  const int lim_d = Lo.d_lds ? SPECV_DOWN_MM1_ROWS : onepass_rows(Lo.mm_d, Lo.F, Lo.nk_d);
+  // int4 GEMMs up to 16 rows run the register-activation one-pass kernel;
+  // with several K parts (residual epilogues) its split buffer holds parts x N
+  // per row
   size_t part = 0;
+  auto onepass_rows = [&](const MmPlan& m, int K, int nk, int N, int epi) {
+    if (m.nw) return std::min(m.rmax, 16);
+    if (Lo.fmt != FMT_INT4) return 0;
+    int lim = 0, nk_mmq = 0;
+    for (int r = 1; r <= 16; ++r) {
+      const int route = int4_route(K, nk, r, epi, &nk_mmq);
+      if (route == INT4_SPLITK) break;
+      lim = r;
+      int nw = 0, gpw = 0, parts = 0;
+      if (route == INT4_MMQR && mmqr_plan(K, &nw, &gpw, &parts) && parts > 1)
+        part = std::max(part, (size_t)parts * N);
+    }
+    return lim;
+  };
+  const int lim_d = Lo.d_lds ? SPECV_DOWN_MM1_ROWS : onepass_rows(Lo.mm_d, Lo.F, Lo.nk_d, Lo.H, EPI_RESID);
   auto need = [&](int lim, size_t floats) {
     if (Lo.max_rows > lim) part = std::max(part, floats);
   };
-  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv), (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
-  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o), (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
-  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu), (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
+  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv, Lo.Nqkv, EPI_QKV), (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
+  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o, Lo.H, EPI_RESID), (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
+  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu, Lo.Ngu, EPI_SWIGLU), (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
   need(lim_d, (size_t)(Lo.F / (Lo.nk_d * 32)) * Lo.H);
-  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm), (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
+  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm, Lo.V, EPI_LM), (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
   Lo.part = take(std::max(part * R * 4, (size_t)256));
   Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
+  Lo.cnt_n = std::max(Lo.cnt_n, Lo.H / 16);  // one per 16-column block of a residual GEMM
   Lo.cnt = take((size_t)Lo.cnt_n * 4);
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
@@ -475,8 +522,12 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
 hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, void* af,
                       hipStream_t st, const void* ready = nullptr) {
   if (m.nw && p0.R <= m.rmax && p0.R <= 16) return launch_mm(p0, m.nw, m.spw, m.ct, m.nbuf, m.gp, max_grid, epi, st);
-  // int4, up to four rows: the one-pass kernel with the split-K kernel's K parts
-  if (fmt == FMT_INT4 && p0.R <= 4 && mmq_supported(p0.K, nk)) return launch_mmq(p0, nk, epi, max_grid, st);
+  if (fmt == FMT_INT4) {
+    int nk_mmq = nk;
+    const int route = int4_route(p0.K, nk, p0.R, epi, &nk_mmq);
+    if (route == INT4_MMQ) return launch_mmq(p0, nk_mmq, epi, max_grid, st);
+    if (route == INT4_MMQR) return launch_mmqr(p0, epi, max_grid, st);
+  }
   if (ready && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
     GemmParams p = p0;
     p.Af = ready;
@@ -727,10 +778,16 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   const Layout& L = c->lo;
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
-  // Enough (sequence, kv head, split) workgroups to fill the chip: each
-  // takes all its query tiles on K and V loaded once; else one tile each.
+  // Enough (sequence, kv head, split) workgroups to fill the chip, and more
+  // than SPECV_ATTN_TPW1_WGS of them with one query tile each: each takes all
+  // its query tiles on K and V loaded once; else one tile each (the tiles of
+  // a long span side by side).
   const int splits = (longest + 255) / 256, n_qt = (S * L.G + 15) / 16;
-  c->attn_tpw = (size_t)n_seq * L.nkv * splits >= 256 ? 16 : 1;
+  auto tiles_per_wg = [&](int sp) {
+    const size_t wg = (size_t)n_seq * L.nkv * sp;
+    return (wg >= 256 && wg * n_qt > (size_t)SPECV_ATTN_TPW1_WGS) ? 16 : 1;
+  };
+  c->attn_tpw = tiles_per_wg(splits);
   // The last split merges its tile group itself when that is short work: few
   // splits per column and at most two tiles; else the merge kernel spreads
   // the columns over the chip.
@@ -738,7 +795,7 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
                   std::min(c->attn_tpw, n_qt) <= 2) ? 1 : 0;
   // sliding-window layers: at most the splits a window touches
   const int splits_l = L.win > 0 ? std::min(splits, L.win_splits) : splits;
-  c->attn_tpw_l = (size_t)n_seq * L.nkv * splits_l >= 256 ? 16 : 1;
+  c->attn_tpw_l = tiles_per_wg(splits_l);
   c->attn_fuse_l = (splits_l <= std::min(SPECV_ATTN_FUSE_SPLITS, attn_fuse_splits(L.hd)) &&
                     std::min(c->attn_tpw_l, n_qt) <= 2) ? 1 : 0;
   StepDev* sd = (StepDev*)c->h_step();
