@@ -437,10 +437,12 @@ def summarize_gaps(trace_csv, out_md, command, n_layers=36):
 
 
 def counters_int4_workload():
-    """Short workload for SQ counter passes over the int4 GEMMs: the 32B-class
-    int4 model (64 layers, hidden 5120), a 64-token prefill, then four S=1
-    verify forwards."""
+    """Short workload for counter passes over the int4 GEMMs: the 32B-class
+    int4 model (64 layers, hidden 5120), a 64-token prefill, four S=1 verify
+    forwards, then one device copy of exactly 1 GiB (the FETCH_SIZE /
+    WRITE_SIZE calibration)."""
     import numpy as np
+    import torch
     from draft_verify_amd import specv, synth
     shape = synth.SHAPES["dense_32b"]
     sess = specv.Session(shape, specv.synth_weights(shape, seed=0, device="cuda", fmt="int4"),
@@ -449,7 +451,129 @@ def counters_int4_workload():
     rng = np.random.default_rng(6)
     specv.spec_time_verify(sess.ctx, rng.integers(0, shape["vocab"], (4, 1)).astype(np.int32))
     sess.close()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
     print("int4 counters workload done", flush=True)
+
+
+def _phase_marker():
+    """A marker between counter phases: the streaming-read kernel over 1 MiB
+    (its warm-up and timed dispatches back to back), at which the summaries
+    split the dispatch order."""
+    import torch
+    from draft_verify_amd import specv
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    specv.spec_measure_read_bw(buf.data_ptr(), buf.numel(), sink.data_ptr(), 1, st.cuda_stream)
+    torch.cuda.synchronize()
+
+
+def counters_mfma_workload(kind):
+    """Short workloads for the MFMA counter passes, phases split by a marker
+    dispatch.  kind "bf16": the Qwen3-4B shape at an 848-token context, four
+    verify forwards each at S = 1, 8 and 16, then 16 sequences of 64 prompt
+    tokens and three batched verify steps of 16 x 8 = 128 rows.  kind "int4":
+    the 32B-class int4 model at a 256-token context, four forwards each at
+    S = 1 and 8."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    rng = np.random.default_rng(6)
+    if kind == "bf16":
+        shape = synth.SHAPES["qwen3_4b"]
+        V = shape["vocab"]
+        wg = synth.weights(shape, seed=0, device="cuda")
+        tw = specv.tree_weights(wg)
+        sess = specv.Session(shape, tw, max_ctx=1024)
+        specv.spec_prefill(sess.ctx, synth.uniform_prompt(2, V, CV_CTX))
+        for S in (1, 8, 16):
+            _phase_marker()
+            specv.spec_time_verify(sess.ctx, rng.integers(0, V, (4, S)).astype(np.int32))
+        _phase_marker()  # the batched session's setup and prefill: not reported
+        sess.close()
+        n = 16
+        sess = specv.Session(shape, tw, max_ctx=256, max_seqs=n, max_rows=n * 8)
+        for i in range(n):
+            specv.spec_prefill_seq(sess.ctx, i, synth.uniform_prompt(300 + i, V, 64))
+        _phase_marker()
+        for _ in range(3):
+            specv.spec_verify_batch(sess.ctx, list(range(n)), rng.integers(0, V, (n, 8)).astype(np.int32))
+        torch.cuda.synchronize()
+        sess.close()
+    else:
+        shape = synth.SHAPES["dense_32b"]
+        V = shape["vocab"]
+        sess = specv.Session(shape, specv.synth_weights(shape, seed=0, device="cuda", fmt="int4"),
+                             max_ctx=512, fmt="int4")
+        specv.spec_prefill(sess.ctx, synth.uniform_prompt(5, V, 256))
+        for S in (1, 8):
+            _phase_marker()
+            specv.spec_time_verify(sess.ctx, rng.integers(0, V, (4, S)).astype(np.int32))
+        sess.close()
+    print(f"mfma counters workload ({kind}) done", flush=True)
+
+
+MFMA_PHASES = {"bf16": ["S=1", "S=8", "S=16", None, "128 rows (16 x 8)"], "int4": ["S=1", "S=8"]}
+
+
+def summarize_mfma(kind, csv_path, out_md, command):
+    """Per phase and GEMM / attention kernel: the median over dispatches of
+    MfmaUtil (MFMA busy cycles over GPU busy cycles x SIMDs, %), MFMA
+    operations (F16 + BF16 MOPS x 512 = flops) and SQ busy cycles, against
+    the dispatch's algorithmic flops where the kernel is a GEMM of known shape
+    (hi + lo passes counted: 2 x 2 x rows x N x K)."""
+    import collections
+    rows = _csv_rows(csv_path)
+    by_disp = collections.defaultdict(dict)
+    names = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        by_disp[d][r["Counter_Name"]] = by_disp[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    order = sorted(by_disp)
+    phases, cur, prev_marker = [], None, False
+    for d in order:
+        if "k_stream_read" in names[d]:  # a marker call is a run of these dispatches
+            if not prev_marker:
+                cur = []
+                phases.append(cur)
+            prev_marker = True
+            continue
+        prev_marker = False
+        if cur is not None and "specv::" in names[d]:
+            cur.append(d)
+    labels = MFMA_PHASES[kind]
+    lines = ["# MFMA utilisation of the verify forward's kernels (rocprofv3 counters)", "",
+             f"Command: `{command}`", "",
+             "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), per dispatch; MFMA "
+             "GFLOP = (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16) x 512 / 1e9.  Medians over the "
+             "phase's dispatches of each kernel.", ""]
+    for lab, ds in zip(labels, phases):
+        if lab is None:
+            continue
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for d in ds:
+            for c, v in by_disp[d].items():
+                agg[names[d]][c].append(v)
+        lines += [f"## {kind} {lab}", "", "| kernel | dispatches | MfmaUtil % | MFMA GFLOP | SQ_BUSY_CYCLES |",
+                  "|---|---|---|---|---|"]
+        for k, cs in sorted(agg.items(), key=lambda kv: -sorted(kv[1].get("SQ_BUSY_CYCLES", [0]))[len(kv[1].get("SQ_BUSY_CYCLES", [0])) // 2]):
+            if "k_embed" in k:
+                continue
+            med = {c: sorted(v)[len(v) // 2] for c, v in cs.items()}
+            fl = (med.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0) + med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0)) * 512 / 1e9
+            n = len(next(iter(cs.values())))
+            lines.append(f"| `{k.replace('specv::', '')[:64]}` | {n} | {med.get('MfmaUtil', 0):.1f} | {fl:.3f} | "
+                         f"{med.get('SQ_BUSY_CYCLES', 0):.0f} |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_sq(csv_path, out_md, command):
@@ -492,7 +616,7 @@ def summarize_counters(fetch_csv, write_csv, out_dir):
     the 1 GiB calibration copy."""
     def per_kernel(path, counter):
         vals = {}
-        for r in _csv_rows(path):
+        for r in sorted(_csv_rows(path), key=lambda r: int(r["Dispatch_Id"])):
             if r.get("Counter_Name") != counter:
                 continue
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
@@ -501,8 +625,8 @@ def summarize_counters(fetch_csv, write_csv, out_dir):
     write = per_kernel(write_csv, "WRITE_SIZE")
     copy_name = next(k for k in fetch if "copyBuffer" in k)  # the runtime's device-to-device copy
     gib_kib = (1 << 30) / 1024.0
-    f_scale = gib_kib / max(fetch[copy_name])
-    w_scale = gib_kib / max(write[copy_name])
+    f_scale = gib_kib / fetch[copy_name][-1]  # the workload's last device copy: exactly 1 GiB
+    w_scale = gib_kib / write[copy_name][-1]
     gu = next(k for k in fetch if GU_KERNEL in k)
     # the last 10 forwards' 36 launches are the S=1 timing loop
     f_kib = sorted(fetch[gu][-360:])[180]
@@ -510,7 +634,7 @@ def summarize_counters(fetch_csv, write_csv, out_dir):
     hbm = (f_kib * f_scale + w_kib * w_scale) * 1024.0
     res = {"kernel_source_hash": kernel_source_hash(),
            "calibration": {"kernel": copy_name[:60], "bytes": 1 << 30,
-                           "fetch_kib": max(fetch[copy_name]), "write_kib": max(write[copy_name]),
+                           "fetch_kib": fetch[copy_name][-1], "write_kib": write[copy_name][-1],
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": {"gateup": {"name": gu[:60], "fetch_kib_median": f_kib, "write_kib_median": w_kib,
                                   "hbm_bytes_per_launch": hbm,
@@ -526,22 +650,22 @@ def summarize_traffic_all(fetch_csv, write_csv, out_md, command, n_fwd=10):
     1 GiB calibration copy, against the algorithmic bytes of its op."""
     def per_kernel(path, counter):
         vals = {}
-        for r in _csv_rows(path):
+        for r in sorted(_csv_rows(path), key=lambda r: int(r["Dispatch_Id"])):
             if r.get("Counter_Name") == counter:
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     copy_name = next(k for k in fetch if "copyBuffer" in k)
     gib_kib = (1 << 30) / 1024.0
-    fs, ws = gib_kib / max(fetch[copy_name]), gib_kib / max(write[copy_name])
+    fs, ws = gib_kib / fetch[copy_name][-1], gib_kib / write[copy_name][-1]  # the last copy: the 1 GiB one
     H, F, DQ, DK, V, hd = 2560, 9728, 4096, 1024, 151936, 128
     algo = {"k_mm<0,": ("QKV", (DQ + 2 * DK) * H * 2), "k_attn<": ("attention (848 ctx)", 849 * DK * 2 * 2),
             "k_mm1<1,": ("O", H * DQ * 2), "k_mm<2,": ("gate/up", 2 * F * H * 2),
             "k_mm1l<": ("down", H * F * 2), "k_mm<3,": ("LM head", V * H * 2)}
     lines = ["# HBM traffic per launch of the S=1 forward's kernels (Qwen3-4B shape, 848-token context)", "",
              f"Command: `{command}`", "",
-             f"Calibration: a 1 GiB device copy reads FETCH_SIZE {max(fetch[copy_name]):.0f} KiB and "
-             f"WRITE_SIZE {max(write[copy_name]):.0f} KiB: factors {fs:.3f} (fetch), {ws:.3f} (write).", "",
+             f"Calibration: a 1 GiB device copy reads FETCH_SIZE {fetch[copy_name][-1]:.0f} KiB and "
+             f"WRITE_SIZE {write[copy_name][-1]:.0f} KiB: factors {fs:.3f} (fetch), {ws:.3f} (write).", "",
              "| op | kernel | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
              "|---|---|---|---|---|---|---|"]
     for key, (op, ab) in algo.items():
@@ -555,6 +679,47 @@ def summarize_traffic_all(fetch_csv, write_csv, out_md, command, n_fwd=10):
         f_b, w_b = f_l[len(f_l) // 2] * fs * 1024, w_l[len(w_l) // 2] * ws * 1024
         lines.append(f"| {op} | `{k[:48]}` | {f_b / 1e6:.2f} | {w_b / 1e6:.2f} | {(f_b + w_b) / 1e6:.2f} | "
                      f"{ab / 1e6:.2f} | {(f_b + w_b) / ab:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_traffic_int4(fetch_csv, write_csv, out_md, command, n_fwd=4):
+    """HBM bytes per launch of the int4 32B-class model's S=1 GEMMs (the int4
+    counters workload's last n_fwd forwards), scaled by the 1 GiB calibration
+    copy, against the algorithmic bytes: packed weights N x K / 2 plus bf16
+    scales N x K / 128 x 2."""
+    def per_kernel(path, counter):
+        vals = {}
+        for r in sorted(_csv_rows(path), key=lambda r: int(r["Dispatch_Id"])):
+            if r.get("Counter_Name") == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "copyBuffer" in k)
+    gib_kib = (1 << 30) / 1024.0
+    fs, ws = gib_kib / fetch[copy_name][-1], gib_kib / write[copy_name][-1]  # the last copy: the 1 GiB one
+    H, F, DQ, DK, V = 5120, 25600, 8192, 1024, 151936
+    wb = lambda N, K: N * K / 2 + N * K / 128 * 2
+    algo = {"k_mmq<0,": ("QKV", wb(DQ + 2 * DK, H), 64), "k_mmq<1,": ("O", wb(H, DQ), 64),
+            "k_mmq<2,": ("gate/up", wb(2 * F, H), 64), "k_mmqr<1,": ("down", wb(H, F), 64),
+            "k_mmq<3,": ("LM head", wb(V, H), 1)}
+    lines = ["# HBM traffic per launch of the int4 S=1 forward's GEMMs (32B-class shape, int4 group-128)", "",
+             f"Command: `{command}`", "",
+             f"Calibration: a 1 GiB device copy reads FETCH_SIZE {fetch[copy_name][-1]:.0f} KiB and "
+             f"WRITE_SIZE {write[copy_name][-1]:.0f} KiB: factors {fs:.3f} (fetch), {ws:.3f} (write).", "",
+             "| op | kernel | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    for key, (op, ab, per) in algo.items():
+        names = [k for k in fetch if key in k]
+        if not names:
+            continue
+        k = names[0]
+        f_l = sorted(fetch[k][-n_fwd * per:])
+        w_l = sorted(write.get(k, [0.0])[-n_fwd * per:])
+        f_b, w_b = f_l[len(f_l) // 2] * fs * 1024, w_l[len(w_l) // 2] * ws * 1024
+        lines.append(f"| {op} | `{k.replace('specv::', '')[:48]}` | {f_b / 1e6:.2f} | {w_b / 1e6:.2f} | "
+                     f"{(f_b + w_b) / 1e6:.2f} | {ab / 1e6:.2f} | {(f_b + w_b) / ab:.3f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -605,11 +770,14 @@ def main():
     ap.add_argument("--counters", action="store_true", help="short workload for rocprofv3 --pmc passes")
     ap.add_argument("--counters-int4", action="store_true", help="short int4 workload for SQ counter passes")
     ap.add_argument("--summarize-sq", nargs=3, metavar=("CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--counters-mfma", choices=["bf16", "int4"], help="short workload for the MFMA counter passes")
+    ap.add_argument("--summarize-mfma", nargs=4, metavar=("KIND", "CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("STATS_CSV", "TRACE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--gaps-workload", type=int, metavar="S", help="short S-row forward workload for a kernel trace")
     ap.add_argument("--summarize-gaps", nargs=3, metavar=("TRACE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--summarize-traffic-int4", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
@@ -621,12 +789,18 @@ def main():
         return summarize_gaps(*args.summarize_gaps)
     if args.summarize_traffic:
         return summarize_traffic_all(*args.summarize_traffic)
+    if args.summarize_traffic_int4:
+        return summarize_traffic_int4(*args.summarize_traffic_int4)
     if args.counters:
         return counters_workload()
     if args.counters_int4:
         return counters_int4_workload()
     if args.summarize_sq:
         return summarize_sq(*args.summarize_sq)
+    if args.counters_mfma:
+        return counters_mfma_workload(args.counters_mfma)
+    if args.summarize_mfma:
+        return summarize_mfma(*args.summarize_mfma)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout "
               f"is a design note, not a measured path.", file=sys.stderr)
