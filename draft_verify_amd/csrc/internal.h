@@ -182,7 +182,7 @@ hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t
 // own the K parts of the int4 split-K kernel with nk-step slices, so the two
 // agree bit for bit; compiled for K / (32 nk) waves of nk / 4 groups in
 // {10 x 4, 16 x 4, 1 x 1}.
-bool mmq_supported(int K, int nk);
+bool mmq_supported(int K, int nk, int epi);
 hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStream_t st);
 bool mmqr_plan(int K, int* nw, int* gpw, int* parts);
 hipError_t launch_mmqr(const GemmParams& p, int epi, int max_grid, hipStream_t st);

@@ -9,8 +9,10 @@
 //   cache advance.
 //
 // Numerics: weights bf16; activations enter the MFMA as a bf16 hi + lo pair
-// (two passes, ~16 mantissa bits); fp32 accumulation, residual and softmax;
-// fp16 KV cache, fp16 query and probabilities in attention.
+// (two passes, ~16 mantissa bits); int4 weights are exact integers, whose
+// activations enter once as fp16 (11 bits, the int4 matvec's own operand
+// precision); fp32 accumulation, residual and softmax; fp16 KV cache, fp16
+// query and probabilities in attention.
 // Row invariance: every row runs the same 16-row MFMA tiles, the same
 // K-split per (N, K) and the same fixed-order reductions whatever S is, so a
 // row's result does not depend on the other rows of the forward.
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
 // ------------------------------------------------------------ skinny GEMM
 //
 // Y[R, N] = A'[R, K] W^T with A' = RMSNorm(A) (optional) split into bf16
-// hi + lo.  A workgroup (4 waves) owns 64 output columns x one K slice of
+// hi + lo (int4: rounded to fp16).  A workgroup (4 waves) owns 64 output columns x one K slice of
 // NK*32 inputs; wave w owns the 16-column tile 4*nb + w.  Each wave first
 // issues all NK fragment loads of its weights (contiguous NK KiB, streamed
 // with non-temporal loads), then stages A for 16 rows of the slice into LDS
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     for (int j = 0; j < NF; ++j) asm volatile("" ::"v"(b[0][j]));
   }
   for (int m0 = 0; m0 < P.R; m0 += 16) {
-    // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo.
+    // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo (int4: fp16).
     if constexpr (PREP) {
 #pragma unroll
       for (int i = 0; i < PUT; ++i) {
@@ -392,16 +394,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * sG[j * 32 + g * 8 + e];
       }
       u32x4 hw, lw;
-      if constexpr (FMT == FMT_INT4) {  // fp16 hi + lo: the operand type of the fp16 MFMA on exact q
-        f16x8 hi, lo;
+      if constexpr (FMT == FMT_INT4) {  // fp16: the operand type of the fp16 MFMA on exact q
+        f16x8 hi;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const _Float16 h = (_Float16)v[e];
-          hi[e] = h;
-          lo[e] = (_Float16)(v[e] - (float)h);
-        }
+        for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
         hw = __builtin_bit_cast(u32x4, hi);
-        lw = __builtin_bit_cast(u32x4, lo);
+        lw = hw;  // unused: one fp16 pass
       } else {
         bf16x8 hi, lo;
 #pragma unroll
@@ -415,7 +413,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
       }
       const int l = g * 16 + row;
       sA[(j * 2) * 64 + l] = hw;
-      sA[(j * 2 + 1) * 64 + l] = lw;
+      if constexpr (FMT != FMT_INT4) sA[(j * 2 + 1) * 64 + l] = lw;
     }
     __syncthreads();
     if (m0 + 16 < P.R) load_a(m0 + 16);  // the next chunk's A loads fly during this chunk's MFMA
@@ -436,7 +434,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
         for (int d = 0; d < 4; ++d) {
           const int j = gi * 4 + d;
           const f16x8 ah = __builtin_bit_cast(f16x8, sA[(j * 2) * 64 + lane]);
-          const f16x8 al = __builtin_bit_cast(f16x8, sA[(j * 2 + 1) * 64 + lane]);
 #pragma unroll
           for (int c = 0; c < CT; ++c) {
             // Opaque per row chunk, so the dequantised operands are rebuilt
@@ -446,7 +443,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
             asm volatile("" : "+v"(w));
             const f16x8 bq = dequant8<EPI != EPI_QKV>(w);
             t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t[c], 0, 0, 0);
-            t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t[c], 0, 0, 0);
           }
         }
 #pragma unroll
@@ -1284,10 +1280,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   }
 }
 
-// The int4 one-pass GEMM for at most four rows (K = hidden or n_q * hd),
-// activations staged in LDS:
+// The int4 one-pass GEMM for at most eight rows (K = hidden or n_q * hd),
+// activations staged in LDS (RL = 4 or 8 staged rows, the same arithmetic):
 // every workgroup stages the whole normalised activation once in LDS as fp16
-// hi + lo in the MFMA A-operand order ([step][hi, lo][lane group][row]),
+// in the MFMA A-operand order ([step][lane group][row]),
 // then walks blocks of CT 16-column tiles (blockIdx.x, + gridDim.x, ...),
 // reading each A fragment from LDS once for the CT tiles.  Wave w owns
 // the K part of groups [w*GPW, (w+1)*GPW) of 128 inputs: per group the four
@@ -1297,9 +1293,9 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 // bit for bit (each tile's sums keep their order whatever CT is).  The next
 // block's fragments are issued as soon as the MFMAs have read the current
 // ones.
-template <int EPI, int NW, int GPW, int CT>
+template <int EPI, int NW, int GPW, int CT, int RL>
 __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
-  constexpr int NT = NW * 64, KG = NW * GPW, KS = KG * 4, RL = 4;
+  constexpr int NT = NW * 64, KG = NW * GPW, KS = KG * 4;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
   constexpr int PPT = (RL * 8 * CT + NT - 1) / NT;                 // epilogue pairs per thread
@@ -1307,7 +1303,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   const int g0 = wave * GPW, row = lane & 15, kg = lane >> 4;
   const int ntile = P.N >> 4, nblk = (ntile + CT - 1) / CT, G = (int)gridDim.x;
 
-  __shared__ u32x4 sA[KS * 2 * 4 * RL];
+  __shared__ u32x4 sA[KS * 4 * RL];  // [step][lane group][row], fp16
   __shared__ f32x4 sAcc[NW * 64 * CT];
   __shared__ float sR[RL];
 
@@ -1362,14 +1358,14 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   };
   int blk = blockIdx.x;
   if (blk < nblk) fetch(b0, s0, blk);
-  if constexpr (NORM) {  // rstd of the rows (rstd16; one wave), after every load is out
-    if (tid < 16 * RL) {
-      const float rs = rstd16(P.ss, P.ss_n, tid >> 4, P.R, tid & 15, P.inv_dim, P.eps);
-      if ((tid & 15) == 0) sR[tid >> 4] = (tid >> 4) < P.R ? rs : 0.0f;
+  if constexpr (NORM) {  // rstd of the rows (rstd16, 16 lanes per row, whole waves), after every load is out
+    for (int t = tid; t < 16 * RL; t += NT) {
+      const float rs = rstd16(P.ss, P.ss_n, t >> 4, P.R, t & 15, P.inv_dim, P.eps);
+      if ((t & 15) == 0) sR[t >> 4] = (t >> 4) < P.R ? rs : 0.0f;
     }
     __syncthreads();
   }
-  // A into LDS as fp16 hi + lo (the int4 split-K kernel's conversion)
+  // A into LDS as fp16 (the int4 split-K kernel's conversion)
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int u = tid + i * NT;
@@ -1386,15 +1382,10 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
       }
-      f16x8 hi, lo;
+      f16x8 hi;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 h = (_Float16)v[e];
-        hi[e] = h;
-        lo[e] = (_Float16)(v[e] - (float)h);
-      }
-      sA[((j * 2) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
-      sA[((j * 2 + 1) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, lo);
+      for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
+      sA[(j * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
     }
   }
   __syncthreads();
@@ -1420,13 +1411,11 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int j = (g0 + gi) * 4 + d;
-        const u32x4 h = sA[((j * 2) * 4 + kg) * RL + rc], l = sA[((j * 2 + 1) * 4 + kg) * RL + rc];
-        const f16x8 ah = __builtin_bit_cast(f16x8, h), al = __builtin_bit_cast(f16x8, l);
+        const f16x8 ah = __builtin_bit_cast(f16x8, sA[(j * 4 + kg) * RL + rc]);
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
           const f16x8 bq = dequant8_ao(bw[c][gi][d]);
           t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t[c], 0, 0, 0);
-          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t[c], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -1493,7 +1482,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 // + gridDim.x / parts, ...).  Every lane loads its own A values once, straight
 // into the MFMA A-operand layout (lane l: row l%16, inputs 8*(l/16)..+8 of
 // each of the wave's 4*GPW steps), applies the RMSNorm (the gains staged in
-// LDS) and keeps them as fp16 hi + lo for the whole walk, so the row count
+// LDS) and keeps them as fp16 for the whole walk, so the row count
 // costs no LDS and no weight is read twice: rows up to 16 run the same
 // instructions as one row.  Per tile and group the four steps' MFMAs on the
 // exact integer weights, then one fused multiply-add by the column's group
@@ -1574,8 +1563,8 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
     }
   }
   __syncthreads();
-  // normalise and split into fp16 hi + lo, in place
-  f16x8 ah[ST], al[ST];
+  // normalise and round to fp16, in place
+  f16x8 ah[ST];
   {
     const float sc = NORM ? sR[row] : 1.0f;
 #pragma unroll
@@ -1591,11 +1580,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 h = (_Float16)v[e];
-        ah[j][e] = h;
-        al[j][e] = (_Float16)(v[e] - (float)h);
-      }
+      for (int e = 0; e < 8; ++e) ah[j][e] = (_Float16)v[e];
     }
   }
   unsigned long long kmax[EPI == EPI_LM ? PPT : 1];
@@ -1617,7 +1602,6 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
         for (int c = 0; c < CT; ++c) {
           const f16x8 bq = dequant8_ao(bw[c][gi][d]);
           t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[gi * 4 + d], bq, t[c], 0, 0, 0);
-          t[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[gi * 4 + d], bq, t[c], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -2375,30 +2359,48 @@ bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp) {
 
 // int4 one-pass (k_mmq) configurations: (waves, groups per wave, 16-column
 // tiles per pass).  K = 5120 takes eight waves of five groups, the K parts of
-// the register-activation kernel that serves five to sixteen rows, so the
+// the register-activation kernel that serves nine to sixteen rows, so the
 // two agree bit for bit (ten waves of four ran 1-6 % faster at one row: LM
 // head 93 vs 99 us).  Two tiles per pass share each read of the A slice from
-// LDS where the LDS holds the second partial tile (K = 5120: 80 KiB of A +
-// 16 KiB of partials; K = 8192 would need 160 KiB); they are taken when
+// LDS where the LDS holds the second partial tile (K = 5120: 80 KiB of A for
+// eight fp16 rows + 16 KiB of partials; K = 8192 has 128 KiB of A and no room
+// for it); they are taken when
 // every workgroup walks at least four such blocks (gate/up 46.9 -> 42.6 us,
 // LM head 129 -> 110 us at the 32B shape), since with fewer the blocks split
 // unevenly over the workgroups (QKV's 640 tiles: 16.4 -> 18.0 us).
 #ifndef SPECV_MMQ_CT
 #define SPECV_MMQ_CT 2
 #endif
-#define SPECV_MMQ(X) X(8, 5, 1) X(8, 5, SPECV_MMQ_CT) X(16, 4, 1) X(1, 1, 1)
+// (waves, groups per wave, tiles per pass, residual epilogue only): sixteen
+// waves of four groups serve O (K = 8192) alone, whose staging holds no gains.
+#define SPECV_MMQ(X) X(8, 5, 1, 0) X(8, 5, SPECV_MMQ_CT, 0) X(16, 4, 1, 1) X(1, 1, 1, 0)
 
-bool mmq_supported(int K, int nk) {
+bool mmq_supported(int K, int nk, int epi) {
   if (nk % 4 || K % (32 * nk)) return false;
   const int gpw = nk / 4, nw = K / (32 * nk);
-#define SPECV_MMQ_HAS(a, b, c) if (nw == a && gpw == b) return true;
+#define SPECV_MMQ_HAS(a, b, c, ro) \
+  if (nw == a && gpw == b && (!(ro) || epi == EPI_RESID)) return true;
   SPECV_MMQ(SPECV_MMQ_HAS)
 #undef SPECV_MMQ_HAS
   return false;
 }
 
+// One k_mmq configuration's launch; a residual-only configuration is never
+// instantiated with another epilogue.
+template <int EPI, int NW, int GPW, int CT, bool RO>
+hipError_t go_mmq(dim3 grid, const GemmParams& p, hipStream_t st) {
+  if constexpr (RO && EPI != EPI_RESID) {
+    return hipErrorInvalidValue;
+  } else {
+    // four staged rows where they suffice (less staging work at one row)
+    if (p.R <= 4) hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 4>), grid, dim3(NW * 64), 0, st, p);
+    else hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 8>), grid, dim3(NW * 64), 0, st, p);
+    return hipGetLastError();
+  }
+}
+
 hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStream_t st) {
-  if (p.R < 1 || p.R > 4 || !p.scales || p.N % 16 || max_grid < 1 || !mmq_supported(p.K, nk))
+  if (p.R < 1 || p.R > 8 || !p.scales || p.N % 16 || max_grid < 1 || !mmq_supported(p.K, nk, epi))
     return hipErrorInvalidValue;
   if (epi != EPI_RESID && (!p.ss || !p.gain || p.ss_n * 16 != p.K)) return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
@@ -2406,18 +2408,17 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
     return hipErrorInvalidValue;
   const int gpw = nk / 4, nw = p.K / (32 * nk), ntile = p.N / 16;
   const int ct = (nw == 8 && ntile >= 8 * max_grid) ? SPECV_MMQ_CT : 1;
-#define SPECV_MMQ_GO(a, b, c)                                                                       \
-  if (nw == a && gpw == b && ct == (c)) {                                                           \
-    const int nblk = (ntile + (c) - 1) / (c);                                                       \
-    const dim3 grid(nblk < max_grid ? nblk : max_grid);                                             \
-    switch (epi) {                                                                                  \
-      case EPI_QKV: hipLaunchKernelGGL((k_mmq<EPI_QKV, a, b, c>), grid, dim3(a * 64), 0, st, p); break;   \
-      case EPI_RESID: hipLaunchKernelGGL((k_mmq<EPI_RESID, a, b, c>), grid, dim3(a * 64), 0, st, p); break; \
-      case EPI_SWIGLU: hipLaunchKernelGGL((k_mmq<EPI_SWIGLU, a, b, c>), grid, dim3(a * 64), 0, st, p); break; \
-      case EPI_LM: hipLaunchKernelGGL((k_mmq<EPI_LM, a, b, c>), grid, dim3(a * 64), 0, st, p); break;     \
-      default: return hipErrorInvalidValue;                                                         \
-    }                                                                                               \
-    return hipGetLastError();                                                                       \
+#define SPECV_MMQ_GO(a, b, c, ro)                                                  \
+  if (nw == a && gpw == b && ct == (c)) {                                          \
+    const int nblk = (ntile + (c) - 1) / (c);                                      \
+    const dim3 grid(nblk < max_grid ? nblk : max_grid);                            \
+    switch (epi) {                                                                 \
+      case EPI_QKV: return go_mmq<EPI_QKV, a, b, c, (ro) != 0>(grid, p, st);       \
+      case EPI_RESID: return go_mmq<EPI_RESID, a, b, c, (ro) != 0>(grid, p, st);   \
+      case EPI_SWIGLU: return go_mmq<EPI_SWIGLU, a, b, c, (ro) != 0>(grid, p, st); \
+      case EPI_LM: return go_mmq<EPI_LM, a, b, c, (ro) != 0>(grid, p, st);         \
+      default: return hipErrorInvalidValue;                                        \
+    }                                                                              \
   }
   SPECV_MMQ(SPECV_MMQ_GO)
 #undef SPECV_MMQ_GO

@@ -52,11 +52,11 @@ inline int slice_steps_int4(int K) {
 // Which int4 kernel serves a GEMM of depth K (split-K slices of nk steps) at
 // R rows; both the forward and the workspace sizing ask this one function.
 // Depths whose register-activation plan is one K part run the one-pass LDS
-// kernel with that plan's K parts up to four rows (INT4_MMQ at depth *nk_mmq)
-// and the register kernel from five to sixteen rows (INT4_MMQR): the two add
+// kernel with that plan's K parts up to eight rows (INT4_MMQ at depth *nk_mmq)
+// and the register kernel from nine to sixteen rows (INT4_MMQR): the two add
 // the same parts in the same order, so rows stay bit-exact across the switch.
 // A depth the LDS kernel serves at its own parts (several register parts: O)
-// keeps the LDS kernel up to four rows and the split-K kernel, which adds
+// keeps the LDS kernel up to eight rows and the split-K kernel, which adds
 // those parts in that order, above; a depth it cannot serve (down) runs the
 // register kernel for every R up to sixteen (several parts end in the residual
 // epilogue's part sum; other epilogues keep the split-K kernel there).
@@ -67,14 +67,14 @@ inline int int4_route(int K, int nk, int R, int epi, int* nk_mmq) {
   *nk_mmq = nk;
   if (R > 16) return INT4_SPLITK;
   if (qr && parts == 1) {
-    if (R <= 4 && mmq_supported(K, 4 * gpw)) {
+    if (R <= 8 && mmq_supported(K, 4 * gpw, epi)) {
       *nk_mmq = 4 * gpw;
       return INT4_MMQ;
     }
     return INT4_MMQR;
   }
-  if (R <= 4 && mmq_supported(K, nk)) return INT4_MMQ;
-  if (qr && epi == EPI_RESID && !mmq_supported(K, nk)) return INT4_MMQR;
+  if (R <= 8 && mmq_supported(K, nk, epi)) return INT4_MMQ;
+  if (qr && epi == EPI_RESID && !mmq_supported(K, nk, epi)) return INT4_MMQR;
   return INT4_SPLITK;
 }
 
@@ -229,9 +229,9 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   // full-depth slices, halving the split partials (R x vocab x 4 bytes each).
   Lo.nk_lm = Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
-  // int4 rows up to four take the one-pass kernel at the QKV depth; more rows
+  // int4 rows up to eight take the one-pass kernel at the QKV depth; more rows
   // keep the same K parts
-  if (Lo.fmt == FMT_INT4 && mmq_supported(Lo.H, Lo.nk_qkv)) Lo.nk_lm = Lo.nk_qkv;
+  if (Lo.fmt == FMT_INT4 && mmq_supported(Lo.H, Lo.nk_qkv, EPI_LM)) Lo.nk_lm = Lo.nk_qkv;
   if (!Lo.nk_qkv || !Lo.nk_o || !Lo.nk_d) return fail("GEMM depths must be multiples of 64");
   Lo.mm_qkv = Lo.mm_o = Lo.mm_gu = Lo.mm_d = Lo.mm_lm = MmPlan{0, 0, 0, 0, 0, 0};
   Lo.d_lds = false;
