@@ -1492,6 +1492,8 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 // (an arrival counter per block) adds the parts in part order and runs the
 // residual epilogue.  Every sum's order depends on the shape of the GEMM
 // alone, never on R, so an S-row forward equals S one-row forwards bit for bit.
+constexpr int kMmqrMaxParts = 8;  // K parts of the register kernel's plans (host-checked)
+
 template <int EPI, int NW, int GPW, int CT>
 __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
   constexpr int NT = NW * 64, KG = NW * GPW, ST = GPW * 4;
@@ -1509,6 +1511,7 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
   __shared__ f32x4 sAcc[NW * 64 * CT];
   __shared__ float sR[16];
   __shared__ int sLast;
+  __shared__ int sDone[64];  // residual parts: blocks this workgroup completes, per round
 
   constexpr bool POS = EPI == EPI_QKV || EPI == EPI_LM;
   int qpos[POS ? PPT : 1], qblk[EPI == EPI_QKV ? PPT : 1];
@@ -1665,38 +1668,50 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
   }
   if constexpr (EPI == EPI_RESID) {
     if (parts == 1) return;
-    // the parts of this workgroup's blocks are stored: the last part of a
-    // block to arrive adds them in part order and runs the epilogue
+    // The parts of this workgroup's blocks are stored.  One arrival per block,
+    // all in flight at once; the blocks this workgroup completed (its part
+    // arrived last) are then gathered together: each pair's parts added in
+    // part order, then the epilogue.  (Block by block, the arrival and the
+    // gather cost two memory round trips per block in series.)
     wait_mem();
     __syncthreads();
-    for (int b = wg; b < nblk; b += GW) {
-      if (tid == 0) {
-        const unsigned old = atomicAdd(&P.cnt[b], 1u);
-        sLast = old == (unsigned)(parts - 1);
-        if (sLast) P.cnt[b] = 0u;  // every part has arrived: ready for the next launch
-      }
+    constexpr int CH = 64;  // blocks per round
+    const int nmine = wg < nblk ? (nblk - 1 - wg) / GW + 1 : 0;
+    for (int i0 = 0; i0 < nmine; i0 += CH) {
+      if (tid == 0) sLast = 0;
       __syncthreads();
-      if (sLast) {
-        const int npairs = P.R * 8 * CT;
-#pragma unroll
-        for (int it = 0; it < PPT; ++it) {
-          const int p = tid + it * NT;
-          const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
-          const int col = (b * CT + ct) * 16 + 2 * pp;
-          if (p < npairs && col < P.N) {
-#pragma clang fp contract(off)
-            float v0 = 0.0f, v1 = 0.0f;
-            for (int s = 0; s < parts; ++s) {
-              const float2 t = ld_dev2(P.part + ((size_t)s * P.R + r) * P.N + col);
-              v0 += t.x;
-              v1 += t.y;
-            }
-            const float s8 = sum8(resid_pair(P, r, col, v0, v1));
-            if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = s8;
-          }
+      for (int i = tid; i < CH && i0 + i < nmine; i += NT) {
+        const int b = wg + (i0 + i) * GW;
+        const unsigned old = atomicAdd(&P.cnt[b], 1u);
+        if (old == (unsigned)(parts - 1)) {
+          P.cnt[b] = 0u;  // every part has arrived: ready for the next launch
+          sDone[atomicAdd(&sLast, 1)] = b;
         }
       }
-      __syncthreads();  // sLast is rewritten for the next block
+      __syncthreads();
+      const int nd = sLast, npairs = P.R * 8 * CT;
+      // q = block index * npairs + pair: every aligned 8 of q are 16 columns
+      // of one row of one block (the shuffle group of the epilogue)
+      for (int q = tid; q < nd * npairs; q += NT) {
+#pragma clang fp contract(off)
+        const int bi = q / npairs, p = q - bi * npairs, b = sDone[bi];
+        const int r = p / (8 * CT), rem = p - r * (8 * CT), ct = rem >> 3, pp = rem & 7;
+        const int col = (b * CT + ct) * 16 + 2 * pp;
+        float2 t[kMmqrMaxParts];
+#pragma unroll
+        for (int s = 0; s < kMmqrMaxParts; ++s)
+          if (s < parts) t[s] = ld_dev2(P.part + ((size_t)s * P.R + r) * P.N + col);
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMmqrMaxParts; ++s)
+          if (s < parts) {
+            v0 += t[s].x;
+            v1 += t[s].y;
+          }
+        const float s8 = sum8(resid_pair(P, r, col, v0, v1));
+        if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = s8;
+      }
+      __syncthreads();  // sLast and sDone are rewritten by the next round
     }
   }
 }
@@ -2430,7 +2445,6 @@ hipError_t launch_mmq(const GemmParams& p, int nk, int epi, int max_grid, hipStr
 // each), so GPW <= 5 with eight waves keeps two waves per SIMD.  K is covered
 // by K / (128 * NW * GPW) workgroup parts, at most kMmqrMaxParts.
 #define SPECV_MMQR(X) X(8, 5) X(8, 4) X(4, 1) X(2, 1) X(1, 1)
-constexpr int kMmqrMaxParts = 8;
 
 bool mmqr_plan(int K, int* nw, int* gpw, int* parts) {
   if (K <= 0 || K % 128) return false;
