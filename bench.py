@@ -756,6 +756,70 @@ def summarize_trace(stats_csv, trace_csv, out_md, command):
     print("\n".join(lines))
 
 
+def launch_floor(out_md, command, gib=4):
+    """The floor of a kernel-per-operation forward: for each operation of the
+    4B S = 1 forward, back-to-back launches (one HIP graph) of the library's
+    streaming-read kernel over never-repeating regions of that operation's
+    algorithmic bytes, best of a few grids; summed over the forward's launches
+    and set against the measured forward."""
+    import numpy as np
+    import torch
+    from draft_verify_amd import specv, synth
+    shape = synth.SHAPES["qwen3_4b"]
+    desc = specv.make_desc(shape, max_ctx=1024)
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    per_fwd = {"embed": 1, "qkv": shape["n_layers"], "attn": shape["n_layers"], "o": shape["n_layers"],
+               "gateup": shape["n_layers"], "down": shape["n_layers"], "lm": 1}
+    rows = [("launch (16 B)", 16, 0)]
+    for op in specv.OPS:
+        b = int(specv.spec_op_bytes(desc, op, 1, CV_CTX)) // 16 * 16
+        rows.append((op, max(16, b), per_fwd[op]))
+    out = []
+    for name, nbytes, n_fwd in rows:
+        n_reg = max(2, min(400, (gib << 30) // nbytes))
+        best = None
+        for grid in (256, 512, 1024, 2048, max(256, min(65535, nbytes // (256 * 16 * 8)))):
+            us = specv.spec_measure_read_chain(buf.data_ptr(), nbytes, n_reg, grid, sink.data_ptr(), st.cuda_stream)
+            if best is None or us < best[0]:
+                best = (us, grid)
+        out.append((name, nbytes, n_fwd, best[0], best[1], n_reg))
+        log(f"  {name}: {nbytes} B, {best[0]:.2f} us (grid {best[1]}, {n_reg} regions)")
+    del buf
+    torch.cuda.empty_cache()
+    # the measured forward on the same box
+    wg = synth.weights(shape, seed=0, device="cuda")
+    sess = specv.Session(shape, specv.tree_weights(wg), max_ctx=1024)
+    del wg
+    torch.cuda.empty_cache()
+    specv.spec_prefill(sess.ctx, synth.uniform_prompt(2, shape["vocab"], CV_CTX))
+    rng = np.random.default_rng(6)
+    fwd_ms = float(np.median(specv.spec_time_verify(sess.ctx, rng.integers(0, shape["vocab"], (30, 1)).astype(np.int32))[5:]))
+    ops_us = {op: specv.spec_time_op(sess.ctx, op, 1, 5) for op in specv.OPS}
+    sess.close()
+    floor_us = sum(us * n for name, _, n, us, _, _ in out if n)
+    fwd_bytes = sum(b * n for name, b, n, _, _, _ in out if n)
+    lines = ["# Launch floor of a kernel-per-operation forward (Qwen3-4B shape, S = 1, 848-token context)", "",
+             f"Command: `{command}`", "",
+             "Each row: back-to-back launches (one HIP graph replay) of the streaming-read kernel over "
+             "never-repeating regions of the operation's algorithmic bytes, best grid; the first row reads "
+             "16 bytes per launch (the launch itself).", "",
+             "| operation | bytes / launch | launches / forward | stream-only us / launch | grid | GB/s | this build's kernel us |",
+             "|---|---|---|---|---|---|---|"]
+    for name, b, n, us, grid, _ in out:
+        mine = f"{ops_us[name]:.2f}" if name in ops_us else ""
+        lines.append(f"| {name} | {b} | {n} | {us:.2f} | {grid} | {b / us / 1e3:.0f} | {mine} |")
+    lines += ["", f"Forward of stream-only launches: {floor_us / 1e3:.3f} ms over {fwd_bytes / 1e9:.3f} GB "
+              f"({fwd_bytes / floor_us / 1e3 / 8000:.3f} of 8 TB/s); the measured forward: {fwd_ms:.3f} ms "
+              f"({fwd_bytes / (fwd_ms * 1e3) / 1e3 / 8000:.3f} of 8 TB/s)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -778,7 +842,11 @@ def main():
     ap.add_argument("--summarize-gaps", nargs=3, metavar=("TRACE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"))
     ap.add_argument("--summarize-traffic-int4", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"))
+    ap.add_argument("--launch-floor", nargs=2, metavar=("OUT_MD", "COMMAND"),
+                    help="stream-only launches at each operation's bytes, against the measured forward")
     args = ap.parse_args()
+    if args.launch_floor:
+        return launch_floor(*args.launch_floor)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters)
     if args.summarize_trace:

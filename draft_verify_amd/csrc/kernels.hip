@@ -544,11 +544,21 @@ __device__ __forceinline__ void for_pairs(const GemmParams& P, int nb, F&& f) {
 // one-pass GEMMs so that both give bit-identical results (contraction off:
 // every product and sum rounds on its own, whatever the surrounding code).
 
+// The (cos, sin) pair RoPE applies to output column c of a row at position
+// pos (a q or k column), or (0, 0) for a v column or a recurrent layer.
+__device__ __forceinline__ float2 rope_cs(const GemmParams& P, int c, int pos) {
+  const int hd = P.hd, DQ = P.n_q * hd, DK = P.n_kv * hd;
+  if (P.rec_kv || c >= DQ + DK) return make_float2(0.0f, 0.0f);
+  const int local = c < DQ ? c : c - DQ, j = (local % hd) >> 1;
+  return *(const float2*)(P.rope + ((size_t)pos * (hd / 2) + j) * 2);
+}
+
 // RoPE on the pair (d, d + hd/2) stored interleaved, then q (fp32) or the
 // K / V cache rows (fp16) at the row's position.
-// pos: the row's absolute position; blk: the KV block holding it.
-__device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, float v0, float v1, int pos,
-                                            int blk) {
+// pos: the row's absolute position; blk: the KV block holding it; cs2: the
+// column's rope_cs.
+__device__ __forceinline__ void qkv_pair_cs(const GemmParams& P, int r, int c, float v0, float v1, int pos,
+                                            int blk, float2 cs2) {
 #pragma clang fp contract(off)
   const int hd = P.hd, half = hd / 2;
   const int DQ = P.n_q * hd, DK = P.n_kv * hd;
@@ -573,7 +583,7 @@ __device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, f
   if (c < DQ + DK) {
     const int local = c < DQ ? c : c - DQ;
     const int head = local / hd, j = (local % hd) >> 1;
-    const float cs = P.rope[((size_t)pos * half + j) * 2], sn = P.rope[((size_t)pos * half + j) * 2 + 1];
+    const float cs = cs2.x, sn = cs2.y;
     const float o0 = v0 * cs - v1 * sn, o1 = v0 * sn + v1 * cs;
     if (c < DQ) {
       float* qr = P.q + (size_t)r * DQ + head * hd;
@@ -593,19 +603,25 @@ __device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, f
   }
 }
 
+__device__ __forceinline__ void qkv_pair_at(const GemmParams& P, int r, int c, float v0, float v1, int pos,
+                                            int blk) {
+  qkv_pair_cs(P, r, c, v0, v1, pos, blk, rope_cs(P, c, pos));
+}
 __device__ __forceinline__ void qkv_pair(const GemmParams& P, int r, int c, float v0, float v1) {
   qkv_pair_at(P, r, c, v0, v1, P.rowinfo[2 * r], P.rowinfo[2 * r + 1]);
 }
 
-// x += (v0, v1); returns the pair's sum of squares of the new residual.
-__device__ __forceinline__ float resid_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+// x += (v0, v1) given x's current pair; returns the pair's sum of squares
+// of the new residual.
+__device__ __forceinline__ float resid_pair_x(const GemmParams& P, int r, int c, float v0, float v1, float2 x) {
 #pragma clang fp contract(off)
-  float2* xp = (float2*)(P.x + (size_t)r * P.N + c);
-  float2 x = *xp;
   x.x = x.x + v0;
   x.y = x.y + v1;
-  *xp = x;
+  *(float2*)(P.x + (size_t)r * P.N + c) = x;
   return x.x * x.x + x.y * x.y;
+}
+__device__ __forceinline__ float resid_pair(const GemmParams& P, int r, int c, float v0, float v1) {
+  return resid_pair_x(P, r, c, v0, v1, *(const float2*)(P.x + (size_t)r * P.N + c));
 }
 
 // Sum over the 8 pairs (16 columns) held by an aligned group of 8 lanes;
@@ -912,6 +928,21 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
       if constexpr (EPI == EPI_QKV) qblk[it] = P.rowinfo[2 * rc + 1];
     }
   }
+  // QKV, one weight buffer: the RoPE (cos, sin) of a block's epilogue pairs
+  // load with the block's weights (rope_cur), the next block's with its
+  // refill (rope_nxt), so the epilogue waits for no load of its own
+  constexpr bool RPF = EPI == EPI_QKV && NBUF == 1;
+  float2 rope_cur[RPF ? PPT : 1], rope_nxt[RPF ? PPT : 1];
+  auto fetch_rope = [&](float2 (&dst)[RPF ? PPT : 1], int blk_) {
+    if constexpr (RPF) {
+#pragma unroll
+      for (int it = 0; it < PPT; ++it) {
+        const int pr = tid + it * NT, rem = pr % (8 * CT);
+        const int col = (blk_ * CT + (rem >> 3)) * 16 + 2 * (rem & 7);
+        dst[it] = pr < P.R * 8 * CT && col < P.N ? rope_cs(P, col, qpos[it]) : make_float2(0.0f, 0.0f);
+      }
+    }
+  };
   Sampling sm = {0.0f, 0u, 0u};
   if constexpr (EPI == EPI_LM) sm = load_sampling(P);
   float gv[NORM ? GPT : 1], sv[NORM ? SSI : 1];
@@ -938,6 +969,7 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
   u32x4 b0[CT][SPW], b1[NBUF == 2 ? CT : 1][NBUF == 2 ? SPW : 1];
   int blk = blockIdx.x;
   fetch(b0, blk);
+  fetch_rope(rope_cur, blk);
   f32x4 a[SPW][2];
   if (row < P.R) {
     const f32x4* ap = (const f32x4*)(P.A + (size_t)row * P.lda + s0 * 32 + kg * 8);
@@ -1006,7 +1038,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w, acc[c], 0, 0, 0);
       }
     }
-    if (refill < nblk) fetch(bw, refill);
+    if (refill < nblk) {
+      fetch(bw, refill);
+      fetch_rope(rope_nxt, refill);
+    }
 #pragma unroll
     for (int c = 0; c < CT; ++c) sAcc[(wave * CT + c) * 64 + lane] = acc[c];
     __syncthreads();
@@ -1025,7 +1060,9 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
         float v0, v1;
         group_sum<NW, GP, CT>(sAcc, ct, e0, v0, v1);
         if (col < P.N) {
-          if constexpr (EPI == EPI_QKV) {
+          if constexpr (RPF) {
+            qkv_pair_cs(P, r, col, v0, v1, qpos[it], qblk[it], rope_cur[it]);
+          } else if constexpr (EPI == EPI_QKV) {
             qkv_pair_at(P, r, col, v0, v1, qpos[it], qblk[it]);
           } else if constexpr (EPI == EPI_RESID) {
             const float t = sum8(resid_pair(P, r, col, v0, v1));
@@ -1042,6 +1079,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
       }
     }
     __syncthreads();  // sAcc is rewritten by the next block
+    if constexpr (RPF) {
+#pragma unroll
+      for (int it = 0; it < PPT; ++it) rope_cur[it] = rope_nxt[it];
+    }
   };
 
   // blocks blk, blk + G, ...; with two buffers b0 and b1 alternate without
@@ -1112,6 +1153,12 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
   const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
   const f32x4* ap = (const f32x4*)(P.A + (size_t)row * P.lda + s0 * 32 + kg * 8);
   const bool arow = row < P.R;
+  static_assert(NT >= 128, "one epilogue pair per thread at 16 rows");
+  const int npairs = P.R * 8, er = tid >> 3, epp = tid & 7, ecol = tile * 16 + 2 * epp;
+  // residual epilogue: this thread's pair of x, issued before everything else
+  float2 xv = make_float2(0.0f, 0.0f);
+  if constexpr (EPI == EPI_RESID)
+    if (tid < npairs) xv = *(const float2*)(P.x + (size_t)er * P.N + ecol);
   u32x4 b[SPP];
   f32x4 a[SPP][2];
 #define SPECV_MM1_LOAD(J0)                                                  \
@@ -1181,20 +1228,17 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
 #undef SPECV_MM1_LOAD
   sAcc[wave * 64 + lane] = acc;
   __syncthreads();
-  const int npairs = P.R * 8;
-  for (int p = tid; p < npairs; p += NT) {
-    const int r = p >> 3, pp = p & 7;
-    const int col = tile * 16 + 2 * pp;
-    const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+  if (tid < npairs) {
+    const int e0 = ((er >> 2) * 16 + 2 * epp) * 4 + (er & 3);
     float v0, v1;
     group_sum<NW, GP, 1>(sAcc, 0, e0, v0, v1);
     if constexpr (EPI == EPI_QKV) {
-      qkv_pair(P, r, col, v0, v1);
+      qkv_pair(P, er, ecol, v0, v1);
     } else if constexpr (EPI == EPI_RESID) {
-      const float t = sum8(resid_pair(P, r, col, v0, v1));
-      if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+      const float t = sum8(resid_pair_x(P, er, ecol, v0, v1, xv));
+      if (epp == 0) P.ss_out[(size_t)er * (P.N >> 4) + (ecol >> 4)] = t;
     } else {
-      swiglu_pair(P, r, col, v0, v1);
+      swiglu_pair(P, er, ecol, v0, v1);
     }
   }
 }
@@ -1213,6 +1257,11 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tile = blockIdx.x, s0 = wave * SPW;
   const int row = lane & 15, kg = lane >> 4;
+  // this thread's pair of x for the residual epilogue (8 R <= 32 pairs), issued first
+  static_assert(NT >= 8 * RL, "one epilogue pair per thread");
+  const int npairs = P.R * 8, er = tid >> 3, epp = tid & 7, ecol = tile * 16 + 2 * epp;
+  float2 xv = make_float2(0.0f, 0.0f);
+  if (tid < npairs) xv = *(const float2*)(P.x + (size_t)er * P.N + ecol);
 
   __shared__ u32x4 sA[KS * 2 * 4 * RL];  // [step][hi, lo][lane group][row]; then the partial tiles
   static_assert(NW * 64 <= KS * 2 * 4 * RL, "the partial tiles fit the A buffer");
@@ -1268,15 +1317,12 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   __syncthreads();  // every wave is done with A
   sAcc[wave * 64 + lane] = acc;
   __syncthreads();
-  const int npairs = P.R * 8;
-  for (int p = tid; p < npairs; p += NT) {
-    const int r = p >> 3, pp = p & 7;
-    const int col = tile * 16 + 2 * pp;
-    const int e0 = ((r >> 2) * 16 + 2 * pp) * 4 + (r & 3);
+  if (tid < npairs) {
+    const int e0 = ((er >> 2) * 16 + 2 * epp) * 4 + (er & 3);
     float v0, v1;
     group_sum<NW, 1, 1>(sAcc, 0, e0, v0, v1);
-    const float t = sum8(resid_pair(P, r, col, v0, v1));
-    if ((p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (col >> 4)] = t;
+    const float t = sum8(resid_pair_x(P, er, ecol, v0, v1, xv));
+    if (epp == 0) P.ss_out[(size_t)er * (P.N >> 4) + (ecol >> 4)] = t;
   }
 }
 
@@ -2504,6 +2550,11 @@ hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t
   if (nw == 16 && spw == 19 && rl == 4) {  // the smallest staging that holds the rows
     if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<16, 19, 2>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
     else hipLaunchKernelGGL((k_mm1l<16, 19, 4>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+    return hipGetLastError();
+  }
+  if (nw == 8 && spw == 16 && rl == 4) {
+    if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<8, 16, 2>), dim3(p.N / 16), dim3(8 * 64), 0, st, p);
+    else hipLaunchKernelGGL((k_mm1l<8, 16, 4>), dim3(p.N / 16), dim3(8 * 64), 0, st, p);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -118,6 +118,9 @@ struct MmPlan {
 #ifndef SPECV_DOWN_LDS
 #define SPECV_DOWN_LDS 1
 #endif
+#ifndef SPECV_O_LDS
+#define SPECV_O_LDS 1
+#endif
 // Rows above four and up to this many take the down projection's one-pass
 // kernel with A read from global memory (the same K parts, summed in the same
 // order as the LDS-staged kernel); more rows take split-K.
@@ -697,6 +700,12 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
+      // up to four rows of the eight-part plan: the same K parts with A staged in LDS
+      if (SPECV_O_LDS && L.fmt == FMT_BF16 && R <= 4 && L.mm_o.nw == 8 && L.mm_o.spw == 16 && L.mm_o.nbuf == 0 &&
+          L.mm_o.gp == 1 && R <= L.mm_o.rmax) {
+        HIPCHK(c, launch_mm1l(go, 8, 16, 4, st));
+        return SPEC_OK;
+      }
       HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_o, R)));
       return SPEC_OK;
     }
@@ -1458,6 +1467,48 @@ int spec_measure_read_bw(const void* buf, size_t bytes, uint32_t* sink, int reps
   (void)hipEventDestroy(e1);
   if (e != hipSuccess || ms <= 0.0f) return SPEC_EHIP;
   *gbps_out = (double)bytes * reps / (ms * 1e-3) / 1e9;
+  return SPEC_OK;
+}
+
+int spec_measure_read_chain(const void* buf, size_t region_bytes, int n_regions, int grid, uint32_t* sink,
+                            void* hip_stream, double* us_out) {
+  if (!buf || !sink || !us_out || !hip_stream || region_bytes < 16 || region_bytes % 16 || n_regions < 1 ||
+      grid < 1 || grid > 65535 || ((uintptr_t)buf & 15))
+    return SPEC_EINVAL;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const char* base = (const char*)buf;
+  if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) return SPEC_EHIP;
+  hipError_t e = hipSuccess;
+  for (int r = 0; r < n_regions && e == hipSuccess; ++r)
+    e = launch_stream_read(base + (size_t)r * region_bytes, region_bytes, sink, grid, st);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(st, &g);
+  if (e != hipSuccess || ec != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    return SPEC_EHIP;
+  }
+  hipGraphExec_t ge = nullptr;
+  e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return SPEC_EHIP;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    (void)hipGraphExecDestroy(ge);
+    return SPEC_EHIP;
+  }
+  e = hipGraphLaunch(ge, st);  // warm
+  if (e == hipSuccess) e = hipEventRecord(e0, st);
+  if (e == hipSuccess) e = hipGraphLaunch(ge, st);
+  if (e == hipSuccess) e = hipEventRecord(e1, st);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  (void)hipGraphExecDestroy(ge);
+  if (e != hipSuccess || ms <= 0.0f) return SPEC_EHIP;
+  *us_out = (double)ms * 1000.0 / n_regions;
   return SPEC_OK;
 }
 

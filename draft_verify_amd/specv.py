@@ -131,6 +131,7 @@ def lib():
         "spec_profile_ops": [P, I, I, i32p, f32p, i32p],
         "spec_op_bytes": [C.POINTER(spec_model_desc), I, I, I, dp],
         "spec_measure_read_bw": [P, C.c_size_t, P, I, P, dp],
+        "spec_measure_read_chain": [P, C.c_size_t, I, I, P, P, dp],
         "spec_time_op": [P, I, I, I, f32p],
         "spec_ngram_create": [I, I, I, C.POINTER(P)],
         "spec_ngram_destroy": [P],
@@ -334,6 +335,13 @@ def spec_measure_read_bw(buf_ptr, nbytes, sink_ptr, reps, stream_ptr):
     _check(lib().spec_measure_read_bw(C.c_void_p(buf_ptr), nbytes, C.c_void_p(sink_ptr), reps,
                                       C.c_void_p(stream_ptr), C.byref(g)))
     return g.value
+
+
+def spec_measure_read_chain(buf_ptr, region_bytes, n_regions, grid, sink_ptr, stream_ptr):
+    us = C.c_double()
+    _check(lib().spec_measure_read_chain(C.c_void_p(buf_ptr), region_bytes, n_regions, grid, C.c_void_p(sink_ptr),
+                                         C.c_void_p(stream_ptr), C.byref(us)))
+    return us.value
 
 
 def spec_op_bytes(desc, op, S, ctx_len):

@@ -300,6 +300,18 @@ SPEC_API int spec_time_op(spec_ctx* ctx, int op, int S, int reps, float* us_per_
 SPEC_API int spec_measure_read_bw(const void* buf, size_t bytes, uint32_t* sink, int reps, void* hip_stream,
                                   double* gbps_out);
 
+/* The floor of a kernel-per-operation forward: n_regions back-to-back
+ * launches of the same streaming-read kernel (grid workgroups of 256 threads,
+ * 1..65535) over consecutive regions of region_bytes (>= 16, a multiple of
+ * 16; 16 bytes is a launch with next to no work) of the caller-owned device
+ * buffer buf, which must hold n_regions * region_bytes bytes (regions never
+ * repeat, so with enough of them the reads come from HBM, not the caches).
+ * The launches are captured once into a HIP graph on hip_stream (not the
+ * null stream), replayed once untimed and once between HIP events; sink: 256
+ * words of caller-owned device memory.  *us_out = the replay's time / n_regions. */
+SPEC_API int spec_measure_read_chain(const void* buf, size_t region_bytes, int n_regions, int grid, uint32_t* sink,
+                                     void* hip_stream, double* us_out);
+
 /* Algorithmic bytes one launch of an op class streams at span S and cache
  * length ctx_len (weights, KV reads and writes; activations excluded). */
 SPEC_API int spec_op_bytes(const spec_model_desc* desc, int op, int S, int ctx_len, double* bytes_out);
