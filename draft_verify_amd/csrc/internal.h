@@ -176,7 +176,8 @@ inline bool gemm_prep_supported(int nk, int fmt) { return fmt == FMT_BF16 && (nk
 // identical to launch_gemm with nk = spw (nslices = nw).
 bool mm_supported(int epi, int nw, int spw, int ct, int nbuf, int gp);
 // The residual one-pass GEMM for at most rl rows with A staged in LDS
-// (kernels.hip: k_mm1l); compiled for nw = 16, spw = 19, rl = 4.
+// (kernels.hip: k_mm1l); compiled for (nw, spw, rl) = (16, 19, 8) (down) and
+// (8, 16, 4) (O); rows up to rl take the smallest staging that holds them.
 hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st);
 // The int4 one-pass GEMM for at most four rows (kernels.hip: k_mmq): waves
 // own the K parts of the int4 split-K kernel with nk-step slices, so the two
@@ -192,11 +193,12 @@ hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st);
 // One workgroup per (kv head, sequence); the rows of each span in order.
 hipError_t launch_recur(const RecParams& p, int hd, hipStream_t st);
 hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st);
-// Repack canonical bf16 [rows][cols] into fragments of a fused matrix whose
-// row for source row s is map(s): kind 0 identity + row0, kind 1 RoPE pair
-// interleave within heads of hd rows (+ row0), kind 2 row 2s + row0.
+// Repack canonical bf16 [rows][cols] as fp16 into fragments of a fused
+// matrix whose row for source row s is map(s): kind 0 identity + row0, kind
+// 1 RoPE pair interleave within heads of hd rows (+ row0), kind 2 row 2s +
+// row0.  A value beyond the fp16 range sets *overflow (device word) to 1.
 hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, int kind, int row0,
-                            int hd, hipStream_t st);
+                            int hd, uint32_t* overflow, hipStream_t st);
 // The same for canonical int4 group-128 (q4 bytes [rows][cols/2], low nibble
 // = even column; bf16 scales [rows][cols/128]) into int4 fragments and the
 // matrix's scale block.

@@ -8,11 +8,12 @@
 //   fused per-row argmax and, in its last workgroup, accept_greedy and the
 //   cache advance.
 //
-// Numerics: weights bf16; activations enter the MFMA as a bf16 hi + lo pair
-// (two passes, ~16 mantissa bits); int4 weights are exact integers, whose
-// activations enter once as fp16 (11 bits, the int4 matvec's own operand
-// precision); fp32 accumulation, residual and softmax; fp16 KV cache, fp16
-// query and probabilities in attention.
+// Numerics: bf16 weights are held as fp16 copies (exact for every value of
+// magnitude 2^-17 .. 65504, which covers the weights); int4 weights are exact
+// integers; the activations enter every GEMM once as fp16 (11 significant
+// bits, above bf16's 8) and the MFMAs are fp16 x fp16 -> fp32; fp32
+// accumulation, residual and softmax; fp16 KV cache, fp16 query and
+// probabilities in attention.
 // Row invariance: every row runs the same 16-row MFMA tiles, the same
 // K-split per (N, K) and the same fixed-order reductions whatever S is, so a
 // row's result does not depend on the other rows of the forward.
@@ -23,7 +24,6 @@
 
 namespace specv {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -67,20 +67,33 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
 
 // ---------------------------------------------------------------- packing
 
+// bf16 weights are packed as fp16: every bf16 value of magnitude 2^-17 ..
+// 65504 is an fp16 value exactly (8 significant bits inside fp16's 11), the
+// few smaller ones round with an absolute error <= 2^-25; a larger one (no
+// fp16 value) sets *overflow, and the load is refused.
 __global__ void k_pack_bf16(const uint16_t* __restrict__ src, int rows, int cols, u32x4* __restrict__ dst,
-                            int kind, int row0, int hd) {
+                            int kind, int row0, int hd, uint32_t* __restrict__ overflow) {
   const int chunks = cols / 8;
   const size_t total = (size_t)rows * chunks;
+  bool over = false;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const int s = (int)(i / chunks), kc = (int)(i % chunks);
     int n;
     if (kind == 0) n = row0 + s;
     else if (kind == 1) n = row0 + rope_pair_row(s, hd);
     else n = row0 + 2 * s;
-    const u32x4 v = *(const u32x4*)(src + (size_t)s * cols + (size_t)kc * 8);
+    const uint16_t* v = src + (size_t)s * cols + (size_t)kc * 8;
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = bf16_bits_to_f32(v[e]);
+      h[e] = (_Float16)f;
+      over |= __builtin_isinf((float)h[e]) && !__builtin_isinf(f);
+    }
     const int tile = n >> 4, r = n & 15, step = kc >> 2, g = kc & 3;
-    dst[((size_t)tile * (cols / 32) + step) * 64 + g * 16 + r] = v;
+    dst[((size_t)tile * (cols / 32) + step) * 64 + g * 16 + r] = __builtin_bit_cast(u32x4, h);
   }
+  if (over) atomicOr(overflow, 1u);
 }
 
 // One thread per (source row, 128-input group): 64 source bytes become one
@@ -156,12 +169,12 @@ __global__ __launch_bounds__(256) void k_embed(EmbedParams P) {
 
 // ------------------------------------------------------------ skinny GEMM
 //
-// Y[R, N] = A'[R, K] W^T with A' = RMSNorm(A) (optional) split into bf16
-// hi + lo (int4: rounded to fp16).  A workgroup (4 waves) owns 64 output columns x one K slice of
-// NK*32 inputs; wave w owns the 16-column tile 4*nb + w.  Each wave first
-// issues all NK fragment loads of its weights (contiguous NK KiB, streamed
-// with non-temporal loads), then stages A for 16 rows of the slice into LDS
-// in the MFMA A-operand order, then runs 2*NK MFMA 16x16x32 bf16.  The split
+// Y[R, N] = A'[R, K] W^T with A' = RMSNorm(A) (optional) rounded to fp16.  A
+// workgroup (4 waves) owns 64 output columns x one K slice of NK*32 inputs;
+// wave w owns the 16-column tile 4*nb + w.  Each wave first issues all NK
+// fragment loads of its weights (contiguous NK KiB, streamed with
+// non-temporal loads), then stages A for 16 rows of the slice into LDS in the
+// MFMA A-operand order, then runs NK MFMA 16x16x32 f16.  The split
 // partial sums go to memory; the last workgroup of a column block to arrive
 // (counted with an atomic) adds the slices in slice order and runs the
 // epilogue, so the result is deterministic and independent of R.
@@ -273,8 +286,8 @@ __device__ __forceinline__ f16x8 dequant8_ao(uint32_t x) {
 template <int NK, int EPI, int FMT, bool PREP>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   static_assert(FMT == FMT_BF16 || NK % 4 == 0, "int4 slices hold whole 128-input groups");
-  static_assert(!PREP || FMT == FMT_BF16, "prepared A is bf16 hi + lo");
-  constexpr int PU = NK * 2 * 64;             // prepared A: fragment lanes of a 16-row chunk
+  static_assert(!PREP || FMT == FMT_BF16, "prepared A serves the fp16 weight path");
+  constexpr int PU = NK * 64;                 // prepared A: fragment lanes of a 16-row chunk
   constexpr int PUT = (PU + 255) / 256;
   constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per tile per slice
   constexpr int CT = gemm_tiles_per_wave(FMT);       // 16-column tiles per wave
@@ -304,13 +317,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   const int nch = (P.R + 15) >> 4;
   auto load_a = [&](int m0) {
     if constexpr (PREP) {
-      // lane u of the chunk's fragments is LDS entry u: (step j, hi/lo, lane)
+      // lane u of the chunk's fragments: (step j, lane)
       const u32x4* af = (const u32x4*)P.Af;
 #pragma unroll
       for (int i = 0; i < PUT; ++i) {
         const int u = tid + i * 256, uc = u < PU ? u : 0;
-        const int j = uc >> 7, hl = (uc >> 6) & 1, l = uc & 63;
-        pf[i] = af[(((size_t)(sl * NK + j) * nch + (m0 >> 4)) * 2 + hl) * 64 + l];
+        const int j = uc >> 6, l = uc & 63;
+        pf[i] = af[((size_t)(sl * NK + j) * nch + (m0 >> 4)) * 64 + l];
       }
       return;
     }
@@ -373,12 +386,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     for (int j = 0; j < NF; ++j) asm volatile("" ::"v"(b[0][j]));
   }
   for (int m0 = 0; m0 < P.R; m0 += 16) {
-    // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as bf16 hi + lo (int4: fp16).
+    // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as fp16.
     if constexpr (PREP) {
 #pragma unroll
       for (int i = 0; i < PUT; ++i) {
         const int u = tid + i * 256;
-        if (u < PU) sA[u] = pf[i];
+        if (u < PU) sA[((u >> 6) * 2) * 64 + (u & 63)] = pf[i];
       }
     }
 #pragma unroll
@@ -393,27 +406,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * sG[j * 32 + g * 8 + e];
       }
-      u32x4 hw, lw;
-      if constexpr (FMT == FMT_INT4) {  // fp16: the operand type of the fp16 MFMA on exact q
-        f16x8 hi;
+      f16x8 hi;  // fp16: the operand type of the fp16 MFMA on the exact fp16 weights (int4: exact q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
-        hw = __builtin_bit_cast(u32x4, hi);
-        lw = hw;  // unused: one fp16 pass
-      } else {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 h = (__bf16)v[e];
-          hi[e] = h;
-          lo[e] = (__bf16)(v[e] - (float)h);
-        }
-        hw = __builtin_bit_cast(u32x4, hi);
-        lw = __builtin_bit_cast(u32x4, lo);
-      }
-      const int l = g * 16 + row;
-      sA[(j * 2) * 64 + l] = hw;
-      if constexpr (FMT != FMT_INT4) sA[(j * 2 + 1) * 64 + l] = lw;
+      for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
+      sA[(j * 2) * 64 + g * 16 + row] = __builtin_bit_cast(u32x4, hi);
     }
     __syncthreads();
     if (m0 + 16 < P.R) load_a(m0 + 16);  // the next chunk's A loads fly during this chunk's MFMA
@@ -453,14 +449,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     } else {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
-        const bf16x8 ah = __builtin_bit_cast(bf16x8, sA[(j * 2) * 64 + lane]);
-        const bf16x8 al = __builtin_bit_cast(bf16x8, sA[(j * 2 + 1) * 64 + lane]);
+        const f16x8 ah = __builtin_bit_cast(f16x8, sA[(j * 2) * 64 + lane]);
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          const bf16x8 bw = __builtin_bit_cast(bf16x8, b[c][j]);
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[c], 0, 0, 0);
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[c], 0, 0, 0);
-        }
+        for (int c = 0; c < CT; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(f16x8, b[c][j]), acc[c], 0, 0, 0);
       }
     }
     // D layout: lane holds column lane%16 of rows 4*(lane/16) + i.
@@ -634,30 +626,21 @@ __device__ __forceinline__ float sum8(float t) {
   return t;
 }
 
-// Prepared A (k_prep's layout, bf16 hi then lo, nch = ceil(R/16) chunks)
-// written by a producer: element (row r, input k) sits at bf16 index
-// (((k/32 * nch + r/16) * 2 + hl) * 64 + r%16 + 16 * (k%32/8)) * 8 + k%8;
-// the split is k_prep's, so the consumer sees the same operands.
-__device__ __forceinline__ size_t prep_index(int nch, int r, int k, int hl) {
-  return ((((size_t)(k >> 5) * nch + (r >> 4)) * 2 + hl) * 64 + (r & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+// Prepared A (k_prep's layout, fp16, nch = ceil(R/16) chunks) written by a
+// producer: element (row r, input k) sits at fp16 index
+// ((k/32 * nch + r/16) * 64 + r%16 + 16 * (k%32/8)) * 8 + k%8; the rounding
+// is k_prep's, so the consumer sees the same operands.
+__device__ __forceinline__ size_t prep_index(int nch, int r, int k) {
+  return (((size_t)(k >> 5) * nch + (r >> 4)) * 64 + (r & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
 }
 __device__ __forceinline__ void prep_store1(void* af, int nch, int r, int k, float v) {
-#pragma clang fp contract(off)
-  const __bf16 h = (__bf16)v, l = (__bf16)(v - (float)h);
-  uint16_t* a = (uint16_t*)af;
-  a[prep_index(nch, r, k, 0)] = __builtin_bit_cast(uint16_t, h);
-  a[prep_index(nch, r, k, 1)] = __builtin_bit_cast(uint16_t, l);
+  ((_Float16*)af)[prep_index(nch, r, k)] = (_Float16)v;
 }
-// k even: the pair (k, k + 1) shares one 4-byte word of each half
+// k even: the pair (k, k + 1) is one 4-byte word
 __device__ __forceinline__ void prep_store2(void* af, int nch, int r, int k, float v0, float v1) {
-#pragma clang fp contract(off)
-  const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
-  const __bf16 l0 = (__bf16)(v0 - (float)h0), l1 = (__bf16)(v1 - (float)h1);
-  uint16_t* a = (uint16_t*)af;
-  *(uint32_t*)(a + prep_index(nch, r, k, 0)) =
+  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+  *(uint32_t*)((_Float16*)af + prep_index(nch, r, k)) =
       (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  *(uint32_t*)(a + prep_index(nch, r, k, 1)) =
-      (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
 }
 
 __device__ __forceinline__ float swiglu_val(float g, float u) {
@@ -866,13 +849,12 @@ __device__ __forceinline__ void group_sum(const f32x4* sAcc, int ct, int e0, flo
 // 16-column tiles, blockIdx.x, blockIdx.x + gridDim.x, ..., over the whole
 // K; wave w owns the K part of steps [w*SPW, (w+1)*SPW).  The prologue loads
 // the wave's A rows once, straight into the MFMA A-operand layout (lane l:
-// row l%16, inputs 8*(l/16)..+8 of every step) and applies the RMSNorm;
-// they then serve every block of the walk (split into bf16 hi + lo per
-// step as the MFMAs need them).
+// row l%16, inputs 8*(l/16)..+8 of every step), applies the RMSNorm and
+// rounds them to fp16 once; they then serve every block of the walk.
 // Weights stream through NBUF register buffers: the fragments of the block
 // NBUF walk steps ahead are issued as soon as the current block's MFMAs have
 // read theirs, so NBUF blocks are in flight while one is reduced.  Per block each wave runs
-// 2*CT*SPW MFMA and leaves its partial tiles in LDS; the workgroup adds the
+// CT*SPW MFMA and leaves its partial tiles in LDS; the workgroup adds the
 // parts in wave order and runs the epilogue.  No partial buffer, arrival
 // counter or second pass, except for the LM head: its threads keep the
 // largest argmax key of their (row, 16 columns) over the walk, each group
@@ -1005,7 +987,7 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
     }
     __syncthreads();
   }
-  if constexpr (NORM) {  // normalised in place; the bf16 split happens per block
+  if constexpr (NORM) {  // normalised in place
     const float rs = sR[row];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -1013,6 +995,14 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
       a[j][0] = (f32x4){(a[j][0].x * rs) * g[0], (a[j][0].y * rs) * g[1], (a[j][0].z * rs) * g[2], (a[j][0].w * rs) * g[3]};
       a[j][1] = (f32x4){(a[j][1].x * rs) * g[4], (a[j][1].y * rs) * g[5], (a[j][1].z * rs) * g[6], (a[j][1].w * rs) * g[7]};
     }
+  }
+  // the A operand of every block: fp16, rounded once
+  f16x8 a16[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a16[j][e] = (_Float16)v[e];
   }
 
   // One block: MFMA on bw, then (bw free) issue the block NBUF steps ahead
@@ -1022,22 +1012,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) acc[c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
-      bf16x8 hi, lo;
+    for (int j = 0; j < SPW; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)v[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(v[e] - (float)h);
-      }
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const bf16x8 w = __builtin_bit_cast(bf16x8, bw[c][j]);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w, acc[c], 0, 0, 0);
-      }
-    }
+      for (int c = 0; c < CT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a16[j], __builtin_bit_cast(f16x8, bw[c][j]), acc[c], 0, 0, 0);
     if (refill < nblk) {
       fetch(bw, refill);
       fetch_rope(rope_nxt, refill);
@@ -1212,16 +1190,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * g[e];
         }
-        bf16x8 hi, lo;
+        f16x8 h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 h = (__bf16)v[e];
-          hi[e] = h;
-          lo[e] = (__bf16)(v[e] - (float)h);
-        }
-        const bf16x8 w = __builtin_bit_cast(bf16x8, b[j]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w, acc, 0, 0, 0);
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(h, __builtin_bit_cast(f16x8, b[j]), acc, 0, 0, 0);
       }
     }
   }
@@ -1245,8 +1217,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
 
 // The same arithmetic as k_mm1 (one tile per workgroup, NW K parts of SPW
 // steps, parts summed in order) for at most RL rows with A staged in LDS:
-// for up to four rows the whole A (split into bf16 hi + lo) fits the LDS
-// even at K = 9728, so each wave keeps all of its SPW weight fragments in
+// up to eight rows of the whole A as fp16 fit the LDS even at K = 9728
+// (155,648 bytes), so each wave keeps all of its SPW weight fragments in
 // flight at once, however long its K part (the residual epilogue only).
 // The A rows are loaded first, the weights second, so the staging waits for
 // the A rows alone and runs while the weights stream.
@@ -1263,42 +1235,51 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   float2 xv = make_float2(0.0f, 0.0f);
   if (tid < npairs) xv = *(const float2*)(P.x + (size_t)er * P.N + ecol);
 
-  __shared__ u32x4 sA[KS * 2 * 4 * RL];  // [step][hi, lo][lane group][row]; then the partial tiles
-  static_assert(NW * 64 <= KS * 2 * 4 * RL, "the partial tiles fit the A buffer");
+  __shared__ u32x4 sA[KS * 4 * RL];  // [step][lane group][row], fp16; then the partial tiles
+  static_assert(NW * 64 <= KS * 4 * RL, "the partial tiles fit the A buffer");
   f32x4* sAcc = (f32x4*)sA;
 
-  f32x4 pa[UPT][2];
+  // A staged in NB batches of UPB units per thread, the first batch's loads
+  // ahead of the weights (at eight rows of K = 9728 a single batch would hold
+  // 80 registers of A beside the 76 of the weights)
+  constexpr int NB = UPT > 6 ? (UPT + 3) / 4 : 1, UPB = (UPT + NB - 1) / NB;
+  f32x4 pa[UPB][2];
+  auto load_a = [&](int bt) {
 #pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + i * NT;
-    const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
-    const bool ok = u < UNITS && r < P.R;
-    const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
-    pa[i][0] = src[0];
-    pa[i][1] = src[1];
-  }
+    for (int i = 0; i < UPB; ++i) {
+      const int u = tid + (bt * UPB + i) * NT;
+      const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+      const bool ok = u < UNITS && r < P.R;
+      const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
+      pa[i][0] = src[0];
+      pa[i][1] = src[1];
+    }
+  };
+  auto stage_a = [&](int bt) {
+#pragma unroll
+    for (int i = 0; i < UPB; ++i) {
+      const int u = tid + (bt * UPB + i) * NT;
+      if (u < UNITS) {
+        const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
+        const bool ok = r < P.R;
+        float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(ok ? v[e] : 0.0f);
+        sA[(j * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, h);
+      }
+    }
+  };
+  load_a(0);
   const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
   u32x4 b[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) b[j] = __builtin_nontemporal_load(wp + j * 64);
+  stage_a(0);
 #pragma unroll
-  for (int i = 0; i < UPT; ++i) {
-    const int u = tid + i * NT;
-    if (u < UNITS) {
-      const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
-      const bool ok = r < P.R;
-      float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
-      bf16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = ok ? v[e] : 0.0f;
-        const __bf16 h = (__bf16)x;
-        hi[e] = h;
-        lo[e] = (__bf16)(x - (float)h);
-      }
-      sA[((j * 2) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
-      sA[((j * 2 + 1) * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, lo);
-    }
+  for (int bt = 1; bt < NB; ++bt) {
+    load_a(bt);
+    stage_a(bt);
   }
   __syncthreads();
   const bool rok = row < P.R && row < RL;
@@ -1307,12 +1288,9 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 h = sA[(((s0 + j) * 2) * 4 + kg) * RL + rc];
-    const u32x4 l = sA[(((s0 + j) * 2 + 1) * 4 + kg) * RL + rc];
-    const bf16x8 ah = __builtin_bit_cast(bf16x8, rok ? h : z), al = __builtin_bit_cast(bf16x8, rok ? l : z);
-    const bf16x8 w = __builtin_bit_cast(bf16x8, b[j]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, w, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, w, acc, 0, 0, 0);
+    const u32x4 h = sA[((s0 + j) * 4 + kg) * RL + rc];
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, rok ? h : z),
+                                                 __builtin_bit_cast(f16x8, b[j]), acc, 0, 0, 0);
   }
   __syncthreads();  // every wave is done with A
   sAcc[wave * 64 + lane] = acc;
@@ -2297,9 +2275,9 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
 }
 
 // Activation rows once in the split-K kernel's A-operand order, for GEMMs of
-// many rows: entry ((ks * nch + ch) * 2 + hl) * 64 + l (16 bytes) holds, for
-// lane l, row 16 ch + l % 16 and inputs 32 ks + 8 (l / 16) .. +8 as bf16 hi
-// (hl = 0) or lo (hl = 1); rows past R are zero.  The RMSNorm is the split-K
+// many rows: entry (ks * nch + ch) * 64 + l (16 bytes) holds, for lane l, row
+// 16 ch + l % 16 and inputs 32 ks + 8 (l / 16) .. +8 as fp16; rows past R are
+// zero.  The RMSNorm is the split-K
 // kernel's own (rstd16, then (x * rstd) * gain), so either path gives the
 // same operands.  Grid (ceil(K/512), ceil(R/16)): 16 steps of one 16-row
 // chunk per workgroup.
@@ -2364,16 +2342,10 @@ __global__ __launch_bounds__(256) void k_prep(GemmParams P, u32x4* af) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * gv[e];
       }
-      bf16x8 hi, lo;
+      f16x8 h;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)v[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(v[e] - (float)h);
-      }
-      u32x4* dst = af + ((size_t)ks * nch + ch) * 2 * 64 + l;
-      dst[0] = __builtin_bit_cast(u32x4, hi);
-      dst[64] = __builtin_bit_cast(u32x4, lo);
+      for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+      af[((size_t)ks * nch + ch) * 64 + l] = __builtin_bit_cast(u32x4, h);
     }
   }
 }
@@ -2547,9 +2519,10 @@ hipError_t launch_mmqr(const GemmParams& p0, int epi, int max_grid, hipStream_t 
 
 hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st) {
   if (p.R < 1 || p.R > rl || p.K != nw * spw * 32 || p.N % 16) return hipErrorInvalidValue;
-  if (nw == 16 && spw == 19 && rl == 4) {  // the smallest staging that holds the rows
+  if (nw == 16 && spw == 19 && rl == 8) {  // the smallest staging that holds the rows
     if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<16, 19, 2>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
-    else hipLaunchKernelGGL((k_mm1l<16, 19, 4>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+    else if (p.R <= 4) hipLaunchKernelGGL((k_mm1l<16, 19, 4>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+    else hipLaunchKernelGGL((k_mm1l<16, 19, 8>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
     return hipGetLastError();
   }
   if (nw == 8 && spw == 16 && rl == 4) {
@@ -2640,10 +2613,12 @@ hipError_t launch_embed(const EmbedParams& p, int R, hipStream_t st) {
 }
 
 hipError_t launch_pack_bf16(const uint16_t* src, int rows, int cols, void* dst, int kind, int row0, int hd,
-                            hipStream_t st) {
+                            uint32_t* overflow, hipStream_t st) {
+  if (!overflow) return hipErrorInvalidValue;
   const size_t total = (size_t)rows * (cols / 8);
   const int grid = (int)((total + 255) / 256 < 65535 ? (total + 255) / 256 : 65535);
-  hipLaunchKernelGGL(k_pack_bf16, dim3(grid), dim3(256), 0, st, src, rows, cols, (u32x4*)dst, kind, row0, hd);
+  hipLaunchKernelGGL(k_pack_bf16, dim3(grid), dim3(256), 0, st, src, rows, cols, (u32x4*)dst, kind, row0, hd,
+                     overflow);
   return hipGetLastError();
 }
 

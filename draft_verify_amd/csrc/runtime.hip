@@ -173,7 +173,7 @@ struct Layout {
   size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t rec_kv, rec_slot;  // recurrent layers: staged keys and values; committed state slot per sequence
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
-  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, argkey, status, step, result, kv_len, bt, rope, apart,
+  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, packflag, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, workspace_bytes;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
@@ -361,6 +361,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.cnt = take((size_t)Lo.cnt_n * 4);
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
+  Lo.packflag = take(4);
   Lo.rowinfo = take(R * 8);
   Lo.rec_kv = Lo.any_rec ? take(R * 2 * Lo.DK * 4) : (size_t)-1;
   Lo.rec_slot = Lo.any_rec ? take((size_t)Lo.max_seqs * 4) : (size_t)-1;
@@ -374,10 +375,11 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.rope = take((size_t)Lo.max_ctx * (Lo.hd / 2) * 2 * 4);
   Lo.apart = take((size_t)Lo.nkv * Lo.max_splits * R * Lo.G * (Lo.hd + 2) * 4);
   Lo.logits = (d.flags & SPEC_FLAG_KEEP_LOGITS) ? take(R * Lo.V * 4) : (size_t)-1;
+  // prepared A (fp16, rows padded to 16)
   Lo.af = (Lo.fmt == FMT_BF16 && R > 16)
-              ? take((R + 15) / 16 * 16 * (size_t)std::max({Lo.H, Lo.DQ, Lo.F}) * 4)
+              ? take((R + 15) / 16 * 16 * (size_t)std::max({Lo.H, Lo.DQ, Lo.F}) * 2)
               : (size_t)-1;
-  Lo.af2 = Lo.af != (size_t)-1 ? take((R + 15) / 16 * 16 * (size_t)std::max(Lo.DQ, Lo.F) * 4) : (size_t)-1;
+  Lo.af2 = Lo.af != (size_t)-1 ? take((R + 15) / 16 * 16 * (size_t)std::max(Lo.DQ, Lo.F) * 2) : (size_t)-1;
   Lo.workspace_bytes = off;
 
   off = 0;
@@ -727,7 +729,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.lda = L.F;
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
-      if (L.d_lds && R <= 4) HIPCHK(c, launch_mm1l(gd, 16, 19, 4, st));
+      if (L.d_lds && R <= 8) HIPCHK(c, launch_mm1l(gd, 16, 19, 8, st));
       else if (L.d_lds && R <= SPECV_DOWN_MM1_ROWS)
         HIPCHK(c, launch_mm(gd, 16, 19, 4, 0, 1, c->mm_grid, EPI_RESID, st));
       else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_d, R)));
@@ -1090,7 +1092,8 @@ static hipError_t pack_matrix(spec_ctx* c, const void* src, const void* scales, 
   if (c->lo.fmt == FMT_INT4)
     return launch_pack_int4((const uint8_t*)src, (const uint16_t*)scales, rows, cols, dst,
                             (uint16_t*)(dst + packed_int4_frag_bytes(fused_rows, cols)), kind, row0, hd, c->st);
-  return launch_pack_bf16((const uint16_t*)src, rows, cols, dst, kind, row0, hd, c->st);
+  return launch_pack_bf16((const uint16_t*)src, rows, cols, dst, kind, row0, hd, c->ws<uint32_t>(c->lo.packflag),
+                          c->st);
 }
 
 int spec_load_matrix(spec_ctx* c, int layer, int which, const void* src, const void* scales) {
@@ -1124,6 +1127,19 @@ int spec_load_matrix(spec_ctx* c, int layer, int which, const void* src, const v
   }
   if (e == hipSuccess) e = hipStreamSynchronize(c->st);
   if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("weight packing: ") + hipGetErrorString(e));
+  if (L.fmt == FMT_BF16 && which != SPEC_MAT_EMB) {
+    // the GEMMs take fp16 copies of bf16 weights: refuse a matrix with a
+    // value beyond the fp16 range
+    uint32_t over = 0;
+    e = hipMemcpy(&over, c->ws<uint32_t>(L.packflag), 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return set_err(c, SPEC_EHIP, std::string("weight packing: ") + hipGetErrorString(e));
+    if (over) {
+      c->loaded[(size_t)slot_id] = 0u;
+      e = launch_fill_u32(c->ws<uint32_t>(L.packflag), 0u, 1, c->st);
+      if (e == hipSuccess) e = hipStreamSynchronize(c->st);
+      return set_err(c, SPEC_EINVAL, "a bf16 weight is beyond the fp16 range (|w| > 65504)");
+    }
+  }
   c->loaded[(size_t)slot_id] = 1u;
   return SPEC_OK;
 }
