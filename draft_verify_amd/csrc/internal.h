@@ -57,8 +57,10 @@ struct GemmParams {
   int N, K, R;           // outputs, inputs, rows
   int nslices;           // K split into nslices slices of NK*32 inputs
   const float* A;        // activation rows [R][lda] (fp32)
+  const _Float16* A16;   // or, for the LDS-staged and phased one-pass residual GEMMs, the same rows
+                         // already rounded to fp16 ([R][lda]), else null
   int lda;
-  const void* Af;        // or, bf16 only: A prepared by k_prep (hi/lo fragments), else null
+  const void* Af;        // or, bf16 only: A prepared by k_prep (fp16 fragments), else null
   const float* ss;       // RMSNorm: per-row partial sums of squares [R][ss_n], or null
   int ss_n;
   const float* gain;     // RMSNorm gain [K]
@@ -85,6 +87,7 @@ struct GemmParams {
   float* ss_out;         // [R][N/64] partial sums of squares of the new residual
   // EPI_SWIGLU
   float* h;              // [R][N/2]
+  _Float16* h16;         // or null: h also rounded to fp16 (the down projection's A16)
   void* af_out;          // or null: h also as the next GEMM's prepared A (k_prep's layout)
   // EPI_LM
   unsigned long long* argkey; // per-row packed (value, index) maxima, zero between forwards
@@ -115,6 +118,7 @@ struct AttnParams {
   float* part;           // [n_kv][max_splits][R*G][2 + hd]: (max, sum, unnormalised o)
   unsigned* cnt;         // [n_seq][n_kv][tile groups] arrival counters of the fused merge, zero between launches
   float* out;            // [R][n_q*hd]
+  _Float16* out16;       // or null: out also rounded to fp16 (the O projection's A16)
   void* af_out;          // or null: out also as the O GEMM's prepared A (k_prep's layout)
   int n_qt;              // query tiles per sequence: ceil(S * n_q / n_kv / 16)
   int tpw;               // query tiles per workgroup (1..n_qt), taken one after another

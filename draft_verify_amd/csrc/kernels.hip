@@ -648,7 +648,10 @@ __device__ __forceinline__ float swiglu_val(float g, float u) {
   return (g / (1.0f + expf(-g))) * u;
 }
 __device__ __forceinline__ void swiglu_pair(const GemmParams& P, int r, int c, float g, float u) {
-  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = swiglu_val(g, u);
+  const float v = swiglu_val(g, u);
+  const size_t i = (size_t)r * (P.N >> 1) + (c >> 1);
+  P.h[i] = v;
+  if (P.h16) P.h16[i] = (_Float16)v;
 }
 
 template <int CT, int SB, int U>
@@ -1098,9 +1101,10 @@ __global__ __launch_bounds__(NW * 64) void k_mm(GemmParams P) {
 // SPP steps: phase p+1's weights and A rows are issued once phase p's MFMAs
 // have read theirs, so a K part too long for the registers still runs in
 // one pass (each phase adds one memory latency, not a second kernel).
-template <int EPI, int NW, int SPW, int PH, int GP>
+template <int EPI, int NW, int SPW, int PH, int GP, bool H16 = false>
 __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
   static_assert(NW % GP == 0, "parts form whole groups");
+  static_assert(!H16 || EPI == EPI_RESID, "fp16 A rows carry no RMSNorm");
   constexpr int NT = NW * 64, KS = NW * SPW, SPP = (SPW + PH - 1) / PH;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int SSN = KS * 2, SSI = (SSN + 15) / 16, GPT = (KS * 32 + NT - 1) / NT;
@@ -1130,6 +1134,8 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
   }
   const u32x4* wp = (const u32x4*)P.W + ((size_t)tile * KS + s0) * 64 + lane;
   const f32x4* ap = (const f32x4*)(P.A + (size_t)row * P.lda + s0 * 32 + kg * 8);
+  const u32x4* ap16 = nullptr;
+  if constexpr (H16) ap16 = (const u32x4*)(P.A16 + (size_t)row * P.lda + s0 * 32 + kg * 8);
   const bool arow = row < P.R;
   static_assert(NT >= 128, "one epilogue pair per thread at 16 rows");
   const int npairs = P.R * 8, er = tid >> 3, epp = tid & 7, ecol = tile * 16 + 2 * epp;
@@ -1138,12 +1144,15 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
   if constexpr (EPI == EPI_RESID)
     if (tid < npairs) xv = *(const float2*)(P.x + (size_t)er * P.N + ecol);
   u32x4 b[SPP];
-  f32x4 a[SPP][2];
+  f32x4 a[H16 ? 1 : SPP][2];
+  u32x4 ah[H16 ? SPP : 1];
 #define SPECV_MM1_LOAD(J0)                                                  \
   _Pragma("unroll") for (int j = 0; j < SPP; ++j) if ((J0) + j < SPW) b[j] = \
       __builtin_nontemporal_load(wp + ((J0) + j) * 64);                       \
   _Pragma("unroll") for (int j = 0; j < SPP; ++j) {                          \
-    if (arow && (J0) + j < SPW) {                                            \
+    if constexpr (H16) {                                                     \
+      ah[j] = (arow && (J0) + j < SPW) ? ap16[((J0) + j) * 4] : (u32x4){0u, 0u, 0u, 0u}; \
+    } else if (arow && (J0) + j < SPW) {                                     \
       a[j][0] = ap[((J0) + j) * 8];                                          \
       a[j][1] = ap[((J0) + j) * 8 + 1];                                      \
     } else {                                                                 \
@@ -1184,15 +1193,19 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
 #pragma unroll
     for (int j = 0; j < SPP; ++j) {
       if (ph * SPP + j < SPW) {
-        float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
-        if constexpr (NORM) {
-          const float* g = sG + (s0 + ph * SPP + j) * 32 + kg * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * g[e];
-        }
         f16x8 h;
+        if constexpr (H16) {
+          h = __builtin_bit_cast(f16x8, ah[j]);
+        } else {
+          float v[8] = {a[j][0].x, a[j][0].y, a[j][0].z, a[j][0].w, a[j][1].x, a[j][1].y, a[j][1].z, a[j][1].w};
+          if constexpr (NORM) {
+            const float* g = sG + (s0 + ph * SPP + j) * 32 + kg * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+            for (int e = 0; e < 8; ++e) v[e] = (v[e] * rs) * g[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+        }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(h, __builtin_bit_cast(f16x8, b[j]), acc, 0, 0, 0);
       }
     }
@@ -1222,7 +1235,7 @@ __global__ __launch_bounds__(NW * 64) void k_mm1(GemmParams P) {
 // flight at once, however long its K part (the residual epilogue only).
 // The A rows are loaded first, the weights second, so the staging waits for
 // the A rows alone and runs while the weights stream.
-template <int NW, int SPW, int RL>
+template <int NW, int SPW, int RL, bool H16 = false>
 __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   constexpr int NT = NW * 64, KS = NW * SPW;
   constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
@@ -1242,17 +1255,25 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
   // A staged in NB batches of UPB units per thread, the first batch's loads
   // ahead of the weights (at eight rows of K = 9728 a single batch would hold
   // 80 registers of A beside the 76 of the weights)
-  constexpr int NB = UPT > 6 ? (UPT + 3) / 4 : 1, UPB = (UPT + NB - 1) / NB;
-  f32x4 pa[UPB][2];
+  // (fp16 rows: half the registers per unit, so up to 12 units in one batch)
+  constexpr int NB = H16 ? (UPT > 12 ? (UPT + 7) / 8 : 1) : (UPT > 6 ? (UPT + 3) / 4 : 1);
+  constexpr int UPB = (UPT + NB - 1) / NB;
+  f32x4 pa[H16 ? 1 : UPB][2];
+  u32x4 ph[H16 ? UPB : 1];
   auto load_a = [&](int bt) {
 #pragma unroll
     for (int i = 0; i < UPB; ++i) {
       const int u = tid + (bt * UPB + i) * NT;
       const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
       const bool ok = u < UNITS && r < P.R;
-      const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
-      pa[i][0] = src[0];
-      pa[i][1] = src[1];
+      const size_t off = (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8;
+      if constexpr (H16) {
+        ph[i] = *(const u32x4*)(P.A16 + off);
+      } else {
+        const f32x4* src = (const f32x4*)(P.A + off);
+        pa[i][0] = src[0];
+        pa[i][1] = src[1];
+      }
     }
   };
   auto stage_a = [&](int bt) {
@@ -1262,11 +1283,17 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
       if (u < UNITS) {
         const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
         const bool ok = r < P.R;
-        float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
-        f16x8 h;
+        u32x4 hv;
+        if constexpr (H16) {
+          hv = ok ? ph[i] : (u32x4){0u, 0u, 0u, 0u};
+        } else {
+          float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+          f16x8 h;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(ok ? v[e] : 0.0f);
-        sA[(j * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, h);
+          for (int e = 0; e < 8; ++e) h[e] = (_Float16)(ok ? v[e] : 0.0f);
+          hv = __builtin_bit_cast(u32x4, h);
+        }
+        sA[(j * 4 + g) * RL + r] = hv;
       }
     }
   };
@@ -2084,7 +2111,13 @@ __device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p,
   for (int i = 0; i < PP; ++i) {
     const int dp = j + 16 * i;
     if (cok && dp < HD / 2) {
-      *(float2*)(P.out + (size_t)(b * P.S + iq) * DQ + head * HD + 2 * dp) = make_float2(o0[i], o1[i]);
+      const size_t oi = (size_t)(b * P.S + iq) * DQ + head * HD + 2 * dp;
+      *(float2*)(P.out + oi) = make_float2(o0[i], o1[i]);
+      if (P.out16) {
+        const _Float16 h0 = (_Float16)o0[i], h1 = (_Float16)o1[i];
+        *(uint32_t*)(P.out16 + oi) =
+            (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      }
       if (P.af_out) prep_store2(P.af_out, (P.n_seq * P.S + 15) >> 4, b * P.S + iq, head * HD + 2 * dp, o0[i], o1[i]);
     }
   }
@@ -2519,17 +2552,24 @@ hipError_t launch_mmqr(const GemmParams& p0, int epi, int max_grid, hipStream_t 
 
 hipError_t launch_mm1l(const GemmParams& p, int nw, int spw, int rl, hipStream_t st) {
   if (p.R < 1 || p.R > rl || p.K != nw * spw * 32 || p.N % 16) return hipErrorInvalidValue;
-  if (nw == 16 && spw == 19 && rl == 8) {  // the smallest staging that holds the rows
-    if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<16, 19, 2>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
-    else if (p.R <= 4) hipLaunchKernelGGL((k_mm1l<16, 19, 4>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
-    else hipLaunchKernelGGL((k_mm1l<16, 19, 8>), dim3(p.N / 16), dim3(16 * 64), 0, st, p);
+  // the smallest staging that holds the rows; A from fp16 rows when given
+#define SPECV_MM1L_GO(a, b, c)                                                                         \
+  do {                                                                                                 \
+    if (p.A16) hipLaunchKernelGGL((k_mm1l<a, b, c, true>), dim3(p.N / 16), dim3(a * 64), 0, st, p);   \
+    else hipLaunchKernelGGL((k_mm1l<a, b, c, false>), dim3(p.N / 16), dim3(a * 64), 0, st, p);        \
+  } while (0)
+  if (nw == 16 && spw == 19 && rl == 8) {
+    if (p.R <= 2) SPECV_MM1L_GO(16, 19, 2);
+    else if (p.R <= 4) SPECV_MM1L_GO(16, 19, 4);
+    else SPECV_MM1L_GO(16, 19, 8);
     return hipGetLastError();
   }
   if (nw == 8 && spw == 16 && rl == 4) {
-    if (p.R <= 2) hipLaunchKernelGGL((k_mm1l<8, 16, 2>), dim3(p.N / 16), dim3(8 * 64), 0, st, p);
-    else hipLaunchKernelGGL((k_mm1l<8, 16, 4>), dim3(p.N / 16), dim3(8 * 64), 0, st, p);
+    if (p.R <= 2) SPECV_MM1L_GO(8, 16, 2);
+    else SPECV_MM1L_GO(8, 16, 4);
     return hipGetLastError();
   }
+#undef SPECV_MM1L_GO
   return hipErrorInvalidValue;
 }
 
@@ -2546,9 +2586,15 @@ hipError_t launch_mm(const GemmParams& p, int nw, int spw, int ct, int nbuf, int
   const int grid = nblk < max_grid ? nblk : max_grid;
 #define SPECV_MM_GO(E, a, b, c, d, e)                                                    \
   if (nw == a && spw == b && ct == c && nbuf == d && gp == e) {                          \
-    if constexpr (d == 0)                                                                \
-      hipLaunchKernelGGL((k_mm1<E, a, b, c, e>), dim3(nblk1), dim3(a * 64), 0, st, p);   \
-    else                                                                                 \
+    if constexpr (d == 0) {                                                              \
+      if constexpr (E == EPI_RESID) {                                                    \
+        if (p.A16) hipLaunchKernelGGL((k_mm1<E, a, b, c, e, true>), dim3(nblk1), dim3(a * 64), 0, st, p); \
+        else hipLaunchKernelGGL((k_mm1<E, a, b, c, e, false>), dim3(nblk1), dim3(a * 64), 0, st, p); \
+      } else {                                                                           \
+        if (p.A16) return hipErrorInvalidValue;                                          \
+        hipLaunchKernelGGL((k_mm1<E, a, b, c, e, false>), dim3(nblk1), dim3(a * 64), 0, st, p); \
+      }                                                                                  \
+    } else                                                                               \
       hipLaunchKernelGGL((k_mm<E, a, b, c, d, e>), dim3(grid), dim3(a * 64), 0, st, p); \
     return hipGetLastError();                                                            \
   }

@@ -173,7 +173,7 @@ struct Layout {
   size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t rec_kv, rec_slot;  // recurrent layers: staged keys and values; committed state slot per sequence
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
-  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, packflag, argkey, status, step, result, kv_len, bt, rope, apart,
+  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, packflag, h16, o16, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, workspace_bytes;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
@@ -362,6 +362,10 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.attn_cnt = take(R * Lo.nq * 4);  // n_seq * n_kv * query tiles <= rows * n_q
   Lo.lm_cnt = take(4);
   Lo.packflag = take(4);
+  // fp16 copies of the SwiGLU and attention outputs for the one-pass down
+  // and O kernels (at most 8 rows)
+  Lo.h16 = Lo.fmt == FMT_BF16 ? take((size_t)std::min(R, (size_t)8) * Lo.F * 2) : (size_t)-1;
+  Lo.o16 = Lo.fmt == FMT_BF16 ? take((size_t)std::min(R, (size_t)8) * Lo.DQ * 2) : (size_t)-1;
   Lo.rowinfo = take(R * 8);
   Lo.rec_kv = Lo.any_rec ? take(R * 2 * Lo.DK * 4) : (size_t)-1;
   Lo.rec_slot = Lo.any_rec ? take((size_t)Lo.max_seqs * 4) : (size_t)-1;
@@ -502,6 +506,18 @@ int reset_rec_slot(spec_ctx* c, int seq) {
 }
 
 // -------------------------------------------------------- forward sequence
+
+// The down projection reads the SwiGLU output as fp16 rows (k_mm1l) and the
+// O projection the attention output (k_mm1l, k_mm1): bf16 weights, at most
+// 8 rows, the one-pass plans; O only after an attention (not recurrent) layer.
+bool down_reads_h16(const spec_ctx* c, int R) {
+  return c->lo.fmt == FMT_BF16 && c->lo.d_lds && R <= 8;
+}
+bool o_reads_o16(const spec_ctx* c, int l, int R) {
+  const Layout& L = c->lo;
+  return L.fmt == FMT_BF16 && !L.rec[(size_t)l] && R <= 8 && R <= L.mm_o.rmax && L.mm_o.nw == 8 &&
+         L.mm_o.spw == 16 && L.mm_o.nbuf == 0;
+}
 
 GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) {
   GemmParams p;
@@ -683,6 +699,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.part = c->ws<float>(L.apart);
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
+      a.out16 = o_reads_o16(c, l, R) ? c->ws<_Float16>(L.o16) : nullptr;
       a.af_out = c->af_next(L.nk_o, R);
       a.n_qt = (S * L.G + 15) / 16;
       const bool loc = L.local[(size_t)l] != 0;
@@ -702,6 +719,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       go.lda = L.DQ;
       go.x = c->ws<float>(L.x);
       go.ss_out = c->ws<float>(L.ss);
+      if (o_reads_o16(c, l, R)) go.A16 = c->ws<_Float16>(L.o16);
       // up to four rows of the eight-part plan: the same K parts with A staged in LDS
       if (SPECV_O_LDS && L.fmt == FMT_BF16 && R <= 4 && L.mm_o.nw == 8 && L.mm_o.spw == 16 && L.mm_o.nbuf == 0 &&
           L.mm_o.gp == 1 && R <= L.mm_o.rmax) {
@@ -719,6 +737,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.ss_n = L.H / 16;
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
+      gu.h16 = down_reads_h16(c, R) ? c->ws<_Float16>(L.h16) : nullptr;
       gu.af_out = c->af_next(L.nk_d, R);
       HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
@@ -729,6 +748,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gd.lda = L.F;
       gd.x = c->ws<float>(L.x);
       gd.ss_out = c->ws<float>(L.ss);
+      if (down_reads_h16(c, R)) gd.A16 = c->ws<_Float16>(L.h16);
       if (L.d_lds && R <= 8) HIPCHK(c, launch_mm1l(gd, 16, 19, 8, st));
       else if (L.d_lds && R <= SPECV_DOWN_MM1_ROWS)
         HIPCHK(c, launch_mm(gd, 16, 19, 4, 0, 1, c->mm_grid, EPI_RESID, st));

@@ -93,6 +93,19 @@ def test_pool_exhaustion_is_refused_cleanly(weights):
     s.close()
 
 
+def test_weight_beyond_fp16_range_is_refused(weights):
+    """The GEMMs hold bf16 weights as exact fp16 copies: a matrix with a
+    value beyond the fp16 range (65504) is refused at load with SPEC_EINVAL
+    instead of turning into an infinity."""
+    bad = {**weights, "layers": [dict(layer) for layer in weights["layers"]]}
+    wq = bad["layers"][1]["wq"].clone()
+    wq[3, 5] = 1.0e6
+    bad["layers"][1]["wq"] = wq
+    with pytest.raises(specv.SpecError) as e:
+        specv.Session(SHAPE, specv.tree_weights(bad), max_ctx=128)
+    assert e.value.code == specv.SPEC_EINVAL and "fp16" in str(e.value)
+
+
 def test_heterogeneous_drafts_per_sequence(weights):
     """spec_verify_batch_k: each sequence brings its own number of drafts
     (0..7) in one padded 8-row step.  Its accept length counts only its own
