@@ -1344,8 +1344,9 @@ __global__ __launch_bounds__(NW * 64) void k_mm1l(GemmParams P) {
 // bit for bit (each tile's sums keep their order whatever CT is).  The next
 // block's fragments are issued as soon as the MFMAs have read the current
 // ones.
-template <int EPI, int NW, int GPW, int CT, int RL>
+template <int EPI, int NW, int GPW, int CT, int RL, bool H16 = false>
 __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
+  static_assert(!H16 || EPI == EPI_RESID, "fp16 A rows carry no RMSNorm");
   constexpr int NT = NW * 64, KG = NW * GPW, KS = KG * 4;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int UNITS = RL * KS * 4, UPT = (UNITS + NT - 1) / NT;  // (row, step, lane group) units of 8 inputs
@@ -1373,16 +1374,22 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
   }
   Sampling sm = {0.0f, 0u, 0u};
   if constexpr (EPI == EPI_LM) sm = load_sampling(P);
-  f32x4 pa[UPT][2], pg[NORM ? UPT : 1][2];
+  f32x4 pa[H16 ? 1 : UPT][2], pg[NORM ? UPT : 1][2];
+  u32x4 ph[H16 ? UPT : 1];  // or the rows already rounded to fp16
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int u = tid + i * NT;
     const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
     const bool ok = u < UNITS && r < P.R;
     const int jc = u < UNITS ? j : 0;
-    const f32x4* src = (const f32x4*)(P.A + (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8);
-    pa[i][0] = src[0];
-    pa[i][1] = src[1];
+    const size_t off = (size_t)(ok ? r : 0) * P.lda + (size_t)(ok ? j : 0) * 32 + g * 8;
+    if constexpr (H16) {
+      ph[i] = *(const u32x4*)(P.A16 + off);
+    } else {
+      const f32x4* src = (const f32x4*)(P.A + off);
+      pa[i][0] = src[0];
+      pa[i][1] = src[1];
+    }
     if constexpr (NORM) {
       const f32x4* gsrc = (const f32x4*)(P.gain + (size_t)jc * 32 + g * 8);
       pg[i][0] = gsrc[0];
@@ -1422,21 +1429,25 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
     const int u = tid + i * NT;
     if (u < UNITS) {
       const int r = u % RL, g = (u / RL) & 3, j = u / (RL * 4);
-      float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
-      if (r >= P.R) {
+      if constexpr (H16) {
+        sA[(j * 4 + g) * RL + r] = r < P.R ? ph[i] : (u32x4){0u, 0u, 0u, 0u};
+      } else {
+        float v[8] = {pa[i][0].x, pa[i][0].y, pa[i][0].z, pa[i][0].w, pa[i][1].x, pa[i][1].y, pa[i][1].z, pa[i][1].w};
+        if (r >= P.R) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+          for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+        if constexpr (NORM) {
+          const float sc = r < P.R ? sR[r] : 0.0f;
+          const float gv[8] = {pg[i][0].x, pg[i][0].y, pg[i][0].z, pg[i][0].w, pg[i][1].x, pg[i][1].y, pg[i][1].z, pg[i][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
+        }
+        f16x8 hi;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
+        sA[(j * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
       }
-      if constexpr (NORM) {
-        const float sc = r < P.R ? sR[r] : 0.0f;
-        const float gv[8] = {pg[i][0].x, pg[i][0].y, pg[i][0].z, pg[i][0].w, pg[i][1].x, pg[i][1].y, pg[i][1].z, pg[i][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (v[e] * sc) * gv[e];
-      }
-      f16x8 hi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hi[e] = (_Float16)v[e];
-      sA[(j * 4 + g) * RL + r] = __builtin_bit_cast(u32x4, hi);
     }
   }
   __syncthreads();
@@ -1545,8 +1556,9 @@ __global__ __launch_bounds__(NW * 64) void k_mmq(GemmParams P) {
 // alone, never on R, so an S-row forward equals S one-row forwards bit for bit.
 constexpr int kMmqrMaxParts = 8;  // K parts of the register kernel's plans (host-checked)
 
-template <int EPI, int NW, int GPW, int CT>
+template <int EPI, int NW, int GPW, int CT, bool H16 = false>
 __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
+  static_assert(!H16 || EPI == EPI_RESID, "fp16 A rows carry no RMSNorm");
   constexpr int NT = NW * 64, KG = NW * GPW, ST = GPW * 4;
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int PPT = (16 * 8 * CT + NT - 1) / NT;  // epilogue pairs per thread
@@ -1576,9 +1588,16 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
   }
   Sampling sm = {0.0f, 0u, 0u};
   if constexpr (EPI == EPI_LM) sm = load_sampling(P);
-  // the lane's A values: 8 per step, rows past R are zeros
-  float a[ST][8];
-  {
+  // the lane's A values: 8 per step, rows past R are zeros (or the rows
+  // already rounded to fp16)
+  float a[H16 ? 1 : ST][8];
+  u32x4 a16[H16 ? ST : 1];
+  if constexpr (H16) {
+    const bool live = row < P.R;
+    const _Float16* src = P.A16 + (size_t)(live ? row : 0) * P.lda + (size_t)g0 * 128 + kg * 8;
+#pragma unroll
+    for (int j = 0; j < ST; ++j) a16[j] = live ? *(const u32x4*)(src + j * 32) : (u32x4){0u, 0u, 0u, 0u};
+  } else {
     const bool live = row < P.R;
     const float* src = P.A + (size_t)(live ? row : 0) * P.lda + (size_t)g0 * 128 + kg * 8;
 #pragma unroll
@@ -1619,7 +1638,10 @@ __global__ __launch_bounds__(NW * 64) void k_mmqr(GemmParams P) {
   __syncthreads();
   // normalise and round to fp16, in place
   f16x8 ah[ST];
-  {
+  if constexpr (H16) {
+#pragma unroll
+    for (int j = 0; j < ST; ++j) ah[j] = __builtin_bit_cast(f16x8, a16[j]);
+  } else {
     const float sc = NORM ? sR[row] : 1.0f;
 #pragma unroll
     for (int j = 0; j < ST; ++j) {
@@ -2459,6 +2481,15 @@ hipError_t go_mmq(dim3 grid, const GemmParams& p, hipStream_t st) {
     return hipErrorInvalidValue;
   } else {
     // four staged rows where they suffice (less staging work at one row)
+    if constexpr (EPI == EPI_RESID) {
+      if (p.A16) {  // the rows already rounded to fp16
+        if (p.R <= 4) hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 4, true>), grid, dim3(NW * 64), 0, st, p);
+        else hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 8, true>), grid, dim3(NW * 64), 0, st, p);
+        return hipGetLastError();
+      }
+    } else {
+      if (p.A16) return hipErrorInvalidValue;
+    }
     if (p.R <= 4) hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 4>), grid, dim3(NW * 64), 0, st, p);
     else hipLaunchKernelGGL((k_mmq<EPI, NW, GPW, CT, 8>), grid, dim3(NW * 64), 0, st, p);
     return hipGetLastError();
@@ -2522,6 +2553,7 @@ hipError_t launch_mmqr(const GemmParams& p0, int epi, int max_grid, hipStream_t 
     return hipErrorInvalidValue;
   if (parts > 1 && (epi != EPI_RESID || !p0.part || !p0.cnt)) return hipErrorInvalidValue;
   if (epi != EPI_RESID && (!p0.ss || !p0.gain || p0.ss_n * 16 != p0.K)) return hipErrorInvalidValue;
+  if (epi != EPI_RESID && p0.A16) return hipErrorInvalidValue;
   if (epi == EPI_RESID && (!p0.x || !p0.ss_out)) return hipErrorInvalidValue;
   if (epi == EPI_QKV && !p0.rowinfo) return hipErrorInvalidValue;
   if (epi == EPI_LM && (!p0.argkey || !p0.lm_cnt || !p0.status || !p0.result || !p0.kd || !p0.step || !p0.rowinfo ||
@@ -2538,7 +2570,10 @@ hipError_t launch_mmqr(const GemmParams& p0, int epi, int max_grid, hipStream_t 
   if (nw == (a) && gpw == (b)) {                                                                              \
     switch (epi) {                                                                                            \
       case EPI_QKV: hipLaunchKernelGGL((k_mmqr<EPI_QKV, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break;     \
-      case EPI_RESID: hipLaunchKernelGGL((k_mmqr<EPI_RESID, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break; \
+      case EPI_RESID:                                                                                         \
+        if (p.A16) hipLaunchKernelGGL((k_mmqr<EPI_RESID, a, b, SPECV_MMQR_CT, true>), grid, dim3(a * 64), 0, st, p); \
+        else hipLaunchKernelGGL((k_mmqr<EPI_RESID, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p);    \
+        break;                                                                                                \
       case EPI_SWIGLU: hipLaunchKernelGGL((k_mmqr<EPI_SWIGLU, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break; \
       case EPI_LM: hipLaunchKernelGGL((k_mmqr<EPI_LM, a, b, SPECV_MMQR_CT>), grid, dim3(a * 64), 0, st, p); break;       \
       default: return hipErrorInvalidValue;                                                                   \

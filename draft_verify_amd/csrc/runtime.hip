@@ -364,8 +364,8 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.packflag = take(4);
   // fp16 copies of the SwiGLU and attention outputs for the one-pass down
   // and O kernels (at most 8 rows)
-  Lo.h16 = Lo.fmt == FMT_BF16 ? take((size_t)std::min(R, (size_t)8) * Lo.F * 2) : (size_t)-1;
-  Lo.o16 = Lo.fmt == FMT_BF16 ? take((size_t)std::min(R, (size_t)8) * Lo.DQ * 2) : (size_t)-1;
+  Lo.h16 = take((size_t)std::min(R, (size_t)16) * Lo.F * 2);
+  Lo.o16 = take((size_t)std::min(R, (size_t)16) * Lo.DQ * 2);
   Lo.rowinfo = take(R * 8);
   Lo.rec_kv = Lo.any_rec ? take(R * 2 * Lo.DK * 4) : (size_t)-1;
   Lo.rec_slot = Lo.any_rec ? take((size_t)Lo.max_seqs * 4) : (size_t)-1;
@@ -507,16 +507,26 @@ int reset_rec_slot(spec_ctx* c, int seq) {
 
 // -------------------------------------------------------- forward sequence
 
-// The down projection reads the SwiGLU output as fp16 rows (k_mm1l) and the
-// O projection the attention output (k_mm1l, k_mm1): bf16 weights, at most
-// 8 rows, the one-pass plans; O only after an attention (not recurrent) layer.
+// The down projection reads the SwiGLU output as fp16 rows and the O
+// projection the attention output, where their one-pass kernels serve the
+// rows: bf16 weights, at most 8 rows (k_mm1l, k_mm1); int4 weights, the LDS
+// or register kernel (k_mmq, k_mmqr); O only after an attention (not
+// recurrent) layer.
+bool int4_onepass(int K, int nk, int R) {
+  int nk_mmq = nk;
+  const int route = int4_route(K, nk, R, EPI_RESID, &nk_mmq);
+  return route == INT4_MMQ || route == INT4_MMQR;
+}
 bool down_reads_h16(const spec_ctx* c, int R) {
-  return c->lo.fmt == FMT_BF16 && c->lo.d_lds && R <= 8;
+  const Layout& L = c->lo;
+  if (L.fmt == FMT_INT4) return R <= 16 && int4_onepass(L.F, L.nk_d, R);
+  return L.d_lds && R <= 8;
 }
 bool o_reads_o16(const spec_ctx* c, int l, int R) {
   const Layout& L = c->lo;
-  return L.fmt == FMT_BF16 && !L.rec[(size_t)l] && R <= 8 && R <= L.mm_o.rmax && L.mm_o.nw == 8 &&
-         L.mm_o.spw == 16 && L.mm_o.nbuf == 0;
+  if (L.rec[(size_t)l]) return false;
+  if (L.fmt == FMT_INT4) return R <= 16 && int4_onepass(L.DQ, L.nk_o, R);
+  return R <= 8 && R <= L.mm_o.rmax && L.mm_o.nw == 8 && L.mm_o.spw == 16 && L.mm_o.nbuf == 0;
 }
 
 GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) {
