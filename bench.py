@@ -909,6 +909,11 @@ def main():
         assert done == K, f"ran {done} of {K} rounds"
         return (n1 - n0) / dt, dt, st, st["forwards"] - f0
 
+    # one untimed pass of each mode first: the session's first generation
+    # (host structures, graph replays from cold) ran ~4 % slower than any later
+    # one, whichever mode came first
+    timed_rounds(True)
+    timed_rounds(False)
     on_tok_s, on_dt, on_st, _ = timed_rounds(True)
     off_tok_s, off_dt, _, _ = timed_rounds(False)
     log(f"timed {K} rounds: spec-on {on_tok_s:.1f} tok/s, spec-off {off_tok_s:.1f} tok/s")
