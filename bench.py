@@ -660,8 +660,8 @@ def summarize_traffic_all(fetch_csv, write_csv, out_md, command, n_fwd=10):
     fs, ws = gib_kib / fetch[copy_name][-1], gib_kib / write[copy_name][-1]  # the last copy: the 1 GiB one
     H, F, DQ, DK, V, hd = 2560, 9728, 4096, 1024, 151936, 128
     algo = {"k_mm<0,": ("QKV", (DQ + 2 * DK) * H * 2), "k_attn<": ("attention (848 ctx)", 849 * DK * 2 * 2),
-            "k_mm1<1,": ("O", H * DQ * 2), "k_mm<2,": ("gate/up", 2 * F * H * 2),
-            "k_mm1l<": ("down", H * F * 2), "k_mm<3,": ("LM head", V * H * 2)}
+            "k_mm1l<8, 16,": ("O", H * DQ * 2), "k_mm<2,": ("gate/up", 2 * F * H * 2),
+            "k_mm1l<16, 19,": ("down", H * F * 2), "k_mm<3,": ("LM head", V * H * 2)}
     lines = ["# HBM traffic per launch of the S=1 forward's kernels (Qwen3-4B shape, 848-token context)", "",
              f"Command: `{command}`", "",
              f"Calibration: a 1 GiB device copy reads FETCH_SIZE {fetch[copy_name][-1]:.0f} KiB and "
