@@ -1909,7 +1909,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[t][dt] = ok ? vf[t][dt] : (f16x4){0, 0, 0, 0};
   }
-  // The group's query tiles, one after another on the same K and V.
+  // The group's query tiles, one after another on the same K and V; each
+  // tile's queries load while the previous tile computes.
   for (;;) {
   f16x8 qf[KST];
 #pragma unroll
@@ -1919,6 +1920,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
                         qa[ks][1].x, qa[ks][1].y, qa[ks][1].z, qa[ks][1].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) qf[ks][e] = use ? (_Float16)v[e] : (_Float16)0.0f;
+  }
+  if (qt + 1 < qt1) {
+    const int ncol = (qt + 1) * 16 + c16, nc = ncol < QC ? ncol : 0;
+    const float* nrow = P.q + (size_t)(b * S + nc / G) * DQ + (kvh * G + nc % G) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) {
+      const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
+      qa[ks][0] = *(const f32x4*)(nrow + dc);
+      qa[ks][1] = *(const f32x4*)(nrow + dc + 4);
+    }
   }
 
   float s[4][4];
@@ -2011,13 +2022,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   iq = colc / G;
   head = kvh * G + colc % G;
   pos_q = p + iq;
-  qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
-#pragma unroll
-  for (int ks = 0; ks < KST; ++ks) {
-    const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
-    qa[ks][0] = *(const f32x4*)(qrow + dc);
-    qa[ks][1] = *(const f32x4*)(qrow + dc + 4);
-  }
   }
   if (!P.fuse) return;
   // Short contexts: the last split of this (sequence, kv head, tile group)

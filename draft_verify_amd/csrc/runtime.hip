@@ -134,7 +134,7 @@ struct MmPlan {
 // Attention workgroups (sequence, kv head, split, query tile) up to which each
 // takes one query tile.
 #ifndef SPECV_ATTN_TPW1_WGS
-#define SPECV_ATTN_TPW1_WGS 2048
+#define SPECV_ATTN_TPW1_WGS 512
 #endif
 #ifndef SPECV_MM_WG_PER_CU
 #define SPECV_MM_WG_PER_CU 1
