@@ -68,7 +68,8 @@ struct GemmParams {
   float* part;           // split partial sums [nslices][R][N]
   unsigned* cnt;         // arrival counter per 64-column block
   // EPI_QKV
-  float* q;              // [R][n_q*hd] rotated queries
+  float* q;              // [R][n_q*hd] rotated queries (recurrent layers: unrotated), or
+  _Float16* q16;         // an attention layer's rotated queries rounded to fp16 (what attention reads)
   _Float16* kpool;       // this layer's K blocks [n_blocks][n_kv][16][hd]
   _Float16* vpool;       // this layer's V blocks [n_blocks][n_kv][hd][16]
   const int32_t* bt;     // block tables [max_seqs][bt_stride]
@@ -106,7 +107,7 @@ struct GemmParams {
 };
 
 struct AttnParams {
-  const float* q;        // [R][n_q*hd]
+  const _Float16* q;     // [R][n_q*hd] rotated queries, fp16 (the QKV epilogue's rounding)
   const int32_t* rowinfo;// [R][2] (k_embed): row b*S's position is sequence b's cache length
   const int32_t* slotbt; // [n_seq][bt_stride] (k_embed): sequence b's block table row
   const _Float16* kpool; // [n_blocks][n_kv][16][hd]

@@ -578,9 +578,15 @@ __device__ __forceinline__ void qkv_pair_cs(const GemmParams& P, int r, int c, f
     const float cs = cs2.x, sn = cs2.y;
     const float o0 = v0 * cs - v1 * sn, o1 = v0 * sn + v1 * cs;
     if (c < DQ) {
-      float* qr = P.q + (size_t)r * DQ + head * hd;
-      qr[j] = o0;
-      qr[j + half] = o1;
+      if (P.q16) {
+        _Float16* qr = P.q16 + (size_t)r * DQ + head * hd;
+        qr[j] = (_Float16)o0;
+        qr[j + half] = (_Float16)o1;
+      } else {
+        float* qr = P.q + (size_t)r * DQ + head * hd;
+        qr[j] = o0;
+        qr[j + half] = o1;
+      }
     } else {
       _Float16* kr = P.kpool + (((size_t)blk * P.n_kv + head) * 16 + slot) * hd;
       kr[j] = (_Float16)o0;
@@ -1815,12 +1821,14 @@ template <int HD, bool COH, int MS>
 __device__ void combine_tile(const AttnParams& P, int b, int kvh, int qt, int p, float* sML);
 constexpr int kMaxCombineSplits = 256;  // host-checked: max_ctx <= 65536
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn(AttnParams P) {
+// Two waves per SIMD also with two tiles per pass (a few registers spill).
+template <int HD, int TP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn(AttnParams P) {
+  static_assert(TP == 1 || TP == 2, "one or two query tiles per pass");
   constexpr int KST = (HD + 31) / 32;  // 32-wide steps over the head dim (zero padded)
   constexpr int DT = HD / 16;          // 16-row tiles of O^T
   constexpr int FS = attn_fuse_splits(HD);
-  static_assert(16 * FS * 2 <= 4 * 16 * (HD + 1), "the fused merge's split table fits sO");
+  static_assert(16 * FS * 2 <= TP * 4 * 16 * (HD + 1), "the fused merge's split table fits sO");
   const int kvh = blockIdx.y;
   const int n_tg = (P.n_qt + P.tpw - 1) / P.tpw;  // groups of tpw query tiles
   const int b = blockIdx.z / n_tg, tg = blockIdx.z - b * n_tg;
@@ -1867,23 +1875,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
     for (int t = 0; t < 4; ++t) blk[t] = (kb0 + t) * 16 < total ? bv[t] : bz;
   }
 
-  __shared__ float sO[4][16][HD + 1];
-  __shared__ float sM[4][16], sL[4][16], sF[4][16];
+  __shared__ float sO[TP][4][16][HD + 1];
+  __shared__ float sM[TP][4][16], sL[TP][4][16], sF[TP][4][16];
 
-  int qt = qt0;
-  int col = qt * 16 + c16;
-  bool qok = col < QC;
-  int colc = qok ? col : 0;
-  int iq = colc / G, head = kvh * G + colc % G;
-  int pos_q = p + iq;
-  const float* qrow = P.q + (size_t)(b * S + iq) * DQ + head * HD;
-  f32x4 qa[KST][2];
+  // the queries of tile t: 8 fp16 per step and lane (column t*16 + c16)
+  auto load_q = [&](u32x4 (&qd)[KST], int t) {
+    const int cl = t * 16 + c16, cc = cl < QC ? cl : 0;
+    const _Float16* qrow = P.q + (size_t)(b * S + cc / G) * DQ + (kvh * G + cc % G) * HD;
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks) {
-    const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
-    qa[ks][0] = *(const f32x4*)(qrow + dc);
-    qa[ks][1] = *(const f32x4*)(qrow + dc + 4);
-  }
+    for (int ks = 0; ks < KST; ++ks) {
+      const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
+      qd[ks] = *(const u32x4*)(qrow + dc);
+    }
+  };
+  int qt = qt0;
+  u32x4 qa[TP][KST];
+#pragma unroll
+  for (int u = 0; u < TP; ++u) load_q(qa[u], qt0 + u < qt1 ? qt0 + u : qt0);
   f16x8 kf[4][KST];
   f16x4 vf[4][DT];
 #pragma unroll
@@ -1909,119 +1917,136 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[t][dt] = ok ? vf[t][dt] : (f16x4){0, 0, 0, 0};
   }
-  // The group's query tiles, one after another on the same K and V; each
-  // tile's queries load while the previous tile computes.
+  // The group's query tiles, TP at a time on the same K and V (the tiles of
+  // a pass interleave their independent MFMA and softmax chains); each pass's
+  // queries load while the previous pass computes.  Every column's arithmetic
+  // is the same whatever TP and the pass it falls in.
   for (;;) {
-  f16x8 qf[KST];
+  f16x8 qf[TP][KST];
+  bool qok[TP];
+  int pos_q[TP];
 #pragma unroll
-  for (int ks = 0; ks < KST; ++ks) {
-    const bool use = qok && ks * 32 + g4 * 8 < HD;
-    const float v[8] = {qa[ks][0].x, qa[ks][0].y, qa[ks][0].z, qa[ks][0].w,
-                        qa[ks][1].x, qa[ks][1].y, qa[ks][1].z, qa[ks][1].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = use ? (_Float16)v[e] : (_Float16)0.0f;
-  }
-  if (qt + 1 < qt1) {
-    const int ncol = (qt + 1) * 16 + c16, nc = ncol < QC ? ncol : 0;
-    const float* nrow = P.q + (size_t)(b * S + nc / G) * DQ + (kvh * G + nc % G) * HD;
+  for (int u = 0; u < TP; ++u) {
+    const int cl = (qt + u) * 16 + c16;
+    qok[u] = qt + u < qt1 && cl < QC;
+    pos_q[u] = p + (qok[u] ? cl : 0) / G;
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
-      const int d = ks * 32 + g4 * 8, dc = d < HD ? d : 0;
-      qa[ks][0] = *(const f32x4*)(nrow + dc);
-      qa[ks][1] = *(const f32x4*)(nrow + dc + 4);
+      const bool use = qok[u] && ks * 32 + g4 * 8 < HD;
+      qf[u][ks] = __builtin_bit_cast(f16x8, use ? qa[u][ks] : (u32x4){0u, 0u, 0u, 0u});
     }
+  }
+  if (qt + TP < qt1) {
+#pragma unroll
+    for (int u = 0; u < TP; ++u) load_q(qa[u], qt + TP + u < qt1 ? qt + TP + u : qt + TP);
   }
 
-  float s[4][4];
-  float mx = -INFINITY;
+  float sc[TP][4][4];
+  float mx[TP];
+#pragma unroll
+  for (int u = 0; u < TP; ++u) mx[u] = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[TP];
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ks], qf[ks], acc, 0, 0, 0);
+    for (int u = 0; u < TP; ++u) acc[u] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = (kb0 + t) * 16 + g4 * 4 + i;
-      const bool vis = qok && key <= pos_q && (P.win == 0 || key > pos_q - P.win);
-      s[t][i] = vis ? acc[i] * P.scale : -INFINITY;
-      mx = fmaxf(mx, s[t][i]);
-    }
+    for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+      for (int u = 0; u < TP; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ks], qf[u][ks], acc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < TP; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = (kb0 + t) * 16 + g4 * 4 + i;
+        const bool vis = qok[u] && key <= pos_q[u] && (P.win == 0 || key > pos_q[u] - P.win);
+        sc[u][t][i] = vis ? acc[u][i] * P.scale : -INFINITY;
+        mx[u] = fmaxf(mx[u], sc[u][t][i]);
+      }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float l = 0.0f;
-  f16x8 pf[2];
+  float l[TP];
+  f16x8 pf[TP][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int u = 0; u < TP; ++u) {
+    mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], 16));
+    mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], 32));
+    l[u] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = (mx == -INFINITY) ? 0.0f : expf(s[t][i] - mx);
-      l += e;
-      pf[t >> 1][(t & 1) * 4 + i] = (_Float16)e;
-    }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = (mx[u] == -INFINITY) ? 0.0f : expf(sc[u][t][i] - mx[u]);
+        l[u] += e;
+        pf[u][t >> 1][(t & 1) * 4 + i] = (_Float16)e;
+      }
+    l[u] += __shfl_xor(l[u], 16);
+    l[u] += __shfl_xor(l[u], 32);
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[TP];
+#pragma unroll
+    for (int u = 0; u < TP; ++u) acc[u] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const f16x4 v0 = vf[2 * s2][dt], v1 = vf[2 * s2 + 1][dt];
       const f16x8 a = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[s2], acc, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < TP; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[u][s2], acc[u], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sO[wave][c16][dt * 16 + g4 * 4 + i] = acc[i];
+    for (int u = 0; u < TP; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[u][wave][c16][dt * 16 + g4 * 4 + i] = acc[u][i];
   }
   if (g4 == 0) {
-    sM[wave][c16] = mx;
-    sL[wave][c16] = l;
+#pragma unroll
+    for (int u = 0; u < TP; ++u) {
+      sM[u][wave][c16] = mx[u];
+      sL[u][wave][c16] = l[u];
+    }
   }
   __syncthreads();
   // Combine the four chunks of this split, in wave order: the weight of
   // each (wave, column) once, then the values.
-  if (tid < 16) {
-    const int c = tid;
+  if (tid < 16 * TP) {
+    const int u = tid >> 4, c = tid & 15;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w][c]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[u][w][c]);
     float L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = (M == -INFINITY) ? 0.0f : expf(sM[w][c] - M);
-      sF[w][c] = f;
-      L += sL[w][c] * f;
+      const float f = (M == -INFINITY) ? 0.0f : expf(sM[u][w][c] - M);
+      sF[u][w][c] = f;
+      L = __builtin_fmaf(sL[u][w][c], f, L);
     }
-    const int qcol = qt * 16 + c;
-    if (qcol < QC) {
+    const int qcol = (qt + u) * 16 + c;
+    if (qt + u < qt1 && qcol < QC) {
       float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
       st_dev(dst, M);
       st_dev(dst + 1, L);
     }
   }
   __syncthreads();
-  for (int e = tid; e < 16 * (HD / 2); e += 256) {
-    const int c = e / (HD / 2), d = 2 * (e % (HD / 2));
-    const int qcol = qt * 16 + c;
-    if (qcol >= QC) continue;
+  for (int e = tid; e < TP * 16 * (HD / 2); e += 256) {
+    const int u = e / (16 * (HD / 2)), eu = e - u * (16 * (HD / 2));
+    const int c = eu / (HD / 2), d = 2 * (eu % (HD / 2));
+    const int qcol = (qt + u) * 16 + c;
+    if (qt + u >= qt1 || qcol >= QC) continue;
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = sF[w][c];
-      o0 += sO[w][c][d] * f;
-      o1 += sO[w][c][d + 1] * f;
+      const float f = sF[u][w][c];
+      o0 = __builtin_fmaf(sO[u][w][c][d], f, o0);
+      o1 = __builtin_fmaf(sO[u][w][c][d + 1], f, o1);
     }
     float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
     st_dev2(dst + 2 + d, o0, o1);
   }
-  if (++qt >= qt1) break;
-  __syncthreads();  // sO, sM, sL and sF are rewritten by the next tile
-  col = qt * 16 + c16;
-  qok = col < QC;
-  colc = qok ? col : 0;
-  iq = colc / G;
-  head = kvh * G + colc % G;
-  pos_q = p + iq;
+  qt += TP;
+  if (qt >= qt1) break;
+  __syncthreads();  // sO, sM, sL and sF are rewritten by the next pass
   }
   if (!P.fuse) return;
   // Short contexts: the last split of this (sequence, kv head, tile group)
@@ -2037,7 +2062,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   __syncthreads();
   if (!sLast) return;
   if (tid == 0) *cnt = 0u;  // ready for the next launch
-  for (int t = qt0; t < qt1; ++t) combine_tile<HD, true, FS>(P, b, kvh, t, p, &sO[0][0][0]);
+  for (int t = qt0; t < qt1; ++t) combine_tile<HD, true, FS>(P, b, kvh, t, p, &sO[0][0][0][0]);
 }
 
 template <bool COH>
@@ -2667,22 +2692,28 @@ hipError_t launch_attn(const AttnParams& p, int hd, hipStream_t st) {
                 p.grid_splits > p.max_splits))
     return hipErrorInvalidValue;
   const dim3 grid(p.win ? p.grid_splits : p.max_splits, p.n_kv, p.n_seq * ((n_qt + p.tpw - 1) / p.tpw));
+  // workgroups with several query tiles take them two per pass
+  const bool two = p.tpw > 1 && n_qt > 1;
   const dim3 cgrid(n_qt, p.n_kv, p.n_seq);
   switch (hd) {
     case 128:
-      hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p);
+      if (two) hipLaunchKernelGGL((k_attn<128, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_attn<128, 1>), grid, dim3(256), 0, st, p);
       if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, st, p);
       break;
     case 64:
-      hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, p);
+      if (two) hipLaunchKernelGGL((k_attn<64, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_attn<64, 1>), grid, dim3(256), 0, st, p);
       if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, st, p);
       break;
     case 32:
-      hipLaunchKernelGGL(k_attn<32>, grid, dim3(256), 0, st, p);
+      if (two) hipLaunchKernelGGL((k_attn<32, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_attn<32, 1>), grid, dim3(256), 0, st, p);
       if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<32>, cgrid, dim3(256), 0, st, p);
       break;
     case 16:
-      hipLaunchKernelGGL(k_attn<16>, grid, dim3(256), 0, st, p);
+      if (two) hipLaunchKernelGGL((k_attn<16, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((k_attn<16, 1>), grid, dim3(256), 0, st, p);
       if (!p.fuse) hipLaunchKernelGGL(k_attn_combine<16>, cgrid, dim3(256), 0, st, p);
       break;
     default: return hipErrorInvalidValue;

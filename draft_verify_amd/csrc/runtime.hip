@@ -173,7 +173,7 @@ struct Layout {
   size_t rowinfo;  // per row: position and KV block, written by k_embed
   size_t rec_kv, rec_slot;  // recurrent layers: staged keys and values; committed state slot per sequence
   size_t slotbt;   // per batch slot: its sequence's block table row, written by k_embed
-  size_t x, ss, q, o, h, part, cnt, attn_cnt, lm_cnt, packflag, h16, o16, argkey, status, step, result, kv_len, bt, rope, apart,
+  size_t x, ss, q, q16, o, h, part, cnt, attn_cnt, lm_cnt, packflag, h16, o16, argkey, status, step, result, kv_len, bt, rope, apart,
       logits, workspace_bytes;
   size_t host_step, host_result, host_kvlen, host_bt, host_bytes;
   int cnt_n;
@@ -324,6 +324,7 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   Lo.x = take(R * Lo.H * 4);
   Lo.ss = take(R * (Lo.H / 16) * 4);
   Lo.q = take(R * Lo.DQ * 4);
+  Lo.q16 = take(R * Lo.DQ * 2);
   Lo.o = take(R * Lo.DQ * 4);
   Lo.h = take(R * Lo.F * 4);
   // Split partial sums, for the GEMMs that run the split-K kernel at some row
@@ -657,6 +658,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       g.ss_n = L.H / 16;
       g.gain = (const float*)(c->W + lw.g_attn);
       g.q = c->ws<float>(L.q);
+      g.q16 = L.rec[(size_t)l] ? nullptr : c->ws<_Float16>(L.q16);  // attention layers: fp16 queries
       g.kpool = c->kpool(l);
       g.vpool = c->vpool(l);
       g.bt = c->ws<int32_t>(L.bt);
@@ -694,7 +696,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
         return SPEC_OK;
       }
       AttnParams a;
-      a.q = c->ws<float>(L.q);
+      a.q = c->ws<_Float16>(L.q16);
       a.kpool = c->kpool(l);
       a.vpool = c->vpool(l);
       a.rowinfo = c->ws<int32_t>(L.rowinfo);

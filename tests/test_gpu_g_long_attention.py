@@ -97,3 +97,33 @@ def test_32b_heads_int4_batch1_long_contexts():
             log(f"  ctx {L}: spans 1/4/8/16 rows, worst logit diff {worst:.2e}")
     finally:
         t.close()
+
+
+@pytest.mark.parametrize("S", [4, 8, 16])
+def test_32b_heads_rows_gate_8192_context(S):
+    """Rows gate where the attention takes its query tiles in groups: near an
+    8192-token context the 32 splits x 8 kv heads fill the chip, so a span of
+    8 or 16 rows (4 or 8 query tiles) runs two tiles per pass in each
+    workgroup (4 rows: one tile per workgroup) while one-row decodes run one
+    tile per workgroup; the S-row forward still equals S one-row decodes bit
+    for bit (every column's arithmetic is the same)."""
+    shape = synth.SHAPES["attn_32b"]
+    V = shape["vocab"]
+    w = synth.weights(shape, seed=0, fmt="int4")
+    sess = specv.Session(shape, specv.tree_weights(w), max_ctx=8192 + 64, flags=specv.SPEC_FLAG_KEEP_LOGITS,
+                         fmt="int4")
+    try:
+        g = specv.spec_prefill(sess.ctx, synth.uniform_prompt(61, V, 8192 - 16))
+        p = specv.spec_cache_len(sess.ctx)
+        span = [g] + [int(t) for t in synth.uniform_prompt(62, V, S - 1)]
+        specv.spec_verify(sess.ctx, span)
+        multi = specv.spec_debug_logits(sess.ctx, S, V)
+        specv.spec_rewind(sess.ctx, p)
+        rows = []
+        for t in span:
+            specv.spec_verify(sess.ctx, [t])
+            rows.append(specv.spec_debug_logits(sess.ctx, 1, V)[0])
+        assert np.array_equal(multi, np.stack(rows)), f"{S}-row forward differs from {S} one-row decodes"
+        log(f"  8176-token context, {S} rows: bit-equal to one-row decodes")
+    finally:
+        sess.close()
