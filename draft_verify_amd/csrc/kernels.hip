@@ -468,6 +468,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     }
     __syncthreads();  // sA is restaged for the next 16 rows
   }
+  // Prepared A (above 16 rows): k_gather, launched next, sums the slices.
+  if constexpr (PREP && EPI != EPI_LM) return;
 
   wait_mem();
   __syncthreads();
@@ -676,13 +678,14 @@ __device__ void epi_resid(const GemmParams& P, int nb) {
 
 // The split-K kernel serves the rows above 16, whose down GEMM reads the
 // prepared layout: h is also written there (af_out), only on this path.
+__device__ __forceinline__ void swiglu_prep_pair(const GemmParams& P, int r, int c, float g, float u) {
+  const float v = swiglu_val(g, u);
+  P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
+  if (P.af_out) prep_store1(P.af_out, (P.R + 15) >> 4, r, c >> 1, v);
+}
 template <int CT, int SB, int U>
 __device__ void epi_swiglu(const GemmParams& P, int nb) {
-  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float g, float u) {
-    const float v = swiglu_val(g, u);
-    P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
-    if (P.af_out) prep_store1(P.af_out, (P.R + 15) >> 4, r, c >> 1, v);
-  });
+  for_pairs<CT, SB, U>(P, nb, [&](int, int r, int c, float g, float u) { swiglu_prep_pair(P, r, c, g, u); });
 }
 
 // Sampled rows (step temperature > 0): a row draws its token from
@@ -827,6 +830,49 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
   else if constexpr (EPI == EPI_RESID) epi_resid<CT, SB, U>(P, nb);
   else if constexpr (EPI == EPI_SWIGLU) epi_swiglu<CT, SB, U>(P, nb);
   else epi_lm<CT, SB, U>(P, nb, sbuf);
+}
+
+// Slice sums of the prepared-A split-K GEMM (above 16 rows) and its
+// epilogue, as a kernel of its own: one (row, column pair) per thread, so the
+// gather has the whole chip's loads in flight instead of one workgroup per
+// column block walking 128 rows.  Pair (r, p) is row r, columns 2p and
+// 2p + 1; a row's pairs are padded to a multiple of 8 so that every aligned
+// group of 8 lanes (one RMSNorm partial sum, 16 columns) holds pairs of one
+// row.  The slices are added in slice order from zero, as in the in-kernel
+// gather, so both give the same sums.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gather(GemmParams P) {
+#pragma clang fp contract(off)
+  static_assert(EPI != EPI_LM, "the LM head keeps its in-kernel gather (row maxima, accept stage)");
+  const int PW = ((P.N >> 1) + 7) & ~7;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int r = idx / PW, p = idx - r * PW, c = 2 * p;
+  const bool ok = r < P.R && c < P.N;
+  float v0 = 0.0f, v1 = 0.0f;
+  if (ok) {
+    const size_t stride = (size_t)P.R * P.N;
+    const float* src = P.part + (size_t)r * P.N + c;
+    for (int s0 = 0; s0 < P.nslices; s0 += 8) {
+      float2 t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < P.nslices) t[i] = *(const float2*)(src + (size_t)(s0 + i) * stride);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < P.nslices) {
+          v0 += t[i].x;
+          v1 += t[i].y;
+        }
+    }
+  }
+  if constexpr (EPI == EPI_QKV) {
+    if (ok) qkv_pair(P, r, c, v0, v1);
+  } else if constexpr (EPI == EPI_RESID) {
+    const float t = sum8(ok ? resid_pair(P, r, c, v0, v1) : 0.0f);  // every lane of the group shuffles
+    if (ok && (p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (c >> 4)] = t;
+  } else {
+    if (ok) swiglu_prep_pair(P, r, c, v0, v1);
+  }
 }
 
 // Sum of the NW K parts' partial tiles (part w at sAcc[(w*CT + ct)*64]) in
@@ -2337,11 +2383,19 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
   }
   if (fmt != FMT_BF16) return hipErrorInvalidValue;
   if (p.Af) {
+    // the gather's 8-pair groups need whole 16-column groups
+    if (EPI != EPI_LM && p.N % 16) return hipErrorInvalidValue;
     switch (nk) {
       case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
       case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
       case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
       default: return hipErrorInvalidValue;
+    }
+    if constexpr (EPI != EPI_LM) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const long long pairs = (long long)p.R * (((p.N >> 1) + 7) & ~7);
+      hipLaunchKernelGGL((k_gather<EPI>), dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, p);
     }
     return hipGetLastError();
   }
