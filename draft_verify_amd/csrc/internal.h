@@ -167,6 +167,16 @@ struct EmbedParams {
 
 // Launchers (kernels.hip).  All return hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st);
+// Above 16 rows (bf16, prepared A in p.Af): the many-row GEMM over ns K
+// slices (ns > 1: slice partials in p.part, summed by a gather kernel; the
+// LM head needs ns = 1) with ct (1 or 2) 16-column tiles per wave.
+hipError_t launch_gemm_big(const GemmParams& p, int ns, int ct, int epi, hipStream_t st);
+#ifndef SPECV_BIG_PD1
+#define SPECV_BIG_PD1 8  // steps in flight, one tile per wave
+#endif
+#ifndef SPECV_BIG_PD2
+#define SPECV_BIG_PD2 4  // two tiles per wave
+#endif
 // Prepare A for the split-K GEMM (kernels.hip: k_prep): the RMSNorm (when
 // p.ss is set) and the bf16 hi/lo split of every row once, in the MFMA
 // A-operand order, into af: ceil(R/16) * 16 * K * 4 bytes.

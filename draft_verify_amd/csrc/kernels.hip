@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace specv {
@@ -27,6 +29,7 @@ namespace specv {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -872,6 +875,188 @@ __global__ __launch_bounds__(256) void k_gather(GemmParams P) {
     if (ok && (p & 7) == 0) P.ss_out[(size_t)r * (P.N >> 4) + (c >> 4)] = t;
   } else {
     if (ok) swiglu_prep_pair(P, r, c, v0, v1);
+  }
+}
+
+// ------------------------------------------------ many-row GEMM (17..128 rows)
+//
+// fp16 weights, prepared A (k_prep's layout, or a producer's).  The 32x32x16
+// MFMA: on gfx950 it issues twice the flops per cycle of the 16x16x32 form
+// the one-pass kernels use (measured: 2.4 against 1.3 PFLOP/s of fp16 on
+// register operands), which matters once 128 rows make the GEMM compute
+// bound.  A workgroup of four waves owns a block of 64*CT columns (TB = 4*CT
+// packed 16-column tiles, NP = 2*CT MFMA column tiles of 32) and every row:
+// wave w rows 32w..32w+31, its NP accumulators (32x32 each) in registers.
+// It walks the K range of slice sl (ksl steps of 32 inputs).  A step's
+// weights (TB packed fragments of 1 KB) are loaded by the 256 lanes, CT
+// 16-byte words each, and pass through a two-slot LDS ring (one barrier per
+// step: a slot is rewritten two steps later, after every wave has passed the
+// barrier between); each wave reads its B operands from there and its two A
+// operands (the step's two 16-input halves) straight from the prepared
+// layout.  Both are issued PD steps ahead into register rings.
+//
+// Operand gathers: the 32x32x16 A operand of rows 32w.. and inputs
+// 16h..16h+15 of a step gives lane l row l%32 and inputs 8*(l/32).., which
+// in the prepared layout (16-row chunks, lane r + 16g: row r, inputs 8g..)
+// is word (l%16) + 16*(2h + l/32) of chunk 2w + (l/16)%2; the B operand of
+// columns 32p.. likewise is word (l%16) + 16*(2h + l/32) of packed tile
+// 2p + (l/16)%2.  D: lane l value v is row 8*(v/4) + 4*(l/32) + v%4, column
+// l%32.  One slice (ns = 1): the epilogue runs here, on the block's outputs
+// staged in LDS; several: the slice's partial block goes to P.part and
+// k_gather sums the slices.
+template <int CT>
+struct BigTile {
+  static constexpr int TB = 4 * CT;        // packed 16-column tiles per block
+  static constexpr int NP = 2 * CT;        // 32-column MFMA tiles per block
+  static constexpr int LDO = 64 * CT + 4;  // output row stride in LDS (floats): rows 4 apart hit other banks
+  static constexpr int RING = 2 * TB * 64;  // u32x4 words: two steps of TB weight fragments
+  static constexpr int BYTES = (kMaxRows * LDO * 4 > RING * 16) ? kMaxRows * LDO * 4 : RING * 16;
+};
+
+// The pairs of a block's outputs staged in LDS (row r at sOut + r*LDO):
+// pair idx = (row idx/(32CT), columns nb*64CT + 2*(idx%(32CT)) + {0,1}), as
+// in for_pairs, so the epilogue bodies (and their lane groups) are the same.
+template <int CT, class F>
+__device__ __forceinline__ void for_pairs_lds(const GemmParams& P, int nb, const float* sOut, F&& f) {
+  constexpr int PR = 32 * CT, LDO = BigTile<CT>::LDO;
+  const int n = P.R * PR;
+  for (int idx = threadIdx.x; idx < n; idx += 256) {
+    const int r = idx / PR, pc = 2 * (idx % PR), c = nb * 64 * CT + pc;
+    if (c < P.N) {
+      const float2 v = *(const float2*)(sOut + r * LDO + pc);
+      f(idx, r, c, v.x, v.y);
+    }
+  }
+}
+
+template <int EPI, int CT, int PD>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmParams P, int ksl) {
+  constexpr int TB = BigTile<CT>::TB, NP = BigTile<CT>::NP;
+  const int NB = (P.N + 64 * CT - 1) / (64 * CT), ns = P.nslices;
+  const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
+  const int nb = (loc / ns) * 8 + xcd, sl = loc % ns;
+  if (nb >= NB) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nch = (P.R + 15) >> 4, KS = P.K >> 5, ks0 = sl * ksl, NT = (P.N + 15) >> 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[BigTile<CT>::BYTES];
+  u32x4* ring = (u32x4*)smem;
+
+  // This lane's A words (a chunk past nch repeats the last one; its rows are
+  // never stored) and B word offsets within a ring slot, half h at +16h.
+  const u32x4* af = (const u32x4*)P.Af;
+  const int sub = (lane >> 4) & 1, g0 = (lane & 15) + 16 * (lane >> 5);
+  const int awo = min(2 * wave + sub, nch - 1) * 64 + g0;
+  const int bwo = sub * 64 + g0;
+  // This lane's weight words: word tid + 256c of the block's TB fragments
+  // (tiles past N load tile 0's; their outputs are never stored).
+  const u32x4* wb[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int u = tid + 256 * c, tile = nb * TB + (u >> 6);
+    wb[c] = (const u32x4*)P.W + (size_t)(tile < NT ? tile : 0) * KS * 64 + (u & 63);
+  }
+  u32x4 ra[PD][2], rb[PD][CT];
+  auto issue_a = [&](int i, int ks) {
+    const u32x4* a = af + (size_t)ks * nch * 64 + awo;
+    ra[i][0] = a[0];
+    ra[i][1] = a[32];
+  };
+  auto issue_b = [&](int i, int ks) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) rb[i][c] = __builtin_nontemporal_load(wb[c] + (size_t)ks * 64);
+  };
+#pragma unroll
+  for (int i = 0; i < PD; ++i) {
+    issue_b(i, ks0 + i);
+    issue_a(i, ks0 + i);
+  }
+
+  f32x16 acc[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[p][v] = 0.0f;
+
+  // ksl is a multiple of PD (the launcher checks): rounds of PD steps, every
+  // round but the last issuing the next round's loads, so the loads in flight
+  // at the loop's back edge are always the same and the waits count them
+  // exactly.  A slot of a register ring is reloaded right after its last read.
+  auto round = [&](int s, auto more) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) {
+      u32x4* slot = ring + ((s + i) & 1) * (TB * 64);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) slot[tid + 256 * c] = rb[i][c];
+      if constexpr (decltype(more)::value) issue_b(i, ks0 + s + i + PD);
+      __syncthreads();
+      f16x8 bf[NP][2];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bf[p][h] = __builtin_bit_cast(f16x8, slot[p * 128 + bwo + 32 * h]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ra[i][h]), bf[p][h], acc[p], 0, 0, 0);
+      if constexpr (decltype(more)::value) issue_a(i, ks0 + s + i + PD);
+    }
+  };
+  int s = 0;
+  for (; s + PD < ksl; s += PD) round(s, std::true_type{});
+  round(s, std::false_type{});
+
+  // D: lane l value v is row 32w + 8*(v/4) + 4*(l/32) + v%4, column 32p + l%32.
+  const int rb0 = 32 * wave + 4 * (lane >> 5), cl = lane & 31;
+  if (ns > 1) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int col = nb * 64 * CT + 32 * p + cl;
+      if (col < P.N)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = rb0 + 8 * (v >> 2) + (v & 3);
+          if (r < P.R) P.part[((size_t)sl * P.R + r) * P.N + col] = acc[p][v];
+        }
+    }
+    return;
+  }
+  constexpr int LDO = BigTile<CT>::LDO;
+  float* sOut = (float*)smem;
+  __syncthreads();  // the ring's last reads are done
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = rb0 + 8 * (v >> 2) + (v & 3);
+      if (r < P.R) sOut[r * LDO + 32 * p + cl] = acc[p][v];
+    }
+  __syncthreads();
+  if constexpr (EPI == EPI_QKV) {
+    for_pairs_lds<CT>(P, nb, sOut, [&](int, int r, int c, float v0, float v1) { qkv_pair(P, r, c, v0, v1); });
+  } else if constexpr (EPI == EPI_RESID) {
+    const int NG = P.N >> 4;
+    for_pairs_lds<CT>(P, nb, sOut, [&](int idx, int r, int c, float v0, float v1) {
+      const float t = sum8(resid_pair(P, r, c, v0, v1));
+      if ((idx & 7) == 0) P.ss_out[(size_t)r * NG + (c >> 4)] = t;
+    });
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for_pairs_lds<CT>(P, nb, sOut, [&](int, int r, int c, float g, float u) { swiglu_prep_pair(P, r, c, g, u); });
+  } else {
+    const Sampling sm = load_sampling(P);
+    for_pairs_lds<CT>(P, nb, sOut, [&](int idx, int r, int c, float v0, float v1) {
+      unsigned long long k0, k1;
+      lm_pair_keys(P, sm, r, c, v0, v1, P.rowinfo[2 * r], k0, k1);
+      unsigned long long kk = k0 > k1 ? k0 : k1;
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(kk, o);
+        kk = t > kk ? t : kk;
+      }
+      if ((idx & 31) == 0) atomicMax(&P.argkey[r], kk);
+    });
+    __syncthreads();  // sOut's last reads are done before lm_finish reuses it
+    lm_finish(P, NB, sOut);
   }
 }
 
@@ -2494,6 +2679,48 @@ hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st) {
   const dim3 grid((p.K / 32 + 15) / 16, (p.R + 15) / 16);
   hipLaunchKernelGGL(k_prep, grid, dim3(256), 0, st, p, (u32x4*)af);
   return hipGetLastError();
+}
+
+// The many-row GEMM: ns slices of K (ns > 1: partials, then k_gather),
+// ct tiles per wave, pd steps in flight.
+template <int EPI, int CT, int PD>
+static hipError_t go_big(const GemmParams& p, hipStream_t st) {
+  const int NB = (p.N + 64 * CT - 1) / (64 * CT);
+  const int ksl = p.K / 32 / p.nslices;
+  if (ksl % PD) return hipErrorInvalidValue;
+  const int grid = ((NB + 7) / 8) * 8 * p.nslices;
+  hipLaunchKernelGGL((k_gemm_big<EPI, CT, PD>), dim3(grid), dim3(256), 0, st, p, ksl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nslices == 1) return e;
+  if constexpr (EPI != EPI_LM) {
+    const long long pairs = (long long)p.R * (((p.N >> 1) + 7) & ~7);
+    hipLaunchKernelGGL((k_gather<EPI>), dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int EPI>
+static hipError_t launch_big_epi(const GemmParams& p, int ct, hipStream_t st) {
+  if (ct == 2) return go_big<EPI, 2, SPECV_BIG_PD2>(p, st);
+  return go_big<EPI, 1, SPECV_BIG_PD1>(p, st);
+}
+
+hipError_t launch_gemm_big(const GemmParams& p, int ns, int ct, int epi, hipStream_t st) {
+  if (!p.Af || !p.W || p.R <= 16 || p.R > kMaxRows || p.K % 32 || ns < 1 || (p.K / 32) % ns || (ct != 1 && ct != 2))
+    return hipErrorInvalidValue;
+  if (ns > 1 && (epi == EPI_LM || p.N % 16 || !p.part)) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && !p.rowinfo) return hipErrorInvalidValue;
+  if (epi == EPI_LM && (!p.kd || !p.step || !p.rowinfo || !p.seq_ids || !p.argkey || !p.lm_cnt)) return hipErrorInvalidValue;
+  GemmParams q = p;
+  q.nslices = ns;
+  switch (epi) {
+    case EPI_QKV: return launch_big_epi<EPI_QKV>(q, ct, st);
+    case EPI_RESID: return launch_big_epi<EPI_RESID>(q, ct, st);
+    case EPI_SWIGLU: return launch_big_epi<EPI_SWIGLU>(q, ct, st);
+    case EPI_LM: return launch_big_epi<EPI_LM>(q, ct, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmParams& p, int nk, int epi, int fmt, hipStream_t st) {

@@ -42,6 +42,34 @@ inline int slice_steps(int K) {
   return 0;
 }
 
+// The many-row GEMM (bf16, above 16 rows, prepared A): the fewest K slices,
+// each a whole number of its pipeline rounds, that give SPECV_BIG_WGS
+// workgroups (one per CU; measured at 128 rows, more slices cost more in
+// partial sums and their gather than they gain in balance: the 4B gate/up
+// runs one slice and no gather); the LM head one slice, since its accept
+// stage wants whole rows.  0: the shape does not fit the kernel.  Fixed per
+// (N, K), whatever the rows.
+#ifndef SPECV_BIG_WGS
+#define SPECV_BIG_WGS 256
+#endif
+#ifndef SPECV_BIG_CT
+#define SPECV_BIG_CT 1
+#endif
+inline int big_slices(int N, int K, int epi) {
+  const int ct = SPECV_BIG_CT, pd = ct == 2 ? SPECV_BIG_PD2 : SPECV_BIG_PD1;
+  if (K % 32 || N < 1) return 0;
+  const int KS = K / 32, NB = (N + 64 * ct - 1) / (64 * ct);
+  if (epi == EPI_LM) return KS % pd ? 0 : 1;
+  if (N % 16) return 0;  // k_gather's groups of 8 pairs
+  int best = 0;
+  for (int ns = 1; ns <= KS; ++ns) {
+    if (KS % ns || (KS / ns) % pd) continue;
+    best = ns;
+    if ((long long)NB * ns >= SPECV_BIG_WGS) break;
+  }
+  return best;
+}
+
 // int4: slices hold whole 128-input groups (16, 8 or 4 steps).
 inline int slice_steps_int4(int K) {
   for (int nk : {16, 8, 4})
@@ -351,11 +379,20 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   auto need = [&](int lim, size_t floats) {
     if (Lo.max_rows > lim) part = std::max(part, floats);
   };
-  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv, Lo.Nqkv, EPI_QKV), (size_t)(Lo.H / (Lo.nk_qkv * 32)) * Lo.Nqkv);
-  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o, Lo.H, EPI_RESID), (size_t)(Lo.DQ / (Lo.nk_o * 32)) * Lo.H);
-  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu, Lo.Ngu, EPI_SWIGLU), (size_t)(Lo.H / (Lo.nk_gu * 32)) * Lo.Ngu);
-  need(lim_d, (size_t)(Lo.F / (Lo.nk_d * 32)) * Lo.H);
-  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm, Lo.V, EPI_LM), (size_t)(Lo.H / (Lo.nk_lm * 32)) * Lo.V);
+  // bf16 above 16 rows: the many-row GEMM where the shape fits it (its
+  // slices' partials; none for one slice), else the split-K kernel
+  auto slices = [&](int N, int K, int nk, int epi) -> size_t {
+    if (Lo.fmt == FMT_BF16 && R > 16) {
+      const int ns = big_slices(N, K, epi);
+      if (ns) return ns > 1 ? (size_t)ns * N : 0;
+    }
+    return (size_t)(K / (nk * 32)) * N;
+  };
+  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv, Lo.Nqkv, EPI_QKV), slices(Lo.Nqkv, Lo.H, Lo.nk_qkv, EPI_QKV));
+  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o, Lo.H, EPI_RESID), slices(Lo.H, Lo.DQ, Lo.nk_o, EPI_RESID));
+  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu, Lo.Ngu, EPI_SWIGLU), slices(Lo.Ngu, Lo.H, Lo.nk_gu, EPI_SWIGLU));
+  need(lim_d, slices(Lo.H, Lo.F, Lo.nk_d, EPI_RESID));
+  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm, Lo.V, EPI_LM), slices(Lo.V, Lo.H, Lo.nk_lm, EPI_LM));
   Lo.part = take(std::max(part * R * 4, (size_t)256));
   Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
   Lo.cnt_n = std::max(Lo.cnt_n, Lo.H / 16);  // one per 16-column block of a residual GEMM
@@ -559,6 +596,19 @@ hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, in
     const int route = int4_route(p0.K, nk, p0.R, epi, &nk_mmq);
     if (route == INT4_MMQ) return launch_mmq(p0, nk_mmq, epi, max_grid, st);
     if (route == INT4_MMQR) return launch_mmqr(p0, epi, max_grid, st);
+  }
+  // bf16 above 16 rows: the many-row GEMM on prepared A (its producer's, or k_prep's)
+  const int ns_big = fmt == FMT_BF16 && p0.R > 16 && (ready || af) ? big_slices(p0.N, p0.K, epi) : 0;
+  if (ns_big) {
+    GemmParams p = p0;
+    if (ready) {
+      p.Af = ready;
+    } else {
+      const hipError_t e = launch_prep_a(p0, af, st);
+      if (e != hipSuccess) return e;
+      p.Af = af;
+    }
+    return launch_gemm_big(p, ns_big, SPECV_BIG_CT, epi, st);
   }
   if (ready && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
     GemmParams p = p0;
