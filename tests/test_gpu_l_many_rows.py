@@ -4,7 +4,10 @@ kernel, or one slice with the epilogue in the kernel) at the Qwen3-4B head
 geometry (hidden 512, 32q/8kv heads of 128, FFN 512, vocab 1024, 2 layers):
 the QKV, gate/up and down GEMMs run two K slices, the O GEMM sixteen and
 the LM head one.  Row counts 128 (16 x 8, the batched step's), 40 (5 x 8:
-an odd number of 16-row chunks) and 18 (3 x 6: a ragged last chunk).  Every
+an odd number of 16-row chunks) and 18 (3 x 6: a ragged last chunk), at
+contexts of 60..400 tokens; and the batched step's whole geometry, 16 x 8
+rows over 2100..2400-token contexts (attention workgroups taking both query
+tiles of a sequence, nine or ten splits merged by the merge kernel).  Every
 sequence is checked against the CPU oracle by the comparison protocol, and
 every accept length against the accept rule on the GPU's own argmax."""
 import numpy as np
@@ -24,16 +27,17 @@ def weights():
     return synth.weights(SHAPE, seed=3)
 
 
-@pytest.mark.parametrize("n_seq,S", [(16, 8), (5, 8), (3, 6)], ids=["128_rows", "40_rows", "18_rows"])
-def test_many_rows_vs_oracle(weights, n_seq, S):
+@pytest.mark.parametrize("n_seq,S,lo,hi", [(16, 8, 60, 400), (5, 8, 60, 400), (3, 6, 60, 400), (16, 8, 2100, 2400)],
+                         ids=["128_rows", "40_rows", "18_rows", "128_rows_merge_kernel"])
+def test_many_rows_vs_oracle(weights, n_seq, S, lo, hi):
     K = S - 1
-    max_ctx = 640
+    max_ctx = hi + 64
     sess = specv.Session(SHAPE, specv.tree_weights(weights), max_ctx=max_ctx, max_seqs=n_seq,
                          max_rows=n_seq * S, flags=specv.SPEC_FLAG_KEEP_LOGITS)
     orc = O.Oracle(SHAPE, synth.to_numpy(weights), max_ctx=max_ctx, n_seq=n_seq)
     try:
         rng = np.random.default_rng(100 + n_seq)
-        lens = [int(x) for x in rng.integers(60, 400, n_seq)]
+        lens = [int(x) for x in rng.integers(lo, hi + 1 - 3 * S, n_seq)]
         ids = list(range(n_seq))
         hist = {}
         for sid, L in zip(ids, lens):
@@ -43,7 +47,7 @@ def test_many_rows_vs_oracle(weights, n_seq, S):
             assert g == go or mg < MARGIN
             hist[sid] = [int(t) for t in pr] + [g]
         log(f"  {n_seq} x {S} rows: prefilled {min(lens)}..{max(lens)} tokens")
-        for step in range(3):
+        for step in range(3 if hi <= 400 else 2):
             spans = np.zeros((n_seq, S), np.int32)
             for b, sid in enumerate(ids):
                 h = hist[sid]
