@@ -177,12 +177,10 @@ hipError_t launch_gemm_big(const GemmParams& p, int ns, int ct, int epi, hipStre
 #ifndef SPECV_BIG_PD2
 #define SPECV_BIG_PD2 4  // two tiles per wave
 #endif
-// Prepare A for the split-K GEMM (kernels.hip: k_prep): the RMSNorm (when
-// p.ss is set) and the bf16 hi/lo split of every row once, in the MFMA
-// A-operand order, into af: ceil(R/16) * 16 * K * 4 bytes.
+// Prepare A for the many-row GEMM (kernels.hip: k_prep): the RMSNorm (when
+// p.ss is set) and the fp16 rounding of every row once, in the 16x16x32 MFMA
+// A-operand order, into af: ceil(R/16) * 16 * K * 2 bytes.
 hipError_t launch_prep_a(const GemmParams& p, void* af, hipStream_t st);
-// Slice depths whose split-K kernel is compiled to read prepared A.
-inline bool gemm_prep_supported(int nk, int fmt) { return fmt == FMT_BF16 && (nk == 19 || nk == 16 || nk == 8); }
 // One-pass GEMM for R <= 16 (kernels.hip: k_mm, k_mm1): nw waves split K
 // into nw parts of spw 32-input steps, summed in groups of gp parts (gp = 1
 // or nw: the plain part order); nbuf 1 or 2: blocks of ct 16-column tiles

@@ -286,12 +286,9 @@ __device__ __forceinline__ f16x8 dequant8_ao(uint32_t x) {
   return (f16x8){v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
-template <int NK, int EPI, int FMT, bool PREP>
+template <int NK, int EPI, int FMT>
 __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   static_assert(FMT == FMT_BF16 || NK % 4 == 0, "int4 slices hold whole 128-input groups");
-  static_assert(!PREP || FMT == FMT_BF16, "prepared A serves the fp16 weight path");
-  constexpr int PU = NK * 64;                 // prepared A: fragment lanes of a 16-row chunk
-  constexpr int PUT = (PU + 255) / 256;
   constexpr int NF = FMT == FMT_INT4 ? NK / 4 : NK;  // weight fragments per tile per slice
   constexpr int CT = gemm_tiles_per_wave(FMT);       // 16-column tiles per wave
   constexpr int UNITS = 16 * NK * 4;          // (row, step, lane group) units of 8 inputs per 16-row chunk
@@ -313,23 +310,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   // and gain, then A of the first 16 rows, and the weights last, so the
   // prologue's arithmetic overlaps the weights' DRAM latency.
   const int ss_row = tid >> 4, ss_part = tid & 15;
-  if (!PREP && P.ss)
+  if (P.ss)
     for (int e = tid; e < NK * 32; e += 256) sG[e] = P.gain[k0 + e];
-  f32x4 pa[PREP ? 1 : UPT][2];
-  u32x4 pf[PREP ? PUT : 1];
-  const int nch = (P.R + 15) >> 4;
+  f32x4 pa[UPT][2];
   auto load_a = [&](int m0) {
-    if constexpr (PREP) {
-      // lane u of the chunk's fragments: (step j, lane)
-      const u32x4* af = (const u32x4*)P.Af;
-#pragma unroll
-      for (int i = 0; i < PUT; ++i) {
-        const int u = tid + i * 256, uc = u < PU ? u : 0;
-        const int j = uc >> 6, l = uc & 63;
-        pf[i] = af[((size_t)(sl * NK + j) * nch + (m0 >> 4)) * 64 + l];
-      }
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * 256;
@@ -372,7 +356,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     }
   }
 
-  if (!PREP && P.ss) {
+  if (P.ss) {
     // rstd of every row, 16 lanes per row (rstd16)
     for (int pass = 0; pass * 16 < P.R; ++pass) {
       const int r = pass * 16 + ss_row;
@@ -382,23 +366,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     __syncthreads();
   }
 
-  if constexpr (PREP) {
-    // The weights are in before the chunk loop, so inside it only the next
-    // chunk's A copy is outstanding and the MFMAs never wait for it.
-#pragma unroll
-    for (int j = 0; j < NF; ++j) asm volatile("" ::"v"(b[0][j]));
-  }
   for (int m0 = 0; m0 < P.R; m0 += 16) {
     // A' for 16 rows x NK*32 inputs into LDS in the MFMA A-operand order, as fp16.
-    if constexpr (PREP) {
 #pragma unroll
-      for (int i = 0; i < PUT; ++i) {
-        const int u = tid + i * 256;
-        if (u < PU) sA[((u >> 6) * 2) * 64 + (u & 63)] = pf[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < (PREP ? 0 : UPT); ++i) {
+    for (int i = 0; i < UPT; ++i) {
       const int u = tid + i * 256;
       if (u >= UNITS) continue;
       const int g = u & 3, j = (u >> 2) % NK, row = u / (4 * NK);
@@ -471,9 +442,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
     }
     __syncthreads();  // sA is restaged for the next 16 rows
   }
-  // Prepared A (above 16 rows): k_gather, launched next, sums the slices.
-  if constexpr (PREP && EPI != EPI_LM) return;
-
   wait_mem();
   __syncthreads();
   if (tid == 0) {
@@ -679,8 +647,8 @@ __device__ void epi_resid(const GemmParams& P, int nb) {
   });
 }
 
-// The split-K kernel serves the rows above 16, whose down GEMM reads the
-// prepared layout: h is also written there (af_out), only on this path.
+// Above 16 rows the down GEMM (the many-row kernel) reads the prepared
+// layout: h is also written there (af_out), only on that path.
 __device__ __forceinline__ void swiglu_prep_pair(const GemmParams& P, int r, int c, float g, float u) {
   const float v = swiglu_val(g, u);
   P.h[(size_t)r * (P.N >> 1) + (c >> 1)] = v;
@@ -835,14 +803,13 @@ __device__ void gemm_epilogue(const GemmParams& P, int nb, float* sbuf) {
   else epi_lm<CT, SB, U>(P, nb, sbuf);
 }
 
-// Slice sums of the prepared-A split-K GEMM (above 16 rows) and its
-// epilogue, as a kernel of its own: one (row, column pair) per thread, so the
-// gather has the whole chip's loads in flight instead of one workgroup per
-// column block walking 128 rows.  Pair (r, p) is row r, columns 2p and
-// 2p + 1; a row's pairs are padded to a multiple of 8 so that every aligned
-// group of 8 lanes (one RMSNorm partial sum, 16 columns) holds pairs of one
-// row.  The slices are added in slice order from zero, as in the in-kernel
-// gather, so both give the same sums.
+// Slice sums of the many-row GEMM (above 16 rows) and its epilogue, as a
+// kernel of its own: one (row, column pair) per thread, so the gather has the
+// whole chip's loads in flight instead of one workgroup per column block
+// walking 128 rows.  Pair (r, p) is row r, columns 2p and 2p + 1; a row's
+// pairs are padded to a multiple of 8 so that every aligned group of 8 lanes
+// (one RMSNorm partial sum, 16 columns) holds pairs of one row.  The slices
+// are added in slice order from zero, as in the split-K kernel's gather.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gather(GemmParams P) {
 #pragma clang fp contract(off)
@@ -2559,51 +2526,34 @@ static hipError_t launch_gemm_epi(const GemmParams& p, int nk, int fmt, hipStrea
   if (fmt == FMT_INT4) {
     if (!p.scales) return hipErrorInvalidValue;
     switch (nk) {
-      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
-      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
-      case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_INT4, false>), dim3(grid), dim3(256), 0, st, p); break;
+      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
+      case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_INT4>), dim3(grid), dim3(256), 0, st, p); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   if (fmt != FMT_BF16) return hipErrorInvalidValue;
-  if (p.Af) {
-    // the gather's 8-pair groups need whole 16-column groups
-    if (EPI != EPI_LM && p.N % 16) return hipErrorInvalidValue;
-    switch (nk) {
-      case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
-      case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
-      case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16, true>), dim3(grid), dim3(256), 0, st, p); break;
-      default: return hipErrorInvalidValue;
-    }
-    if constexpr (EPI != EPI_LM) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const long long pairs = (long long)p.R * (((p.N >> 1) + 7) & ~7);
-      hipLaunchKernelGGL((k_gather<EPI>), dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, p);
-    }
-    return hipGetLastError();
-  }
+  if (p.Af) return hipErrorInvalidValue;  // prepared A is the many-row GEMM's (launch_gemm_big)
   switch (nk) {
-    case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 10: hipLaunchKernelGGL((k_gemm<10, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 5: hipLaunchKernelGGL((k_gemm<5, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16, false>), dim3(grid), dim3(256), 0, st, p); break;
+    case 19: hipLaunchKernelGGL((k_gemm<19, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_gemm<16, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 10: hipLaunchKernelGGL((k_gemm<10, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_gemm<8, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 5: hipLaunchKernelGGL((k_gemm<5, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_gemm<4, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<2, EPI, FMT_BF16>), dim3(grid), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Activation rows once in the split-K kernel's A-operand order, for GEMMs of
-// many rows: entry (ks * nch + ch) * 64 + l (16 bytes) holds, for lane l, row
-// 16 ch + l % 16 and inputs 32 ks + 8 (l / 16) .. +8 as fp16; rows past R are
-// zero.  The RMSNorm is the split-K
-// kernel's own (rstd16, then (x * rstd) * gain), so either path gives the
-// same operands.  Grid (ceil(K/512), ceil(R/16)): 16 steps of one 16-row
-// chunk per workgroup.
+// Activation rows once in the 16x16x32 MFMA A-operand order, for the
+// many-row GEMM: entry (ks * nch + ch) * 64 + l (16 bytes) holds, for lane l,
+// row 16 ch + l % 16 and inputs 32 ks + 8 (l / 16) .. +8 as fp16; rows past R
+// are zero.  The RMSNorm is the one every GEMM applies (rstd16, then
+// (x * rstd) * gain), with the same fp16 rounding.  Grid (ceil(K/512),
+// ceil(R/16)): 16 steps of one 16-row chunk per workgroup.
 constexpr int kPrepSs = 32;  // RMSNorm partial sums per lane in k_prep: hidden <= 16 * 16 * 32
 
 __global__ __launch_bounds__(256) void k_prep(GemmParams P, u32x4* af) {

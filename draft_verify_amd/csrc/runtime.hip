@@ -460,11 +460,11 @@ struct spec_ctx {
 
   template <class T> T* ws(size_t off) { return (T*)(WS + off); }
   void* af() { return lo.af == (size_t)-1 ? nullptr : (void*)(WS + lo.af); }
-  // the prepared A that a producer writes for the GEMM of depth nk after it
-  // (O after attention, down after gate/up), or null when that GEMM will
-  // not read prepared A
-  void* af_next(int nk, int R) {
-    return lo.af2 != (size_t)-1 && R > 16 && gemm_prep_supported(nk, lo.fmt) ? (void*)(WS + lo.af2) : nullptr;
+  // the prepared A that a producer writes for the residual GEMM (N outputs,
+  // depth K) after it (O after attention, down after gate/up), or null when
+  // that GEMM is not the many-row one and reads its fp32 A
+  void* af_next(int N, int K, int R) {
+    return lo.af2 != (size_t)-1 && R > 16 && big_slices(N, K, EPI_RESID) ? (void*)(WS + lo.af2) : nullptr;
   }
   int32_t* h_step() { return (int32_t*)(HB + lo.host_step); }
   int32_t* h_result() { return (int32_t*)(HB + lo.host_result); }
@@ -583,9 +583,9 @@ GemmParams gemm_common(spec_ctx* c, const void* W, int N, int K, int nk, int R) 
   return p;
 }
 
-// R <= the plan's rmax (<= 16): the one-pass GEMM; otherwise split-K, whose
-// A above 16 rows (bf16, af set) is prepared once by k_prep rather than by
-// every workgroup.
+// R <= the plan's rmax (<= 16): the one-pass GEMM; above 16 rows (bf16) the
+// many-row GEMM where the shape fits it, on A prepared once (by k_prep, or
+// by its producer); otherwise split-K.
 // ready: A already in the prepared layout, written by its producer (the
 // SwiGLU epilogue, the attention merge) for this GEMM, or null.
 hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, int fmt, int max_grid, void* af,
@@ -609,18 +609,6 @@ hipError_t gemm_or_mm(const GemmParams& p0, const MmPlan& m, int nk, int epi, in
       p.Af = af;
     }
     return launch_gemm_big(p, ns_big, SPECV_BIG_CT, epi, st);
-  }
-  if (ready && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
-    GemmParams p = p0;
-    p.Af = ready;
-    return launch_gemm(p, nk, epi, fmt, st);
-  }
-  if (af && p0.R > 16 && gemm_prep_supported(nk, fmt)) {
-    hipError_t e = launch_prep_a(p0, af, st);
-    if (e != hipSuccess) return e;
-    GemmParams p = p0;
-    p.Af = af;
-    return launch_gemm(p, nk, epi, fmt, st);
   }
   return launch_gemm(p0, nk, epi, fmt, st);
 }
@@ -736,7 +724,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
         rp.slot = c->ws<int32_t>(L.rec_slot);
         rp.seq_ids = seq_ids;
         rp.out = c->ws<float>(L.o);
-        rp.af_out = c->af_next(L.nk_o, R);
+        rp.af_out = c->af_next(L.H, L.DQ, R);
         rp.S = S;
         rp.n_seq = n_seq;
         rp.n_q = L.nq;
@@ -762,7 +750,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       a.cnt = c->ws<unsigned>(L.attn_cnt);
       a.out = c->ws<float>(L.o);
       a.out16 = o_reads_o16(c, l, R) ? c->ws<_Float16>(L.o16) : nullptr;
-      a.af_out = c->af_next(L.nk_o, R);
+      a.af_out = c->af_next(L.H, L.DQ, R);
       a.n_qt = (S * L.G + 15) / 16;
       const bool loc = L.local[(size_t)l] != 0;
       a.tpw = std::min(loc ? c->attn_tpw_l : c->attn_tpw, a.n_qt);
@@ -788,7 +776,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
         HIPCHK(c, launch_mm1l(go, 8, 16, 4, st));
         return SPEC_OK;
       }
-      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_o, R)));
+      HIPCHK(c, gemm_or_mm(go, L.mm_o, L.nk_o, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.H, L.DQ, R)));
       return SPEC_OK;
     }
     case SPEC_OP_GATEUP: {
@@ -800,7 +788,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       gu.gain = (const float*)(c->W + lw.g_ffn);
       gu.h = c->ws<float>(L.h);
       gu.h16 = down_reads_h16(c, R) ? c->ws<_Float16>(L.h16) : nullptr;
-      gu.af_out = c->af_next(L.nk_d, R);
+      gu.af_out = c->af_next(L.H, L.F, R);
       HIPCHK(c, gemm_or_mm(gu, L.mm_gu, L.nk_gu, EPI_SWIGLU, L.fmt, c->mm_grid, c->af(), st));
       return SPEC_OK;
     }
@@ -814,7 +802,7 @@ int launch_op(spec_ctx* c, int op, int l, int n_seq, int S) {
       if (L.d_lds && R <= 8) HIPCHK(c, launch_mm1l(gd, 16, 19, 8, st));
       else if (L.d_lds && R <= SPECV_DOWN_MM1_ROWS)
         HIPCHK(c, launch_mm(gd, 16, 19, 4, 0, 1, c->mm_grid, EPI_RESID, st));
-      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.nk_d, R)));
+      else HIPCHK(c, gemm_or_mm(gd, L.mm_d, L.nk_d, EPI_RESID, L.fmt, c->mm_grid, c->af(), st, c->af_next(L.H, L.F, R)));
       return SPEC_OK;
     }
   }
