@@ -2222,8 +2222,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qcol = (qt + u) * 16 + c;
     if (qt + u < qt1 && qcol < QC) {
       float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-      st_dev(dst, M);
-      st_dev(dst + 1, L);
+      // device-coherent stores only where another workgroup of this kernel
+      // reads them (the fused merge); the merge kernel reads after the launch
+      if (P.fuse) {
+        st_dev(dst, M);
+        st_dev(dst + 1, L);
+      } else {
+        *(float2*)dst = make_float2(M, L);
+      }
     }
   }
   __syncthreads();
@@ -2240,7 +2246,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       o1 = __builtin_fmaf(sO[u][w][c][d + 1], f, o1);
     }
     float* dst = P.part + (((size_t)kvh * P.max_splits + split) * (P.n_seq * QC) + b * QC + qcol) * (HD + 2);
-    st_dev2(dst + 2 + d, o0, o1);
+    if (P.fuse) st_dev2(dst + 2 + d, o0, o1);
+    else *(float2*)(dst + 2 + d) = make_float2(o0, o1);
   }
   qt += TP;
   if (qt >= qt1) break;
