@@ -254,10 +254,10 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
   auto steps = [&](int K) { return Lo.fmt == FMT_INT4 ? slice_steps_int4(K) : slice_steps(K); };
   Lo.nk_qkv = steps(Lo.H); Lo.nk_o = steps(Lo.DQ); Lo.nk_gu = Lo.nk_qkv;
   Lo.nk_d = steps(Lo.F);
-  // The split-K LM head serves int4 and, in bf16, more than 16 rows (the
-  // one-pass kernel takes fewer): int4 runs ~10^4 workgroups, where
-  // half-depth slices keep more of them resident; bf16 rows above 16 take
-  // full-depth slices, halving the split partials (R x vocab x 4 bytes each).
+  // The split-K LM head serves int4 above its one-pass rows (~10^4
+  // workgroups, where half-depth slices keep more of them resident) and, in
+  // bf16 above 16 rows, only shapes the many-row GEMM does not fit, with
+  // full-depth slices (half the split partials, R x vocab x 4 bytes each).
   Lo.nk_lm = Lo.fmt == FMT_BF16 ? Lo.nk_qkv : std::min(Lo.nk_qkv, 8);
   if (Lo.fmt == FMT_INT4 && Lo.nk_lm % 4) Lo.nk_lm = Lo.nk_qkv;
   // int4 rows up to eight take the one-pass kernel at the QKV depth; more rows
