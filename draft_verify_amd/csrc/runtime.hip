@@ -825,8 +825,8 @@ int enqueue_forward(spec_ctx* c, int n_seq, int S, OpTimer* tm) {
 }
 
 int get_graph(spec_ctx* c, int n_seq, int S, hipGraphExec_t* out) {
-  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16) | ((c->attn_tpw > 1) << 17) | (c->attn_fuse_l << 18) |
-                                       ((c->attn_tpw_l > 1) << 19));
+  auto key = std::make_pair(n_seq, S | (c->attn_fuse << 16) | (c->attn_fuse_l << 17) | ((c->attn_tpw & 31) << 18) |
+                                       ((c->attn_tpw_l & 31) << 23));
   auto it = c->graphs.find(key);
   if (it != c->graphs.end()) {
     *out = it->second;
@@ -860,13 +860,16 @@ int upload_step(spec_ctx* c, int mode, int n_seq, int S, const int32_t* tokens, 
   int longest = 0;
   for (int b = 0; b < n_seq; ++b) longest = std::max(longest, c->len[(size_t)seq_ids[b]] + S);
   // Enough (sequence, kv head, split) workgroups to fill the chip, and more
-  // than SPECV_ATTN_TPW1_WGS of them with one query tile each: each takes all
-  // its query tiles on K and V loaded once; else one tile each (the tiles of
-  // a long span side by side).
+  // than SPECV_ATTN_TPW1_WGS of them with one query tile each: each takes its
+  // query tiles on K and V loaded once, all of them when they are at most two
+  // (one pass of the two-tile kernel), else two per workgroup (three or four
+  // tiles in one workgroup took two passes each: 35.2 against 33.8 us at five
+  // rows of the 32B-class heads over 8192 tokens); else one tile each (the
+  // tiles of a long span side by side).
   const int splits = (longest + 255) / 256, n_qt = (S * L.G + 15) / 16;
   auto tiles_per_wg = [&](int sp) {
     const size_t wg = (size_t)n_seq * L.nkv * sp;
-    return (wg >= 256 && wg * n_qt > (size_t)SPECV_ATTN_TPW1_WGS) ? 16 : 1;
+    return (wg >= 256 && wg * n_qt > (size_t)SPECV_ATTN_TPW1_WGS) ? (n_qt >= 3 ? 2 : 16) : 1;
   };
   c->attn_tpw = tiles_per_wg(splits);
   // The last split merges its tile group itself when that is short work: few
