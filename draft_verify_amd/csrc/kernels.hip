@@ -850,8 +850,8 @@ __global__ __launch_bounds__(256) void k_gather(GemmParams P) {
 // fp16 weights, prepared A (k_prep's layout, or a producer's).  The 32x32x16
 // MFMA: on gfx950 it issues twice the flops per cycle of the 16x16x32 form
 // the one-pass kernels use (measured: 2.4 against 1.3 PFLOP/s of fp16 on
-// register operands), which matters once 128 rows make the GEMM compute
-// bound.  A workgroup of four waves owns a block of 64*CT columns (TB = 4*CT
+// register operands), which matters at 128 rows (256 flop per weight
+// element, against at most 32 on the one-pass paths).  A workgroup of four waves owns a block of 64*CT columns (TB = 4*CT
 // packed 16-column tiles, NP = 2*CT MFMA column tiles of 32) and every row:
 // wave w rows 32w..32w+31, its NP accumulators (32x32 each) in registers.
 // It walks the K range of slice sl (ksl steps of 32 inputs).  A step's
