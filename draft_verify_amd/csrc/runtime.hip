@@ -376,23 +376,25 @@ bool build_layout(const spec_model_desc& d, Layout& Lo, std::string& err) {
     return lim;
   };
   const int lim_d = Lo.d_lds ? SPECV_DOWN_MM1_ROWS : onepass_rows(Lo.mm_d, Lo.F, Lo.nk_d, Lo.H, EPI_RESID);
-  auto need = [&](int lim, size_t floats) {
-    if (Lo.max_rows > lim) part = std::max(part, floats);
-  };
-  // bf16 above 16 rows: the many-row GEMM where the shape fits it (its
-  // slices' partials; none for one slice), else the split-K kernel
-  auto slices = [&](int N, int K, int nk, int epi) -> size_t {
-    if (Lo.fmt == FMT_BF16 && R > 16) {
-      const int ns = big_slices(N, K, epi);
-      if (ns) return ns > 1 ? (size_t)ns * N : 0;
+  // Row counts above a GEMM's one-pass limit `lim` and at most 16 run the
+  // split-K kernel (its nk-deep slices); above 16, bf16 runs the many-row
+  // GEMM where the shape fits it (its slices' partials, none for one slice),
+  // int4 and the shapes it does not fit the split-K kernel.  A description
+  // can take both (up to 16 rows per sequence, more over a batch), so the
+  // buffer holds the larger.
+  auto need = [&](int lim, int N, int K, int nk, int epi) {
+    const size_t split = (size_t)(K / (nk * 32)) * N;
+    if (std::min(Lo.max_rows, 16) > lim) part = std::max(part, split);
+    if (Lo.max_rows > 16) {
+      const int ns = Lo.fmt == FMT_BF16 ? big_slices(N, K, epi) : 0;
+      part = std::max(part, ns ? (ns > 1 ? (size_t)ns * N : (size_t)0) : split);
     }
-    return (size_t)(K / (nk * 32)) * N;
   };
-  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv, Lo.Nqkv, EPI_QKV), slices(Lo.Nqkv, Lo.H, Lo.nk_qkv, EPI_QKV));
-  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o, Lo.H, EPI_RESID), slices(Lo.H, Lo.DQ, Lo.nk_o, EPI_RESID));
-  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu, Lo.Ngu, EPI_SWIGLU), slices(Lo.Ngu, Lo.H, Lo.nk_gu, EPI_SWIGLU));
-  need(lim_d, slices(Lo.H, Lo.F, Lo.nk_d, EPI_RESID));
-  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm, Lo.V, EPI_LM), slices(Lo.V, Lo.H, Lo.nk_lm, EPI_LM));
+  need(onepass_rows(Lo.mm_qkv, Lo.H, Lo.nk_qkv, Lo.Nqkv, EPI_QKV), Lo.Nqkv, Lo.H, Lo.nk_qkv, EPI_QKV);
+  need(onepass_rows(Lo.mm_o, Lo.DQ, Lo.nk_o, Lo.H, EPI_RESID), Lo.H, Lo.DQ, Lo.nk_o, EPI_RESID);
+  need(onepass_rows(Lo.mm_gu, Lo.H, Lo.nk_gu, Lo.Ngu, EPI_SWIGLU), Lo.Ngu, Lo.H, Lo.nk_gu, EPI_SWIGLU);
+  need(lim_d, Lo.H, Lo.F, Lo.nk_d, EPI_RESID);
+  need(onepass_rows(Lo.mm_lm, Lo.H, Lo.nk_lm, Lo.V, EPI_LM), Lo.V, Lo.H, Lo.nk_lm, EPI_LM);
   Lo.part = take(std::max(part * R * 4, (size_t)256));
   Lo.cnt_n = std::max({Lo.Nqkv, Lo.H, Lo.Ngu, Lo.V}) / 64;
   Lo.cnt_n = std::max(Lo.cnt_n, Lo.H / 16);  // one per 16-column block of a residual GEMM

@@ -106,3 +106,20 @@ def test_static_create_checks_before_touching_the_device():
     with pytest.raises(specv.SpecError) as e:
         specv.spec_create_static(small, bufs, 0)
     assert e.value.code == specv.SPEC_EINVAL
+
+
+def test_split_partials_cover_both_row_regimes():
+    """A bf16 description with no one-pass plan at its dims (the 32B-class
+    shape: hidden 5120, FFN 25600) runs the split-K kernel for forwards of up
+    to 16 rows even when max_rows > 16 lets batches use the many-row GEMM: the
+    workspace must hold the split-K partials of those forwards (the down
+    projection: 25600 / 512 = 50 slices x 5120 columns x 4 bytes per row)
+    beside the many-row GEMM's.  Sized for the many-row GEMM alone it held
+    2.6 MB at 32 rows and the 16-row forwards wrote past it."""
+    sh = synth.shrink(synth.SHAPES["dense_32b"], n_layers=2)
+    s16 = specv.spec_query_buffers(specv.make_desc(sh, max_ctx=512, max_rows=16))
+    s32 = specv.spec_query_buffers(specv.make_desc(sh, max_ctx=512, max_rows=32))
+    down_split_per_row = 50 * 5120 * 4
+    assert s16.workspace_bytes >= 16 * down_split_per_row
+    assert s32.workspace_bytes >= 32 * down_split_per_row
+    assert s32.workspace_bytes >= s16.workspace_bytes
